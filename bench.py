@@ -1,0 +1,240 @@
+"""Benchmark of the Llama-3.1-8B GQA attention block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_p1000]
+
+Headline workload: one decode block-step at the pages' decode point (B = 1,
+P = 1,000 cached positions, row 1,000 written, rows 0-1,000 read).  A step is
+one gqa_block_decode call: QKV projection + RoPE + cache append, attention,
+wo.  Inputs are seeded synthetic bf16 tensors already resident in HBM.  The
+timed loop cycles through 8 independent weight + cache sets (8 x 84 MiB),
+so the 256 MB Infinity Cache cannot hold what a step reads.
+
+Printed: one JSON line with the step time, HBM throughput, the roofline of
+the dominant kernel (HIP events around each kernel, on the stream the library
+launches on), the oracle timed on this host's cores, and a prefill
+(B = 4, T = 2,048) record with tokens/s and matrix-core utilisation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/block-step & HBM TB/s (% peak); prefill tokens/s & MFMA util"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16/fp16
+N_SETS = 8
+
+D, NQKV, KVH, HD = 4096, 6144, 8, 128
+
+
+def decode_bytes(B: int, P: int) -> dict:
+    """Algorithmic HBM bytes of one decode block-step and of each kernel."""
+    w_qkv = NQKV * D * 2
+    w_o = D * D * 2
+    kv_read = B * (P + 1) * KVH * HD * 2 * 2      # rows 0..P of K and V (row P just written)
+    kv_write = B * KVH * HD * 2 * 2
+    qkv = w_qkv + B * D * 2 + kv_write + B * D * 4 + 64 * 8      # x in, Q fp32 out, rope row
+    attn = kv_read + B * D * 4 + B * D * 2 * 2                     # K/V, Q in, O hi/lo out
+    wo = w_o + B * D * 2 * 2 + B * D * 4                           # Wo, O hi/lo in, out fp32
+    # whole step as the pages count it: weights + cache read + cache write + x + out + rope
+    step = w_qkv + w_o + B * P * KVH * HD * 2 * 2 + kv_write + B * D * 2 + B * D * 4 + 64 * 8
+    return {"qkv": qkv, "attn": attn, "wo": wo, "step": step}
+
+
+def prefill_flops(B: int, T: int) -> dict:
+    M = B * T
+    qkv = 2.0 * M * NQKV * D
+    causal_pairs = B * T * (T + 1) / 2
+    attn = 4.0 * causal_pairs * 32 * HD             # QK^T and PV over visible pairs, 32 heads
+    wo = 2.0 * M * D * D
+    return {"qkv": qkv, "attn": attn, "wo": wo, "total": qkv + attn + wo}
+
+
+def _events_ms(ev, i, j):
+    return ev.elapsed_ms(i, j)
+
+
+def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024):
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(N_SETS):
+        x, w, kc_rows, vc_rows = synth.decode_workload(s, B, P)
+        kc, vc = G.empty_caches(B, T_max, dev)
+        kc.zero_()
+        vc.zero_()
+        G.kcache_by_position(kc)[:, :P] = kc_rows.to(dev)
+        G.vcache_by_position(vc)[:, :P] = vc_rows.to(dev)
+        sets.append(dict(x=x.to(dev), w=[t.to(dev) for t in w], kc=kc, vc=vc))
+    rope = G.rope_table(T_max, device=dev)
+    ws = G.workspace(B, 1, T_max, dev)
+    out = torch.empty((B, D), dtype=torch.float32, device=dev)
+
+    def step(i, events=None):
+        st = sets[i % N_SETS]
+        G.block_decode(st["x"], *st["w"], st["kc"], st["vc"], rope, P, out=out, ws=ws,
+                       events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed loop: plain calls
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1)
+    us_step = ms * 1000.0 / steps
+
+    # the same loop through the profiled entry point: HIP events recorded on
+    # the library's stream around each kernel
+    ev = G.HipEvents(G.DECODE_STAGES + 1)
+    per = np.zeros((steps, G.DECODE_STAGES))
+    for i in range(steps):
+        step(i, events=ev)
+        for k in range(G.DECODE_STAGES):
+            per[i, k] = ev.elapsed_ms(k, k + 1)
+    ev.close()
+    kern_us = per.mean(axis=0) * 1000.0
+    return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps,
+                kern_us=dict(zip(["qkv", "attn", "wo"], kern_us.tolist())),
+                profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
+
+
+def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
+    dev = torch.device("cuda:0")
+    x, w = synth.prefill_workload(0, B, T)
+    x = x.to(dev)
+    w = [t.to(dev) for t in w]
+    kc, vc = G.empty_caches(B, T, dev)
+    rope = G.rope_table(T, device=dev)
+    ws = G.workspace(B, T, T, dev)
+    out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        G.block_prefill(x, *w, kc, vc, rope, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ev = G.HipEvents(G.PREFILL_STAGES + 1)
+    per = np.zeros((steps, G.PREFILL_STAGES))
+    tot = []
+    for i in range(steps):
+        G.block_prefill(x, *w, kc, vc, rope, out=out, ws=ws, events=ev)
+        for k in range(G.PREFILL_STAGES):
+            per[i, k] = ev.elapsed_ms(k, k + 1)
+        tot.append(ev.elapsed_ms(0, G.PREFILL_STAGES))
+    ev.close()
+    us = float(np.mean(tot) * 1000.0)
+    fl = prefill_flops(B, T)
+    kern = dict(zip(["wo_fp16", "qkv", "attn", "wo"], (per.mean(axis=0) * 1000.0).tolist()))
+    return dict(B=B, T=T, us_step=us, tokens_per_s=B * T / (us * 1e-6),
+                mfma_util=fl["total"] / (us * 1e-6) / (MFMA_PEAK_TFLOPS * 1e12),
+                algorithmic_gflop=fl["total"] / 1e9, kern_us=kern,
+                kern_tflops={k: fl[k] / (kern[k] * 1e-6) / 1e12 for k in ("qkv", "attn", "wo")})
+
+
+def cpu_baseline(synth, B=1, P=1000, budget_s=12.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the
+    same workload (whole decode block-steps, repeated until ~budget_s)."""
+    from oracle import gqa_oracle as O
+    x, w, kc, vc = synth.decode_workload(0, B, P)
+    f = lambda t: t.float().numpy().astype(np.float64)
+    xs, ws = f(x)[:, None, :], [f(t) for t in w]
+    kcs, vcs = f(kc), f(vc)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.gqa_block(xs, *ws, kcs, vcs, P)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 2000:
+            break
+    return {"value": el / n * 1e6, "unit": "us/block-step", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} whole decode block-steps (B={B}, P={P}) of the fp64 NumPy oracle, "
+                      f"{el:.1f} s of CPU time on inputs already converted to fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill record")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import grouped_query_attention_gemv_amd as G
+    from grouped_query_attention_gemv_amd import synth
+    G.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    B, P = 1, 1000
+    dec = bench_decode(G, synth, args.steps, args.warmup, B, P)
+    nb = decode_bytes(B, P)
+    step_tbs = nb["step"] / (dec["us_step"] * 1e-6) / 1e12
+    qkv_us = dec["kern_us"]["qkv"]
+    qkv_gbs = nb["qkv"] / (qkv_us * 1e-6) / 1e9
+
+    record = {
+        "metric": METRIC,
+        "value": round(dec["us_step"], 3),
+        "unit": "us/block-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["us_step"] / 1000.0,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) x and cache, N(0,0.02) weights; 8 rotated sets)",
+        "config": {"workload": "Llama-3.1-8B GQA block decode, B=1, P=1000 (write row 1000, "
+                               "read rows 0-1000)",
+                   "B": B, "P": P, "T_max": 1024, "d": 4096, "heads": 32, "kv_heads": 8,
+                   "head_dim": 128, "rope": "scaled, theta=5e5", "hip_graph": False},
+        "hbm_tbs": round(step_tbs, 4),
+        "hbm_frac_of_peak": round(step_tbs * 1000.0 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": B / (dec["us_step"] * 1e-6),
+        "algorithmic_bytes_per_step": nb["step"],
+        "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
+        "profiled_us_step": round(dec["profiled_us_step"], 3),
+        "roofline": {"kernel": "decode_qkv_kernel<1> (QKV GEMV + RoPE + cache append)",
+                     "bound": "hbm", "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(qkv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nb["qkv"]},
+    }
+    if not args.no_prefill:
+        record["prefill"] = bench_prefill(G, synth, steps=10, warmup=3)
+    if not args.no_cpu:
+        record["cpu_baseline"] = cpu_baseline(synth, B, P)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+// C ABI of libgqa.so (declared in include/gqa.h): argument validation on the
+// host, workspace layout and kernel dispatch.  Every check runs before the
+// first HIP call, so a rejected call launches nothing and changes nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace gqa;
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Outputs must not overlap each other or any input.
+bool any_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (int j = i + 1; j < n_out; ++j)
+      if (outs[j].lo != outs[j].hi && overlaps(outs[i], outs[j])) return true;
+    for (int j = 0; j < n_in; ++j)
+      if (ins[j].lo != ins[j].hi && overlaps(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+int check_common(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                 const void* kc, const void* vc, int T_max, const void* rope, int B,
+                 const void* out, const void* ws) {
+  if (!x || !wq || !wk || !wv || !wo || !kc || !vc || !rope || !out || !ws) return GQA_ERR_NULL;
+  if (B < 1 || B > GQA_MAX_BATCH || T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
+  if (T_max % 8 != 0) return GQA_ERR_ALIGN;
+  const void* ptrs[] = {x, wq, wk, wv, wo, kc, vc, rope, out, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+size_t cache_bytes(int B, int T_max) { return (size_t)B * KVH * T_max * HD * 2; }
+
+// Record events[i] when events is non-NULL.
+inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
+  return events ? hipEventRecord(events[i], s) : hipSuccess;
+}
+
+int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                 const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                 const float* rope, int B, int T, float* out, void* ws, size_t ws_bytes,
+                 float* probe, hipStream_t stream, hipEvent_t* events) {
+  int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
+  if (st != GQA_OK) return st;
+  if (T < 1 || (long)B * T > (1L << 24)) return GQA_ERR_SHAPE;
+  if (T > T_max) return GQA_ERR_RANGE;
+  if (probe && !aligned16(probe)) return GQA_ERR_ALIGN;
+  if (ws_bytes < gqa_workspace_bytes(B, T, T_max)) return GQA_ERR_WORKSPACE;
+  const size_t M = (size_t)B * T;
+  const Range outs[] = {span(out, M * D * 4), span(kcache, cache_bytes(B, T_max)),
+                        span(vcache, cache_bytes(B, T_max)), span(ws, ws_bytes),
+                        span(probe, probe ? M * NQKV * 4 : 0)};
+  const Range ins[] = {span(x, M * D * 2), span(wq, (size_t)D * D * 2),
+                       span(wk, (size_t)KVH * HD * D * 2), span(wv, (size_t)KVH * HD * D * 2),
+                       span(wo, (size_t)D * D * 2), span(rope, (size_t)T_max * PAIRS * 8)};
+  if (any_alias(outs, 5, ins, 6)) return GQA_ERR_ALIAS;
+
+  PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.wq = wq; p.wk = wk; p.wv = wv; p.wo = wo;
+  p.kcache = kcache; p.vcache = vcache; p.rope = rope; p.out = out; p.probe = probe;
+  p.T_max = T_max; p.B = B; p.T = T;
+  p.Tp = (T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+  prefill_ws_carve(ws, B, T, &p);
+
+  (void)hipGetLastError();
+  hipError_t e;
+  if ((e = mark(events, 0, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_convert_wo(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 1, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_prefill_qkv(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 2, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_prefill_attn(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 3, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_prefill_wo(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 4, stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                const float* rope, int start_pos, int B, float* out, gqa_bf16* out_bf16,
+                int accumulate, void* ws, size_t ws_bytes, float* probe, hipStream_t stream,
+                hipEvent_t* events) {
+  int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
+  if (st != GQA_OK) return st;
+  if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
+  if ((probe && !aligned16(probe)) || (out_bf16 && !aligned16(out_bf16))) return GQA_ERR_ALIGN;
+  if (accumulate != 0 && accumulate != 1) return GQA_ERR_ARG;
+  if (ws_bytes < gqa_workspace_bytes(B, 1, T_max)) return GQA_ERR_WORKSPACE;
+  const size_t Bz = (size_t)B;
+  const Range outs[] = {span(out, Bz * D * 4), span(out_bf16, out_bf16 ? Bz * D * 2 : 0),
+                        span(kcache, cache_bytes(B, T_max)), span(vcache, cache_bytes(B, T_max)),
+                        span(ws, ws_bytes), span(probe, probe ? Bz * NQKV * 4 : 0)};
+  const Range ins[] = {span(x, Bz * D * 2), span(wq, (size_t)D * D * 2),
+                       span(wk, (size_t)KVH * HD * D * 2), span(wv, (size_t)KVH * HD * D * 2),
+                       span(wo, (size_t)D * D * 2), span(rope, (size_t)T_max * PAIRS * 8)};
+  if (any_alias(outs, 6, ins, 6)) return GQA_ERR_ALIAS;
+
+  DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x; p.wq = wq; p.wk = wk; p.wv = wv; p.wo = wo;
+  p.kcache = kcache; p.vcache = vcache; p.rope = rope;
+  p.out = out; p.out_bf16 = out_bf16; p.probe = probe;
+  p.T_max = T_max; p.start_pos = start_pos; p.B = B; p.accumulate = accumulate;
+  decode_ws_carve(ws, B, &p);
+  decode_split(B, start_pos + 1, &p.nsplit, &p.chunk);
+
+  (void)hipGetLastError();
+  hipError_t e;
+  if ((e = mark(events, 0, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_decode_qkv(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 1, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_decode_attn(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 2, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if ((e = launch_decode_wo(p, stream)) != hipSuccess) return hip_status(e);
+  if ((e = mark(events, 3, stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_NULL: return "GQA_ERR_NULL: a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE: B, T or T_max out of range";
+    case GQA_ERR_RANGE: return "GQA_ERR_RANGE: start_pos/T outside [0, T_max)";
+    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned or T_max % 8 != 0";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace too small";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: a HIP call or kernel launch failed";
+    case GQA_ERR_ALIAS: return "GQA_ERR_ALIAS: an output overlaps another buffer";
+    case GQA_ERR_ARG: return "GQA_ERR_ARG: invalid argument";
+    default: return "unknown gqa status";
+  }
+}
+
+int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t stream) {
+  if (T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
+  if (!(theta > 0.0) || (scaled != 0 && scaled != 1)) return GQA_ERR_ARG;
+  if (!rope) return GQA_ERR_NULL;
+  if (!aligned16(rope)) return GQA_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(launch_rope_table(rope, T_max, theta, scaled, stream));
+}
+
+size_t gqa_workspace_bytes(int B, int T, int T_max) {
+  if (B < 1 || B > GQA_MAX_BATCH || T < 1 || T_max < 1 || T_max > GQA_MAX_T_MAX) return 0;
+  if ((long)B * T > (1L << 24)) return 0;
+  const size_t a = prefill_ws_bytes(B, T);
+  const size_t b = decode_ws_bytes(B);
+  return a > b ? a : b;
+}
+
+int gqa_block_prefill(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                      const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                      gqa_bf16* vcache, int T_max, const float* rope, int B, int T, float* out,
+                      void* ws, size_t ws_bytes, float* probe, hipStream_t stream) {
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, T, out, ws, ws_bytes,
+                      probe, stream, nullptr);
+}
+
+int gqa_block_prefill_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                               const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                               gqa_bf16* vcache, int T_max, const float* rope, int B, int T,
+                               float* out, void* ws, size_t ws_bytes, float* probe,
+                               hipStream_t stream, hipEvent_t* events) {
+  if (!events) return GQA_ERR_NULL;
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, T, out, ws, ws_bytes,
+                      probe, stream, events);
+}
+
+int gqa_block_decode(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                     const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache,
+                     int T_max, const float* rope, int start_pos, int B, float* out,
+                     gqa_bf16* out_bf16, int accumulate, void* ws, size_t ws_bytes, float* probe,
+                     hipStream_t stream) {
+  return decode_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, out, out_bf16,
+                     accumulate, ws, ws_bytes, probe, stream, nullptr);
+}
+
+int gqa_block_decode_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                              const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                              gqa_bf16* vcache, int T_max, const float* rope, int start_pos,
+                              int B, float* out, gqa_bf16* out_bf16, int accumulate, void* ws,
+                              size_t ws_bytes, float* probe, hipStream_t stream,
+                              hipEvent_t* events) {
+  if (!events) return GQA_ERR_NULL;
+  return decode_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, out, out_bf16,
+                     accumulate, ws, ws_bytes, probe, stream, events);
+}
+
+}  // extern "C"

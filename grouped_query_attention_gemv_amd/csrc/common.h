@@ -1,0 +1,125 @@
+// Shared device helpers for the gfx950 kernels of the attention block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gqa.h"
+
+namespace gqa {
+
+constexpr int D = GQA_D_MODEL;          // 4096
+constexpr int H = GQA_N_HEADS;          // 32
+constexpr int KVH = GQA_N_KV_HEADS;     // 8
+constexpr int HD = GQA_HEAD_DIM;        // 128
+constexpr int NQKV = GQA_QKV_DIM;       // 6144
+constexpr int REP = H / KVH;            // 4 query heads per KV head
+constexpr int PAIRS = GQA_ROPE_PAIRS;   // 64
+
+// log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale into exp2.
+constexpr float kScoreLog2 = 0.12751743074843916f;
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane
+// ---------------------------------------------------------------------------
+
+// DPP control codes (GFX9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHL4 = 0x104;      // lane i <- lane i+4 within a row of 16
+constexpr int DPP_ROW_SHR4 = 0x114;      // lane i <- lane i-4 within a row of 16
+constexpr int DPP_ROW_MIRROR = 0x140;    // lane i <- lane 15-i within a row
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of each row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+// Sum over all 64 lanes, result uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// ---------------------------------------------------------------------------
+// Memory
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld_nt_u32x4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// MFMA wrappers (gfx950, 16x16 output tile, K = 32 per instruction).
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+}  // namespace gqa

@@ -1,0 +1,492 @@
+// Decode path of the attention block: one new token per sequence at position
+// start_pos (page "Llama 3.1 8B . Grouped-query attention", decode mode:
+// cache row start_pos written, rows 0..start_pos read).
+//
+//   decode_qkv_kernel   Q|K|V = x [Wq;Wk;Wv]^T as a bandwidth GEMV, RoPE on the
+//                       Q and K pairs, K/V appended to the bf16 cache
+//   decode_attn_kernel  flash-decode on the matrix cores: positions split over
+//                       workgroups, online softmax, (m, l, o) merge by the
+//                       last-arriving workgroup of each (sequence, kv head)
+//   decode_wo_kernel    Delta = O Wo^T as a bandwidth GEMV (+ residual)
+#include <math.h>
+
+#include "kernels.h"
+
+namespace gqa {
+
+// ---------------------------------------------------------------------------
+// Bandwidth GEMV core
+// ---------------------------------------------------------------------------
+//
+// One wave computes two adjacent weight rows for NB token vectors.  Lane l
+// reads 16-byte pieces (c*64 + l)*8 .. +8 of each 4096-element row, c < 8, so
+// a wave streams 16 KiB with every load coalesced and all 16 loads in flight
+// before the first product.  The token vectors sit in LDS as NPARTS bf16 parts
+// (the vector is the sum of its parts); products use the packed bf16 dot
+// instruction with fp32 accumulation.
+template <int NB, int NPARTS>
+__device__ __forceinline__ void gemv_rows2(const uint16_t* __restrict__ w0,
+                                           const uint16_t* __restrict__ w1,
+                                           const uint32_t* xs, int lane, float (&acc)[2][NB]) {
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int e = (c * 64 + lane) * 8;
+    a[c] = ld_nt_u32x4(w0 + e);
+    b[c] = ld_nt_u32x4(w1 + e);
+  }
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int e2 = (c * 64 + lane) * 4;
+#pragma unroll
+    for (int part = 0; part < NPARTS; ++part) {
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + (part * NB + t) * (D / 2) + e2);
+        float s0 = acc[0][t], s1 = acc[1][t];
+        s0 = dot2_bf16(a[c].x, xv.x, s0);
+        s1 = dot2_bf16(b[c].x, xv.x, s1);
+        s0 = dot2_bf16(a[c].y, xv.y, s0);
+        s1 = dot2_bf16(b[c].y, xv.y, s1);
+        s0 = dot2_bf16(a[c].z, xv.z, s0);
+        s1 = dot2_bf16(b[c].z, xv.z, s1);
+        s0 = dot2_bf16(a[c].w, xv.w, s0);
+        s1 = dot2_bf16(b[c].w, xv.w, s1);
+        acc[0][t] = s0;
+        acc[1][t] = s1;
+      }
+    }
+  }
+}
+
+// Copy NB rows of 4096 bf16 (one part) from global into LDS.
+template <int NB>
+__device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restrict__ src) {
+  for (int i = threadIdx.x; i < NB * (D / 8); i += blockDim.x) {
+    const int t = i / (D / 8), u = i % (D / 8);
+    *reinterpret_cast<u32x4*>(xs + t * (D / 2) + u * 4) = ld_u32x4(src + (size_t)t * D + u * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// QKV projection + RoPE + cache append
+// ---------------------------------------------------------------------------
+
+template <int NB>
+__global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
+  __shared__ uint32_t xs[NB * (D / 2)];
+  stage_rows<NB>(xs, p.x + (size_t)b0 * D);
+  if (blockIdx.x == 0 && b0 == 0) {
+    // the attention kernel that follows counts split arrivals from zero
+    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + wave) * 2;     // even output feature, 0..6142
+  const uint16_t* wbase;
+  int rr;
+  if (r0 < D) {
+    wbase = p.wq; rr = r0;
+  } else if (r0 < D + KVH * HD) {
+    wbase = p.wk; rr = r0 - D;
+  } else {
+    wbase = p.wv; rr = r0 - D - KVH * HD;
+  }
+  float acc[2][NB];
+  gemv_rows2<NB, 1>(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, xs, lane, acc);
+
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const float s0 = wave_sum(acc[0][t]);
+    const float s1 = wave_sum(acc[1][t]);
+    if (lane == t) { v0 = s0; v1 = s1; }
+  }
+  if (lane >= NB) return;
+
+  const int b = b0 + lane;
+  const int pos = p.start_pos;
+  const bool is_v = r0 >= D + KVH * HD;
+  if (!is_v) {
+    // rotate the pair (2i, 2i+1) of this head by position * f_i
+    const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * PAIRS + ((rr & (HD - 1)) >> 1)];
+    const float a = v0 * cs.x - v1 * cs.y;
+    const float c = v0 * cs.y + v1 * cs.x;
+    v0 = a;
+    v1 = c;
+  }
+  if (p.probe) {
+    *reinterpret_cast<float2*>(p.probe + (size_t)b * NQKV + r0) = make_float2(v0, v1);
+  }
+  if (r0 < D) {
+    *reinterpret_cast<float2*>(p.q + (size_t)b * D + r0) = make_float2(v0, v1);
+  } else if (!is_v) {
+    const int g = rr / HD, d = rr % HD;
+    uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v0, v1);
+  } else {
+    const int g = rr / HD, d = rr % HD;
+    uint16_t* dst = p.vcache + ((size_t)(b * KVH + g) * HD + d) * p.T_max + pos;
+    dst[0] = (uint16_t)f32_to_bf16_bits(v0);
+    dst[p.T_max] = (uint16_t)f32_to_bf16_bits(v1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Flash-decode on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// Workgroup (split, g, b) owns positions [split*chunk, min(L, (split+1)*chunk))
+// of kv head g of sequence b and serves its 4 query heads.  Each wave steps
+// over 32-position tiles:
+//   S^T[32 keys x 16 cols] = K[keys x 128] . Qext^T, where Qext's 16 columns
+//     are the 4 heads' bf16 high parts (cols 0-3), their low parts q - hi
+//     (cols 4-7) and zeros, so hi + lo restores Q to ~16 significant bits and
+//     each K row is read from HBM once for all 4 heads;
+//   O^T[128 dims x 16 cols] += V^T[dims x keys] . Pext^T with the same hi/lo
+//     split of the probabilities, V^T read directly from the dimension-major
+//     value cache.
+// The A-operand rows of the score tiles are assigned to positions so that
+// each lane's 8 score values are 8 consecutive positions: exactly the B
+// operand of the following P.V instruction, with no data movement.
+__global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, rg = lane >> 4;
+  const int head = col & 3;
+  const bool valid_col = col < 8;
+  const bool is_lo = (col & 4) != 0;
+  const int L = p.start_pos + 1;
+  const int j_begin = split * p.chunk;
+  const int j_end = min(L, j_begin + p.chunk);
+  const int T_max = p.T_max;
+
+  __shared__ float sm_o[kAttnWaves][REP][HD];
+  __shared__ float sm_m[kAttnWaves][REP];
+  __shared__ float sm_l[kAttnWaves][REP];
+  __shared__ int sm_last;
+
+  // Q fragments, pre-scaled by log2(e)/sqrt(128)
+  u32x4 qf[4];
+  {
+    const float* qrow = p.q + (size_t)b * D + (g * REP + head) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = rg * 8 + 32 * ks;
+      const float4 qa = *reinterpret_cast<const float4*>(qrow + d0);
+      const float4 qb = *reinterpret_cast<const float4*>(qrow + d0 + 4);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = qv[2 * e] * kScoreLog2, x1 = qv[2 * e + 1] * kScoreLog2;
+        uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+        if (is_lo) {
+          h0 = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0));
+          h1 = f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1));
+        }
+        pk[e] = valid_col ? (h0 | (h1 << 16)) : 0u;
+      }
+      qf[ks] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
+  }
+
+  const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
+  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * HD * T_max;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int tile = j_begin + w * kAttnTile; tile < j_end; tile += kAttnWaves * kAttnTile) {
+    u32x4 kf[2][4], vf[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j = tile + (col >> 2) * 8 + mt * 4 + (col & 3);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[mt][ks] = (j < j_end) ? ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks) : zero4;
+    }
+    const int jv = tile + rg * 8;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      vf[dt] = (jv < j_end) ? ld_nt_u32x4(vbase + (size_t)(col + 16 * dt) * T_max + jv) : zero4;
+    if (jv < j_end && jv + 8 > j_end) {
+      // positions past the last visible one may hold anything: clear them
+      const int nv = j_end - jv;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint32_t* u = reinterpret_cast<uint32_t*>(&vf[dt]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv ? 0x0000ffffu : 0u);
+          u[q] &= keep;
+        }
+      }
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) s[mt] = mfma_bf16(kf[mt][ks], qf[ks], s[mt]);
+    }
+
+    // lane (col, rg) holds position tile + rg*8 + mt*4 + i in s[mt][i]
+    float sv[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = s[mt][i];
+        const float sum = v + dpp<DPP_ROW_SHL4>(v);      // hi + lo, valid in cols 0-3
+        const float bc = dpp<DPP_ROW_SHR4>(sum);          // copy to cols 4-7
+        const float full = (col < 4) ? sum : bc;
+        const int j = tile + rg * 8 + mt * 4 + i;
+        sv[mt * 4 + i] = (j < j_end) ? full : -INFINITY;
+        tmax = fmaxf(tmax, sv[mt * 4 + i]);
+      }
+    }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = valid_col ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float p0 = __builtin_amdgcn_exp2f(sv[2 * q] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_new);
+      psum += p0 + p1;
+      uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+      if (is_lo) {
+        h0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
+        h1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
+      }
+      pk[q] = valid_col ? (h0 | (h1 << 16)) : 0u;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const u32x4 pf = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[dt] *= alpha;
+      oacc[dt] = mfma_bf16(vf[dt], pf, oacc[dt]);
+    }
+  }
+
+  // wave result: l summed over the 4 lane rows, O = hi column + lo column
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = oacc[dt][i];
+      const float o = v + dpp<DPP_ROW_SHL4>(v);
+      if (col < 4) sm_o[w][col][rg * 4 + i + 16 * dt] = o;
+    }
+  }
+  if (lane < 4) {
+    sm_m[w][lane] = m_run;
+    sm_l[w][lane] = l_run;
+  }
+  __syncthreads();
+
+  // merge the 4 waves: thread -> (head, two dims)
+  const int mh = tid >> 6, d2 = (tid & 63) * 2;
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][mh]);
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kAttnWaves; ++ww) {
+    const float f = __builtin_amdgcn_exp2f(sm_m[ww][mh] - M);
+    lsum += sm_l[ww][mh] * f;
+    o0 += sm_o[ww][mh][d2] * f;
+    o1 += sm_o[ww][mh][d2 + 1] * f;
+  }
+
+  const size_t out_off = (size_t)b * D + (g * REP + mh) * HD + d2;
+  if (p.nsplit == 1) {
+    const float r0 = o0 / lsum, r1 = o1 / lsum;
+    const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);
+    const uint32_t lo0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(h0));
+    const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
+    *reinterpret_cast<uint32_t*>(p.o_hi + out_off) = h0 | (h1 << 16);
+    *reinterpret_cast<uint32_t*>(p.o_lo + out_off) = lo0 | (lo1 << 16);
+    return;
+  }
+
+  const size_t split_stride = (size_t)REP * kPartStride;
+  float* part0 = p.part + ((size_t)(b * KVH + g) * p.nsplit) * split_stride + (size_t)mh * kPartStride;
+  float* mine = part0 + (size_t)split * split_stride;
+  if (d2 == 0) {
+    mine[0] = M;
+    mine[1] = lsum;
+  }
+  mine[4 + d2] = o0;
+  mine[5 + d2] = o1;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(p.counters + b * KVH + g, 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = (prev == p.nsplit - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+
+  // last workgroup of this (b, g): merge every split in a fixed order
+  float GM = -INFINITY;
+  for (int sidx = 0; sidx < p.nsplit; ++sidx)
+    GM = fmaxf(GM, __builtin_nontemporal_load(part0 + sidx * split_stride));
+  float gl = 0.f, g0 = 0.f, g1 = 0.f;
+  for (int sidx = 0; sidx < p.nsplit; ++sidx) {
+    const float* ps = part0 + sidx * split_stride;
+    const float f = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(ps) - GM);
+    gl += __builtin_nontemporal_load(ps + 1) * f;
+    g0 += __builtin_nontemporal_load(ps + 4 + d2) * f;
+    g1 += __builtin_nontemporal_load(ps + 5 + d2) * f;
+  }
+  const float r0 = g0 / gl, r1 = g1 / gl;
+  const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);
+  const uint32_t lo0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(h0));
+  const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
+  *reinterpret_cast<uint32_t*>(p.o_hi + out_off) = h0 | (h1 << 16);
+  *reinterpret_cast<uint32_t*>(p.o_lo + out_off) = lo0 | (lo1 << 16);
+  if (tid == 0) p.counters[b * KVH + g] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// wo projection (+ residual)
+// ---------------------------------------------------------------------------
+
+template <int NB>
+__global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) {
+  __shared__ uint32_t xs[2 * NB * (D / 2)];
+  stage_rows<NB>(xs, p.o_hi + (size_t)b0 * D);
+  stage_rows<NB>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + wave) * 2;
+  float acc[2][NB];
+  gemv_rows2<NB, 2>(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, xs, lane, acc);
+
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const float s0 = wave_sum(acc[0][t]);
+    const float s1 = wave_sum(acc[1][t]);
+    if (lane == t) { v0 = s0; v1 = s1; }
+  }
+  if (lane >= NB) return;
+  const int b = b0 + lane;
+  float2* o = reinterpret_cast<float2*>(p.out + (size_t)b * D + r0);
+  float2 r = make_float2(v0, v1);
+  if (p.accumulate) {
+    const float2 prev = *o;
+    r.x += prev.x;
+    r.y += prev.y;
+  }
+  *o = r;
+  if (p.out_bf16)
+    *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+int decode_max_split(int B) {
+  const int pairs = B * KVH;
+  const int want = (1024 + pairs - 1) / pairs;
+  return max(1, min(kMaxSplit, want));
+}
+
+void decode_split(int B, int L, int* nsplit, int* chunk) {
+  const int per_wg = kAttnWaves * kAttnTile;
+  const int by_len = (L + per_wg - 1) / per_wg;
+  int n = max(1, min(by_len, decode_max_split(B)));
+  int c = (L + n - 1) / n;
+  c = (c + kAttnTile - 1) / kAttnTile * kAttnTile;
+  n = (L + c - 1) / c;
+  *nsplit = n;
+  *chunk = c;
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t decode_ws_bytes(int B) {
+  size_t n = 0;
+  n += align256((size_t)B * D * 4);                       // q
+  n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
+  n += align256((size_t)B * KVH * 4);                     // counters
+  n += align256((size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4);  // partials
+  return n;
+}
+
+void decode_ws_carve(void* ws, int B, DecodeParams* p) {
+  char* c = static_cast<char*>(ws);
+  p->q = reinterpret_cast<float*>(c);
+  c += align256((size_t)B * D * 4);
+  p->o_hi = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)B * D * 2);
+  p->o_lo = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)B * D * 2);
+  p->counters = reinterpret_cast<int*>(c);
+  c += align256((size_t)B * KVH * 4);
+  p->part = reinterpret_cast<float*>(c);
+}
+
+#define GQA_NB_SWITCH(NB_VAR, CALL) \
+  switch (NB_VAR) {                 \
+    case 1: CALL(1); break;         \
+    case 2: CALL(2); break;         \
+    case 3: CALL(3); break;         \
+    case 4: CALL(4); break;         \
+    case 5: CALL(5); break;         \
+    case 6: CALL(6); break;         \
+    case 7: CALL(7); break;         \
+    default: CALL(8); break;        \
+  }
+
+hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
+  const int blocks = NQKV / 2 / 4;    // one wave per row pair, 4 waves per workgroup
+  for (int b0 = 0; b0 < p.B; b0 += kGemvMaxNB) {
+    const int nb = min(kGemvMaxNB, p.B - b0);
+#define GQA_LAUNCH_QKV(N) \
+    hipLaunchKernelGGL(decode_qkv_kernel<N>, dim3(blocks), dim3(256), 0, s, p, b0)
+    GQA_NB_SWITCH(nb, GQA_LAUNCH_QKV)
+#undef GQA_LAUNCH_QKV
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decode_attn_kernel, dim3(p.nsplit, KVH, p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
+  const int blocks = D / 2 / 4;
+  for (int b0 = 0; b0 < p.B; b0 += kWoMaxNB) {
+    const int nb = min(kWoMaxNB, p.B - b0);
+#define GQA_LAUNCH_WO(N) \
+    hipLaunchKernelGGL(decode_wo_kernel<N>, dim3(blocks), dim3(256), 0, s, p, b0)
+    GQA_NB_SWITCH(nb, GQA_LAUNCH_WO)
+#undef GQA_LAUNCH_WO
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,89 @@
+// Host-side launchers of the block's kernels and the workspace layout.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace gqa {
+
+// ---------------------------------------------------------------------------
+// Decode
+// ---------------------------------------------------------------------------
+
+constexpr int kAttnTile = 32;        // keys per wave step of the flash-decode kernel
+constexpr int kAttnWaves = 4;        // waves per flash-decode workgroup
+constexpr int kMaxSplit = 64;        // most position splits per (sequence, kv head)
+constexpr int kPartStride = 132;     // floats per (split, head) partial: m, l, pad, pad, o[128]
+constexpr int kGemvMaxNB = 8;        // tokens per pass of the QKV bandwidth GEMV
+constexpr int kWoMaxNB = 4;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
+
+struct DecodeParams {
+  const uint16_t* x;        // [B][4096] bf16
+  const uint16_t* wq;       // [4096][4096]
+  const uint16_t* wk;       // [1024][4096]
+  const uint16_t* wv;       // [1024][4096]
+  const uint16_t* wo;       // [4096][4096]
+  uint16_t* kcache;         // [B][8][T_max][128]
+  uint16_t* vcache;         // [B][8][128][T_max]
+  const float* rope;        // [T_max][64][2]
+  float* out;               // [B][4096]
+  uint16_t* out_bf16;       // optional [B][4096]
+  float* probe;             // optional [B][6144]
+  int T_max, start_pos, B, accumulate;
+  // workspace
+  float* q;                 // [B][4096] post-RoPE Q, fp32
+  uint16_t* o_hi;           // [B][4096] attention output, bf16 high part
+  uint16_t* o_lo;           // [B][4096] bf16 low part (o - hi)
+  int* counters;            // [B][8] split arrival counters
+  float* part;              // [B][8][nsplit][4][kPartStride]
+  int nsplit, chunk;        // positions split over nsplit workgroups of chunk keys
+};
+
+// Split of the L = start_pos + 1 visible positions over workgroups.
+void decode_split(int B, int L, int* nsplit, int* chunk);
+int decode_max_split(int B);
+size_t decode_ws_bytes(int B);
+void decode_ws_carve(void* ws, int B, DecodeParams* p);
+
+hipError_t launch_rope_table(float* rope, int T_max, double theta, int scaled, hipStream_t s);
+hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Prefill
+// ---------------------------------------------------------------------------
+
+struct PrefillParams {
+  const uint16_t* x;        // [M][4096] bf16, M = B*T
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const uint16_t* wv;
+  const uint16_t* wo;
+  uint16_t* kcache;
+  uint16_t* vcache;
+  const float* rope;
+  float* out;               // [M][4096]
+  float* probe;             // optional [M][6144]
+  int T_max, B, T, Tp;      // Tp = T rounded up to the attention tile
+  // workspace
+  uint16_t* wo16;           // [4096][4096] fp16 copy of wo
+  uint16_t* q16;            // [M][4096] fp16 Q * log2(e)/sqrt(128)
+  uint16_t* k16;            // [B][8][Tp][128] fp16 copy of the appended keys
+  uint16_t* v16t;           // [B][8][128][Tp] fp16 copy of the appended values
+  uint16_t* o16;            // [M][4096] fp16 attention output
+};
+
+constexpr int kPrefillTile = 64;     // query and key tile of the prefill attention
+
+size_t prefill_ws_bytes(int B, int T);
+void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p);
+
+hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s);
+
+}  // namespace gqa

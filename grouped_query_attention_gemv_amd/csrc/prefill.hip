@@ -1,0 +1,534 @@
+// Prefill path of the attention block: T new tokens per sequence from
+// position 0, causal mask (page "Llama 3.1 8B . Grouped-query attention",
+// evidence "scores": key j hidden from query row i iff j > i here).
+//
+//   convert_wo_kernel    wo bf16 -> fp16 copy in the workspace
+//   gemm_kernel<QKV>     [Q|K|V] = x [Wq;Wk;Wv]^T on bf16 matrix cores; the
+//                        epilogue rotates Q/K pairs (RoPE), appends K/V to
+//                        the bf16 cache and writes fp16 copies of Q (scaled
+//                        by log2(e)/sqrt(128)), K and V^T for attention
+//   prefill_attn_kernel  causal flash attention on fp16 matrix cores, one
+//                        workgroup per (sequence, kv head, 64 queries) with
+//                        the kv head's 4 query heads sharing every K/V tile
+//   gemm_kernel<OUT>     Delta = O Wo^T on fp16 matrix cores, fp32 out
+//
+// Precision: the GEMM inputs x and W are bf16 already, products are exact and
+// sums are fp32.  Attention and wo use fp16 operands: the cached K/V values
+// are bf16 and convert to fp16 exactly (except fp16-subnormal magnitudes),
+// while Q, P and O gain 3 significant bits over bf16.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace gqa {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// Workspace
+// ---------------------------------------------------------------------------
+
+size_t prefill_ws_bytes(int B, int T) {
+  const size_t M = (size_t)B * T;
+  const size_t Tp = (size_t)(T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+  size_t n = 0;
+  n += align256((size_t)D * D * 2);                 // wo16
+  n += align256(M * D * 2);                         // q16
+  n += align256((size_t)B * KVH * Tp * HD * 2);     // k16
+  n += align256((size_t)B * KVH * HD * Tp * 2);     // v16t
+  n += align256(M * D * 2);                         // o16
+  return n;
+}
+
+void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
+  const size_t M = (size_t)B * T;
+  const size_t Tp = (size_t)p->Tp;
+  char* c = static_cast<char*>(ws);
+  p->wo16 = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)D * D * 2);
+  p->q16 = reinterpret_cast<uint16_t*>(c);
+  c += align256(M * D * 2);
+  p->k16 = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)B * KVH * Tp * HD * 2);
+  p->v16t = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)B * KVH * HD * Tp * 2);
+  p->o16 = reinterpret_cast<uint16_t*>(c);
+}
+
+// ---------------------------------------------------------------------------
+// wo -> fp16
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) convert_wo_kernel(const uint16_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int n8) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n8; i += gridDim.x * 256) {
+    const u32x4 v = ld_nt_u32x4(src + (size_t)i * 8);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u = v[q];
+      o[q] = pack_f16x2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
+    }
+    *reinterpret_cast<u32x4*>(dst + (size_t)i * 8) = o;
+  }
+}
+
+hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s) {
+  const int n8 = D * D / 8;
+  hipLaunchKernelGGL(convert_wo_kernel, dim3(2048), dim3(256), 0, s, p.wo, p.wo16, n8);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 256 x 256 x 64 GEMM on the matrix cores, C = A B^T with A [M][4096] and
+// B [N][4096] both K-contiguous.
+// ---------------------------------------------------------------------------
+//
+// 4 waves in a 2 x 2 grid, each owning a 128 x 128 block of C as 8 x 8
+// 16x16 tiles.  A and B tiles stream from global memory straight into LDS
+// (global_load_lds, 16 bytes a lane), double-buffered.  In LDS a tile row of
+// 64 elements is 8 chunks of 16 bytes stored at chunk ^ (row & 7), so the 16
+// rows one matrix-core operand read touches fall in distinct banks.
+
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int kGemmLds = 2 * (GBM + GBN) * GBK * 2;   // 128 KiB
+constexpr int kGroupM = 4;                             // m-tiles per tile-order group
+
+enum GemmKind { GEMM_QKV = 0, GEMM_OUT = 1 };
+
+// Row of B feeding tile column j of an n-tile starting at n0.  For the QKV
+// projection each 32-column block holds the even features of 16 rotation
+// pairs in its first 16 columns and the odd ones in the next 16, so the two
+// members of a pair land in the same lane of neighbouring accumulators.
+template <int KIND>
+__device__ __forceinline__ int b_row_of(int n0, int j) {
+  if (KIND == GEMM_QKV) return n0 + (j & ~31) + 2 * (j & 15) + ((j >> 4) & 1);
+  return n0 + j;
+}
+
+template <int KIND>
+__device__ __forceinline__ const uint16_t* b_row_ptr(const uint16_t* b0, const uint16_t* b1,
+                                                     const uint16_t* b2, int row) {
+  if (KIND == GEMM_QKV) {
+    if (row < D) return b0 + (size_t)row * D;
+    if (row < D + KVH * HD) return b1 + (size_t)(row - D) * D;
+    return b2 + (size_t)(row - D - KVH * HD) * D;
+  }
+  return b0 + (size_t)row * D;
+}
+
+struct GemmArgs {
+  const uint16_t* a;     // [M][4096]
+  const uint16_t* b0;    // rows 0..   (Wq or wo16)
+  const uint16_t* b1;    // Wk (QKV only)
+  const uint16_t* b2;    // Wv (QKV only)
+  int M, N;
+  PrefillParams p;
+};
+
+template <int REGION>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][8], int mw,
+                                             int fw, int lane);
+
+template <int KIND>
+__global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+
+  // XCD-aware tile order: workgroup id i runs on XCD i % 8; give each XCD a
+  // contiguous range of the grouped tile order so its L2 serves 4 m-tiles
+  // against a sweep of n-tiles.
+  const int num_m = (g.M + GBM - 1) / GBM, num_n = g.N / GBN;
+  const int total = num_m * num_n;
+  int tl = blockIdx.x;
+  if ((total & 7) == 0) tl = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int group = tl / (kGroupM * num_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(kGroupM, num_m - first_m);
+  const int within = tl - group * kGroupM * num_n;
+  const int mt0 = first_m + within % gm;
+  const int nt0 = within / gm;
+  const int m0 = mt0 * GBM, n0 = nt0 * GBN;
+
+  // per-lane global sources of the 8 A and 8 B load instructions of this wave
+  // (wave w fills tile rows w*64 .. w*64+63, 8 rows per instruction; lane l
+  // writes LDS chunk l & 7 of row l >> 3, holding logical chunk (l&7)^(l>>3))
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  const uint16_t* a_src[8];
+  const uint16_t* b_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = w * 64 + i * 8 + lrow;
+    const int am = min(m0 + r, g.M - 1);
+    a_src[i] = g.a + (size_t)am * D + lchunk * 8;
+    const int br = b_row_of<KIND>(n0, r);
+    b_src[i] = b_row_ptr<KIND>(g.b0, g.b1, g.b2, br) + lchunk * 8;
+  }
+
+  auto load_stage = [&](int stage, int k0) {
+    char* sa = smem + stage * (GBM + GBN) * GBK * 2;
+    char* sb = sa + GBM * GBK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_void*)(sa + (w * 64 + i * 8) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_src[i] + k0, (lds_void*)(sb + (w * 64 + i * 8) * 128), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int nk = D / GBK;
+  load_stage(0, 0);
+  for (int kb = 0; kb < nk; ++kb) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nk) load_stage((kb + 1) & 1, (kb + 1) * GBK);
+    const char* sa = smem + (kb & 1) * (GBM + GBN) * GBK * 2;
+    const char* sb = sa + GBM * GBK * 2;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = ks * 4 + (lane >> 4);
+      u32x4 af[8], bf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ra = wm * 128 + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const u32x4*>(sa + ra * 128 + ((chunk ^ (ra & 7)) << 4));
+        const int rb = wn * 128 + i * 16 + (lane & 15);
+        bf[i] = *reinterpret_cast<const u32x4*>(sb + rb * 128 + ((chunk ^ (rb & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (KIND == GEMM_QKV)
+            acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+          else
+            acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
+        }
+    }
+  }
+
+  // epilogue: acc[i][j][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
+  //                             [tile col wn*128 + j*16 + (lane&15)]
+  // The region (Q, K or V features) is uniform over the workgroup's n-tile,
+  // so each region gets its own small, fully unrolled loop nest and the
+  // accumulators stay in registers.
+  if (KIND == GEMM_QKV) {
+    if (n0 < D)
+      qkv_epilogue<0>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+    else if (n0 < D + KVH * HD)
+      qkv_epilogue<1>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+    else
+      qkv_epilogue<2>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wn * 128 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * 128 + i * 16 + (lane >> 4) * 4 + e;
+          if (m < g.M) g.p.out[(size_t)m * D + n] = acc[i][j][e];
+        }
+      }
+  }
+}
+
+// QKV epilogue over a wave's 128 x 128 block (rows from mw, features from fw).
+// REGION 0: Q (rotate, scale by log2(e)/sqrt(128), fp16 to the workspace);
+// REGION 1: K (rotate, bf16 to the cache, fp16 copy); REGION 2: V (bf16 to the
+// dimension-major cache, fp16 copy).  Column pair (acc[i][2u], acc[i][2u+1])
+// of lane l holds features (f, f+1) with f = fw + 32u + 2*(l & 15).
+template <int REGION>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][8], int mw,
+                                             int fw, int lane) {
+  const PrefillParams& p = g.p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = mw + i * 16 + (lane >> 4) * 4 + e;
+      if (m >= g.M) continue;
+      const int b = m / p.T, t = m - b * p.T;
+      const float2* rope_row = reinterpret_cast<const float2*>(p.rope) + (size_t)t * PAIRS;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = fw + 32 * u + 2 * (lane & 15);
+        float a = acc[i][2 * u][e], c = acc[i][2 * u + 1][e];
+        if (REGION < 2) {
+          const float2 cs = rope_row[(f & (HD - 1)) >> 1];
+          const float ra = a * cs.x - c * cs.y;
+          const float rc = a * cs.y + c * cs.x;
+          a = ra;
+          c = rc;
+        }
+        if (p.probe) *reinterpret_cast<float2*>(p.probe + (size_t)m * NQKV + f) = make_float2(a, c);
+        if (REGION == 0) {
+          *reinterpret_cast<uint32_t*>(p.q16 + (size_t)m * D + f) =
+              pack_f16x2(a * kScoreLog2, c * kScoreLog2);
+        } else if (REGION == 1) {
+          const int ff = f - D, gg = ff / HD, d = ff % HD;
+          const uint32_t kb = pack_bf16x2(a, c);
+          *reinterpret_cast<uint32_t*>(p.kcache + ((size_t)(b * KVH + gg) * p.T_max + t) * HD + d) = kb;
+          *reinterpret_cast<uint32_t*>(p.k16 + ((size_t)(b * KVH + gg) * p.Tp + t) * HD + d) =
+              pack_f16x2(bf16_bits_to_f32(kb & 0xffffu), bf16_bits_to_f32(kb >> 16));
+        } else {
+          const int ff = f - D - KVH * HD, gg = ff / HD, d = ff % HD;
+          const uint32_t v0 = f32_to_bf16_bits(a), v1 = f32_to_bf16_bits(c);
+          uint16_t* vc = p.vcache + ((size_t)(b * KVH + gg) * HD + d) * p.T_max + t;
+          vc[0] = (uint16_t)v0;
+          vc[p.T_max] = (uint16_t)v1;
+          uint16_t* vt = p.v16t + ((size_t)(b * KVH + gg) * HD + d) * p.Tp + t;
+          const _Float16 h0 = (_Float16)bf16_bits_to_f32(v0), h1 = (_Float16)bf16_bits_to_f32(v1);
+          vt[0] = __builtin_bit_cast(uint16_t, h0);
+          vt[p.Tp] = __builtin_bit_cast(uint16_t, h1);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND>
+static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<KIND>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+  if (e != hipSuccess) return e;
+  const int tiles = ((g.M + GBM - 1) / GBM) * (g.N / GBN);
+  hipLaunchKernelGGL(gemm_kernel<KIND>, dim3(tiles), dim3(256), kGemmLds, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s) {
+  GemmArgs g;
+  g.a = p.x;
+  g.b0 = p.wq;
+  g.b1 = p.wk;
+  g.b2 = p.wv;
+  g.M = p.B * p.T;
+  g.N = NQKV;
+  g.p = p;
+  return launch_gemm<GEMM_QKV>(g, s);
+}
+
+hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
+  GemmArgs g;
+  g.a = p.o16;
+  g.b0 = p.wo16;
+  g.b1 = nullptr;
+  g.b2 = nullptr;
+  g.M = p.B * p.T;
+  g.N = D;
+  g.p = p;
+  return launch_gemm<GEMM_OUT>(g, s);
+}
+
+// ---------------------------------------------------------------------------
+// Causal flash attention (prefill)
+// ---------------------------------------------------------------------------
+//
+// Workgroup = (sequence b, kv head g, query tile of 64 positions); wave w
+// handles query head 4g + w.  Per 64-key tile, in fp16 on the matrix cores:
+//   S^T[64 keys x 64 q] = K . Q^T      (A = K tile from LDS, B = Q in VGPRs)
+//   O^T[128 dims x 64 q] += V^T . P^T  (A = V^T tile from LDS, B = P in VGPRs)
+// Within each 32-key half, A-operand row r of score tile "sub" holds key
+// (r >> 2)*8 + sub*4 + (r & 3); each lane then owns 8 consecutive keys of
+// its query column, which is exactly its B operand for the P.V step.
+constexpr int AQ = kPrefillTile;      // queries per workgroup
+constexpr int AK = kPrefillTile;      // keys per tile
+
+__global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char sK[AK * HD * 2];     // [64 keys][128 dims], 16 KiB
+  __shared__ __attribute__((aligned(16))) char sV[HD * AK * 2];     // [128 dims][64 keys], 16 KiB
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, rg = lane >> 4;
+  const int nqt = p.Tp / AQ;
+  const int pairs = p.B * KVH;
+  const int bg = blockIdx.x % pairs;
+  const int qt = nqt - 1 - blockIdx.x / pairs;      // longest rows first
+  const int b = bg / KVH, g = bg % KVH;
+  const int h = g * REP + w;
+  const int T = p.T, Tp = p.Tp;
+
+  // Q^T fragments: query qt*64 + nt*16 + col, dims rg*8 + 32*ks
+  u32x4 qf[4][4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int t = qt * AQ + nt * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[nt][ks] = (t < T) ? ld_u32x4(p.q16 + ((size_t)b * T + t) * D + h * HD + rg * 8 + 32 * ks)
+                           : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
+  const uint16_t* vg = p.v16t + (size_t)bg * HD * Tp;
+
+  f32x4 oacc[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
+
+  // staging of one K/V tile: thread -> 4 K chunks and 4 V^T chunks of 16 bytes
+  u32x4 kreg[4], vreg[4];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r;
+      const int key = i >> 4, c = i & 15;
+      const int j = kt * AK + key;
+      kreg[r] = (j < T) ? ld_u32x4(kg + (size_t)j * HD + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int dim = i >> 3, cv = i & 7;
+      const int j0 = kt * AK + cv * 8;
+      u32x4 v = ld_u32x4(vg + (size_t)dim * Tp + j0);
+      if (j0 + 8 > T) {
+        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = j0 + 2 * q;
+          u[q] &= (e + 1 < T) ? 0xffffffffu : (e < T ? 0x0000ffffu : 0u);
+        }
+      }
+      vreg[r] = v;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r;
+      const int key = i >> 4, c = i & 15;
+      *reinterpret_cast<u32x4*>(sK + key * 256 + ((c ^ (key & 15)) << 4)) = kreg[r];
+      const int dim = i >> 3, cv = i & 7;
+      *reinterpret_cast<u32x4*>(sV + dim * 128 + ((cv ^ (dim & 7)) << 4)) = vreg[r];
+    }
+  };
+
+  fetch(0);
+  for (int kt = 0; kt <= qt; ++kt) {
+    __syncthreads();                 // previous tile's LDS reads are done
+    store();
+    __syncthreads();
+    if (kt < qt) fetch(kt + 1);      // next tile's global loads overlap this tile's math
+
+    // ---- scores ----
+    f32x4 sacc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int key = 32 * (mt >> 1) + (col >> 2) * 8 + (mt & 1) * 4 + (col & 3);
+        const int c = ks * 4 + rg;
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sK + key * 256 + ((c ^ (key & 15)) << 4));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) sacc[mt][nt] = mfma_f16(kf, qf[nt][ks], sacc[mt][nt]);
+      }
+    }
+
+    // ---- online softmax per query column ----
+    // sacc[mt][nt][e]: key kt*64 + 32*(mt>>1) + rg*8 + (mt&1)*4 + e, query nt*16 + col
+    const bool diag = (kt == qt);
+    u32x4 pf[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int q = qt * AQ + nt * 16 + col;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = sacc[mt][nt][e];
+          if (diag) {
+            const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
+            v = (key > q) ? -INFINITY : v;
+          }
+          sacc[mt][nt][e] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run[nt], tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+      m_run[nt] = m_new;
+      float psum = 0.f;
+      uint32_t pk[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int mt = half * 2 + sub;
+          const float p0 = __builtin_amdgcn_exp2f(sacc[mt][nt][0] - m_new);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[mt][nt][1] - m_new);
+          const float p2 = __builtin_amdgcn_exp2f(sacc[mt][nt][2] - m_new);
+          const float p3 = __builtin_amdgcn_exp2f(sacc[mt][nt][3] - m_new);
+          psum += (p0 + p1) + (p2 + p3);
+          pk[half][sub * 2] = pack_f16x2(p0, p1);
+          pk[half][sub * 2 + 1] = pack_f16x2(p2, p3);
+        }
+      l_run[nt] = l_run[nt] * alpha + psum;
+      pf[nt][0] = u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
+      pf[nt][1] = u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int dim = dt * 16 + col;
+        const int c = half * 4 + rg;
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(sV + dim * 128 + ((c ^ (dim & 7)) << 4));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_f16(vf, pf[nt][half], oacc[dt][nt]);
+      }
+    }
+  }
+
+  // ---- normalise and store O (fp16) ----
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    float l = l_run[nt];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const int t = qt * AQ + nt * 16 + col;
+    if (t < T) {
+      uint16_t* orow = p.o16 + ((size_t)b * T + t) * D + h * HD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 o = oacc[dt][nt];
+        const u32x2 v = {pack_f16x2(o[0] * inv, o[1] * inv), pack_f16x2(o[2] * inv, o[3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + dt * 16 + rg * 4) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+  const int nqt = p.Tp / AQ;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(p.B * KVH * nqt), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,270 @@
+"""Python binding of libgqa.so: argument marshalling only.
+
+Every function checks dtypes, devices, shapes and contiguity of the torch
+tensors it is given, then passes raw device pointers and the current HIP
+stream to the C ABI declared in ``include/gqa.h``.  All computation happens
+in the library's kernels; if the library is missing or fails to load, calls
+raise instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+D_MODEL = 4096
+N_HEADS = 32
+N_KV_HEADS = 8
+HEAD_DIM = 128
+QKV_DIM = 6144
+ROPE_PAIRS = 64
+DECODE_STAGES = 3
+PREFILL_STAGES = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa.so")
+
+STATUS = {
+    0: "GQA_OK", -1: "GQA_ERR_NULL", -2: "GQA_ERR_SHAPE", -3: "GQA_ERR_RANGE",
+    -4: "GQA_ERR_ALIGN", -5: "GQA_ERR_WORKSPACE", -6: "GQA_ERR_HIP", -7: "GQA_ERR_ALIAS",
+    -8: "GQA_ERR_ARG",
+}
+
+# exported entry points and their C signatures
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "gqa_status_string": (ctypes.c_char_p, [_I]),
+    "gqa_rope_table": (_I, [_I, ctypes.c_double, _I, _P, _P]),
+    "gqa_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "gqa_block_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
+                               ctypes.c_size_t, _P, _P]),
+    "gqa_block_prefill_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
+                                        ctypes.c_size_t, _P, _P, _P]),
+    "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
+                              ctypes.c_size_t, _P, _P]),
+    "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
+                                       _P, ctypes.c_size_t, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    """A libgqa call returned an error status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgqa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m grouped_query_attention_gemv_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gqa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GQAError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------
+# Allocation helpers (layouts of include/gqa.h)
+# ----------------------------------------------------------------------------
+
+def workspace_bytes(B: int, T: int, T_max: int) -> int:
+    return int(lib().gqa_workspace_bytes(int(B), int(T), int(T_max)))
+
+
+def workspace(B: int, T: int, T_max: int, device) -> torch.Tensor:
+    n = workspace_bytes(B, T, T_max)
+    if n == 0:
+        raise ValueError(f"no workspace size for B={B}, T={T}, T_max={T_max}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def empty_caches(B: int, T_max: int, device):
+    """(kcache [B, 8, T_max, 128], vcache [B, 8, 128, T_max]) bf16, uninitialised."""
+    k = torch.empty((B, N_KV_HEADS, T_max, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, N_KV_HEADS, HEAD_DIM, T_max), dtype=torch.bfloat16, device=device)
+    return k, v
+
+
+def kcache_by_position(kcache: torch.Tensor) -> torch.Tensor:
+    """View [B, T_max, 8, 128] of the head-major key cache."""
+    return kcache.permute(0, 2, 1, 3)
+
+
+def vcache_by_position(vcache: torch.Tensor) -> torch.Tensor:
+    """View [B, T_max, 8, 128] of the dimension-major value cache."""
+    return vcache.permute(0, 3, 1, 2)
+
+
+class HipEvents:
+    """A set of HIP events created through the HIP runtime, for the
+    *_profiled entry points."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds between events i and j (synchronises on j)."""
+        if self._hip.hipEventSynchronize(self.events[j]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i], self.events[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.n):
+            if self.events[i]:
+                self._hip.hipEventDestroy(self.events[i])
+                self.events[i] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------
+# Entry points
+# ----------------------------------------------------------------------------
+
+def rope_table(T_max: int, theta: float = 500000.0, scaled: bool = True, device="cuda",
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """[T_max, 64, 2] fp32 (cos, sin) table on ``device``."""
+    device = torch.device(device)
+    if out is None:
+        out = torch.empty((T_max, ROPE_PAIRS, 2), dtype=torch.float32, device=device)
+    _need(out, "rope", torch.float32, (T_max, ROPE_PAIRS, 2), out.device)
+    _check(lib().gqa_rope_table(int(T_max), float(theta), int(bool(scaled)), _ptr(out),
+                                _stream(out.device)), "gqa_rope_table")
+    return out
+
+
+def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope):
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    _need(wq, "wq", torch.bfloat16, (D_MODEL, D_MODEL), dev)
+    _need(wk, "wk", torch.bfloat16, (N_KV_HEADS * HEAD_DIM, D_MODEL), dev)
+    _need(wv, "wv", torch.bfloat16, (N_KV_HEADS * HEAD_DIM, D_MODEL), dev)
+    _need(wo, "wo", torch.bfloat16, (D_MODEL, D_MODEL), dev)
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be [B, 8, T_max, 128]")
+    B, T_max = kcache.shape[0], kcache.shape[2]
+    _need(kcache, "kcache", torch.bfloat16, (B, N_KV_HEADS, T_max, HEAD_DIM), dev)
+    _need(vcache, "vcache", torch.bfloat16, (B, N_KV_HEADS, HEAD_DIM, T_max), dev)
+    if rope.dim() != 3 or rope.shape[0] < T_max:
+        raise ValueError("rope must be [>= T_max, 64, 2]")
+    _need(rope, "rope", torch.float32, (rope.shape[0], ROPE_PAIRS, 2), dev)
+    return dev, B, T_max
+
+
+def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, probe=None,
+                  events: HipEvents | None = None) -> torch.Tensor:
+    """Delta_attn [B, T, 4096] fp32 for x [B, T, 4096] bf16 from position 0;
+    writes cache rows 0..T-1."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, 4096]")
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    T = x.shape[1]
+    _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
+    if out is None:
+        out = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, T, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, T, QKV_DIM), dev)
+    if ws is None:
+        ws = workspace(B, T, T_max, dev)
+    args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
+            int(T_max), _ptr(rope), int(B), int(T), _ptr(out), _ptr(ws), ws.numel(),
+            _ptr(probe), _stream(dev)]
+    if events is None:
+        _check(lib().gqa_block_prefill(*args), "gqa_block_prefill")
+    else:
+        _check(lib().gqa_block_prefill_profiled(*args, events.events), "gqa_block_prefill_profiled")
+    return out
+
+
+def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=None,
+                 out_bf16=None, accumulate: bool = False, ws=None, probe=None,
+                 events: HipEvents | None = None) -> torch.Tensor:
+    """One token per sequence at position start_pos: x [B, 4096] bf16 ->
+    out [B, 4096] fp32 (= Delta, or += Delta with accumulate)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [B, 4096]")
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, D_MODEL), dev)
+    if out_bf16 is not None:
+        _need(out_bf16, "out_bf16", torch.bfloat16, (B, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, QKV_DIM), dev)
+    if ws is None:
+        ws = workspace(B, 1, T_max, dev)
+    args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
+            int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
+            int(bool(accumulate)), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)]
+    if events is None:
+        _check(lib().gqa_block_decode(*args), "gqa_block_decode")
+    else:
+        _check(lib().gqa_block_decode_profiled(*args, events.events), "gqa_block_decode_profiled")
+    return out

@@ -1,0 +1,190 @@
+/*
+ * gqa.h -- C ABI of libgqa.so: one Llama 3.1 8B grouped-query attention block
+ * (d = 4096, 32 query heads, 8 KV heads of width 128, no biases, scaled RoPE)
+ * on one MI355X (gfx950).
+ *
+ * The operation is the one stated on the model-atlas page "Llama 3.1 8B .
+ * Grouped-query attention" (header: in x [B, T, 4096] and R [positions, 64
+ * pairs], out Delta_attn [B, T, 4096]; mode decode at P cached positions; state
+ * "KV cache: writes row P, reads rows 0..P"), with the pieces shown in its
+ * evidence sections:
+ *   qkv       Q = x Wq^T, K = x Wk^T, V = x Wv^T (weights stored [out, in], as on
+ *             page "Llama 3.1 8B . Query projection"), viewed as heads of 128;
+ *   rope      adjacent pairs (2i, 2i+1) of each Q and K head rotated by the
+ *             angle position * f_i;
+ *   gqa       KV head g serves query heads 4g .. 4g+3;
+ *   scores    softmax over keys of Q K^T / sqrt(128), causal: query at
+ *             position p sees keys 0..p;
+ *   retrieval P V, heads merged to feature h*128 + d, Delta = O Wo^T.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller, contiguous, and
+ *     16-byte aligned.  bf16 values are passed as their 16-bit patterns
+ *     (gqa_bf16).
+ *   - Work is enqueued on `stream` (NULL = the null stream); calls return
+ *     without synchronising.  Calls on different streams are safe when their
+ *     buffers are disjoint.  The library holds no mutable global state.
+ *   - Every argument is validated on the host before any HIP call.  On an
+ *     error nothing is launched and no buffer is modified.  No C++ exception
+ *     crosses this interface.
+ *   - Returns GQA_OK (0) or a negative gqa_status.
+ *
+ * KV cache layout (bf16, updated in place; T_max = rows per sequence):
+ *   kcache [B][8][T_max][128]   key of position t, kv head g, dim d at
+ *                               ((b*8 + g)*T_max + t)*128 + d
+ *   vcache [B][8][128][T_max]   value of position t, kv head g, dim d at
+ *                               ((b*8 + g)*128 + d)*T_max + t
+ * Keys are head-major so that a run of positions of one head is contiguous;
+ * values are stored dimension-major so that the positions one probability
+ * multiplies are contiguous for the matrix cores.  A call writes exactly the
+ * rows start_pos .. start_pos+T-1 of sequences 0..B-1 and leaves every other
+ * element bit-for-bit unchanged.  The appended values are the post-RoPE keys
+ * and the values rounded to bf16 (nearest, ties to even); attention reads the
+ * appended rows back in that rounded form.
+ *
+ * RoPE table layout: rope[T_max][64][2] fp32, (cos, sin) of position * f_i.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Shapes fixed by the Llama 3.1 8B catalogue entry (dim 4096, n_heads 32,
+ * n_kv_heads 8; head_dim = dim / n_heads). */
+#define GQA_D_MODEL     4096
+#define GQA_N_HEADS     32
+#define GQA_N_KV_HEADS  8
+#define GQA_HEAD_DIM    128
+#define GQA_QKV_DIM     6144            /* 4096 (Q) + 1024 (K) + 1024 (V) */
+#define GQA_ROPE_PAIRS  64
+#define GQA_MAX_BATCH   1024
+#define GQA_MAX_T_MAX   (1 << 20)
+
+/* Number of stages whose boundaries the *_profiled entry points record. */
+#define GQA_DECODE_STAGES   3           /* QKV+RoPE+append, attention, wo */
+#define GQA_PREFILL_STAGES  4           /* wo to fp16, QKV+RoPE+append, attention, wo */
+
+typedef uint16_t gqa_bf16;
+
+typedef enum {
+    GQA_OK            = 0,
+    GQA_ERR_NULL      = -1,  /* a required pointer is NULL */
+    GQA_ERR_SHAPE     = -2,  /* B, T or T_max outside the supported range */
+    GQA_ERR_RANGE     = -3,  /* start_pos < 0 or start_pos + T > T_max */
+    GQA_ERR_ALIGN     = -4,  /* a pointer is not 16-byte aligned, or T_max % 8 != 0 */
+    GQA_ERR_WORKSPACE = -5,  /* ws_bytes < gqa_workspace_bytes(...) */
+    GQA_ERR_HIP       = -6,  /* a HIP call or kernel launch failed */
+    GQA_ERR_ALIAS     = -7,  /* an output overlaps an input or another output */
+    GQA_ERR_ARG       = -8   /* any other invalid argument (theta <= 0, flags) */
+} gqa_status;
+
+/* Readable name of a status code; never NULL. */
+const char* gqa_status_string(int status);
+
+/*
+ * gqa_rope_table -- fill rope[T_max][64][2] with (cos, sin)(p * f_i) for
+ * positions p < T_max (the table R of the block's header).
+ *
+ * f_i = theta^(-2i/128).  With scaled != 0 the Llama 3.1 long-context rule is
+ * applied (catalogue entry use_scaled_rope: True; the page "Llama 3 8B .
+ * Attention update" shows the unscaled Llama 3 setting): wavelengths
+ * 2*pi/f_i below 8192/4 keep f_i, above 8192 use f_i/8, and in between f_i is
+ * blended linearly in 8192/wavelength.  Angles are formed and evaluated in
+ * fp64 and rounded once to fp32.
+ *   T_max  1 .. GQA_MAX_T_MAX
+ *   theta  > 0 (500000.0 for Llama 3 and 3.1)
+ *   rope   device, T_max*64*2 floats
+ * Errors: GQA_ERR_SHAPE, GQA_ERR_ARG, GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_HIP.
+ */
+int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t stream);
+
+/*
+ * gqa_workspace_bytes -- device scratch needed by gqa_block_prefill(B, T) and
+ * by gqa_block_decode(B, start_pos < T_max) with these arguments; 0 when the
+ * arguments are out of range.  The workspace needs no initialisation and
+ * holds nothing the caller reads; calls that share one must be ordered.
+ */
+size_t gqa_workspace_bytes(int B, int T, int T_max);
+
+/*
+ * gqa_block_prefill -- the block over T new tokens of B sequences starting
+ * at position 0 (the "Prefill" mode of the pages), with a causal mask.
+ *   x        [B][T][4096] bf16, the block input
+ *   wq       [4096][4096] bf16 [out, in];  wk, wv [1024][4096];  wo [4096][4096]
+ *   kcache, vcache   layouts above; rows 0..T-1 of each sequence are written
+ *   T_max    rows per sequence in the caches and the table; T <= T_max
+ *   rope     [T_max][64][2] fp32 from gqa_rope_table
+ *   out      [B][T][4096] fp32, Delta_attn
+ *   ws       workspace of ws_bytes >= gqa_workspace_bytes(B, T, T_max)
+ *   probe    NULL, or [B][T][6144] fp32 receiving the post-RoPE Q | K and the V
+ *            features exactly as computed before any rounding (for checking)
+ * Aliasing: out, probe, ws and the caches must not overlap each other or the
+ * inputs.
+ */
+int gqa_block_prefill(const gqa_bf16* x,
+                      const gqa_bf16* wq, const gqa_bf16* wk,
+                      const gqa_bf16* wv, const gqa_bf16* wo,
+                      gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                      const float* rope, int B, int T,
+                      float* out, void* ws, size_t ws_bytes, float* probe,
+                      hipStream_t stream);
+
+/*
+ * gqa_block_decode -- one new token per sequence at position start_pos (the
+ * page's decode mode): writes cache row start_pos and attends over rows
+ * 0..start_pos of each of the B sequences (one start_pos for all of them).
+ *   x          [B][4096] bf16
+ *   weights, caches, T_max, rope, ws, probe as for prefill (probe [B][6144])
+ *   start_pos  0 .. T_max-1
+ *   out        [B][4096] fp32: out = Delta when accumulate == 0,
+ *              out += Delta when accumulate != 0 (the block residual
+ *              h = x + attention(...), with the caller's fp32 residual in out)
+ *   out_bf16   NULL, or [B][4096] bf16 receiving the bf16 rounding of out
+ *              after the update (the next block's input in a stack of blocks)
+ * Aliasing: out, out_bf16, probe, ws and the caches must not overlap each
+ * other or the inputs.
+ */
+int gqa_block_decode(const gqa_bf16* x,
+                     const gqa_bf16* wq, const gqa_bf16* wk,
+                     const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                     const float* rope, int start_pos, int B,
+                     float* out, gqa_bf16* out_bf16, int accumulate,
+                     void* ws, size_t ws_bytes, float* probe,
+                     hipStream_t stream);
+
+/*
+ * Same as gqa_block_prefill / gqa_block_decode, and additionally records
+ * events[0] on `stream` before the first kernel and events[i] after stage i
+ * (GQA_PREFILL_STAGES / GQA_DECODE_STAGES stages), so that a caller can time
+ * each kernel with hipEventElapsedTime.  events must hold that many + 1
+ * created hipEvent_t handles.
+ */
+int gqa_block_prefill_profiled(const gqa_bf16* x,
+                               const gqa_bf16* wq, const gqa_bf16* wk,
+                               const gqa_bf16* wv, const gqa_bf16* wo,
+                               gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                               const float* rope, int B, int T,
+                               float* out, void* ws, size_t ws_bytes, float* probe,
+                               hipStream_t stream, hipEvent_t* events);
+
+int gqa_block_decode_profiled(const gqa_bf16* x,
+                              const gqa_bf16* wq, const gqa_bf16* wk,
+                              const gqa_bf16* wv, const gqa_bf16* wo,
+                              gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                              const float* rope, int start_pos, int B,
+                              float* out, gqa_bf16* out_bf16, int accumulate,
+                              void* ws, size_t ws_bytes, float* probe,
+                              hipStream_t stream, hipEvent_t* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -5,12 +5,40 @@ other tests run on the CPU.
 """
 import os
 import sys
+import time
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PROGRESS = os.path.join(ROOT, "gpurun_out", "progress.log")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built libgqa.so")
-    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Build libgqa.so when nothing is built yet (a fresh checkout)."""
+    from grouped_query_attention_gemv_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+
+
+@pytest.fixture(autouse=True)
+def _progress(request):
+    """Name each GPU test in gpurun_out/progress.log before it runs, so a run
+    that ends abruptly still shows which case was running."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    os.makedirs(os.path.dirname(PROGRESS), exist_ok=True)
+    with open(PROGRESS, "a") as f:
+        f.write(f"{time.strftime('%H:%M:%S')} start {request.node.nodeid}\n")
+    t0 = time.time()
+    yield
+    with open(PROGRESS, "a") as f:
+        f.write(f"{time.strftime('%H:%M:%S')} end   {request.node.nodeid} {time.time() - t0:.1f}s\n")

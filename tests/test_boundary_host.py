@@ -1,0 +1,139 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/gqa.h declares, and
+reject bad arguments with the documented status before making any HIP call
+(so the fake device addresses used here are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import grouped_query_attention_gemv_amd as G
+from grouped_query_attention_gemv_amd import gqa as GB
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, ENULL, ESHAPE, ERANGE, EALIGN, EWS, EHIP, EALIAS, EARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared_functions()
+    for n in ("gqa_rope_table", "gqa_workspace_bytes", "gqa_block_prefill", "gqa_block_decode",
+              "gqa_status_string", "gqa_block_prefill_profiled", "gqa_block_decode_profiled"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = G.lib()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", GB.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in _declared_functions():
+        assert n in exported, n
+    assert set(GB._SIGS) == set(_declared_functions())
+
+
+def test_status_strings():
+    for code in (OK, ENULL, ESHAPE, ERANGE, EALIGN, EWS, EHIP, EALIAS, EARG):
+        assert G.status_string(code).startswith(GB.STATUS[code])
+    assert "unknown" in G.status_string(12345)
+
+
+def test_workspace_bytes():
+    assert G.workspace_bytes(0, 1, 64) == 0
+    assert G.workspace_bytes(1, 0, 64) == 0
+    assert G.workspace_bytes(1, 1, 0) == 0
+    # prefill needs fp16 Q and O, fp16 K/V copies and an fp16 Wo: at B=4, T=2048
+    n = G.workspace_bytes(4, 2048, 2048)
+    assert n >= 4 * 2048 * 4096 * 2 * 2 + 2 * 4 * 8 * 2048 * 128 * 2 + 4096 * 4096 * 2
+    assert G.workspace_bytes(8, 1, 131072) > 0
+
+
+# fake, 16-byte aligned device addresses: validation rejects every call below
+# before any of them could be used
+BASE = 0x7F0000000000
+
+
+def _fake(i, size=1 << 32):
+    return ctypes.c_void_p(BASE + i * size)
+
+
+def _decode_args(**kw):
+    a = dict(x=_fake(0), wq=_fake(1), wk=_fake(2), wv=_fake(3), wo=_fake(4), kc=_fake(5),
+             vc=_fake(6), T_max=1024, rope=_fake(7), start_pos=10, B=1, out=_fake(8),
+             out_bf16=None, accumulate=0, ws=_fake(9), ws_bytes=1 << 40, probe=None,
+             stream=None)
+    a.update(kw)
+    return [a[k] for k in ("x", "wq", "wk", "wv", "wo", "kc", "vc", "T_max", "rope", "start_pos",
+                           "B", "out", "out_bf16", "accumulate", "ws", "ws_bytes", "probe",
+                           "stream")]
+
+
+def _prefill_args(**kw):
+    a = dict(x=_fake(0), wq=_fake(1), wk=_fake(2), wv=_fake(3), wo=_fake(4), kc=_fake(5),
+             vc=_fake(6), T_max=1024, rope=_fake(7), B=1, T=16, out=_fake(8), ws=_fake(9),
+             ws_bytes=1 << 40, probe=None, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("x", "wq", "wk", "wv", "wo", "kc", "vc", "T_max", "rope", "B", "T",
+                           "out", "ws", "ws_bytes", "probe", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), ENULL), (dict(wo=None), ENULL), (dict(kc=None), ENULL), (dict(ws=None), ENULL),
+    (dict(rope=None), ENULL), (dict(out=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(B=100000), ESHAPE), (dict(T_max=0), ESHAPE),
+    (dict(T_max=1004), EALIGN), (dict(x=ctypes.c_void_p(BASE + 2)), EALIGN),
+    (dict(probe=ctypes.c_void_p(BASE + (20 << 32) + 4)), EALIGN),
+    (dict(start_pos=-1), ERANGE), (dict(start_pos=1024), ERANGE),
+    (dict(ws_bytes=1024), EWS), (dict(accumulate=2), EARG),
+    (dict(out=_fake(0)), EALIAS), (dict(probe=_fake(8)), EALIAS),
+    (dict(out_bf16=_fake(5)), EALIAS), (dict(ws=_fake(6)), EALIAS),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert G.lib().gqa_block_decode(*_decode_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), ENULL), (dict(vc=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(T=0), ESHAPE), (dict(T_max=-8), ESHAPE),
+    (dict(T_max=1020), EALIGN), (dict(wq=ctypes.c_void_p(BASE + (1 << 32) + 8)), EALIGN),
+    (dict(T=1025), ERANGE),
+    (dict(ws_bytes=4096), EWS),
+    (dict(out=_fake(3)), EALIAS), (dict(kc=_fake(6)), EALIAS),
+])
+def test_prefill_rejects_bad_arguments(kw, code):
+    assert G.lib().gqa_block_prefill(*_prefill_args(**kw)) == code
+
+
+def test_profiled_variants_need_events():
+    l = G.lib()
+    assert l.gqa_block_decode_profiled(*_decode_args(), None) == ENULL
+    assert l.gqa_block_prefill_profiled(*_prefill_args(), None) == ENULL
+
+
+def test_rope_table_rejects_bad_arguments():
+    l = G.lib()
+    assert l.gqa_rope_table(0, 5e5, 1, _fake(0), None) == ESHAPE
+    assert l.gqa_rope_table(16, 0.0, 1, _fake(0), None) == EARG
+    assert l.gqa_rope_table(16, 5e5, 2, _fake(0), None) == EARG
+    assert l.gqa_rope_table(16, 5e5, 1, None, None) == ENULL
+    assert l.gqa_rope_table(16, 5e5, 1, ctypes.c_void_p(BASE + 4), None) == EALIGN
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 4096, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        G.block_decode(x, x, x, x, x, x, x, x, 0)
