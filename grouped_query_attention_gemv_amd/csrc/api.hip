@@ -40,7 +40,7 @@ int check_common(const void* x, const void* wq, const void* wk, const void* wv, 
                  const void* out, const void* ws) {
   if (!x || !wq || !wk || !wv || !wo || !kc || !vc || !rope || !out || !ws) return GQA_ERR_NULL;
   if (B < 1 || B > GQA_MAX_BATCH || T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
-  if (T_max % 8 != 0) return GQA_ERR_ALIGN;
+  if (T_max % GQA_V_BLOCK != 0) return GQA_ERR_ALIGN;
   const void* ptrs[] = {x, wq, wk, wv, wo, kc, vc, rope, out, ws};
   for (const void* q : ptrs)
     if (!aligned16(q)) return GQA_ERR_ALIGN;
@@ -148,7 +148,7 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_NULL: return "GQA_ERR_NULL: a required pointer is NULL";
     case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE: B, T or T_max out of range";
     case GQA_ERR_RANGE: return "GQA_ERR_RANGE: start_pos/T outside [0, T_max)";
-    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned or T_max % 8 != 0";
+    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned or T_max % 32 != 0";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: a HIP call or kernel launch failed";
     case GQA_ERR_ALIAS: return "GQA_ERR_ALIAS: an output overlaps another buffer";

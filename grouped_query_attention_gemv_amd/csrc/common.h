@@ -15,6 +15,12 @@ constexpr int HD = GQA_HEAD_DIM;        // 128
 constexpr int NQKV = GQA_QKV_DIM;       // 6144
 constexpr int REP = H / KVH;            // 4 query heads per KV head
 constexpr int PAIRS = GQA_ROPE_PAIRS;   // 64
+constexpr int VB = GQA_V_BLOCK;         // 32 positions per value-cache block
+
+// Element offset of value (b, g, t, d) in the blocked value cache.
+__device__ __forceinline__ size_t vcache_index(int b, int g, int t, int d, int T_max) {
+  return ((size_t)(b * KVH + g) * (T_max / VB) + t / VB) * (HD * VB) + d * VB + (t % VB);
+}
 
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale into exp2.
 constexpr float kScoreLog2 = 0.12751743074843916f;

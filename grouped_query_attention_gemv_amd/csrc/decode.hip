@@ -129,9 +129,9 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
     *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v0, v1);
   } else {
     const int g = rr / HD, d = rr % HD;
-    uint16_t* dst = p.vcache + ((size_t)(b * KVH + g) * HD + d) * p.T_max + pos;
+    uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
     dst[0] = (uint16_t)f32_to_bf16_bits(v0);
-    dst[p.T_max] = (uint16_t)f32_to_bf16_bits(v1);
+    dst[VB] = (uint16_t)f32_to_bf16_bits(v1);
   }
 }
 
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // The A-operand rows of the score tiles are assigned to positions so that
 // each lane's 8 score values are 8 consecutive positions: exactly the B
 // operand of the following P.V instruction, with no data movement.
-__global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
@@ -195,37 +195,39 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
   }
 
   const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
-  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * HD * T_max;
+  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * (T_max / VB) * (HD * VB);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int tile = j_begin + w * kAttnTile; tile < j_end; tile += kAttnWaves * kAttnTile) {
-    u32x4 kf[2][4], vf[8];
+  // Loads of one 32-position tile (tiles start at multiples of 32, so a tile
+  // is one value-cache block).  Key rows past the last visible position are
+  // clamped onto it (their scores are masked); value positions past it are
+  // cleared after the load, since the cache may hold anything there.
+  auto load_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int j = tile + (col >> 2) * 8 + mt * 4 + (col & 3);
+      const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[mt][ks] = (j < j_end) ? ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks) : zero4;
+      for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks);
     }
-    const int jv = tile + rg * 8;
+    const uint16_t* vblk = vbase + (size_t)(tile / VB) * (HD * VB) + rg * 8;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      vf[dt] = (jv < j_end) ? ld_nt_u32x4(vbase + (size_t)(col + 16 * dt) * T_max + jv) : zero4;
-    if (jv < j_end && jv + 8 > j_end) {
-      // positions past the last visible one may hold anything: clear them
-      const int nv = j_end - jv;
+    for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
+  };
+
+  auto compute_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
+    const int jv = tile + rg * 8;
+    if (jv + 8 > j_end) {
+      const int nv = j_end - jv;    // may be <= 0: the whole group is cleared
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        uint32_t* u = reinterpret_cast<uint32_t*>(&vf[dt]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv ? 0x0000ffffu : 0u);
-          u[q] &= keep;
+          vf[dt][q] &= keep;
         }
       }
     }
@@ -249,7 +251,7 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
         const float sum = v + dpp<DPP_ROW_SHL4>(v);      // hi + lo, valid in cols 0-3
         const float bc = dpp<DPP_ROW_SHR4>(sum);          // copy to cols 4-7
         const float full = (col < 4) ? sum : bc;
-        const int j = tile + rg * 8 + mt * 4 + i;
+        const int j = jv + mt * 4 + i;
         sv[mt * 4 + i] = (j < j_end) ? full : -INFINITY;
         tmax = fmaxf(tmax, sv[mt * 4 + i]);
       }
@@ -280,6 +282,23 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
       oacc[dt] *= alpha;
       oacc[dt] = mfma_bf16(vf[dt], pf, oacc[dt]);
     }
+  };
+
+  // software pipeline: the next tile's loads are in flight during this one's math
+  constexpr int kStride = kAttnWaves * kAttnTile;
+  u32x4 kA[2][4], vA[8], kB[2][4], vB[8];
+  int tile = j_begin + w * kAttnTile;
+  if (tile < j_end) load_tile(tile, kA, vA);
+  while (tile < j_end) {
+    int next = tile + kStride;
+    if (next < j_end) load_tile(next, kB, vB);
+    compute_tile(tile, kA, vA);
+    tile = next;
+    if (tile >= j_end) break;
+    next = tile + kStride;
+    if (next < j_end) load_tile(next, kA, vA);
+    compute_tile(tile, kB, vB);
+    tile = next;
   }
 
   // wave result: l summed over the 4 lane rows, O = hi column + lo column
@@ -345,17 +364,38 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeParams p) {
   if (!sm_last) return;
   __threadfence();
 
-  // last workgroup of this (b, g): merge every split in a fixed order
+  // last workgroup of this (b, g): merge every split in a fixed order, with
+  // the loads of 8 splits in flight at a time
+  constexpr int U = 8;
   float GM = -INFINITY;
-  for (int sidx = 0; sidx < p.nsplit; ++sidx)
-    GM = fmaxf(GM, __builtin_nontemporal_load(part0 + sidx * split_stride));
+  for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      mv[u] = (s0 + u < p.nsplit) ? __builtin_nontemporal_load(part0 + (s0 + u) * split_stride)
+                                  : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) GM = fmaxf(GM, mv[u]);
+  }
   float gl = 0.f, g0 = 0.f, g1 = 0.f;
-  for (int sidx = 0; sidx < p.nsplit; ++sidx) {
-    const float* ps = part0 + sidx * split_stride;
-    const float f = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(ps) - GM);
-    gl += __builtin_nontemporal_load(ps + 1) * f;
-    g0 += __builtin_nontemporal_load(ps + 4 + d2) * f;
-    g1 += __builtin_nontemporal_load(ps + 5 + d2) * f;
+  for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+    float mv[U], lv[U], ov0[U], ov1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < p.nsplit;
+      const float* ps = part0 + (ok ? s0 + u : 0) * split_stride;
+      mv[u] = ok ? __builtin_nontemporal_load(ps) : -INFINITY;
+      lv[u] = __builtin_nontemporal_load(ps + 1);
+      ov0[u] = __builtin_nontemporal_load(ps + 4 + d2);
+      ov1[u] = __builtin_nontemporal_load(ps + 5 + d2);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = __builtin_amdgcn_exp2f(mv[u] - GM);
+      gl += lv[u] * f;
+      g0 += ov0[u] * f;
+      g1 += ov1[u] * f;
+    }
   }
   const float r0 = g0 / gl, r1 = g1 / gl;
   const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);

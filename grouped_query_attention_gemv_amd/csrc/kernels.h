@@ -26,7 +26,7 @@ struct DecodeParams {
   const uint16_t* wv;       // [1024][4096]
   const uint16_t* wo;       // [4096][4096]
   uint16_t* kcache;         // [B][8][T_max][128]
-  uint16_t* vcache;         // [B][8][128][T_max]
+  uint16_t* vcache;         // [B][8][T_max/32][128][32]
   const float* rope;        // [T_max][64][2]
   float* out;               // [B][4096]
   uint16_t* out_bf16;       // optional [B][4096]
@@ -72,7 +72,7 @@ struct PrefillParams {
   uint16_t* wo16;           // [4096][4096] fp16 copy of wo
   uint16_t* q16;            // [M][4096] fp16 Q * log2(e)/sqrt(128)
   uint16_t* k16;            // [B][8][Tp][128] fp16 copy of the appended keys
-  uint16_t* v16t;           // [B][8][128][Tp] fp16 copy of the appended values
+  uint16_t* v16t;           // [B][8][Tp/64][128][64] fp16 copy of the appended values
   uint16_t* o16;            // [M][4096] fp16 attention output
 };
 

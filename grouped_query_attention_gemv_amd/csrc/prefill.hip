@@ -93,6 +93,8 @@ hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s) {
 // rows one matrix-core operand read touches fall in distinct banks.
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int AQ = kPrefillTile;      // queries per attention workgroup
+constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V^T block)
 constexpr int kGemmLds = 2 * (GBM + GBN) * GBK * 2;   // 128 KiB
 constexpr int kGroupM = 4;                             // m-tiles per tile-order group
 
@@ -284,13 +286,13 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
         } else {
           const int ff = f - D - KVH * HD, gg = ff / HD, d = ff % HD;
           const uint32_t v0 = f32_to_bf16_bits(a), v1 = f32_to_bf16_bits(c);
-          uint16_t* vc = p.vcache + ((size_t)(b * KVH + gg) * HD + d) * p.T_max + t;
+          uint16_t* vc = p.vcache + vcache_index(b, gg, t, d, p.T_max);
           vc[0] = (uint16_t)v0;
-          vc[p.T_max] = (uint16_t)v1;
-          uint16_t* vt = p.v16t + ((size_t)(b * KVH + gg) * HD + d) * p.Tp + t;
+          vc[VB] = (uint16_t)v1;
+          uint16_t* vt = p.v16t + (((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK;
           const _Float16 h0 = (_Float16)bf16_bits_to_f32(v0), h1 = (_Float16)bf16_bits_to_f32(v1);
           vt[0] = __builtin_bit_cast(uint16_t, h0);
-          vt[p.Tp] = __builtin_bit_cast(uint16_t, h1);
+          vt[AK] = __builtin_bit_cast(uint16_t, h1);
         }
       }
     }
@@ -342,8 +344,6 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 // Within each 32-key half, A-operand row r of score tile "sub" holds key
 // (r >> 2)*8 + sub*4 + (r & 3); each lane then owns 8 consecutive keys of
 // its query column, which is exactly its B operand for the P.V step.
-constexpr int AQ = kPrefillTile;      // queries per workgroup
-constexpr int AK = kPrefillTile;      // keys per tile
 
 __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char sK[AK * HD * 2];     // [64 keys][128 dims], 16 KiB
@@ -396,7 +396,7 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
       kreg[r] = (j < T) ? ld_u32x4(kg + (size_t)j * HD + c * 8) : u32x4{0u, 0u, 0u, 0u};
       const int dim = i >> 3, cv = i & 7;
       const int j0 = kt * AK + cv * 8;
-      u32x4 v = ld_u32x4(vg + (size_t)dim * Tp + j0);
+      u32x4 v = ld_u32x4(vg + (size_t)kt * (HD * AK) + dim * AK + cv * 8);
       if (j0 + 8 > T) {
         uint32_t* u = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll

@@ -19,6 +19,7 @@ N_KV_HEADS = 8
 HEAD_DIM = 128
 QKV_DIM = 6144
 ROPE_PAIRS = 64
+V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
 
@@ -122,9 +123,13 @@ def workspace(B: int, T: int, T_max: int, device) -> torch.Tensor:
 
 
 def empty_caches(B: int, T_max: int, device):
-    """(kcache [B, 8, T_max, 128], vcache [B, 8, 128, T_max]) bf16, uninitialised."""
+    """(kcache [B, 8, T_max, 128], vcache [B, 8, T_max/32, 128, 32]) bf16,
+    uninitialised; T_max must be a multiple of 32."""
+    if T_max % V_BLOCK:
+        raise ValueError(f"T_max must be a multiple of {V_BLOCK}")
     k = torch.empty((B, N_KV_HEADS, T_max, HEAD_DIM), dtype=torch.bfloat16, device=device)
-    v = torch.empty((B, N_KV_HEADS, HEAD_DIM, T_max), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, N_KV_HEADS, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dtype=torch.bfloat16,
+                    device=device)
     return k, v
 
 
@@ -133,9 +138,45 @@ def kcache_by_position(kcache: torch.Tensor) -> torch.Tensor:
     return kcache.permute(0, 2, 1, 3)
 
 
-def vcache_by_position(vcache: torch.Tensor) -> torch.Tensor:
-    """View [B, T_max, 8, 128] of the dimension-major value cache."""
-    return vcache.permute(0, 3, 1, 2)
+def vcache_blocks(vcache: torch.Tensor) -> torch.Tensor:
+    """View [B, T_max/32, 32, 8, 128] of the blocked value cache: block,
+    position within the block, kv head, dim."""
+    return vcache.permute(0, 2, 4, 1, 3)
+
+
+def _block_pieces(lo: int, hi: int):
+    """Split positions [lo, hi) into (block, first, last) pieces of 32-blocks."""
+    pos = lo
+    while pos < hi:
+        blk, r0 = divmod(pos, V_BLOCK)
+        r1 = min(V_BLOCK, r0 + hi - pos)
+        yield blk, r0, r1
+        pos += r1 - r0
+
+
+def vcache_read(vcache: torch.Tensor, lo: int, hi: int) -> torch.Tensor:
+    """Copy of value rows [lo, hi) as [B, hi - lo, 8, 128]."""
+    v5 = vcache_blocks(vcache)
+    return torch.cat([v5[:, b, r0:r1] for b, r0, r1 in _block_pieces(lo, hi)], dim=1)
+
+
+def vcache_write(vcache: torch.Tensor, lo: int, rows: torch.Tensor) -> None:
+    """Store rows [B, n, 8, 128] at positions lo .. lo + n - 1."""
+    v5 = vcache_blocks(vcache)
+    off = 0
+    n = rows.shape[1]
+    first_full = -(-lo // V_BLOCK)
+    last_full = (lo + n) // V_BLOCK
+    for b, r0, r1 in _block_pieces(lo, lo + n):
+        if first_full <= b < last_full and r0 == 0 and r1 == V_BLOCK:
+            if b == first_full:   # all full blocks in one strided copy
+                nb = last_full - first_full
+                v5[:, b:b + nb] = rows[:, off:off + nb * V_BLOCK].reshape(
+                    rows.shape[0], nb, V_BLOCK, N_KV_HEADS, HEAD_DIM)
+                off += nb * V_BLOCK
+            continue
+        v5[:, b, r0:r1] = rows[:, off:off + r1 - r0]
+        off += r1 - r0
 
 
 class HipEvents:
@@ -207,7 +248,8 @@ def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope):
         raise ValueError("kcache must be [B, 8, T_max, 128]")
     B, T_max = kcache.shape[0], kcache.shape[2]
     _need(kcache, "kcache", torch.bfloat16, (B, N_KV_HEADS, T_max, HEAD_DIM), dev)
-    _need(vcache, "vcache", torch.bfloat16, (B, N_KV_HEADS, HEAD_DIM, T_max), dev)
+    _need(vcache, "vcache", torch.bfloat16,
+          (B, N_KV_HEADS, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dev)
     if rope.dim() != 3 or rope.shape[0] < T_max:
         raise ValueError("rope must be [>= T_max, 64, 2]")
     _need(rope, "rope", torch.float32, (rope.shape[0], ROPE_PAIRS, 2), dev)

@@ -29,14 +29,17 @@
  *     crosses this interface.
  *   - Returns GQA_OK (0) or a negative gqa_status.
  *
- * KV cache layout (bf16, updated in place; T_max = rows per sequence):
- *   kcache [B][8][T_max][128]   key of position t, kv head g, dim d at
- *                               ((b*8 + g)*T_max + t)*128 + d
- *   vcache [B][8][128][T_max]   value of position t, kv head g, dim d at
- *                               ((b*8 + g)*128 + d)*T_max + t
- * Keys are head-major so that a run of positions of one head is contiguous;
- * values are stored dimension-major so that the positions one probability
- * multiplies are contiguous for the matrix cores.  A call writes exactly the
+ * KV cache layout (bf16, updated in place; T_max = rows per sequence, a
+ * multiple of 32):
+ *   kcache [B][8][T_max][128]        key of position t, kv head g, dim d at
+ *                                    ((b*8 + g)*T_max + t)*128 + d
+ *   vcache [B][8][T_max/32][128][32] value of position t, kv head g, dim d at
+ *                                    ((b*8 + g)*(T_max/32) + t/32)*4096
+ *                                      + d*32 + t%32
+ * Keys are head-major so that a run of positions of one head is contiguous.
+ * Values come in blocks of 32 positions stored dimension-major, so the
+ * positions that one probability multiplies are contiguous for the matrix
+ * cores while a 32-position block stays one contiguous 8 KiB piece.  A call writes exactly the
  * rows start_pos .. start_pos+T-1 of sequences 0..B-1 and leaves every other
  * element bit-for-bit unchanged.  The appended values are the post-RoPE keys
  * and the values rounded to bf16 (nearest, ties to even); attention reads the
@@ -63,6 +66,7 @@ extern "C" {
 #define GQA_HEAD_DIM    128
 #define GQA_QKV_DIM     6144            /* 4096 (Q) + 1024 (K) + 1024 (V) */
 #define GQA_ROPE_PAIRS  64
+#define GQA_V_BLOCK     32              /* positions per value-cache block */
 #define GQA_MAX_BATCH   1024
 #define GQA_MAX_T_MAX   (1 << 20)
 
@@ -77,7 +81,7 @@ typedef enum {
     GQA_ERR_NULL      = -1,  /* a required pointer is NULL */
     GQA_ERR_SHAPE     = -2,  /* B, T or T_max outside the supported range */
     GQA_ERR_RANGE     = -3,  /* start_pos < 0 or start_pos + T > T_max */
-    GQA_ERR_ALIGN     = -4,  /* a pointer is not 16-byte aligned, or T_max % 8 != 0 */
+    GQA_ERR_ALIGN     = -4,  /* a pointer is not 16-byte aligned, or T_max % 32 != 0 */
     GQA_ERR_WORKSPACE = -5,  /* ws_bytes < gqa_workspace_bytes(...) */
     GQA_ERR_HIP       = -6,  /* a HIP call or kernel launch failed */
     GQA_ERR_ALIAS     = -7,  /* an output overlaps an input or another output */

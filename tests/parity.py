@@ -98,7 +98,7 @@ class DecodeCase:
             self.kcache.copy_(synth.sentinel_like(self.kcache.shape, self.dev))
             self.vcache.copy_(synth.sentinel_like(self.vcache.shape, self.dev))
             G.kcache_by_position(self.kcache)[:, :P] = self.kc_rows.to(self.dev)
-            G.vcache_by_position(self.vcache)[:, :P] = self.vc_rows.to(self.dev)
+            G.vcache_write(self.vcache, 0, self.vc_rows.to(self.dev))
         else:
             # large caches: x and weights from the host generator, cache values
             # drawn on the device straight into the cache buffers
@@ -108,9 +108,9 @@ class DecodeCase:
             dgen = synth.generator(seed + 1, self.dev)
             synth.fill_randn_bf16_(self.kcache, dgen)
             synth.fill_randn_bf16_(self.vcache, dgen)
-            sent = synth.sentinel_like((1,), self.dev)
-            G.kcache_by_position(self.kcache)[:, P:] = sent
-            G.vcache_by_position(self.vcache)[:, P:] = sent
+            n = T_max - P
+            G.kcache_by_position(self.kcache)[:, P:] = synth.sentinel_like((B, n, 8, 128), self.dev)
+            G.vcache_write(self.vcache, P, synth.sentinel_like((B, n, 8, 128), self.dev))
             self.kc_rows = self.vc_rows = None
         self.k_before = self.kcache.clone()
         self.v_before = self.vcache.clone()
@@ -134,7 +134,7 @@ class DecodeCase:
             kc, vc = f64(self.kc_rows[seqs]), f64(self.vc_rows[seqs])
         else:   # the generator's values, as staged before the call
             kc = f64(G.kcache_by_position(self.k_before)[seqs, :self.P])
-            vc = f64(G.vcache_by_position(self.v_before)[seqs, :self.P])
+            vc = f64(G.vcache_read(self.v_before[seqs], 0, self.P))
         return O.gqa_block(x, *w, kc, vc, self.P, self.theta, self.scaled)
 
     def check(self, res, seqs=None):
@@ -150,25 +150,29 @@ class DecodeCase:
             errs["k"] = assert_close("K", pr[:, 4096:5120], res.k.reshape(B, 1024))
             errs["v"] = assert_close("V", pr[:, 5120:], res.v.reshape(B, 1024))
         kpos = G.kcache_by_position(self.kcache)
-        vpos = G.vcache_by_position(self.vcache)
+        vrow = G.vcache_read(self.vcache[seqs], P, P + 1)[:, 0]
         kp = vp = None
         if self.probe is not None:
             kp = pr[:, 4096:5120].reshape(B, 8, 128)
             vp = pr[:, 5120:].reshape(B, 8, 128)
         errs["k_flips"] = assert_bf16_rows("kcache row", bits(kpos[seqs, P]), res.k_bits[:, 0], kp)
-        errs["v_flips"] = assert_bf16_rows("vcache row", bits(vpos[seqs, P]), res.v_bits[:, 0], vp)
+        errs["v_flips"] = assert_bf16_rows("vcache row", bits(vrow), res.v_bits[:, 0], vp)
         log_errs(f"decode B={self.B} P={P} seqs={seqs if len(seqs) < self.B else 'all'}", errs)
         return errs
 
     def check_untouched(self):
         """Every cache element except row P is bit-identical to before."""
-        for cur, before, pos_view in ((self.kcache, self.k_before, G.kcache_by_position),
-                                      (self.vcache, self.v_before, G.vcache_by_position)):
-            a = pos_view(cur).contiguous().view(torch.int16)
-            b = pos_view(before).contiguous().view(torch.int16)
-            a[:, self.P] = 0
-            b[:, self.P] = 0
-            assert torch.equal(a, b), "cache elements outside row start_pos changed"
+        P = self.P
+        a = self.kcache.clone()
+        b = self.k_before.clone()
+        G.kcache_by_position(a)[:, P] = 0
+        G.kcache_by_position(b)[:, P] = 0
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "key cache changed off row P"
+        a = self.vcache.clone()
+        b = self.v_before.clone()
+        G.vcache_blocks(a)[:, P // G.V_BLOCK, P % G.V_BLOCK] = 0
+        G.vcache_blocks(b)[:, P // G.V_BLOCK, P % G.V_BLOCK] = 0
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "value cache changed off row P"
 
 
 class PrefillCase:
@@ -210,21 +214,24 @@ class PrefillCase:
             errs["k"] = assert_close("K", pr[..., 4096:5120], res.k.reshape(B, T, 1024))
             errs["v"] = assert_close("V", pr[..., 5120:], res.v.reshape(B, T, 1024))
         kpos = G.kcache_by_position(self.kcache)
-        vpos = G.vcache_by_position(self.vcache)
+        vrows = G.vcache_read(self.vcache[seqs], 0, T)
         kp = vp = None
         if self.probe is not None:
             kp = pr[..., 4096:5120].reshape(B, T, 8, 128)
             vp = pr[..., 5120:].reshape(B, T, 8, 128)
         errs["k_flips"] = assert_bf16_rows("kcache rows", bits(kpos[seqs, :T]), res.k_bits, kp)
-        errs["v_flips"] = assert_bf16_rows("vcache rows", bits(vpos[seqs, :T]), res.v_bits, vp)
+        errs["v_flips"] = assert_bf16_rows("vcache rows", bits(vrows), res.v_bits, vp)
         log_errs(f"prefill B={self.B} T={T}", errs)
         return errs
 
     def check_untouched(self):
         """Rows T.. of every sequence keep their bits (the sentinel)."""
-        for cur, before, pos_view in ((self.kcache, self.k_before, G.kcache_by_position),
-                                      (self.vcache, self.v_before, G.vcache_by_position)):
-            a = pos_view(cur)[:, self.T:].contiguous().view(torch.int16)
-            b = pos_view(before)[:, self.T:].contiguous().view(torch.int16)
-            assert torch.equal(a, b), "cache rows at or after T changed"
-            assert bool((b == synth.SENTINEL_BITS).all())
+        T, T_max = self.T, self.T_max
+        if T == T_max:
+            return
+        a = G.kcache_by_position(self.kcache)[:, T:].contiguous().view(torch.int16)
+        b = G.kcache_by_position(self.k_before)[:, T:].contiguous().view(torch.int16)
+        assert torch.equal(a, b) and bool((b == synth.SENTINEL_BITS).all()), "key rows >= T changed"
+        a = G.vcache_read(self.vcache, T, T_max).view(torch.int16)
+        b = G.vcache_read(self.v_before, T, T_max).view(torch.int16)
+        assert torch.equal(a, b) and bool((b == synth.SENTINEL_BITS).all()), "value rows >= T changed"

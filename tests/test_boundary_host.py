@@ -94,7 +94,7 @@ def _prefill_args(**kw):
     (dict(x=None), ENULL), (dict(wo=None), ENULL), (dict(kc=None), ENULL), (dict(ws=None), ENULL),
     (dict(rope=None), ENULL), (dict(out=None), ENULL),
     (dict(B=0), ESHAPE), (dict(B=100000), ESHAPE), (dict(T_max=0), ESHAPE),
-    (dict(T_max=1004), EALIGN), (dict(x=ctypes.c_void_p(BASE + 2)), EALIGN),
+    (dict(T_max=1004), EALIGN), (dict(T_max=1000), EALIGN), (dict(x=ctypes.c_void_p(BASE + 2)), EALIGN),
     (dict(probe=ctypes.c_void_p(BASE + (20 << 32) + 4)), EALIGN),
     (dict(start_pos=-1), ERANGE), (dict(start_pos=1024), ERANGE),
     (dict(ws_bytes=1024), EWS), (dict(accumulate=2), EARG),

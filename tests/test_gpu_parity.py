@@ -74,7 +74,7 @@ def test_decode_batches(B):
 
 def test_decode_unscaled_rope():
     """Llama 3 setting (use_scaled_rope False) at a position where scaling matters."""
-    _decode_full(1, 5000, 5008, scaled=False)
+    _decode_full(1, 5000, 5024, scaled=False)
 
 
 def test_decode_accumulate_and_bf16_out():
@@ -97,7 +97,7 @@ def test_decode_batched_b64_p8192_sampled():
     """B=64 sequences with 8,192 cached positions each (caches ~2 GiB), one new
     token each; sampled sequences against the oracle, every cache bit outside
     row 8,192 unchanged."""
-    c = DecodeCase(64, 8192, 8200, dev=DEV, cache_on_device=True)
+    c = DecodeCase(64, 8192, 8224, dev=DEV, cache_on_device=True)
     c.run()
     seqs = [0, 13, 63]
     c.check(c.oracle(seqs), seqs)
@@ -130,7 +130,7 @@ def test_decode_rejects_small_workspace_without_side_effects():
 @pytest.mark.parametrize("B,T", [(1, 1), (2, 63), (1, 64), (2, 65), (3, 130), (1, 257),
                                  (2, 300)])
 def test_prefill_small(B, T):
-    c = PrefillCase(B, T, ((T + 7) // 8) * 8 + 8, dev=DEV)
+    c = PrefillCase(B, T, ((T + 31) // 32) * 32 + 32, dev=DEV)
     c.run()
     c.check(c.oracle())
     c.check_untouched()
@@ -174,7 +174,7 @@ def test_decode_after_prefill_equals_prefill_1001():
     assert_close("decode vs gpu prefill", f64(out), f64(full.out[:, T]))
     # rows 0..999 come from the same GEMM tiles on both routes: bit-identical;
     # row 1000 (GEMV vs GEMM summation order) may sit one bf16 step away
-    for view, a, b in ((G.kcache_by_position, kc, full.kcache),
-                       (G.vcache_by_position, vc, full.vcache)):
-        assert np.array_equal(bits(view(a)[:, :T]), bits(view(b)[:, :T]))
+    assert np.array_equal(bits(G.kcache_by_position(kc)[:, :T]),
+                          bits(G.kcache_by_position(full.kcache)[:, :T]))
+    assert np.array_equal(bits(G.vcache_read(vc, 0, T)), bits(G.vcache_read(full.vcache, 0, T)))
     assert_bf16_rows("row 1000", bits(G.kcache_by_position(kc)[:, T]), ref.k_bits[:, T])
