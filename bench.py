@@ -64,7 +64,7 @@ def _events_ms(ev, i, j):
     return ev.elapsed_ms(i, j)
 
 
-def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024):
+def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use_graph=True):
     dev = torch.device("cuda:0")
     sets = []
     for s in range(N_SETS):
@@ -102,6 +102,37 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024):
     ms = t0.elapsed_time(t1)
     us_step = ms * 1000.0 / steps
 
+    # the same steps replayed from a captured HIP graph (8 steps per graph,
+    # one per weight set), which removes the host-side launch cost
+    graph_us = None
+    if use_graph:
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    step(i)
+            return g
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(N_SETS):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        g8 = capture(N_SETS)
+        rem = steps % N_SETS
+        grem = capture(rem) if rem else None
+        for _ in range(3):
+            g8.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps // N_SETS):
+            g8.replay()
+        if grem is not None:
+            grem.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        graph_us = t0.elapsed_time(t1) * 1000.0 / steps
+
     # the same loop through the profiled entry point: HIP events recorded on
     # the library's stream around each kernel
     ev = G.HipEvents(G.DECODE_STAGES + 1)
@@ -112,7 +143,7 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024):
             per[i, k] = ev.elapsed_ms(k, k + 1)
     ev.close()
     kern_us = per.mean(axis=0) * 1000.0
-    return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps,
+    return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps, graph_us_step=graph_us,
                 kern_us=dict(zip(["qkv", "attn", "wo"], kern_us.tolist())),
                 profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
 
@@ -180,6 +211,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill record")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -195,20 +227,23 @@ def main():
         sys.exit(2)
 
     B, P = 1, 1000
-    dec = bench_decode(G, synth, args.steps, args.warmup, B, P)
+    dec = bench_decode(G, synth, args.steps, args.warmup, B, P, use_graph=not args.no_graph)
+    # headline: HIP-graph replay when available (what a serving loop runs),
+    # with the eager figure reported beside it
+    headline_us = dec["graph_us_step"] if dec["graph_us_step"] is not None else dec["us_step"]
     nb = decode_bytes(B, P)
-    step_tbs = nb["step"] / (dec["us_step"] * 1e-6) / 1e12
+    step_tbs = nb["step"] / (headline_us * 1e-6) / 1e12
     qkv_us = dec["kern_us"]["qkv"]
     qkv_gbs = nb["qkv"] / (qkv_us * 1e-6) / 1e9
 
     record = {
         "metric": METRIC,
-        "value": round(dec["us_step"], 3),
+        "value": round(headline_us, 3),
         "unit": "us/block-step",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": dec["us_step"] / 1000.0,
+        "ms_per_step": headline_us / 1000.0,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -217,10 +252,13 @@ def main():
         "config": {"workload": "Llama-3.1-8B GQA block decode, B=1, P=1000 (write row 1000, "
                                "read rows 0-1000)",
                    "B": B, "P": P, "T_max": 1024, "d": 4096, "heads": 32, "kv_heads": 8,
-                   "head_dim": 128, "rope": "scaled, theta=5e5", "hip_graph": False},
+                   "head_dim": 128, "rope": "scaled, theta=5e5",
+                   "hip_graph": dec["graph_us_step"] is not None},
         "hbm_tbs": round(step_tbs, 4),
         "hbm_frac_of_peak": round(step_tbs * 1000.0 / HBM_PEAK_GBS, 4),
-        "tokens_per_s": B / (dec["us_step"] * 1e-6),
+        "tokens_per_s": B / (headline_us * 1e-6),
+        "eager_us_step": round(dec["us_step"], 3),
+        "host_us_per_eager_step": round(dec["wall_us_step"], 3),
         "algorithmic_bytes_per_step": nb["step"],
         "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
         "profiled_us_step": round(dec["profiled_us_step"], 3),

@@ -108,6 +108,11 @@ __device__ __forceinline__ u32x4 ld_nt_u32x4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Device-scope coherent scalar load (reads past other XCDs' L2 caches).
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -25,16 +25,8 @@ namespace gqa {
 // (the vector is the sum of its parts); products use the packed bf16 dot
 // instruction with fp32 accumulation.
 template <int NB, int NPARTS>
-__device__ __forceinline__ void gemv_rows2(const uint16_t* __restrict__ w0,
-                                           const uint16_t* __restrict__ w1,
+__device__ __forceinline__ void gemv_rows2(const u32x4 (&a)[8], const u32x4 (&b)[8],
                                            const uint32_t* xs, int lane, float (&acc)[2][NB]) {
-  u32x4 a[8], b[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int e = (c * 64 + lane) * 8;
-    a[c] = ld_nt_u32x4(w0 + e);
-    b[c] = ld_nt_u32x4(w1 + e);
-  }
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[0][t] = acc[1][t] = 0.f;
 #pragma unroll
@@ -61,6 +53,18 @@ __device__ __forceinline__ void gemv_rows2(const uint16_t* __restrict__ w0,
   }
 }
 
+// Issue the 16 loads of two weight rows (lane l: pieces (c*64 + l)*8, c < 8).
+__device__ __forceinline__ void load_rows2(const uint16_t* __restrict__ w0,
+                                           const uint16_t* __restrict__ w1, int lane,
+                                           u32x4 (&a)[8], u32x4 (&b)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int e = (c * 64 + lane) * 8;
+    a[c] = ld_nt_u32x4(w0 + e);
+    b[c] = ld_nt_u32x4(w1 + e);
+  }
+}
+
 // Copy NB rows of 4096 bf16 (one part) from global into LDS.
 template <int NB>
 __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restrict__ src) {
@@ -77,13 +81,6 @@ __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restr
 template <int NB>
 __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[NB * (D / 2)];
-  stage_rows<NB>(xs, p.x + (size_t)b0 * D);
-  if (blockIdx.x == 0 && b0 == 0) {
-    // the attention kernel that follows counts split arrivals from zero
-    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
-  }
-  __syncthreads();
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = (blockIdx.x * 4 + wave) * 2;     // even output feature, 0..6142
   const uint16_t* wbase;
@@ -95,8 +92,19 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
   } else {
     wbase = p.wv; rr = r0 - D - KVH * HD;
   }
+  // the weight stream does not depend on x: start it before staging x
+  u32x4 wa[8], wb[8];
+  load_rows2(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, lane, wa, wb);
+
+  stage_rows<NB>(xs, p.x + (size_t)b0 * D);
+  if (blockIdx.x == 0 && b0 == 0) {
+    // the attention kernel that follows counts split arrivals from zero
+    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+  }
+  __syncthreads();
+
   float acc[2][NB];
-  gemv_rows2<NB, 1>(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, xs, lane, acc);
+  gemv_rows2<NB, 1>(wa, wb, xs, lane, acc);
 
   float v0 = 0.f, v1 = 0.f;
 #pragma unroll
@@ -138,7 +146,7 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // ---------------------------------------------------------------------------
 // Flash-decode on the matrix cores
 // ---------------------------------------------------------------------------
-//
+
 // Workgroup (split, g, b) owns positions [split*chunk, min(L, (split+1)*chunk))
 // of kv head g of sequence b and serves its 4 query heads.  Each wave steps
 // over 32-position tiles:
@@ -152,8 +160,10 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // The A-operand rows of the score tiles are assigned to positions so that
 // each lane's 8 score values are 8 consecutive positions: exactly the B
 // operand of the following P.V instruction, with no data movement.
-__global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
+  const int split = blockIdx.x % p.nsplit;
+  const int g = (blockIdx.x / p.nsplit) % KVH;
+  const int b = blockIdx.x / (p.nsplit * KVH);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
   const int head = col & 3;
@@ -168,6 +178,30 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
   __shared__ float sm_m[kAttnWaves][REP];
   __shared__ float sm_l[kAttnWaves][REP];
   __shared__ int sm_last;
+
+  const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
+  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * (T_max / VB) * (HD * VB);
+
+  // Loads of one 32-position tile (tiles start at multiples of 32, so a tile
+  // is one value-cache block).  Key rows past the last visible position are
+  // clamped onto it (their scores are masked); value positions past it are
+  // cleared after the load, since the cache may hold anything there.
+  auto load_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks);
+    }
+    const uint16_t* vblk = vbase + (size_t)(tile / VB) * (HD * VB) + rg * 8;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
+  };
+
+  // the first tile's loads go out before the Q loads, so both round trips overlap
+  u32x4 kf[2][4], vf[8];
+  int tile = j_begin + w * kAttnTile;
+  if (tile < j_end) load_tile(tile, kf, vf);
 
   // Q fragments, pre-scaled by log2(e)/sqrt(128)
   u32x4 qf[4];
@@ -194,29 +228,10 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
     }
   }
 
-  const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
-  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * (T_max / VB) * (HD * VB);
-
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Loads of one 32-position tile (tiles start at multiples of 32, so a tile
-  // is one value-cache block).  Key rows past the last visible position are
-  // clamped onto it (their scores are masked); value positions past it are
-  // cleared after the load, since the cache may hold anything there.
-  auto load_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks);
-    }
-    const uint16_t* vblk = vbase + (size_t)(tile / VB) * (HD * VB) + rg * 8;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
-  };
 
   auto compute_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
     const int jv = tile + rg * 8;
@@ -284,21 +299,12 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
     }
   };
 
-  // software pipeline: the next tile's loads are in flight during this one's math
-  constexpr int kStride = kAttnWaves * kAttnTile;
-  u32x4 kA[2][4], vA[8], kB[2][4], vB[8];
-  int tile = j_begin + w * kAttnTile;
-  if (tile < j_end) load_tile(tile, kA, vA);
+  // One tile in registers per wave; latency is hidden by the other waves
+  // resident on the SIMD (the kernel is sized for 3 waves per SIMD).
   while (tile < j_end) {
-    int next = tile + kStride;
-    if (next < j_end) load_tile(next, kB, vB);
-    compute_tile(tile, kA, vA);
-    tile = next;
-    if (tile >= j_end) break;
-    next = tile + kStride;
-    if (next < j_end) load_tile(next, kA, vA);
-    compute_tile(tile, kB, vB);
-    tile = next;
+    compute_tile(tile, kf, vf);
+    tile += kAttnWaves * kAttnTile;
+    if (tile < j_end) load_tile(tile, kf, vf);
   }
 
   // wave result: l summed over the 4 lane rows, O = hi column + lo column
@@ -344,58 +350,59 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
     return;
   }
 
+  // Publish this split's partial without an L2 write-back: device-scope
+  // stores go through to the coherence point shared by all XCDs, the wait
+  // makes sure they have landed, then a relaxed device-scope count.  The
+  // last workgroup to arrive reads every partial with device-scope loads.
   const size_t split_stride = (size_t)REP * kPartStride;
   float* part0 = p.part + ((size_t)(b * KVH + g) * p.nsplit) * split_stride + (size_t)mh * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
   if (d2 == 0) {
-    mine[0] = M;
-    mine[1] = lsum;
+    __hip_atomic_store(mine, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  mine[4 + d2] = o0;
-  mine[5 + d2] = o1;
-  __threadfence();
+  __hip_atomic_store(mine + 4 + d2, o0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(mine + 5 + d2, o1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(p.counters + b * KVH + g, 1, __ATOMIC_ACQ_REL,
+    const int prev = __hip_atomic_fetch_add(p.counters + b * KVH + g, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     sm_last = (prev == p.nsplit - 1);
   }
   __syncthreads();
   if (!sm_last) return;
-  __threadfence();
 
-  // last workgroup of this (b, g): merge every split in a fixed order, with
-  // the loads of 8 splits in flight at a time
+  // last workgroup of this (b, g): merge every split in a fixed order, one
+  // round trip per 8 splits, rescaling the running sums as the maximum grows
   constexpr int U = 8;
-  float GM = -INFINITY;
-  for (int s0 = 0; s0 < p.nsplit; s0 += U) {
-    float mv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      mv[u] = (s0 + u < p.nsplit) ? __builtin_nontemporal_load(part0 + (s0 + u) * split_stride)
-                                  : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) GM = fmaxf(GM, mv[u]);
-  }
-  float gl = 0.f, g0 = 0.f, g1 = 0.f;
+  float GM = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
   for (int s0 = 0; s0 < p.nsplit; s0 += U) {
     float mv[U], lv[U], ov0[U], ov1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s0 + u < p.nsplit;
       const float* ps = part0 + (ok ? s0 + u : 0) * split_stride;
-      mv[u] = ok ? __builtin_nontemporal_load(ps) : -INFINITY;
-      lv[u] = __builtin_nontemporal_load(ps + 1);
-      ov0[u] = __builtin_nontemporal_load(ps + 4 + d2);
-      ov1[u] = __builtin_nontemporal_load(ps + 5 + d2);
+      mv[u] = ok ? ld_dev(ps) : -INFINITY;
+      lv[u] = ld_dev(ps + 1);
+      ov0[u] = ld_dev(ps + 4 + d2);
+      ov1[u] = ld_dev(ps + 5 + d2);
     }
+    float cm = GM;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cm = fmaxf(cm, mv[u]);
+    const float r = __builtin_amdgcn_exp2f(GM - cm);
+    gl *= r;
+    g0 *= r;
+    g1 *= r;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = __builtin_amdgcn_exp2f(mv[u] - GM);
+      const float f = __builtin_amdgcn_exp2f(mv[u] - cm);
       gl += lv[u] * f;
       g0 += ov0[u] * f;
       g1 += ov1[u] * f;
     }
+    GM = cm;
   }
   const float r0 = g0 / gl, r1 = g1 / gl;
   const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);
@@ -403,7 +410,7 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
   const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
   *reinterpret_cast<uint32_t*>(p.o_hi + out_off) = h0 | (h1 << 16);
   *reinterpret_cast<uint32_t*>(p.o_lo + out_off) = lo0 | (lo1 << 16);
-  if (tid == 0) p.counters[b * KVH + g] = 0;
+  if (tid == 0) __hip_atomic_store(p.counters + b * KVH + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,14 +420,16 @@ __global__ void __launch_bounds__(256, 2) decode_attn_kernel(DecodeParams p) {
 template <int NB>
 __global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[2 * NB * (D / 2)];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + wave) * 2;
+  u32x4 wa[8], wb[8];
+  load_rows2(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, lane, wa, wb);
   stage_rows<NB>(xs, p.o_hi + (size_t)b0 * D);
   stage_rows<NB>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = (blockIdx.x * 4 + wave) * 2;
   float acc[2][NB];
-  gemv_rows2<NB, 2>(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, xs, lane, acc);
+  gemv_rows2<NB, 2>(wa, wb, xs, lane, acc);
 
   float v0 = 0.f, v1 = 0.f;
 #pragma unroll
@@ -441,6 +450,133 @@ __global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) 
   *o = r;
   if (p.out_bf16)
     *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
+}
+
+// ---------------------------------------------------------------------------
+// Batched decode projections on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// For more tokens than the bandwidth GEMV handles in one pass, the weights
+// are streamed once through v_mfma_f32_16x16x32_bf16:
+//   C^T[16 features x 16 columns] += W[16 features x k] . X^T[k x 16 columns]
+// A workgroup owns 16 output features; its 8 waves split K = 4096 into
+// slices of 512.  Lane (r = lane & 15, q = lane >> 4) loads W[f0 + r][slice
+// + 32 ks + 8 q .. +8] for ks < 16: exactly its A operand, 16 KiB per wave in
+// flight, as in the GEMV.  The B operand (activation columns) is read from
+// L2.  Slices are summed in LDS; each lane of the result then holds 4
+// consecutive features of one column, so RoPE pairs are register-local.
+// Columns are tokens for the QKV projection, and (token, hi/lo part) pairs
+// for wo, whose input O is the sum of two bf16 parts.
+constexpr int kProjWaves = 8;
+constexpr int kProjTiles = 4;            // column tiles of 16 per pass
+
+template <int MODE>   // 0: QKV + RoPE + cache append, 1: wo (+ residual)
+__global__ void __launch_bounds__(512) decode_proj_mfma_kernel(DecodeParams p) {
+  __shared__ f32x4 red[kProjWaves][kProjTiles][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int f0 = blockIdx.x * 16;
+  if (MODE == 0 && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+  }
+
+  const uint16_t* wrow;
+  if (MODE == 0) {
+    const int f = f0 + r;
+    wrow = f < D ? p.wq + (size_t)f * D
+                 : (f < D + KVH * HD ? p.wk + (size_t)(f - D) * D
+                                     : p.wv + (size_t)(f - D - KVH * HD) * D);
+  } else {
+    wrow = p.wo + (size_t)(f0 + r) * D;
+  }
+  const int k0 = w * (D / kProjWaves) + q * 8;
+  u32x4 wa[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) wa[ks] = ld_nt_u32x4(wrow + k0 + ks * 32);
+
+  const int ncols = MODE == 0 ? p.B : 2 * p.B;
+  for (int c0 = 0; c0 < ncols; c0 += 16 * kProjTiles) {
+    f32x4 acc[kProjTiles];
+#pragma unroll
+    for (int t = 0; t < kProjTiles; ++t) {
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int c = c0 + t * 16 + r;
+      if (c0 + t * 16 >= ncols) continue;                       // wave-uniform
+      const int cc = min(c, ncols - 1);
+      const uint16_t* xrow = MODE == 0 ? p.x + (size_t)cc * D
+                                       : ((cc & 1) ? p.o_lo : p.o_hi) + (size_t)(cc >> 1) * D;
+      u32x4 xb[16];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) xb[ks] = ld_u32x4(xrow + k0 + ks * 32);
+      if (c >= ncols) {
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) xb[ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) acc[t] = mfma_bf16(wa[ks], xb[ks], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < kProjTiles; ++t) red[w][t][lane] = acc[t];
+    __syncthreads();
+    if (w < kProjTiles && c0 + w * 16 < ncols) {
+      f32x4 v = red[0][w][lane];
+#pragma unroll
+      for (int ww = 1; ww < kProjWaves; ++ww) v += red[ww][w][lane];
+      // lane holds features f0 + 4q + e (e < 4) of column c0 + 16w + r
+      const int c = c0 + w * 16 + r;
+      const int f = f0 + 4 * q;
+      if (MODE == 0) {
+        if (c < ncols) {
+          const int b = c, pos = p.start_pos;
+          float y[4] = {v[0], v[1], v[2], v[3]};
+          if (f < D + KVH * HD) {
+            const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)pos * PAIRS;
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const float2 cs = rrow[((f + e) & (HD - 1)) >> 1];
+              const float a = y[e] * cs.x - y[e + 1] * cs.y;
+              const float bb = y[e] * cs.y + y[e + 1] * cs.x;
+              y[e] = a;
+              y[e + 1] = bb;
+            }
+          }
+          if (p.probe)
+            *reinterpret_cast<float4*>(p.probe + (size_t)b * NQKV + f) = make_float4(y[0], y[1], y[2], y[3]);
+          if (f < D) {
+            *reinterpret_cast<float4*>(p.q + (size_t)b * D + f) = make_float4(y[0], y[1], y[2], y[3]);
+          } else if (f < D + KVH * HD) {
+            const int ff = f - D, g = ff / HD, d = ff % HD;
+            uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          } else {
+            const int ff = f - D - KVH * HD, g = ff / HD, d = ff % HD;
+            uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
+          }
+        }
+      } else {
+        // columns 2t (hi part) and 2t+1 (lo part) of token t sit in lanes r, r^1
+        f32x4 other;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) other[e] = dpp<DPP_QUAD_XOR1>(v[e]);
+        if ((r & 1) == 0 && c < ncols) {
+          const int b = c >> 1;
+          float4 y = make_float4(v[0] + other[0], v[1] + other[1], v[2] + other[2], v[3] + other[3]);
+          float4* o = reinterpret_cast<float4*>(p.out + (size_t)b * D + f);
+          if (p.accumulate) {
+            const float4 prev = *o;
+            y.x += prev.x; y.y += prev.y; y.z += prev.z; y.w += prev.w;
+          }
+          *o = y;
+          if (p.out_bf16)
+            *reinterpret_cast<u32x2*>(p.out_bf16 + (size_t)b * D + f) =
+                u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)};
+        }
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -501,6 +637,10 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   }
 
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
+  if (p.B > kGemvMaxB) {
+    hipLaunchKernelGGL(decode_proj_mfma_kernel<0>, dim3(NQKV / 16), dim3(512), 0, s, p);
+    return hipGetLastError();
+  }
   const int blocks = NQKV / 2 / 4;    // one wave per row pair, 4 waves per workgroup
   for (int b0 = 0; b0 < p.B; b0 += kGemvMaxNB) {
     const int nb = min(kGemvMaxNB, p.B - b0);
@@ -513,11 +653,15 @@ hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(p.nsplit, KVH, p.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(decode_attn_kernel, dim3(p.nsplit * KVH * p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
+  if (p.B > kGemvMaxB) {
+    hipLaunchKernelGGL(decode_proj_mfma_kernel<1>, dim3(D / 16), dim3(512), 0, s, p);
+    return hipGetLastError();
+  }
   const int blocks = D / 2 / 4;
   for (int b0 = 0; b0 < p.B; b0 += kWoMaxNB) {
     const int nb = min(kWoMaxNB, p.B - b0);

@@ -17,6 +17,7 @@ constexpr int kAttnWaves = 4;        // waves per flash-decode workgroup
 constexpr int kMaxSplit = 64;        // most position splits per (sequence, kv head)
 constexpr int kPartStride = 132;     // floats per (split, head) partial: m, l, pad, pad, o[128]
 constexpr int kGemvMaxNB = 8;        // tokens per pass of the QKV bandwidth GEMV
+constexpr int kGemvMaxB = 8;         // larger batches use the matrix-core projections
 constexpr int kWoMaxNB = 4;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
 
 struct DecodeParams {

@@ -26,6 +26,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+constexpr float kLazyRescale = 8.f;   // log2 headroom before the softmax reference moves
+constexpr int AQ = kPrefillTile;      // queries per attention workgroup
+constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V^T block)
+
 // ---------------------------------------------------------------------------
 // Workspace
 // ---------------------------------------------------------------------------
@@ -61,23 +65,42 @@ void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
 // wo -> fp16
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) convert_wo_kernel(const uint16_t* __restrict__ src,
-                                                         uint16_t* __restrict__ dst, int n8) {
+// Converts wo to fp16 and clears the positions [T, Tp) of the fp16 K and
+// V^T workspace copies (the attention tiles read them; they must be finite).
+__global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
+  const int n8 = D * D / 8;
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n8; i += gridDim.x * 256) {
-    const u32x4 v = ld_nt_u32x4(src + (size_t)i * 8);
+    const u32x4 v = ld_nt_u32x4(p.wo + (size_t)i * 8);
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t u = v[q];
       o[q] = pack_f16x2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
     }
-    *reinterpret_cast<u32x4*>(dst + (size_t)i * 8) = o;
+    *reinterpret_cast<u32x4*>(p.wo16 + (size_t)i * 8) = o;
+  }
+  const int pad = p.Tp - p.T;
+  if (pad == 0) return;
+  const int pairs = p.B * KVH;
+  // K rows: pairs * pad rows of 128; V^T: pairs * 128 dims of pad positions
+  const long nk = (long)pairs * pad * HD;
+  const long total = 2 * nk;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long e = i < nk ? i : i - nk;
+    const int pair = (int)(e / ((long)pad * HD));
+    const int r = (int)(e % ((long)pad * HD));
+    if (i < nk) {
+      const int t = p.T + r / HD, d = r % HD;
+      p.k16[((size_t)pair * p.Tp + t) * HD + d] = 0;
+    } else {
+      const int d = r / pad, t = p.T + r % pad;
+      p.v16t[(((size_t)pair * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] = 0;
+    }
   }
 }
 
 hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s) {
-  const int n8 = D * D / 8;
-  hipLaunchKernelGGL(convert_wo_kernel, dim3(2048), dim3(256), 0, s, p.wo, p.wo16, n8);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(2048), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -86,15 +109,14 @@ hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s) {
 // B [N][4096] both K-contiguous.
 // ---------------------------------------------------------------------------
 //
-// 4 waves in a 2 x 2 grid, each owning a 128 x 128 block of C as 8 x 8
-// 16x16 tiles.  A and B tiles stream from global memory straight into LDS
+// 8 waves in a 2 (M) x 4 (N) grid, each owning a 128 x 64 block of C as
+// 8 x 4 16x16 tiles (128 accumulators, so two waves fit on a SIMD without the
+// accumulators spilling into copies).  A and B tiles stream from global memory straight into LDS
 // (global_load_lds, 16 bytes a lane), double-buffered.  In LDS a tile row of
 // 64 elements is 8 chunks of 16 bytes stored at chunk ^ (row & 7), so the 16
 // rows one matrix-core operand read touches fall in distinct banks.
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int AQ = kPrefillTile;      // queries per attention workgroup
-constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V^T block)
 constexpr int kGemmLds = 2 * (GBM + GBN) * GBK * 2;   // 128 KiB
 constexpr int kGroupM = 4;                             // m-tiles per tile-order group
 
@@ -131,14 +153,14 @@ struct GemmArgs {
 };
 
 template <int REGION>
-__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][8], int mw,
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], int mw,
                                              int fw, int lane);
 
 template <int KIND>
-__global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
 
   // XCD-aware tile order: workgroup id i runs on XCD i % 8; give each XCD a
   // contiguous range of the grouped tile order so its L2 serves 4 m-tiles
@@ -155,16 +177,17 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
   const int nt0 = within / gm;
   const int m0 = mt0 * GBM, n0 = nt0 * GBN;
 
-  // per-lane global sources of the 8 A and 8 B load instructions of this wave
-  // (wave w fills tile rows w*64 .. w*64+63, 8 rows per instruction; lane l
-  // writes LDS chunk l & 7 of row l >> 3, holding logical chunk (l&7)^(l>>3))
+  // per-lane global sources of the 4 A and 4 B load instructions of this
+  // wave (wave w fills tile rows w*32 .. w*32+31, 8 rows per instruction;
+  // lane l writes LDS chunk l & 7 of row l >> 3, holding logical chunk
+  // (l & 7) ^ (l >> 3))
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow;
-  const uint16_t* a_src[8];
-  const uint16_t* b_src[8];
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 64 + i * 8 + lrow;
+  for (int i = 0; i < 4; ++i) {
+    const int r = w * 32 + i * 8 + lrow;
     const int am = min(m0 + r, g.M - 1);
     a_src[i] = g.a + (size_t)am * D + lchunk * 8;
     const int br = b_row_of<KIND>(n0, r);
@@ -175,17 +198,17 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
     char* sa = smem + stage * (GBM + GBN) * GBK * 2;
     char* sb = sa + GBM * GBK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_void*)(sa + (w * 64 + i * 8) * 128), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(b_src[i] + k0, (lds_void*)(sb + (w * 64 + i * 8) * 128), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_void*)(sa + (w * 32 + i * 8) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_src[i] + k0, (lds_void*)(sb + (w * 32 + i * 8) * 128), 16, 0, 0);
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int nk = D / GBK;
   load_stage(0, 0);
@@ -198,18 +221,21 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int chunk = ks * 4 + (lane >> 4);
-      u32x4 af[8], bf[8];
+      u32x4 af[8], bf[4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ra = wm * 128 + i * 16 + (lane & 15);
         af[i] = *reinterpret_cast<const u32x4*>(sa + ra * 128 + ((chunk ^ (ra & 7)) << 4));
-        const int rb = wn * 128 + i * 16 + (lane & 15);
-        bf[i] = *reinterpret_cast<const u32x4*>(sb + rb * 128 + ((chunk ^ (rb & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rb = wn * 64 + j * 16 + (lane & 15);
+        bf[j] = *reinterpret_cast<const u32x4*>(sb + rb * 128 + ((chunk ^ (rb & 7)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
           if (KIND == GEMM_QKV)
             acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
           else
@@ -219,23 +245,23 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
   }
 
   // epilogue: acc[i][j][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
-  //                             [tile col wn*128 + j*16 + (lane&15)]
+  //                             [tile col wn*64 + j*16 + (lane&15)]
   // The region (Q, K or V features) is uniform over the workgroup's n-tile,
   // so each region gets its own small, fully unrolled loop nest and the
   // accumulators stay in registers.
   if (KIND == GEMM_QKV) {
     if (n0 < D)
-      qkv_epilogue<0>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+      qkv_epilogue<0>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
     else if (n0 < D + KVH * HD)
-      qkv_epilogue<1>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+      qkv_epilogue<1>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
     else
-      qkv_epilogue<2>(g, acc, m0 + wm * 128, n0 + 128 * wn, lane);
+      qkv_epilogue<2>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = n0 + wn * 128 + j * 16 + (lane & 15);
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + wm * 128 + i * 16 + (lane >> 4) * 4 + e;
@@ -251,7 +277,7 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmArgs g) {
 // dimension-major cache, fp16 copy).  Column pair (acc[i][2u], acc[i][2u+1])
 // of lane l holds features (f, f+1) with f = fw + 32u + 2*(l & 15).
 template <int REGION>
-__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][8], int mw,
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], int mw,
                                              int fw, int lane) {
   const PrefillParams& p = g.p;
 #pragma unroll
@@ -263,7 +289,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
       const int b = m / p.T, t = m - b * p.T;
       const float2* rope_row = reinterpret_cast<const float2*>(p.rope) + (size_t)t * PAIRS;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int f = fw + 32 * u + 2 * (lane & 15);
         float a = acc[i][2 * u][e], c = acc[i][2 * u + 1][e];
         if (REGION < 2) {
@@ -305,7 +331,7 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
   if (e != hipSuccess) return e;
   const int tiles = ((g.M + GBM - 1) / GBM) * (g.N / GBN);
-  hipLaunchKernelGGL(gemm_kernel<KIND>, dim3(tiles), dim3(256), kGemmLds, s, g);
+  hipLaunchKernelGGL(gemm_kernel<KIND>, dim3(tiles), dim3(512), kGemmLds, s, g);
   return hipGetLastError();
 }
 
@@ -346,8 +372,8 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 // its query column, which is exactly its B operand for the P.V step.
 
 __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) char sK[AK * HD * 2];     // [64 keys][128 dims], 16 KiB
-  __shared__ __attribute__((aligned(16))) char sV[HD * AK * 2];     // [128 dims][64 keys], 16 KiB
+  // two stages of [64 keys][128 dims] K and [128 dims][64 keys] V^T, fp16
+  __shared__ __attribute__((aligned(16))) char sKV[2][2][AK * HD * 2];    // 64 KiB
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
@@ -359,6 +385,37 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
   const int h = g * REP + w;
   const int T = p.T, Tp = p.Tp;
 
+  const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
+  const uint16_t* vg = p.v16t + (size_t)bg * HD * Tp;
+
+  // Tile loads go straight to LDS (16 bytes a lane, a wave writes 1 KiB of
+  // consecutive LDS per instruction).  Each lane picks the global chunk that
+  // belongs at its LDS slot under the XOR swizzle: K rows (256 B) hold chunk
+  // c at c ^ (key & 15), V^T rows (128 B) hold chunk c at c ^ (dim & 7).
+  // Wave w fills K rows w*16 .. +16 and V^T rows w*32 .. +32.  Positions in
+  // [T, Tp) of the workspace copies are zero, so no masking is needed here.
+  const uint16_t* k_src[4];
+  const uint16_t* v_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = w * 16 + i * 4 + (lane >> 4);
+    k_src[i] = kg + (size_t)key * HD + (((lane & 15) ^ (key & 15)) * 8);
+    const int dim = w * 32 + i * 8 + (lane >> 3);
+    v_src[i] = vg + (size_t)dim * AK + (((lane & 7) ^ (dim & 7)) * 8);
+  }
+  auto issue_tile = [&](int kt, int stage) {
+    char* dk = sKV[stage][0];
+    char* dv = sKV[stage][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds(k_src[i] + (size_t)kt * AK * HD,
+                                       (lds_void*)(dk + (w * 16 + i * 4) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v_src[i] + (size_t)kt * (HD * AK),
+                                       (lds_void*)(dv + (w * 32 + i * 8) * 128), 16, 0, 0);
+    }
+  };
+  issue_tile(0, 0);
+
   // Q^T fragments: query qt*64 + nt*16 + col, dims rg*8 + 32*ks
   u32x4 qf[4][4];
 #pragma unroll
@@ -369,9 +426,6 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
       qf[nt][ks] = (t < T) ? ld_u32x4(p.q16 + ((size_t)b * T + t) * D + h * HD + rg * 8 + 32 * ks)
                            : u32x4{0u, 0u, 0u, 0u};
   }
-
-  const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
-  const uint16_t* vg = p.v16t + (size_t)bg * HD * Tp;
 
   f32x4 oacc[8][4];
 #pragma unroll
@@ -385,46 +439,14 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
     l_run[nt] = 0.f;
   }
 
-  // staging of one K/V tile: thread -> 4 K chunks and 4 V^T chunks of 16 bytes
-  u32x4 kreg[4], vreg[4];
-  auto fetch = [&](int kt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = tid + 256 * r;
-      const int key = i >> 4, c = i & 15;
-      const int j = kt * AK + key;
-      kreg[r] = (j < T) ? ld_u32x4(kg + (size_t)j * HD + c * 8) : u32x4{0u, 0u, 0u, 0u};
-      const int dim = i >> 3, cv = i & 7;
-      const int j0 = kt * AK + cv * 8;
-      u32x4 v = ld_u32x4(vg + (size_t)kt * (HD * AK) + dim * AK + cv * 8);
-      if (j0 + 8 > T) {
-        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = j0 + 2 * q;
-          u[q] &= (e + 1 < T) ? 0xffffffffu : (e < T ? 0x0000ffffu : 0u);
-        }
-      }
-      vreg[r] = v;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = tid + 256 * r;
-      const int key = i >> 4, c = i & 15;
-      *reinterpret_cast<u32x4*>(sK + key * 256 + ((c ^ (key & 15)) << 4)) = kreg[r];
-      const int dim = i >> 3, cv = i & 7;
-      *reinterpret_cast<u32x4*>(sV + dim * 128 + ((cv ^ (dim & 7)) << 4)) = vreg[r];
-    }
-  };
-
-  fetch(0);
   for (int kt = 0; kt <= qt; ++kt) {
-    __syncthreads();                 // previous tile's LDS reads are done
-    store();
+    // this tile has landed for every wave, and every wave is done reading
+    // the other stage, which the next tile's loads now overwrite
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt < qt) fetch(kt + 1);      // next tile's global loads overlap this tile's math
+    if (kt < qt) issue_tile(kt + 1, (kt + 1) & 1);
+    const char* sK = sKV[kt & 1][0];
+    const char* sV = sKV[kt & 1][1];
 
     // ---- scores ----
     f32x4 sacc[4][4];
@@ -446,29 +468,52 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
 
     // ---- online softmax per query column ----
     // sacc[mt][nt][e]: key kt*64 + 32*(mt>>1) + rg*8 + (mt&1)*4 + e, query nt*16 + col
-    const bool diag = (kt == qt);
-    u32x4 pf[4][2];
+    if (kt == qt) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int q = qt * AQ + nt * 16 + col;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
+            if (key > q) sacc[mt][nt][e] = -INFINITY;
+          }
+      }
+    }
+    float tmax[4];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int q = qt * AQ + nt * 16 + col;
-      float tmax = -INFINITY;
+      float t = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = sacc[mt][nt][e];
-          if (diag) {
-            const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
-            v = (key > q) ? -INFINITY : v;
-          }
-          sacc[mt][nt][e] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[nt], tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-      m_run[nt] = m_new;
+        for (int e = 0; e < 4; ++e) t = fmaxf(t, sacc[mt][nt][e]);
+      t = fmaxf(t, shfl_xor(t, 16));
+      t = fmaxf(t, shfl_xor(t, 32));
+      tmax[nt] = t;
+      grow |= t > m_run[nt] + kLazyRescale;
+    }
+    // Lazy rescaling: the reference maximum only moves (and O, l are only
+    // rescaled) when a column's maximum grows by more than 2^8 over it, so
+    // p = exp2(s - m) <= 256 (exact in range for fp16).  The decision is
+    // wave-uniform, and most tiles skip the rescale entirely.
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float m_new = fmaxf(m_run[nt], tmax[nt]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        m_run[nt] = m_new;
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
+      }
+    }
+    u32x4 pf[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const float m_ref = m_run[nt];
       float psum = 0.f;
       uint32_t pk[2][4];
 #pragma unroll
@@ -476,19 +521,17 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const int mt = half * 2 + sub;
-          const float p0 = __builtin_amdgcn_exp2f(sacc[mt][nt][0] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[mt][nt][1] - m_new);
-          const float p2 = __builtin_amdgcn_exp2f(sacc[mt][nt][2] - m_new);
-          const float p3 = __builtin_amdgcn_exp2f(sacc[mt][nt][3] - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(sacc[mt][nt][0] - m_ref);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[mt][nt][1] - m_ref);
+          const float p2 = __builtin_amdgcn_exp2f(sacc[mt][nt][2] - m_ref);
+          const float p3 = __builtin_amdgcn_exp2f(sacc[mt][nt][3] - m_ref);
           psum += (p0 + p1) + (p2 + p3);
           pk[half][sub * 2] = pack_f16x2(p0, p1);
           pk[half][sub * 2 + 1] = pack_f16x2(p2, p3);
         }
-      l_run[nt] = l_run[nt] * alpha + psum;
+      l_run[nt] += psum;
       pf[nt][0] = u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
       pf[nt][1] = u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
     }
 
     // ---- O^T += V^T P^T ----

@@ -111,6 +111,31 @@ def test_decode_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_decode_in_hip_graph_matches_eager():
+    """A captured decode call, replayed several times with eager work and
+    synchronisations between replays, reproduces the eager result bit for bit
+    (the library issues no memset, so nothing in the graph depends on one)."""
+    c = DecodeCase(2, 300, 320, dev=DEV)
+    eager = c.run(probe=False).clone()
+    out = torch.zeros_like(eager)
+    ws = G.workspace(2, 1, 320, DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        G.block_decode(c.xd, *c.wd, c.kcache, c.vcache, c.rope, c.P, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        G.block_decode(c.xd, *c.wd, c.kcache, c.vcache, c.rope, c.P, out=out, ws=ws)
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    c.check_untouched()
+
+
 def test_decode_rejects_small_workspace_without_side_effects():
     c = DecodeCase(1, 64, 128, dev=DEV)
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
