@@ -60,8 +60,21 @@ def prefill_flops(B: int, T: int) -> dict:
     return {"qkv": qkv, "attn": attn, "wo": wo, "total": qkv + attn + wo}
 
 
-def _events_ms(ev, i, j):
-    return ev.elapsed_ms(i, j)
+def counter_traffic(summary: str, source: str):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a known-size copy), as recorded in a profile summary; None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", summary)).read()
+        fields = dict(l.strip().split(": ", 1) for l in text.splitlines()
+                      if l.strip().startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256") != digest:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use_graph=True):
@@ -178,6 +191,107 @@ def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
                 kern_tflops={k: fl[k] / (kern[k] * 1e-6) / 1e12 for k in ("qkv", "attn", "wo")})
 
 
+def _timed_steps(step, steps, warmup, use_graph):
+    """Median-free whole-loop timing of `steps` calls of step(i) (graph replay
+    of the whole loop when use_graph), HIP events on the current stream."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        g.replay()
+        t1.record()
+    else:
+        t0.record()
+        for i in range(steps):
+            step(i)
+        t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1000.0 / steps
+
+
+def bench_batched(G, synth, steps, warmup, B=64, P=8192, T_max=8224):
+    """Batched decode: B=64 sequences, 8,192 cached positions each."""
+    dev = torch.device("cuda:0")
+    n_w = 4   # weight sets rotated (the 2.15 GB cache already defeats the MALL)
+    gen = synth.generator(0)
+    xs = [synth.randn_bf16(gen, (B, D)).to(dev) for _ in range(n_w)]
+    ws_sets = [[t.to(dev) for t in synth.block_weights(gen)] for _ in range(n_w)]
+    kc, vc = G.empty_caches(B, T_max, dev)
+    dgen = synth.generator(1, dev)
+    synth.fill_randn_bf16_(kc, dgen)
+    synth.fill_randn_bf16_(vc, dgen)
+    rope = G.rope_table(T_max, device=dev)
+    ws = G.workspace(B, 1, T_max, dev)
+    out = torch.empty((B, D), dtype=torch.float32, device=dev)
+
+    def step(i, events=None):
+        G.block_decode(xs[i % n_w], *ws_sets[i % n_w], kc, vc, rope, P, out=out, ws=ws,
+                       events=events)
+
+    us = _timed_steps(step, steps, warmup, True)
+    ev = G.HipEvents(G.DECODE_STAGES + 1)
+    per = np.zeros((steps, G.DECODE_STAGES))
+    for i in range(steps):
+        step(i, events=ev)
+        for k in range(G.DECODE_STAGES):
+            per[i, k] = ev.elapsed_ms(k, k + 1)
+    ev.close()
+    kern = dict(zip(["qkv", "attn", "wo"], (per.mean(axis=0) * 1000.0).tolist()))
+    nb = decode_bytes(B, P)
+    return us, kern, nb
+
+
+def bench_stacked(G, synth, steps, warmup, B=8, P=131071, T_max=131072, L=32):
+    """32 stacked blocks, B=8, 131,071 cached positions per sequence per
+    block (128 GiB of cache), residual h <- h + Delta, no norms or FFN."""
+    dev = torch.device("cuda:0")
+    dgen = synth.generator(0, dev)
+    x0 = synth.randn_bf16(dgen, (B, D), device=dev)
+    blocks = []
+    t_start = time.perf_counter()
+    for l in range(L):
+        w = synth.block_weights(dgen, device=dev)
+        kc, vc = G.empty_caches(B, T_max, dev)
+        synth.fill_randn_bf16_(kc, dgen)
+        synth.fill_randn_bf16_(vc, dgen)
+        blocks.append((w, kc, vc))
+        torch.cuda.synchronize()
+        print(f"stacked: block {l + 1}/{L} staged ({time.perf_counter() - t_start:.1f} s)",
+              file=sys.stderr, flush=True)
+    rope = G.rope_table(T_max, device=dev)
+    ws = G.workspace(B, 1, T_max, dev)
+    h = torch.empty((B, D), dtype=torch.float32, device=dev)
+    xa = torch.empty_like(x0)
+    xb = torch.empty_like(x0)
+
+    def step(i):
+        h.copy_(x0)
+        xa.copy_(x0)
+        a, b = xa, xb
+        for w, kc, vc in blocks:
+            G.block_decode(a, *w, kc, vc, rope, P, out=h, out_bf16=b, accumulate=True, ws=ws)
+            a, b = b, a
+
+    us_step = _timed_steps(step, steps, warmup, False)
+    nb = decode_bytes(B, P)
+    finite = bool(torch.isfinite(h).all())
+    return us_step, nb, finite
+
+
 def cpu_baseline(synth, B=1, P=1000, budget_s=12.0):
     """The oracle as it stands, timed on this host on a bounded sample of the
     same workload (whole decode block-steps, repeated until ~budget_s)."""
@@ -212,6 +326,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill record")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
+    ap.add_argument("--workload", default="decode_p1000",
+                    choices=["decode_p1000", "decode_p128", "batched", "stacked_long"],
+                    help="decode_p1000 (headline), batched (B=64, P=8192) or "
+                         "stacked_long (32 blocks, B=8, P=131071)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -226,8 +347,51 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    B, P = 1, 1000
-    dec = bench_decode(G, synth, args.steps, args.warmup, B, P, use_graph=not args.no_graph)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if args.workload == "batched":
+        us, kern, nb = bench_batched(G, synth, args.steps if args.steps != 400 else 50,
+                                     min(args.warmup, 10))
+        tbs = nb["step"] / (us * 1e-6) / 1e12
+        attn_gbs = nb["attn"] / (kern["attn"] * 1e-6) / 1e9
+        print(json.dumps({
+            "metric": METRIC, "value": round(us, 3), "unit": "us/block-step", "n_gpus": 1,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "Llama-3.1-8B GQA block batched decode, B=64, P=8192",
+                       "B": 64, "P": 8192, "T_max": 8224, "hip_graph": True},
+            "hbm_tbs": round(tbs, 4), "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": 64 / (us * 1e-6), "kernels_us": {k: round(v, 3) for k, v in kern.items()},
+            "roofline": {"kernel": "decode_attn_kernel", "bound": "hbm",
+                         "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": nb["attn"]}}), flush=True)
+        return
+    if args.workload == "stacked_long":
+        us, nb, finite = bench_stacked(G, synth, args.steps if args.steps != 400 else 5,
+                                       min(args.warmup, 2))
+        per_block = us / 32
+        tbs = nb["step"] / (per_block * 1e-6) / 1e12
+        print(json.dumps({
+            "metric": METRIC, "value": round(per_block, 3), "unit": "us/block-step", "n_gpus": 1,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "32 stacked Llama-3.1-8B GQA blocks, decode B=8, P=131071 "
+                                   "(128 GiB cache), residual, no norms/FFN",
+                       "B": 8, "P": 131071, "T_max": 131072, "blocks": 32, "hip_graph": False},
+            "ms_per_32_block_step": round(us / 1000, 4), "hbm_tbs": round(tbs, 4),
+            "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": 8 / (us * 1e-6), "outputs_finite": finite}), flush=True)
+        return
+
+    B, P, T_max = (1, 128, 256) if args.workload == "decode_p128" else (1, 1000, 1024)
+    dec = bench_decode(G, synth, args.steps, args.warmup, B, P, T_max, use_graph=not args.no_graph)
     # headline: HIP-graph replay when available (what a serving loop runs),
     # with the eager figure reported beside it
     headline_us = dec["graph_us_step"] if dec["graph_us_step"] is not None else dec["us_step"]
@@ -249,9 +413,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded bf16 N(0,1) x and cache, N(0,0.02) weights; 8 rotated sets)",
-        "config": {"workload": "Llama-3.1-8B GQA block decode, B=1, P=1000 (write row 1000, "
-                               "read rows 0-1000)",
-                   "B": B, "P": P, "T_max": 1024, "d": 4096, "heads": 32, "kv_heads": 8,
+        "config": {"workload": f"Llama-3.1-8B GQA block decode, B=1, P={P} (write row {P}, "
+                               f"read rows 0-{P})",
+                   "B": B, "P": P, "T_max": T_max, "d": 4096, "heads": 32, "kv_heads": 8,
                    "head_dim": 128, "rope": "scaled, theta=5e5",
                    "hip_graph": dec["graph_us_step"] is not None},
         "hbm_tbs": round(step_tbs, 4),
@@ -265,8 +429,12 @@ def main():
         "roofline": {"kernel": "decode_qkv_kernel<1> (QKV GEMV + RoPE + cache append)",
                      "bound": "hbm", "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(qkv_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": nb["qkv"]},
+                     "traffic": counter_traffic("decode_qkv_p1000_hbm_traffic.md",
+                                                "grouped_query_attention_gemv_amd/csrc/decode.hip"),
+                     "algorithmic_bytes": nb["qkv"]},
     }
+    if args.workload == "decode_p128":
+        record["roofline"]["traffic"] = None    # counters were taken on the P=1000 run
     if not args.no_prefill:
         record["prefill"] = bench_prefill(G, synth, steps=10, warmup=3)
     if not args.no_cpu:

@@ -468,6 +468,38 @@ __global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) 
 // Columns are tokens for the QKV projection, and (token, hi/lo part) pairs
 // for wo, whose input O is the sum of two bf16 parts.
 constexpr int kProjWaves = 8;
+
+// QKV epilogue of one column (token b) and features f .. f+3 (one head):
+// RoPE on Q/K pairs, Q to the workspace, K/V rounded into the cache.
+__device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, int b, int f) {
+  const int pos = p.start_pos;
+  float y[4] = {v[0], v[1], v[2], v[3]};
+  if (f < D + KVH * HD) {
+    const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)pos * PAIRS;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float2 cs = rrow[((f + e) & (HD - 1)) >> 1];
+      const float a = y[e] * cs.x - y[e + 1] * cs.y;
+      const float bb = y[e] * cs.y + y[e + 1] * cs.x;
+      y[e] = a;
+      y[e + 1] = bb;
+    }
+  }
+  if (p.probe)
+    *reinterpret_cast<float4*>(p.probe + (size_t)b * NQKV + f) = make_float4(y[0], y[1], y[2], y[3]);
+  if (f < D) {
+    *reinterpret_cast<float4*>(p.q + (size_t)b * D + f) = make_float4(y[0], y[1], y[2], y[3]);
+  } else if (f < D + KVH * HD) {
+    const int ff = f - D, g = ff / HD, d = ff % HD;
+    uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  } else {
+    const int ff = f - D - KVH * HD, g = ff / HD, d = ff % HD;
+    uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
+  }
+}
 constexpr int kProjTiles = 4;            // column tiles of 16 per pass
 
 template <int MODE>   // 0: QKV + RoPE + cache append, 1: wo (+ residual)
@@ -497,23 +529,28 @@ __global__ void __launch_bounds__(512) decode_proj_mfma_kernel(DecodeParams p) {
   const int ncols = MODE == 0 ? p.B : 2 * p.B;
   for (int c0 = 0; c0 < ncols; c0 += 16 * kProjTiles) {
     f32x4 acc[kProjTiles];
+    // activation operands in two halves of 8 k-steps, so the kernel fits in
+    // 128 VGPRs and two workgroups (every one of the grid) stay resident per CU
 #pragma unroll
     for (int t = 0; t < kProjTiles; ++t) {
       acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int c = c0 + t * 16 + r;
       if (c0 + t * 16 >= ncols) continue;                       // wave-uniform
+      const int c = c0 + t * 16 + r;
       const int cc = min(c, ncols - 1);
       const uint16_t* xrow = MODE == 0 ? p.x + (size_t)cc * D
                                        : ((cc & 1) ? p.o_lo : p.o_hi) + (size_t)(cc >> 1) * D;
-      u32x4 xb[16];
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) xb[ks] = ld_u32x4(xrow + k0 + ks * 32);
-      if (c >= ncols) {
+      for (int h = 0; h < 2; ++h) {
+        u32x4 xb[8];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) xb[ks] = u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < 8; ++ks) xb[ks] = ld_u32x4(xrow + k0 + (h * 8 + ks) * 32);
+        if (c >= ncols) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) xb[ks] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) acc[t] = mfma_bf16(wa[h * 8 + ks], xb[ks], acc[t]);
       }
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) acc[t] = mfma_bf16(wa[ks], xb[ks], acc[t]);
     }
 #pragma unroll
     for (int t = 0; t < kProjTiles; ++t) red[w][t][lane] = acc[t];
@@ -526,35 +563,7 @@ __global__ void __launch_bounds__(512) decode_proj_mfma_kernel(DecodeParams p) {
       const int c = c0 + w * 16 + r;
       const int f = f0 + 4 * q;
       if (MODE == 0) {
-        if (c < ncols) {
-          const int b = c, pos = p.start_pos;
-          float y[4] = {v[0], v[1], v[2], v[3]};
-          if (f < D + KVH * HD) {
-            const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)pos * PAIRS;
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-              const float2 cs = rrow[((f + e) & (HD - 1)) >> 1];
-              const float a = y[e] * cs.x - y[e + 1] * cs.y;
-              const float bb = y[e] * cs.y + y[e + 1] * cs.x;
-              y[e] = a;
-              y[e + 1] = bb;
-            }
-          }
-          if (p.probe)
-            *reinterpret_cast<float4*>(p.probe + (size_t)b * NQKV + f) = make_float4(y[0], y[1], y[2], y[3]);
-          if (f < D) {
-            *reinterpret_cast<float4*>(p.q + (size_t)b * D + f) = make_float4(y[0], y[1], y[2], y[3]);
-          } else if (f < D + KVH * HD) {
-            const int ff = f - D, g = ff / HD, d = ff % HD;
-            uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          } else {
-            const int ff = f - D - KVH * HD, g = ff / HD, d = ff % HD;
-            uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
-          }
-        }
+        if (c < ncols) proj_qkv_store(p, v, c, f);
       } else {
         // columns 2t (hi part) and 2t+1 (lo part) of token t sit in lanes r, r^1
         f32x4 other;

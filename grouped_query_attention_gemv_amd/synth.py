@@ -54,7 +54,8 @@ def fill_randn_bf16_(dst: torch.Tensor, gen: torch.Generator, scale: float = 1.0
 
 
 def block_weights(gen: torch.Generator, device="cpu"):
-    """(Wq, Wk, Wv, Wo), [out, in] bf16, N(0, 0.02^2)."""
+    """(Wq, Wk, Wv, Wo), [out, in] bf16, N(0, 0.02^2), drawn on ``device``
+    (which must be the generator's device)."""
     wq = randn_bf16(gen, (N_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
     wk = randn_bf16(gen, (N_KV_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
     wv = randn_bf16(gen, (N_KV_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)

@@ -104,6 +104,54 @@ def test_decode_batched_b64_p8192_sampled():
     c.check_untouched()
 
 
+def test_decode_long_context_p131071_sampled():
+    """One block at the long-context point: B=8 sequences with 131,071 cached
+    positions each (2 GiB per cache tensor), row 131,071 written; sampled
+    sequences against the oracle, every other cache bit unchanged."""
+    c = DecodeCase(8, 131071, 131072, dev=DEV, cache_on_device=True)
+    c.run()
+    seqs = [0, 5]
+    c.check(c.oracle(seqs), seqs)
+    c.check_untouched()
+
+
+def test_decode_stacked_blocks_residual():
+    """32 stacked blocks, each with its own weights and cache, h <- h + Delta
+    (no norms, no FFN), the next block's input being bf16(h): B=8, P=4095,
+    against the oracle's block-by-block chain for sampled sequences."""
+    from grouped_query_attention_gemv_amd import synth
+    from oracle import gqa_oracle as O
+    B, P, T_max, L = 8, 4095, 4096, 32
+    gen = synth.generator(7)
+    x0 = synth.randn_bf16(gen, (B, 4096))
+    blocks = []
+    dgen = synth.generator(8, DEV)
+    for _ in range(L):
+        w = [t.to(DEV) for t in synth.block_weights(gen)]
+        kc, vc = G.empty_caches(B, T_max, DEV)
+        synth.fill_randn_bf16_(kc, dgen)
+        synth.fill_randn_bf16_(vc, dgen)
+        blocks.append((w, kc, vc, kc.clone(), vc.clone()))
+    rope = G.rope_table(T_max, device=DEV)
+    ws = G.workspace(B, 1, T_max, DEV)
+    h = x0.to(DEV).float()
+    xa = x0.to(DEV)
+    xb = torch.empty_like(xa)
+    for w, kc, vc, _, _ in blocks:
+        G.block_decode(xa, *w, kc, vc, rope, P, out=h, out_bf16=xb, accumulate=True, ws=ws)
+        xa, xb = xb, xa
+    torch.cuda.synchronize()
+    seqs = [1, 6]
+    # generators: one block's fp64 copies exist on the host at a time
+    ws_ = ([f64(t) for t in w] for w, *_ in blocks)
+    kcs = (f64(G.kcache_by_position(k0[seqs])[:, :P]) for *_, k0, _ in blocks)
+    vcs = (f64(G.vcache_read(v0[seqs], 0, P)) for *_, v0 in blocks)
+    h_ref, _ = O.stacked_decode(f64(x0[seqs]), ws_, kcs, vcs, P)
+    # compare the accumulated residual update h - x0 (the 32 summed deltas)
+    assert_close("stacked residual", f64(h[seqs]) - f64(x0[seqs]), h_ref - f64(x0[seqs]))
+    assert torch.equal(xa.cpu(), h.cpu().to(torch.bfloat16))
+
+
 def test_decode_is_deterministic():
     c = DecodeCase(4, 1000, 1024, dev=DEV)
     a = c.run().clone()
