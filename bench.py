@@ -5,14 +5,18 @@
 Headline workload: one decode block-step at the pages' decode point (B = 1,
 P = 1,000 cached positions, row 1,000 written, rows 0-1,000 read).  A step is
 one gqa_block_decode call: QKV projection + RoPE + cache append, attention,
-wo.  Inputs are seeded synthetic bf16 tensors already resident in HBM.  The
+wo (one launch under the fused schedule the library picks for this shape;
+the three-launch schedule is timed beside it).  Inputs are seeded synthetic
+bf16 tensors already resident in HBM.  The
 timed loop cycles through 8 independent weight + cache sets (8 x 84 MiB),
 so the 256 MB Infinity Cache cannot hold what a step reads.
 
 Printed: one JSON line with the step time, HBM throughput, the roofline of
-the dominant kernel (HIP events around each kernel, on the stream the library
-launches on), the oracle timed on this host's cores, and a prefill
-(B = 4, T = 2,048) record with tokens/s and matrix-core utilisation.
+the dominant kernel (under the one-launch schedule the step time itself,
+measured with HIP events over the timed region on the stream the kernel runs
+on; under the three-launch schedule HIP events around each kernel), the
+oracle timed on this host's cores, and a prefill (B = 4, T = 2,048) record
+with tokens/s and matrix-core utilisation.
 """
 from __future__ import annotations
 
@@ -60,25 +64,39 @@ def prefill_flops(B: int, T: int) -> dict:
     return {"qkv": qkv, "attn": attn, "wo": wo, "total": qkv + attn + wo}
 
 
-def counter_traffic(summary: str, source: str):
-    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
-    calibrated on a known-size copy), as recorded in a profile summary; None
-    when the kernel source has changed since the counters were taken."""
+def counter_traffic(summary: str, kernel: str, source: str):
+    """HBM bytes per launch of `kernel` measured by rocprofv3 (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a known-size copy), as recorded in a profile
+    summary; None when the kernel source has changed since the counters were
+    taken."""
     import hashlib
     try:
-        text = open(os.path.join(ROOT, "profiles", summary)).read()
-        fields = dict(l.strip().split(": ", 1) for l in text.splitlines()
-                      if l.strip().startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+        fields = {}
+        for line in open(os.path.join(ROOT, "profiles", summary)).read().splitlines():
+            line = line.strip()
+            if line.startswith(("traffic_bytes_per_launch[", "kernel_source_sha256:")):
+                k, v = line.split(": ", 1)
+                fields[k] = v
         digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256") != digest:
             return None
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[f"traffic_bytes_per_launch[{kernel}]"])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use_graph=True):
+def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use_graph=True,
+                 schedule=None):
+    """Eager, graph-replay and per-kernel timings of decode steps under the
+    given decode schedule (the library's choice when None)."""
+    if schedule is not None:
+        prev = G.set_decode_schedule(schedule)
+        try:
+            return bench_decode(G, synth, steps, warmup, B, P, T_max, use_graph, None)
+        finally:
+            G.set_decode_schedule(prev)
     dev = torch.device("cuda:0")
+    fused = G.decode_schedule(B, P, T_max) == G.DECODE_FUSED
     sets = []
     for s in range(N_SETS):
         x, w, kc_rows, vc_rows = synth.decode_workload(s, B, P)
@@ -156,8 +174,11 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
             per[i, k] = ev.elapsed_ms(k, k + 1)
     ev.close()
     kern_us = per.mean(axis=0) * 1000.0
+    # the fused schedule is one kernel: stage 1 covers it, the others are empty
+    names = ["decode_step"] if fused else ["qkv", "attn", "wo"]
     return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps, graph_us_step=graph_us,
-                kern_us=dict(zip(["qkv", "attn", "wo"], kern_us.tolist())),
+                schedule="fused" if fused else "split",
+                kern_us=dict(zip(names, kern_us.tolist())),
                 profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
 
 
@@ -329,6 +350,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused"],
+                    help="decode schedule of the headline workloads (auto: the library's "
+                         "choice, which is the one-launch schedule where it applies)")
     ap.add_argument("--workload", default="decode_p1000",
                     choices=["decode_p1000", "decode_p128", "batched", "stacked_long"],
                     help="decode_p1000 (headline), batched (B=64, P=8192) or "
@@ -391,14 +415,38 @@ def main():
         return
 
     B, P, T_max = (1, 128, 256) if args.workload == "decode_p128" else (1, 1000, 1024)
-    dec = bench_decode(G, synth, args.steps, args.warmup, B, P, T_max, use_graph=not args.no_graph)
+    sched = {"auto": None, "split": G.DECODE_SPLIT, "fused": G.DECODE_FUSED}[args.schedule]
+    dec = bench_decode(G, synth, args.steps, args.warmup, B, P, T_max,
+                       use_graph=not args.no_graph, schedule=sched)
     # headline: HIP-graph replay when available (what a serving loop runs),
     # with the eager figure reported beside it
     headline_us = dec["graph_us_step"] if dec["graph_us_step"] is not None else dec["us_step"]
     nb = decode_bytes(B, P)
     step_tbs = nb["step"] / (headline_us * 1e-6) / 1e12
-    qkv_us = dec["kern_us"]["qkv"]
-    qkv_gbs = nb["qkv"] / (qkv_us * 1e-6) / 1e9
+    src = "grouped_query_attention_gemv_amd/csrc/decode.hip"
+    if dec["schedule"] == "fused":
+        # one kernel carries the whole step, so the step time measured over
+        # the timed region (HIP events on the stream the graph or the calls
+        # run on) is that kernel's average duration
+        dom_us = headline_us
+        dom_bytes = nb["step"]
+        roof_kernel = ("decode_step_kernel<1> (whole step in one launch: QKV + RoPE + append, "
+                       "attention, wo)")
+        traffic = counter_traffic("decode_p1000_hbm_traffic.md", "decode_step_kernel<1>", src)
+    else:
+        dom_us = dec["kern_us"]["qkv"]
+        dom_bytes = nb["qkv"]
+        roof_kernel = "decode_qkv_kernel<1> (QKV GEMV + RoPE + cache append)"
+        traffic = counter_traffic("decode_p1000_hbm_traffic.md", "decode_qkv_kernel<1>", src)
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    other = None
+    if dec["schedule"] == "fused":
+        # the three-launch schedule on the same workload, for comparison
+        alt = bench_decode(G, synth, args.steps, args.warmup, B, P, T_max,
+                           use_graph=not args.no_graph, schedule=G.DECODE_SPLIT)
+        alt_us = alt["graph_us_step"] if alt["graph_us_step"] is not None else alt["us_step"]
+        other = {"schedule": "split", "us_step": round(alt_us, 3),
+                 "kernels_us": {k: round(v, 3) for k, v in alt["kern_us"].items()}}
 
     record = {
         "metric": METRIC,
@@ -417,7 +465,8 @@ def main():
                                f"read rows 0-{P})",
                    "B": B, "P": P, "T_max": T_max, "d": 4096, "heads": 32, "kv_heads": 8,
                    "head_dim": 128, "rope": "scaled, theta=5e5",
-                   "hip_graph": dec["graph_us_step"] is not None},
+                   "hip_graph": dec["graph_us_step"] is not None,
+                   "schedule": dec["schedule"]},
         "hbm_tbs": round(step_tbs, 4),
         "hbm_frac_of_peak": round(step_tbs * 1000.0 / HBM_PEAK_GBS, 4),
         "tokens_per_s": B / (headline_us * 1e-6),
@@ -426,13 +475,13 @@ def main():
         "algorithmic_bytes_per_step": nb["step"],
         "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
         "profiled_us_step": round(dec["profiled_us_step"], 3),
-        "roofline": {"kernel": "decode_qkv_kernel<1> (QKV GEMV + RoPE + cache append)",
-                     "bound": "hbm", "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(qkv_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("decode_qkv_p1000_hbm_traffic.md",
-                                                "grouped_query_attention_gemv_amd/csrc/decode.hip"),
-                     "algorithmic_bytes": nb["qkv"]},
+        "roofline": {"kernel": roof_kernel,
+                     "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes},
     }
+    if other is not None:
+        record["other_schedule"] = other
     if args.workload == "decode_p128":
         record["roofline"]["traffic"] = None    # counters were taken on the P=1000 run
     if not args.no_prefill:

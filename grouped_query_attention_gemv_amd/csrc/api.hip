@@ -4,11 +4,30 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.h"
 
 using namespace gqa;
 
+static_assert(kSyncBytes == GQA_SYNC_BYTES, "sync region size differs from the header");
+
 namespace {
+
+std::atomic<int> g_decode_schedule{GQA_DECODE_AUTO};
+
+// Schedule a decode call of this shape runs with under the current setting;
+// -1 when the setting demands the fused schedule and the shape does not admit it.
+int pick_schedule(int B, int start_pos) {
+  int nsplit = 0, chunk = 0;
+  decode_split(B, start_pos + 1, &nsplit, &chunk);
+  const bool ok = decode_fused_eligible(B, nsplit);
+  switch (g_decode_schedule.load()) {
+    case GQA_DECODE_SPLIT: return GQA_DECODE_SPLIT;
+    case GQA_DECODE_FUSED: return ok ? GQA_DECODE_FUSED : -1;
+    default: return ok ? GQA_DECODE_FUSED : GQA_DECODE_SPLIT;
+  }
+}
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -125,10 +144,18 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   p.T_max = T_max; p.start_pos = start_pos; p.B = B; p.accumulate = accumulate;
   decode_ws_carve(ws, B, &p);
   decode_split(B, start_pos + 1, &p.nsplit, &p.chunk);
+  const int sched = pick_schedule(B, start_pos);
+  if (sched < 0) return GQA_ERR_ARG;
 
   (void)hipGetLastError();
   hipError_t e;
   if ((e = mark(events, 0, stream)) != hipSuccess) return GQA_ERR_HIP;
+  if (sched == GQA_DECODE_FUSED) {
+    if ((e = launch_decode_fused(p, stream)) != hipSuccess) return hip_status(e);
+    for (int i = 1; i <= GQA_DECODE_STAGES; ++i)
+      if ((e = mark(events, i, stream)) != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+  }
   if ((e = launch_decode_qkv(p, stream)) != hipSuccess) return hip_status(e);
   if ((e = mark(events, 1, stream)) != hipSuccess) return GQA_ERR_HIP;
   if ((e = launch_decode_attn(p, stream)) != hipSuccess) return hip_status(e);
@@ -164,6 +191,27 @@ int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t
   if (!aligned16(rope)) return GQA_ERR_ALIGN;
   (void)hipGetLastError();
   return hip_status(launch_rope_table(rope, T_max, theta, scaled, stream));
+}
+
+int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return GQA_ERR_NULL;
+  if (!aligned16(ws)) return GQA_ERR_ALIGN;
+  if (ws_bytes < (size_t)GQA_SYNC_BYTES) return GQA_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return hip_status(hipMemsetAsync(ws, 0, GQA_SYNC_BYTES, stream));
+}
+
+int gqa_set_decode_schedule(int schedule) {
+  if (schedule != GQA_DECODE_AUTO && schedule != GQA_DECODE_SPLIT && schedule != GQA_DECODE_FUSED)
+    return GQA_ERR_ARG;
+  return g_decode_schedule.exchange(schedule);
+}
+
+int gqa_decode_schedule(int B, int start_pos, int T_max) {
+  if (B < 1 || B > GQA_MAX_BATCH || T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
+  if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
+  const int sched = pick_schedule(B, start_pos);
+  return sched < 0 ? GQA_ERR_ARG : sched;
 }
 
 size_t gqa_workspace_bytes(int B, int T, int T_max) {

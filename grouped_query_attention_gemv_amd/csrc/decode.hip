@@ -78,11 +78,29 @@ __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restr
 // QKV projection + RoPE + cache append
 // ---------------------------------------------------------------------------
 
-template <int NB>
-__global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
-  __shared__ uint32_t xs[NB * (D / 2)];
+// Output features of QKV workgroup `blk`: 8 consecutive features, 2 per wave.
+// The three-launch schedule takes them in feature order.  The fused schedule
+// takes them kv head by kv head (Q of its 4 query heads: 64 workgroups, then
+// K: 16, then V: 16), so that each kv head's inputs to attention complete
+// together and early heads can start attention while later ones stream.
+template <bool FUSED>
+__device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
+  if (!FUSED) {
+    *grp = 0;
+    return blk * 8;
+  }
+  const int g = blk / 96, r = blk % 96;
+  *grp = g;
+  if (r < 64) return g * (REP * HD) + r * 8;
+  if (r < 80) return D + g * HD + (r - 64) * 8;
+  return D + KVH * HD + g * HD + (r - 80) * 8;
+}
+
+template <int NB, bool FUSED>
+__device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = (blockIdx.x * 4 + wave) * 2;     // even output feature, 0..6142
+  int grp;
+  const int r0 = qkv_first_feature<FUSED>(blk, &grp) + wave * 2;   // even feature, 0..6142
   const uint16_t* wbase;
   int rr;
   if (r0 < D) {
@@ -97,7 +115,7 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
   load_rows2(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, lane, wa, wb);
 
   stage_rows<NB>(xs, p.x + (size_t)b0 * D);
-  if (blockIdx.x == 0 && b0 == 0) {
+  if (!FUSED && blk == 0 && b0 == 0) {
     // the attention kernel that follows counts split arrivals from zero
     for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
   }
@@ -113,34 +131,61 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
     const float s1 = wave_sum(acc[1][t]);
     if (lane == t) { v0 = s0; v1 = s1; }
   }
-  if (lane >= NB) return;
 
-  const int b = b0 + lane;
-  const int pos = p.start_pos;
-  const bool is_v = r0 >= D + KVH * HD;
-  if (!is_v) {
-    // rotate the pair (2i, 2i+1) of this head by position * f_i
-    const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * PAIRS + ((rr & (HD - 1)) >> 1)];
-    const float a = v0 * cs.x - v1 * cs.y;
-    const float c = v0 * cs.y + v1 * cs.x;
-    v0 = a;
-    v1 = c;
+  if (lane < NB) {
+    const int b = b0 + lane;
+    const int pos = p.start_pos;
+    const bool is_v = r0 >= D + KVH * HD;
+    if (!is_v) {
+      // rotate the pair (2i, 2i+1) of this head by position * f_i
+      const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * PAIRS + ((rr & (HD - 1)) >> 1)];
+      const float a = v0 * cs.x - v1 * cs.y;
+      const float c = v0 * cs.y + v1 * cs.x;
+      v0 = a;
+      v1 = c;
+    }
+    if (p.probe) {
+      *reinterpret_cast<float2*>(p.probe + (size_t)b * NQKV + r0) = make_float2(v0, v1);
+    }
+    if (r0 < D) {
+      float* qd = p.q + (size_t)b * D + r0;
+      if (FUSED) {
+        st_dev(qd, v0);
+        st_dev(qd + 1, v1);
+      } else {
+        *reinterpret_cast<float2*>(qd) = make_float2(v0, v1);
+      }
+    } else {
+      const int g = rr / HD, d = rr % HD;
+      const uint32_t pair = pack_bf16x2(v0, v1);
+      if (!is_v) {
+        uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+        *reinterpret_cast<uint32_t*>(dst) = pair;
+      } else {
+        uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
+        dst[0] = (uint16_t)(pair & 0xffffu);
+        dst[VB] = (uint16_t)(pair >> 16);
+      }
+      // the attention workgroups of the same launch read the new row from here
+      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2, pair);
+    }
   }
-  if (p.probe) {
-    *reinterpret_cast<float2*>(p.probe + (size_t)b * NQKV + r0) = make_float2(v0, v1);
+
+  if (FUSED) {
+    // Count this workgroup towards its kv head once all of its device-scope
+    // stores have landed.  The head's attention workgroups wait for the
+    // count to reach 96; the last of them rearms it.
+    wait_vm();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(p.sync + kSyncGroup + 32 * grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (r0 < D) {
-    *reinterpret_cast<float2*>(p.q + (size_t)b * D + r0) = make_float2(v0, v1);
-  } else if (!is_v) {
-    const int g = rr / HD, d = rr % HD;
-    uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v0, v1);
-  } else {
-    const int g = rr / HD, d = rr % HD;
-    uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
-    dst[0] = (uint16_t)f32_to_bf16_bits(v0);
-    dst[VB] = (uint16_t)f32_to_bf16_bits(v1);
-  }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
+  __shared__ uint32_t xs[NB * (D / 2)];
+  qkv_body<NB, false>(p, b0, blockIdx.x, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -160,24 +205,35 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // The A-operand rows of the score tiles are assigned to positions so that
 // each lane's 8 score values are 8 consecutive positions: exactly the B
 // operand of the following P.V instruction, with no data movement.
-__global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
-  const int split = blockIdx.x % p.nsplit;
-  const int g = (blockIdx.x / p.nsplit) % KVH;
-  const int b = blockIdx.x / (p.nsplit * KVH);
+//
+// In the fused schedule the workgroup loads its first tiles before Q exists,
+// waits for its kv head's release, then replaces the row of position
+// start_pos (which the same launch writes) with the copy in kv_new.
+constexpr int kAttnLdsWords = kAttnWaves * REP * HD + 2 * kAttnWaves * REP + 1;
+
+// FUSED: Q, K and V come from the same launch.  The workgroup waits on its kv
+// head's counter, reads Q and the appended row with device-scope loads, and
+// hands O to the wo workgroups of the launch.
+template <bool FUSED>
+__device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float* lds) {
+  const int split = blk % p.nsplit;
+  const int g = (blk / p.nsplit) % KVH;
+  const int b = blk / (p.nsplit * KVH);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
   const int head = col & 3;
   const bool valid_col = col < 8;
   const bool is_lo = (col & 4) != 0;
   const int L = p.start_pos + 1;
+  const int P = p.start_pos;
   const int j_begin = split * p.chunk;
   const int j_end = min(L, j_begin + p.chunk);
   const int T_max = p.T_max;
 
-  __shared__ float sm_o[kAttnWaves][REP][HD];
-  __shared__ float sm_m[kAttnWaves][REP];
-  __shared__ float sm_l[kAttnWaves][REP];
-  __shared__ int sm_last;
+  float (*sm_o)[REP][HD] = reinterpret_cast<float (*)[REP][HD]>(lds);
+  float (*sm_m)[REP] = reinterpret_cast<float (*)[REP]>(lds + kAttnWaves * REP * HD);
+  float (*sm_l)[REP] = reinterpret_cast<float (*)[REP]>(lds + kAttnWaves * REP * HD + kAttnWaves * REP);
+  int* sm_last = reinterpret_cast<int*>(lds + kAttnWaves * REP * HD + 2 * kAttnWaves * REP);
 
   const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
   const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * (T_max / VB) * (HD * VB);
@@ -198,10 +254,73 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
     for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
   };
 
+  // Fused schedule: replace the appended row (position start_pos, written by
+  // this launch) with the device-scope copy in kv_new, for the lanes that
+  // hold it.
+  auto patch_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
+    if (P < tile || P >= tile + kAttnTile) return;     // wave-uniform
+    const uint32_t kn_off = (uint32_t)(((b * 2) * KVH + g) * HD) * 2u;   // bytes into kv_new
+    const uint32_t* vn = p.kv_new + ((size_t)(b * 2 + 1) * KVH + g) * (HD / 2);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
+      if (j == P) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kf[mt][ks] = ld_dev_x4(p.kv_new, kn_off + (uint32_t)(rg * 8 + 32 * ks) * 2u);
+      }
+    }
+    const int e = P - tile - rg * 8;     // element of this lane's 8 positions
+    if (e >= 0 && e < 8) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = col + 16 * dt;
+        const uint32_t wv = ld_dev(vn + d / 2);
+        const uint32_t h = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q == (e >> 1)) {
+            vf[dt][q] = (e & 1) ? ((vf[dt][q] & 0x0000ffffu) | (h << 16))
+                                : ((vf[dt][q] & 0xffff0000u) | h);
+          }
+        }
+      }
+    }
+  };
+
   // the first tile's loads go out before the Q loads, so both round trips overlap
   u32x4 kf[2][4], vf[8];
   int tile = j_begin + w * kAttnTile;
   if (tile < j_end) load_tile(tile, kf, vf);
+
+  // Fused schedule: wait until the 96 QKV workgroups of kv head g have
+  // counted themselves (each after its stores landed), count this workgroup
+  // too (the last of the head's nsplit*B attention workgroups rearms the
+  // counter at its end), then read Q and the appended row in one round trip.
+  int* grp_cnt = p.sync + kSyncGroup + 32 * g;
+  int grp_prev = 0;
+  u32x4 qraw[8];
+  if (FUSED) {
+    if (tid == 0) {
+      int polls = 0;
+      while (ld_dev(grp_cnt) < 96) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > kMaxPolls) {
+          __hip_atomic_fetch_or(p.sync + kSyncErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      grp_prev = __hip_atomic_fetch_add(grp_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const uint32_t qoff = (uint32_t)((b * D + (g * REP + head) * HD + rg * 8) * 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qraw[2 * ks] = ld_dev_x4(p.q, qoff + ks * 128);
+      qraw[2 * ks + 1] = ld_dev_x4(p.q, qoff + ks * 128 + 16);
+    }
+    if (tile < j_end) patch_tile(tile, kf, vf);
+  }
 
   // Q fragments, pre-scaled by log2(e)/sqrt(128)
   u32x4 qf[4];
@@ -210,9 +329,19 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int d0 = rg * 8 + 32 * ks;
-      const float4 qa = *reinterpret_cast<const float4*>(qrow + d0);
-      const float4 qb = *reinterpret_cast<const float4*>(qrow + d0 + 4);
-      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      float qv[8];
+      if (FUSED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[e] = __uint_as_float(qraw[2 * ks][e]);
+          qv[4 + e] = __uint_as_float(qraw[2 * ks + 1][e]);
+        }
+      } else {
+        const float4 qa = *reinterpret_cast<const float4*>(qrow + d0);
+        const float4 qb = *reinterpret_cast<const float4*>(qrow + d0 + 4);
+        qv[0] = qa.x; qv[1] = qa.y; qv[2] = qa.z; qv[3] = qa.w;
+        qv[4] = qb.x; qv[5] = qb.y; qv[6] = qb.z; qv[7] = qb.w;
+      }
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -304,7 +433,10 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
   while (tile < j_end) {
     compute_tile(tile, kf, vf);
     tile += kAttnWaves * kAttnTile;
-    if (tile < j_end) load_tile(tile, kf, vf);
+    if (tile < j_end) {
+      load_tile(tile, kf, vf);
+      if (FUSED) patch_tile(tile, kf, vf);
+    }
   }
 
   // wave result: l summed over the 4 lane rows, O = hi column + lo column
@@ -325,7 +457,7 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // merge the 4 waves: thread -> (head, two dims)
+  // merge the 4 waves: thread -> (head, two dims); wave w holds head w
   const int mh = tid >> 6, d2 = (tid & 63) * 2;
   float M = -INFINITY;
 #pragma unroll
@@ -340,50 +472,76 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
   }
 
   const size_t out_off = (size_t)b * D + (g * REP + mh) * HD + d2;
-  if (p.nsplit == 1) {
-    const float r0 = o0 / lsum, r1 = o1 / lsum;
+  // O of (b, g) leaves as bf16 hi/lo parts; in the fused schedule through
+  // device-scope stores, after which every wo workgroup is told
+  auto emit = [&](float r0, float r1) {
     const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);
     const uint32_t lo0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(h0));
     const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
-    *reinterpret_cast<uint32_t*>(p.o_hi + out_off) = h0 | (h1 << 16);
-    *reinterpret_cast<uint32_t*>(p.o_lo + out_off) = lo0 | (lo1 << 16);
+    uint32_t* ph = reinterpret_cast<uint32_t*>(p.o_hi + out_off);
+    uint32_t* pl = reinterpret_cast<uint32_t*>(p.o_lo + out_off);
+    if (FUSED) {
+      st_dev(ph, h0 | (h1 << 16));
+      st_dev(pl, lo0 | (lo1 << 16));
+      wait_vm();
+      __syncthreads();
+      for (int wg = tid; wg < kFusedWoWG; wg += blockDim.x) st_dev(p.sync + kSyncWoSlot + 16 * wg + b * KVH + g, 1);
+    } else {
+      *ph = h0 | (h1 << 16);
+      *pl = lo0 | (lo1 << 16);
+    }
+  };
+
+  // the head's last attention workgroup to pass its wait rearms the counter
+  auto rearm_group = [&]() {
+    if (FUSED && tid == 0 && grp_prev == 96 + p.nsplit * p.B - 1) st_dev(grp_cnt, 0);
+  };
+
+  if (p.nsplit == 1) {
+    rearm_group();
+    emit(o0 / lsum, o1 / lsum);
     return;
   }
 
   // Publish this split's partial without an L2 write-back: device-scope
   // stores go through to the coherence point shared by all XCDs, the wait
   // makes sure they have landed, then a relaxed device-scope count.  The
-  // last workgroup to arrive reads every partial with device-scope loads.
+  // last workgroup to arrive merges every partial.
   const size_t split_stride = (size_t)REP * kPartStride;
   float* part0 = p.part + ((size_t)(b * KVH + g) * p.nsplit) * split_stride + (size_t)mh * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
+  int* split_cnt = p.counters + b * KVH + g;
   if (d2 == 0) {
-    __hip_atomic_store(mine, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(mine + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_dev(mine, M);
+    st_dev(mine + 1, lsum);
   }
-  __hip_atomic_store(mine + 4 + d2, o0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(mine + 5 + d2, o1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  st_dev(mine + 4 + d2, o0);
+  st_dev(mine + 5 + d2, o1);
+  wait_vm();
   __syncthreads();
   if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(p.counters + b * KVH + g, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = (prev == p.nsplit - 1);
+    const int prev = __hip_atomic_fetch_add(split_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sm_last = (prev == p.nsplit - 1);
   }
   __syncthreads();
-  if (!sm_last) return;
+  rearm_group();
+  if (!*sm_last) return;
 
-  // last workgroup of this (b, g): merge every split in a fixed order, one
-  // round trip per 8 splits, rescaling the running sums as the maximum grows
+  // merge every split in a fixed order, one round trip per 8 splits,
+  // rescaling the running sums as the maximum grows
   constexpr int U = 8;
   float GM = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
   for (int s0 = 0; s0 < p.nsplit; s0 += U) {
     float mv[U], lv[U], ov0[U], ov1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = s0 + u < p.nsplit;
-      const float* ps = part0 + (ok ? s0 + u : 0) * split_stride;
-      mv[u] = ok ? ld_dev(ps) : -INFINITY;
+      const int s = s0 + u;
+      if (s >= p.nsplit) {
+        mv[u] = -INFINITY; lv[u] = 0.f; ov0[u] = 0.f; ov1[u] = 0.f;
+        continue;
+      }
+      const float* ps = part0 + (size_t)s * split_stride;
+      mv[u] = ld_dev(ps);
       lv[u] = ld_dev(ps + 1);
       ov0[u] = ld_dev(ps + 4 + d2);
       ov1[u] = ld_dev(ps + 5 + d2);
@@ -404,28 +562,61 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
     }
     GM = cm;
   }
-  const float r0 = g0 / gl, r1 = g1 / gl;
-  const uint32_t h0 = f32_to_bf16_bits(r0), h1 = f32_to_bf16_bits(r1);
-  const uint32_t lo0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(h0));
-  const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
-  *reinterpret_cast<uint32_t*>(p.o_hi + out_off) = h0 | (h1 << 16);
-  *reinterpret_cast<uint32_t*>(p.o_lo + out_off) = lo0 | (lo1 << 16);
-  if (tid == 0) __hip_atomic_store(p.counters + b * KVH + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) st_dev(split_cnt, 0);
+  emit(g0 / gl, g1 / gl);
+}
+
+__global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
+  __shared__ float lds[kAttnLdsWords];
+  attn_body<false>(p, blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
 // wo projection (+ residual)
 // ---------------------------------------------------------------------------
 
-template <int NB>
-__global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) {
-  __shared__ uint32_t xs[2 * NB * (D / 2)];
+template <int NB, bool FUSED>
+__device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = (blockIdx.x * 4 + wave) * 2;
+  const int r0 = (blk * 4 + wave) * 2;
   u32x4 wa[8], wb[8];
   load_rows2(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, lane, wa, wb);
-  stage_rows<NB>(xs, p.o_hi + (size_t)b0 * D);
-  stage_rows<NB>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
+  if (FUSED) {
+    // wave 0 waits until every (b, g) has published O, one word per lane
+    if (wave == 0) {
+      int* slot = p.sync + kSyncWoSlot + 16 * blk;
+      const int nwords = p.B * KVH;
+      int polls = 0;
+      while (true) {
+        const int v = lane < nwords ? ld_dev(slot + lane) : 1;
+        if (__all(v == 1)) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > kMaxPolls) {
+          if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      if (lane < nwords) st_dev(slot + lane, 0);
+    }
+    __syncthreads();
+    // every load goes out before the first LDS write (one round trip)
+    constexpr int kPer = NB * (D / 8) / 256;       // 16-byte pieces per thread and part
+    u32x4 hv[kPer], lv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const uint32_t off = (uint32_t)(((size_t)b0 * D) * 2 + (threadIdx.x + 256 * k) * 16);
+      hv[k] = ld_dev_x4(p.o_hi, off);
+      lv[k] = ld_dev_x4(p.o_lo, off);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      reinterpret_cast<u32x4*>(xs)[threadIdx.x + 256 * k] = hv[k];
+      reinterpret_cast<u32x4*>(xs + NB * (D / 2))[threadIdx.x + 256 * k] = lv[k];
+    }
+  } else {
+    stage_rows<NB>(xs, p.o_hi + (size_t)b0 * D);
+    stage_rows<NB>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
+  }
   __syncthreads();
 
   float acc[2][NB];
@@ -450,6 +641,45 @@ __global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) 
   *o = r;
   if (p.out_bf16)
     *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) {
+  __shared__ uint32_t xs[2 * NB * (D / 2)];
+  wo_body<NB, false>(p, b0, blockIdx.x, xs);
+}
+
+// ---------------------------------------------------------------------------
+// Fused schedule: the whole block step in one launch
+// ---------------------------------------------------------------------------
+//
+// Workgroups [0, 768) run the QKV projection (kv head by kv head), the next
+// nsplit*8*B flash-decode, the last 512 wo.  Every QKV workgroup is resident
+// from the start; each consumer starts its own HBM reads (K/V tiles, wo rows)
+// before it waits, so the three phases overlap instead of paying a launch
+// boundary each:
+//   QKV -> attention: per-kv-head arrival counter, which the head's attention
+//     workgroups poll until it reaches 96;
+//   attention -> wo: the workgroup that completes O of (b, g) sets word
+//     b*8 + g of every wo workgroup's slot.
+// Producers publish with device-scope stores and wait for them to land before
+// they signal; consumers read with device-scope loads.  Every wait is bounded
+// (kMaxPolls) and only the consumers wait.  The host admits a shape only if
+// all waiting workgroups together fit in less than the chip's resident
+// capacity, so producers always find room to run whatever order the hardware
+// dispatches in.
+template <int NB>
+__global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
+  __shared__ uint32_t lds[2 * NB * (D / 2) > kAttnLdsWords ? 2 * NB * (D / 2) : kAttnLdsWords];
+  const int na = p.nsplit * KVH * p.B;
+  const int blk = blockIdx.x;
+  if (blk < kFusedQkvWG) {
+    qkv_body<NB, true>(p, 0, blk, lds);
+  } else if (blk < kFusedQkvWG + na) {
+    attn_body<true>(p, blk - kFusedQkvWG, reinterpret_cast<float*>(lds));
+  } else {
+    wo_body<NB, true>(p, 0, blk - kFusedQkvWG - na, lds);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -612,16 +842,19 @@ void decode_split(int B, int L, int* nsplit, int* chunk) {
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t decode_ws_bytes(int B) {
-  size_t n = 0;
+  size_t n = kSyncBytes;
   n += align256((size_t)B * D * 4);                       // q
   n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
   n += align256((size_t)B * KVH * 4);                     // counters
   n += align256((size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4);  // partials
+  n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new
   return n;
 }
 
 void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   char* c = static_cast<char*>(ws);
+  p->sync = reinterpret_cast<int*>(c);
+  c += kSyncBytes;
   p->q = reinterpret_cast<float*>(c);
   c += align256((size_t)B * D * 4);
   p->o_hi = reinterpret_cast<uint16_t*>(c);
@@ -631,6 +864,8 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   p->counters = reinterpret_cast<int*>(c);
   c += align256((size_t)B * KVH * 4);
   p->part = reinterpret_cast<float*>(c);
+  c += align256((size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4);
+  p->kv_new = reinterpret_cast<uint32_t*>(c);
 }
 
 #define GQA_NB_SWITCH(NB_VAR, CALL) \
@@ -679,6 +914,25 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
     GQA_NB_SWITCH(nb, GQA_LAUNCH_WO)
 #undef GQA_LAUNCH_WO
   }
+  return hipGetLastError();
+}
+
+// The fused schedule keeps every waiting workgroup (attention and wo) below
+// the resident capacity of the chip: 256 CUs x 3 workgroups of 256 threads at
+// the kernel's register budget, with room left for at least 128 producers.
+bool decode_fused_eligible(int B, int nsplit) {
+  return B >= 1 && B <= kFusedMaxB && nsplit * KVH * B <= kFusedMaxAttnWG;
+}
+
+hipError_t launch_decode_fused(const DecodeParams& p0, hipStream_t s) {
+  if (!decode_fused_eligible(p0.B, p0.nsplit)) return hipErrorInvalidValue;
+  DecodeParams p = p0;
+  p.counters = p.sync + kSyncSplit;     // zero at entry, rearmed by the last split
+  const int grid = kFusedQkvWG + p.nsplit * KVH * p.B + kFusedWoWG;
+  if (p.B == 1)
+    hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -20,6 +20,22 @@ constexpr int kGemvMaxNB = 8;        // tokens per pass of the QKV bandwidth GEM
 constexpr int kGemvMaxB = 8;         // larger batches use the matrix-core projections
 constexpr int kWoMaxNB = 4;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
 
+// Synchronisation words at the start of every workspace, used by the fused
+// decode schedule (one launch whose workgroups hand results to each other).
+// They must be zero before the first decode call on a workspace; every call
+// leaves them zero, and prefill never touches them.  Offsets are in ints.
+constexpr int kSyncBytes = 64 * 1024;
+constexpr int kSyncErr = 0;          // sticky error bits: 1 attention wait, 2 wo wait timed out
+constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups of kv head g
+constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
+constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
+constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
+constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
+constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
+constexpr int kFusedWoWG = 512;      // 8 wo rows each
+constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
+static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncBytes / 4, "sync region too small");
+
 struct DecodeParams {
   const uint16_t* x;        // [B][4096] bf16
   const uint16_t* wq;       // [4096][4096]
@@ -39,6 +55,8 @@ struct DecodeParams {
   uint16_t* o_lo;           // [B][4096] bf16 low part (o - hi)
   int* counters;            // [B][8] split arrival counters
   float* part;              // [B][8][nsplit][4][kPartStride]
+  uint32_t* kv_new;         // [B][2][8][64] appended K, V rows as packed bf16 pairs
+  int* sync;                // the workspace's synchronisation words
   int nsplit, chunk;        // positions split over nsplit workgroups of chunk keys
 };
 
@@ -52,6 +70,10 @@ hipError_t launch_rope_table(float* rope, int T_max, double theta, int scaled, h
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s);
+// Whether the fused one-launch schedule applies to this call's shape.
+bool decode_fused_eligible(int B, int nsplit);
+hipError_t launch_decode_fused(const DecodeParams& p, hipStream_t s);
+
 
 // ---------------------------------------------------------------------------
 // Prefill

@@ -37,7 +37,7 @@ constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V
 size_t prefill_ws_bytes(int B, int T) {
   const size_t M = (size_t)B * T;
   const size_t Tp = (size_t)(T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
-  size_t n = 0;
+  size_t n = kSyncBytes;                            // decode's synchronisation words, untouched
   n += align256((size_t)D * D * 2);                 // wo16
   n += align256(M * D * 2);                         // q16
   n += align256((size_t)B * KVH * Tp * HD * 2);     // k16
@@ -49,7 +49,7 @@ size_t prefill_ws_bytes(int B, int T) {
 void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
   const size_t M = (size_t)B * T;
   const size_t Tp = (size_t)p->Tp;
-  char* c = static_cast<char*>(ws);
+  char* c = static_cast<char*>(ws) + kSyncBytes;
   p->wo16 = reinterpret_cast<uint16_t*>(c);
   c += align256((size_t)D * D * 2);
   p->q16 = reinterpret_cast<uint16_t*>(c);

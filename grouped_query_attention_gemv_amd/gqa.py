@@ -22,6 +22,8 @@ ROPE_PAIRS = 64
 V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
+SYNC_BYTES = 65536
+DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
@@ -39,6 +41,9 @@ _SIGS = {
     "gqa_status_string": (ctypes.c_char_p, [_I]),
     "gqa_rope_table": (_I, [_I, ctypes.c_double, _I, _P, _P]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "gqa_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
+    "gqa_set_decode_schedule": (_I, [_I]),
+    "gqa_decode_schedule": (_I, [_I, _I, _I]),
     "gqa_block_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
                                ctypes.c_size_t, _P, _P]),
     "gqa_block_prefill_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
@@ -116,10 +121,38 @@ def workspace_bytes(B: int, T: int, T_max: int) -> int:
 
 
 def workspace(B: int, T: int, T_max: int, device) -> torch.Tensor:
+    """A workspace for these arguments, initialised (gqa_workspace_init) on
+    the current stream."""
     n = workspace_bytes(B, T, T_max)
     if n == 0:
         raise ValueError(f"no workspace size for B={B}, T={T}, T_max={T_max}")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().gqa_workspace_init(_ptr(ws), n, _stream(ws.device)), "gqa_workspace_init")
+    return ws
+
+
+def workspace_errors(ws: torch.Tensor) -> int:
+    """The workspace's sticky error word (nonzero after a fused decode whose
+    bounded waits timed out).  Synchronises with the device."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def set_decode_schedule(schedule: int) -> int:
+    """Process-wide decode schedule (DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED);
+    returns the previous one."""
+    prev = int(lib().gqa_set_decode_schedule(int(schedule)))
+    if prev < 0:
+        raise GQAError(prev, "gqa_set_decode_schedule")
+    return prev
+
+
+def decode_schedule(B: int, start_pos: int, T_max: int) -> int:
+    """The schedule a decode call of this shape runs (DECODE_SPLIT or
+    DECODE_FUSED) under the current setting."""
+    r = int(lib().gqa_decode_schedule(int(B), int(start_pos), int(T_max)))
+    if r < 0:
+        raise GQAError(r, "gqa_decode_schedule")
+    return r
 
 
 def empty_caches(B: int, T_max: int, device):

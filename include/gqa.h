@@ -70,6 +70,14 @@ extern "C" {
 #define GQA_MAX_BATCH   1024
 #define GQA_MAX_T_MAX   (1 << 20)
 
+/* Leading bytes of every workspace that hold the decode synchronisation words. */
+#define GQA_SYNC_BYTES  65536
+
+/* Decode schedules (gqa_set_decode_schedule). */
+#define GQA_DECODE_AUTO   0             /* fused where the shape admits it, else split */
+#define GQA_DECODE_SPLIT  1             /* three launches: QKV, attention, wo */
+#define GQA_DECODE_FUSED  2             /* one launch; shapes it does not admit fail */
+
 /* Number of stages whose boundaries the *_profiled entry points record. */
 #define GQA_DECODE_STAGES   3           /* QKV+RoPE+append, attention, wo */
 #define GQA_PREFILL_STAGES  4           /* wo to fp16, QKV+RoPE+append, attention, wo */
@@ -111,10 +119,45 @@ int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t
 /*
  * gqa_workspace_bytes -- device scratch needed by gqa_block_prefill(B, T) and
  * by gqa_block_decode(B, start_pos < T_max) with these arguments; 0 when the
- * arguments are out of range.  The workspace needs no initialisation and
- * holds nothing the caller reads; calls that share one must be ordered.
+ * arguments are out of range.  Calls that share a workspace must be ordered
+ * (one stream, or events): they reuse its contents.
+ *
+ * The first GQA_SYNC_BYTES bytes hold the synchronisation words of the fused
+ * decode schedule.  They must be zero before the first call on a workspace
+ * (gqa_workspace_init); every call leaves them zero and prefill never writes
+ * them.  Their first int is a sticky error word: nonzero after a fused decode
+ * whose bounded waits timed out (that call's outputs are invalid; initialise
+ * the workspace again).  The rest holds nothing the caller reads.
  */
 size_t gqa_workspace_bytes(int B, int T, int T_max);
+
+/*
+ * gqa_workspace_init -- zero the synchronisation words of a workspace of
+ * ws_bytes bytes (one hipMemsetAsync on stream, not to be captured in a graph).
+ * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (< GQA_SYNC_BYTES),
+ * GQA_ERR_HIP.
+ */
+int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Decode schedule.  GQA_DECODE_SPLIT runs the three stages as three kernels.
+ * GQA_DECODE_FUSED runs the whole step as one kernel whose workgroups pass
+ * results to each other through the workspace (Q/K/V -> attention -> wo), so
+ * that each consumer's HBM reads overlap its producer's; it admits B <= 2 and
+ * contexts short enough for at most 128 attention workgroups (start_pos + 1
+ * <= 2048 at B = 1, <= 1024 at B = 2).  GQA_DECODE_AUTO (the default) takes
+ * the fused schedule where it is admitted.  Results agree between schedules
+ * to rounding; each schedule is deterministic.
+ *
+ * gqa_set_decode_schedule sets the process-wide choice and returns the
+ * previous one (GQA_ERR_ARG for an unknown value); gqa_decode_schedule
+ * returns the schedule a decode call of this shape would run
+ * (GQA_DECODE_SPLIT or GQA_DECODE_FUSED), or GQA_ERR_ARG when the setting is
+ * GQA_DECODE_FUSED and the shape is not admitted (the call would fail with
+ * that code), GQA_ERR_SHAPE / GQA_ERR_RANGE for invalid arguments.
+ */
+int gqa_set_decode_schedule(int schedule);
+int gqa_decode_schedule(int B, int start_pos, int T_max);
 
 /*
  * gqa_block_prefill -- the block over T new tokens of B sequences starting
@@ -153,6 +196,8 @@ int gqa_block_prefill(const gqa_bf16* x,
  *              after the update (the next block's input in a stack of blocks)
  * Aliasing: out, out_bf16, probe, ws and the caches must not overlap each
  * other or the inputs.
+ * Runs the schedule gqa_decode_schedule(B, start_pos, T_max) names; returns
+ * GQA_ERR_ARG if that is an error.
  */
 int gqa_block_decode(const gqa_bf16* x,
                      const gqa_bf16* wq, const gqa_bf16* wk,
@@ -168,7 +213,9 @@ int gqa_block_decode(const gqa_bf16* x,
  * events[0] on `stream` before the first kernel and events[i] after stage i
  * (GQA_PREFILL_STAGES / GQA_DECODE_STAGES stages), so that a caller can time
  * each kernel with hipEventElapsedTime.  events must hold that many + 1
- * created hipEvent_t handles.
+ * created hipEvent_t handles.  Under the fused decode schedule the step is
+ * one kernel: events[1] follows it and the later events are recorded
+ * immediately after.
  */
 int gqa_block_prefill_profiled(const gqa_bf16* x,
                                const gqa_bf16* wq, const gqa_bf16* wk,

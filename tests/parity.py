@@ -121,9 +121,11 @@ class DecodeCase:
     def run(self, probe=True):
         self.probe = torch.empty((self.B, G.QKV_DIM), dtype=torch.float32, device=self.dev) \
             if probe else None
+        self.ws = G.workspace(self.B, 1, self.T_max, self.dev)
         self.out = G.block_decode(self.xd, *self.wd, self.kcache, self.vcache, self.rope,
-                                  self.P, probe=self.probe)
+                                  self.P, ws=self.ws, probe=self.probe)
         torch.cuda.synchronize()
+        assert G.workspace_errors(self.ws) == 0, "a bounded wait of the fused decode timed out"
         return self.out
 
     def oracle(self, seqs=None):

@@ -137,3 +137,55 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros(1, 4096, dtype=torch.bfloat16)
     with pytest.raises((ValueError, TypeError)):
         G.block_decode(x, x, x, x, x, x, x, x, 0)
+
+
+def test_workspace_starts_with_the_sync_region():
+    assert G.SYNC_BYTES == 65536
+    for args in ((1, 1, 64), (4, 2048, 2048), (64, 1, 8224)):
+        assert G.workspace_bytes(*args) > G.SYNC_BYTES
+    src = open(HEADER).read()
+    assert "#define GQA_SYNC_BYTES  65536" in src
+
+
+def test_workspace_init_rejections():
+    lib = G.lib()
+    assert lib.gqa_workspace_init(None, 1 << 20, None) == ENULL
+    assert lib.gqa_workspace_init(ctypes.c_void_p(BASE + 8), 1 << 20, None) == EALIGN
+    assert lib.gqa_workspace_init(_fake(1), G.SYNC_BYTES - 1, None) == EWS
+
+
+def test_decode_schedule_selection():
+    prev = G.set_decode_schedule(G.DECODE_AUTO)
+    try:
+        F, S = G.DECODE_FUSED, G.DECODE_SPLIT
+        # fused while the attention grid (splits of 128 positions x 8 kv heads x B)
+        # stays within 128 workgroups, and B <= 2
+        assert G.decode_schedule(1, 0, 64) == F
+        assert G.decode_schedule(1, 1000, 1024) == F
+        assert G.decode_schedule(1, 2047, 4096) == F
+        assert G.decode_schedule(1, 2048, 4096) == S
+        assert G.decode_schedule(2, 1023, 2048) == F
+        assert G.decode_schedule(2, 1024, 2048) == S
+        assert G.decode_schedule(3, 10, 64) == S
+        assert G.decode_schedule(64, 8192, 8224) == S
+        G.set_decode_schedule(G.DECODE_SPLIT)
+        assert G.decode_schedule(1, 1000, 1024) == S
+        G.set_decode_schedule(G.DECODE_FUSED)
+        assert G.decode_schedule(1, 1000, 1024) == F
+        with pytest.raises(G.GQAError):
+            G.decode_schedule(3, 10, 64)
+        assert G.lib().gqa_decode_schedule(1, 64, 64) == ERANGE
+        assert G.lib().gqa_decode_schedule(0, 1, 64) == ESHAPE
+        assert G.lib().gqa_set_decode_schedule(7) == EARG
+    finally:
+        G.set_decode_schedule(prev)
+
+
+def test_fused_schedule_rejects_shapes_it_does_not_admit():
+    # B = 3 under a forced fused schedule: rejected before any device call
+    prev = G.set_decode_schedule(G.DECODE_FUSED)
+    try:
+        assert G.lib().gqa_block_decode(*_decode_args(B=3)) == EARG
+        assert G.lib().gqa_block_decode(*_decode_args(B=1, start_pos=4000, T_max=4096)) == EARG
+    finally:
+        G.set_decode_schedule(prev)

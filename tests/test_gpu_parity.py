@@ -40,6 +40,16 @@ def test_rope_table_matches_oracle(scaled):
 # Decode
 # ----------------------------------------------------------------------------
 
+@pytest.fixture(params=["split", "fused"])
+def schedule(request):
+    """Run the test under the three-launch and under the one-launch decode
+    schedule (every shape these tests use is admitted by both)."""
+    mode = {"split": G.DECODE_SPLIT, "fused": G.DECODE_FUSED}[request.param]
+    prev = G.set_decode_schedule(mode)
+    yield request.param
+    G.set_decode_schedule(prev)
+
+
 def _decode_full(B, P, T_max, **kw):
     c = DecodeCase(B, P, T_max, dev=DEV, **kw)
     c.run()
@@ -48,12 +58,12 @@ def _decode_full(B, P, T_max, **kw):
     return c, errs
 
 
-def test_decode_start_pos_128():
+def test_decode_start_pos_128(schedule):
     """B=1, start_pos=128: rows 0-127 cached, row 128 written, rows 0-128 read."""
     _decode_full(1, 128, 256)
 
 
-def test_decode_p1000():
+def test_decode_p1000(schedule):
     """B=1 at the pages' decode point: P = 1,000 cached, row 1,000 written."""
     _, errs = _decode_full(1, 1000, 1024)
     # fp32 Q/P/O with hi/lo bf16 matrix-core operands: far inside the bound
@@ -61,7 +71,7 @@ def test_decode_p1000():
 
 
 @pytest.mark.parametrize("P", [0, 1, 31, 32, 33, 127, 128, 129, 255, 1023])
-def test_decode_positions(P):
+def test_decode_positions(P, schedule):
     """Single key, tile and split edges."""
     _decode_full(2, P, 1024)
 
@@ -77,7 +87,7 @@ def test_decode_unscaled_rope():
     _decode_full(1, 5000, 5024, scaled=False)
 
 
-def test_decode_accumulate_and_bf16_out():
+def test_decode_accumulate_and_bf16_out(schedule):
     """out += Delta with the bf16 copy of the updated residual."""
     c = DecodeCase(2, 100, 128, dev=DEV)
     res = c.oracle()
@@ -152,14 +162,44 @@ def test_decode_stacked_blocks_residual():
     assert torch.equal(xa.cpu(), h.cpu().to(torch.bfloat16))
 
 
+def test_decode_fused_largest_admitted_context(schedule):
+    """B=1 at start_pos 2,047: 16 splits x 8 kv heads, the most attention
+    workgroups the one-launch schedule admits."""
+    _decode_full(1, 2047, 2048)
+
+
+def test_decode_schedules_agree_bitwise():
+    """Both schedules run the same arithmetic in the same order: identical
+    outputs and caches; the workspace's synchronisation words are zero again
+    after every call of either schedule."""
+    outs, caches = [], []
+    ws = G.workspace(2, 1, 1024, DEV)
+    for mode in (G.DECODE_FUSED, G.DECODE_SPLIT, G.DECODE_FUSED):
+        prev = G.set_decode_schedule(mode)
+        try:
+            c = DecodeCase(2, 777, 1024, dev=DEV)
+            out = G.block_decode(c.xd, *c.wd, c.kcache, c.vcache, c.rope, c.P, ws=ws)
+            torch.cuda.synchronize()
+        finally:
+            G.set_decode_schedule(prev)
+        outs.append(out.clone())
+        caches.append((c.kcache.clone(), c.vcache.clone()))
+        assert int(ws[:G.SYNC_BYTES].view(torch.int32).abs().sum().item()) == 0
+    for o, (k, v) in zip(outs[1:], caches[1:]):
+        assert torch.equal(o, outs[0])
+        assert torch.equal(k.view(torch.int16), caches[0][0].view(torch.int16))
+        assert torch.equal(v.view(torch.int16), caches[0][1].view(torch.int16))
+
+
 def test_decode_is_deterministic():
-    c = DecodeCase(4, 1000, 1024, dev=DEV)
-    a = c.run().clone()
-    b = c.run().clone()
-    assert torch.equal(a, b)
+    for B in (1, 4):     # one-launch and three-launch schedules
+        c = DecodeCase(B, 1000, 1024, dev=DEV)
+        a = c.run().clone()
+        b = c.run().clone()
+        assert torch.equal(a, b)
 
 
-def test_decode_in_hip_graph_matches_eager():
+def test_decode_in_hip_graph_matches_eager(schedule):
     """A captured decode call, replayed several times with eager work and
     synchronisations between replays, reproduces the eager result bit for bit
     (the library issues no memset, so nothing in the graph depends on one)."""
