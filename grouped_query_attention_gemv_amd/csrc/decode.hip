@@ -10,6 +10,8 @@
 //   decode_wo_kernel    Delta = O Wo^T as a bandwidth GEMV (+ residual)
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -686,31 +688,37 @@ __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
 // Batched decode projections on the matrix cores
 // ---------------------------------------------------------------------------
 //
-// For more tokens than the bandwidth GEMV handles in one pass, the weights
-// are streamed once through v_mfma_f32_16x16x32_bf16:
-//   C^T[16 features x 16 columns] += W[16 features x k] . X^T[k x 16 columns]
-// A workgroup owns 16 output features; its 8 waves split K = 4096 into
-// slices of 512.  Lane (r = lane & 15, q = lane >> 4) loads W[f0 + r][slice
-// + 32 ks + 8 q .. +8] for ks < 16: exactly its A operand, 16 KiB per wave in
-// flight, as in the GEMV.  The B operand (activation columns) is read from
-// L2.  Slices are summed in LDS; each lane of the result then holds 4
-// consecutive features of one column, so RoPE pairs are register-local.
-// Columns are tokens for the QKV projection, and (token, hi/lo part) pairs
-// for wo, whose input O is the sum of two bf16 parts.
-constexpr int kProjWaves = 8;
-
+// Above 8 tokens the weights are streamed once through
+// v_mfma_f32_16x16x32_bf16 as a split-K GEMM, C^T[features x columns] +=
+// W[features x k] . X^T[k x columns]:
+//  - workgroup (fb, ks) owns 128 output features and one of KS equal K
+//    ranges (KS = 4 for QKV, 8 for wo); its 4 waves own 32 features each
+//    (two 16-row A tiles);
+//  - K advances in chunks of 128.  The chunk of the activation columns (up to
+//    64 per launch) is copied once into LDS (global_load_lds) and read by all
+//    4 waves as the B operand, so each activation byte leaves L2 once per
+//    workgroup.  Each wave's weight rows come straight from HBM into
+//    registers (its A operand).  Both stream three chunks ahead;
+//  - the KS K ranges of a feature block are summed by the last of its KS
+//    workgroups to finish (device-scope partials and counter, fixed order),
+//    which then runs the epilogue.
+// Workgroup i runs on XCD i % 8, and the K ranges alternate with i, so every
+// workgroup of an XCD reads the same activation range from its L2.
+// Columns are tokens.  For wo the input O is the sum of two bf16 parts: each
+// weight fragment multiplies both parts into the same accumulator.
 // QKV epilogue of one column (token b) and features f .. f+3 (one head):
-// RoPE on Q/K pairs, Q to the workspace, K/V rounded into the cache.
-__device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, int b, int f) {
+// RoPE on Q/K pairs with the table entries cs0 (pair f/2) and cs1 (pair
+// f/2 + 1), Q to the workspace, K/V rounded into the cache.
+__device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, int b, int f,
+                                               float2 cs0, float2 cs1) {
   const int pos = p.start_pos;
   float y[4] = {v[0], v[1], v[2], v[3]};
   if (f < D + KVH * HD) {
-    const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)pos * PAIRS;
+    const float2 cs[2] = {cs0, cs1};
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
-      const float2 cs = rrow[((f + e) & (HD - 1)) >> 1];
-      const float a = y[e] * cs.x - y[e + 1] * cs.y;
-      const float bb = y[e] * cs.y + y[e + 1] * cs.x;
+      const float a = y[e] * cs[e / 2].x - y[e + 1] * cs[e / 2].y;
+      const float bb = y[e] * cs[e / 2].y + y[e + 1] * cs[e / 2].x;
       y[e] = a;
       y[e + 1] = bb;
     }
@@ -730,92 +738,218 @@ __device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, i
     for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
   }
 }
-constexpr int kProjTiles = 4;            // column tiles of 16 per pass
+constexpr int kP2Feat = 128;                 // features per workgroup
+constexpr int kP2Kc = 128;                   // K per chunk
+// K splits: 4 for QKV (192 workgroups), 8 for wo (256 workgroups)
+template <int MODE>
+constexpr int p2_splits() { return MODE == 0 ? 4 : 8; }
+constexpr int kP2Cols = 64;                  // columns per launch
+constexpr int kP2Ring = 4;                   // chunks in flight: loaded 3 ahead
+
+// 16-byte device-scope store at base + byte_off (base wave-uniform).
+__device__ __forceinline__ void st_dev_x4(void* base, uint32_t byte_off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16);
+}
 
 template <int MODE>   // 0: QKV + RoPE + cache append, 1: wo (+ residual)
-__global__ void __launch_bounds__(512) decode_proj_mfma_kernel(DecodeParams p) {
-  __shared__ f32x4 red[kProjWaves][kProjTiles][64];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4;
-  const int f0 = blockIdx.x * 16;
-  if (MODE == 0 && blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+__global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_base) {
+  constexpr int NP = MODE == 0 ? 1 : 2;        // activation parts (wo: hi, lo)
+  constexpr int kP2KS = p2_splits<MODE>();
+  constexpr int kP2Kr = D / kP2KS;             // K range of a workgroup
+  constexpr int kP2Chunks = kP2Kr / kP2Kc;
+  // [NP][kP2Ring buffers][64 rows][128 K] bf16, dynamic
+  extern __shared__ __attribute__((aligned(16))) uint16_t sx_dyn[];
+  __shared__ int sm_last;
+#define GQA_SX(part, buf) (sx_dyn + ((part) * kP2Ring + (buf)) * (kP2Cols * kP2Kc))
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int ks = blockIdx.x % kP2KS, fb = blockIdx.x / kP2KS;
+  const int ncols = min(kP2Cols, p.B - c_base);
+  const int kbase = ks * kP2Kr;
+  if (MODE == 0 && blockIdx.x == 0 && c_base == 0) {
+    // the attention kernel that follows counts split arrivals from zero
+    for (int i = tid; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
   }
 
-  const uint16_t* wrow;
-  if (MODE == 0) {
-    const int f = f0 + r;
-    wrow = f < D ? p.wq + (size_t)f * D
-                 : (f < D + KVH * HD ? p.wk + (size_t)(f - D) * D
-                                     : p.wv + (size_t)(f - D - KVH * HD) * D);
-  } else {
-    wrow = p.wo + (size_t)(f0 + r) * D;
-  }
-  const int k0 = w * (D / kProjWaves) + q * 8;
-  u32x4 wa[16];
+  // A operand: weight row of tile ft, k offset (lane >> 4) * 8 in each step
+  const uint16_t* wrow[2];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) wa[ks] = ld_nt_u32x4(wrow + k0 + ks * 32);
+  for (int ft = 0; ft < 2; ++ft) {
+    const int f = fb * kP2Feat + 32 * w + 16 * ft + (lane & 15);
+    if (MODE == 0)
+      wrow[ft] = (f < D ? p.wq + (size_t)f * D
+                        : (f < D + KVH * HD ? p.wk + (size_t)(f - D) * D
+                                            : p.wv + (size_t)(f - D - KVH * HD) * D)) +
+                 kbase + (lane >> 4) * 8;
+    else
+      wrow[ft] = p.wo + (size_t)f * D + kbase + (lane >> 4) * 8;
+  }
+  // activation copies: instruction j of this wave fills rows (4w + j) * 4 ..
+  // + 3 of the chunk (256 bytes each); lane i writes row +i/16, LDS chunk
+  // i % 16, which holds logical chunk (i % 16) ^ (row & 7)
+  const uint16_t* xsrc[NP][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * w + j) * 4 + (lane >> 4);
+    const int col = c_base + min(row, ncols - 1);
+    const int lchunk = (lane & 15) ^ (row & 7);
+#pragma unroll
+    for (int part = 0; part < NP; ++part) {
+      const uint16_t* base = MODE == 0 ? p.x : (part == 0 ? p.o_hi : p.o_lo);
+      xsrc[part][j] = base + (size_t)col * D + kbase + lchunk * 8;
+    }
+  }
 
-  const int ncols = MODE == 0 ? p.B : 2 * p.B;
-  for (int c0 = 0; c0 < ncols; c0 += 16 * kProjTiles) {
-    f32x4 acc[kProjTiles];
-    // activation operands in two halves of 8 k-steps, so the kernel fits in
-    // 128 VGPRs and two workgroups (every one of the grid) stay resident per CU
+  u32x4 wb[kP2Ring][2][4];                      // [ring slot][tile][k-step]
+  auto load_w = [&](int chunk, u32x4 (&dst)[2][4]) {
 #pragma unroll
-    for (int t = 0; t < kProjTiles; ++t) {
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (c0 + t * 16 >= ncols) continue;                       // wave-uniform
-      const int c = c0 + t * 16 + r;
-      const int cc = min(c, ncols - 1);
-      const uint16_t* xrow = MODE == 0 ? p.x + (size_t)cc * D
-                                       : ((cc & 1) ? p.o_lo : p.o_hi) + (size_t)(cc >> 1) * D;
+    for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 xb[8];
+      for (int s = 0; s < 4; ++s) dst[ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kP2Kc + s * 32);
+  };
+  auto load_x = [&](int chunk, int buf) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) xb[ks] = ld_u32x4(xrow + k0 + (h * 8 + ks) * 32);
-        if (c >= ncols) {
+    for (int part = 0; part < NP; ++part)
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) xb[ks] = u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xsrc[part][j] + chunk * kP2Kc),
+                                         (lds_void*)(GQA_SX(part, buf) + (4 * w + j) * 4 * kP2Kc), 16, 0, 0);
+  };
+
+  f32x4 acc[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) acc[t] = mfma_bf16(wa[h * 8 + ks], xb[ks], acc[t]);
-      }
-    }
+  for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int t = 0; t < kProjTiles; ++t) red[w][t][lane] = acc[t];
-    __syncthreads();
-    if (w < kProjTiles && c0 + w * 16 < ncols) {
-      f32x4 v = red[0][w][lane];
+    for (int t = 0; t < 4; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Chunks are loaded kP2Ring - 1 ahead, each as W(c) then X(c) (8 + 4 NP
+  // loads per wave).  Chunk c has landed once no more than the loads of the
+  // chunks issued after it remain in flight.
+  constexpr int kPerChunk = 8 + 4 * NP;
 #pragma unroll
-      for (int ww = 1; ww < kProjWaves; ++ww) v += red[ww][w][lane];
-      // lane holds features f0 + 4q + e (e < 4) of column c0 + 16w + r
-      const int c = c0 + w * 16 + r;
-      const int f = f0 + 4 * q;
-      if (MODE == 0) {
-        if (c < ncols) proj_qkv_store(p, v, c, f);
-      } else {
-        // columns 2t (hi part) and 2t+1 (lo part) of token t sit in lanes r, r^1
-        f32x4 other;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) other[e] = dpp<DPP_QUAD_XOR1>(v[e]);
-        if ((r & 1) == 0 && c < ncols) {
-          const int b = c >> 1;
-          float4 y = make_float4(v[0] + other[0], v[1] + other[1], v[2] + other[2], v[3] + other[3]);
-          float4* o = reinterpret_cast<float4*>(p.out + (size_t)b * D + f);
-          if (p.accumulate) {
-            const float4 prev = *o;
-            y.x += prev.x; y.y += prev.y; y.z += prev.z; y.w += prev.w;
-          }
-          *o = y;
-          if (p.out_bf16)
-            *reinterpret_cast<u32x2*>(p.out_bf16 + (size_t)b * D + f) =
-                u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)};
-        }
-      }
-    }
-    __syncthreads();
+  for (int c = 0; c < kP2Ring - 1; ++c) {
+    load_w(c, wb[c]);
+    load_x(c, c);
   }
+#pragma unroll
+  for (int c = 0; c < kP2Chunks; ++c) {
+    const int later = min(kP2Ring - 2, kP2Chunks - 1 - c);    // chunks issued after c
+    if (later == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerChunk) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerChunk) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // bare barrier: the waits are explicit above; every wave finished reading
+    // the slot refilled below in the previous chunk
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + kP2Ring - 1 < kP2Chunks) {
+      load_w(c + kP2Ring - 1, wb[(c + kP2Ring - 1) % kP2Ring]);
+      load_x(c + kP2Ring - 1, (c + kP2Ring - 1) % kP2Ring);
+    }
+    // all of the chunk's B fragments of a part are read before its matrix
+    // work, so the LDS reads overlap one another (column tiles past ncols
+    // read rows of the copy that clamped onto the last column; their
+    // results are never stored)
+#pragma unroll
+    for (int part = 0; part < NP; ++part) {
+      u32x4 xb[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = 16 * t + (lane & 15);
+          const int off = row * kP2Kc + (((4 * s + (lane >> 4)) ^ (row & 7)) << 3);
+          xb[s][t] = *reinterpret_cast<const u32x4*>(GQA_SX(part, c % kP2Ring) + off);
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int ft = 0; ft < 2; ++ft) acc[ft][t] = mfma_bf16(wb[c % kP2Ring][ft][s], xb[s][t], acc[ft][t]);
+    }
+  }
+
+  // partials [fb][ks][64 columns][128 features] fp32; lane holds features
+  // 32w + 16ft + 4(lane >> 4) + e (e < 4) of column 16t + (lane & 15)
+  float* part_fb = p.part;
+  const uint32_t pbase = (uint32_t)((fb * kP2KS + ks) * kP2Cols) * kP2Feat * 4u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = 16 * t + (lane & 15);
+    if (col >= ncols) continue;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const int fl = 32 * w + 16 * ft + 4 * (lane >> 4);
+      st_dev_x4(part_fb, pbase + (uint32_t)(col * kP2Feat + fl) * 4u,
+                __builtin_bit_cast(u32x4, acc[ft][t]));
+    }
+  }
+  wait_vm();
+  __syncthreads();
+  int* cnt = p.sync + kSyncProj + 32 * fb;
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = prev == kP2KS - 1;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  if (tid == 0) st_dev(cnt, 0);
+
+  // last of the feature block: sum the K ranges in order, then the epilogue;
+  // all of a thread's loads (partials, RoPE entries, the residual) go out
+  // before the first is used
+  constexpr int kItems = kP2Cols * (kP2Feat / 4) / 256;     // 8 per thread
+  constexpr int kBatch = kP2KS <= 4 ? kItems : kItems / 2;  // items whose loads go out together
+  const int nitems = ncols * (kP2Feat / 4);
+  const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)p.start_pos * PAIRS;
+  for (int it0 = 0; it0 < kItems; it0 += kBatch) {
+  u32x4 parts[kBatch][kP2KS];
+  float4 aux[kBatch];                          // RoPE pair entries, or the residual
+#pragma unroll
+  for (int it = 0; it < kBatch; ++it) {
+    const int i = tid + 256 * (it0 + it);
+    if (i >= nitems) continue;
+    const int col = i / (kP2Feat / 4), f4 = i % (kP2Feat / 4);
+    const int f = fb * kP2Feat + 4 * f4;
+#pragma unroll
+    for (int k = 0; k < kP2KS; ++k)
+      parts[it][k] = ld_dev_x4(part_fb, (uint32_t)((((fb * kP2KS + k) * kP2Cols + col) * kP2Feat) + 4 * f4) * 4u);
+    if (MODE == 0) {
+      // pairs (f, f+1) and (f+2, f+3): two consecutive table entries
+      aux[it] = *reinterpret_cast<const float4*>(rrow + ((f & (HD - 1)) >> 1));
+    } else if (p.accumulate) {
+      aux[it] = *reinterpret_cast<const float4*>(p.out + (size_t)(c_base + col) * D + f);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kBatch; ++it) {
+    const int i = tid + 256 * (it0 + it);
+    if (i >= nitems) continue;
+    const int col = i / (kP2Feat / 4), f4 = i % (kP2Feat / 4);
+    f32x4 v = __builtin_bit_cast(f32x4, parts[it][0]);
+#pragma unroll
+    for (int k = 1; k < kP2KS; ++k) v += __builtin_bit_cast(f32x4, parts[it][k]);
+    const int b = c_base + col;
+    const int f = fb * kP2Feat + 4 * f4;
+    if (MODE == 0) {
+      proj_qkv_store(p, v, b, f, make_float2(aux[it].x, aux[it].y), make_float2(aux[it].z, aux[it].w));
+    } else {
+      float4 y = make_float4(v[0], v[1], v[2], v[3]);
+      if (p.accumulate) {
+        y.x += aux[it].x; y.y += aux[it].y; y.z += aux[it].z; y.w += aux[it].w;
+      }
+      *reinterpret_cast<float4*>(p.out + (size_t)b * D + f) = y;
+      if (p.out_bf16)
+        *reinterpret_cast<u32x2*>(p.out_bf16 + (size_t)b * D + f) =
+            u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)};
+    }
+  }
+  }
+#undef GQA_SX
 }
 
 // ---------------------------------------------------------------------------
@@ -841,12 +975,24 @@ void decode_split(int B, int L, int* nsplit, int* chunk) {
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Partials: the attention splits' (m, l, o), and for B > 8 also the split-K
+// partials of the projections (the two never live at the same time).
+static size_t decode_part_bytes(int B) {
+  size_t n = (size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4;
+  if (B > kGemvMaxB) {
+    const size_t qkv = (size_t)NQKV * p2_splits<0>() * kP2Cols * 4;
+    const size_t wo = (size_t)D * p2_splits<1>() * kP2Cols * 4;
+    n = std::max(n, std::max(qkv, wo));
+  }
+  return n;
+}
+
 size_t decode_ws_bytes(int B) {
   size_t n = kSyncBytes;
   n += align256((size_t)B * D * 4);                       // q
   n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
   n += align256((size_t)B * KVH * 4);                     // counters
-  n += align256((size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4);  // partials
+  n += align256(decode_part_bytes(B));                   // partials
   n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new
   return n;
 }
@@ -864,7 +1010,7 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   p->counters = reinterpret_cast<int*>(c);
   c += align256((size_t)B * KVH * 4);
   p->part = reinterpret_cast<float*>(c);
-  c += align256((size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4);
+  c += align256(decode_part_bytes(B));
   p->kv_new = reinterpret_cast<uint32_t*>(c);
 }
 
@@ -882,7 +1028,9 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
 
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
-    hipLaunchKernelGGL(decode_proj_mfma_kernel<0>, dim3(NQKV / 16), dim3(512), 0, s, p);
+    for (int c = 0; c < p.B; c += kP2Cols)
+      hipLaunchKernelGGL(decode_proj_kernel<0>, dim3(NQKV / kP2Feat * p2_splits<0>()), dim3(256),
+                         kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
     return hipGetLastError();
   }
   const int blocks = NQKV / 2 / 4;    // one wave per row pair, 4 waves per workgroup
@@ -903,7 +1051,9 @@ hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
-    hipLaunchKernelGGL(decode_proj_mfma_kernel<1>, dim3(D / 16), dim3(512), 0, s, p);
+    for (int c = 0; c < p.B; c += kP2Cols)
+      hipLaunchKernelGGL(decode_proj_kernel<1>, dim3(D / kP2Feat * p2_splits<1>()), dim3(256),
+                         2 * kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
     return hipGetLastError();
   }
   const int blocks = D / 2 / 4;

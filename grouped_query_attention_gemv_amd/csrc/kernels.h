@@ -29,12 +29,14 @@ constexpr int kSyncErr = 0;          // sticky error bits: 1 attention wait, 2 w
 constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups of kv head g
 constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
 constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
+constexpr int kSyncProj = 10752;     // + 32*fb: K ranges of projection feature block fb summed
 constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
 constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
 constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
 constexpr int kFusedWoWG = 512;      // 8 wo rows each
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
-static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncBytes / 4, "sync region too small");
+static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
+static_assert(kSyncProj + 32 * (6144 / 128) <= kSyncBytes / 4, "sync region too small");
 
 struct DecodeParams {
   const uint16_t* x;        // [B][4096] bf16

@@ -22,7 +22,6 @@
 
 namespace gqa {
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 

@@ -189,3 +189,12 @@ def test_fused_schedule_rejects_shapes_it_does_not_admit():
         assert G.lib().gqa_block_decode(*_decode_args(B=1, start_pos=4000, T_max=4096)) == EARG
     finally:
         G.set_decode_schedule(prev)
+
+
+def test_library_has_no_unresolved_symbols_of_its_own():
+    # a kernel whose host-side launch stub failed to instantiate shows up as
+    # an undefined gqa:: symbol; loading the library lazily would not notice
+    out = subprocess.run(["nm", "-D", "--undefined-only", "-C", GB.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    mine = [l for l in out.splitlines() if "gqa::" in l or "gqa_" in l]
+    assert mine == [], mine
