@@ -121,14 +121,14 @@ constexpr int kGroupM = 4;                             // m-tiles per tile-order
 
 enum GemmKind { GEMM_QKV = 0, GEMM_OUT = 1 };
 
-// Row of B feeding tile column j of an n-tile starting at n0.  For the QKV
-// projection each 32-column block holds the even features of 16 rotation
-// pairs in its first 16 columns and the odd ones in the next 16, so the two
-// members of a pair land in the same lane of neighbouring accumulators.
-template <int KIND>
+// Row of B feeding tile column j of an n-tile starting at n0.  Each
+// 32-column block holds the even features of 16 consecutive pairs in its
+// first 16 columns and the odd ones in the next 16, so features (f, f+1) land
+// in the same lane of neighbouring accumulators: the QKV epilogue rotates
+// RoPE pairs in place, and both epilogues stage feature pairs as one 8-byte
+// LDS write.
 __device__ __forceinline__ int b_row_of(int n0, int j) {
-  if (KIND == GEMM_QKV) return n0 + (j & ~31) + 2 * (j & 15) + ((j >> 4) & 1);
-  return n0 + j;
+  return n0 + (j & ~31) + 2 * (j & 15) + ((j >> 4) & 1);
 }
 
 template <int KIND>
@@ -151,9 +151,12 @@ struct GemmArgs {
   PrefillParams p;
 };
 
-template <int REGION>
-__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], int mw,
-                                             int fw, int lane);
+template <int REGION, int HALF>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
+                                             int mw, int fw, int lane);
+template <int HALF>
+__device__ __forceinline__ void out_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
+                                             int mw, int fw, int lane);
 
 template <int KIND>
 __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
@@ -189,7 +192,7 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     const int r = w * 32 + i * 8 + lrow;
     const int am = min(m0 + r, g.M - 1);
     a_src[i] = g.a + (size_t)am * D + lchunk * 8;
-    const int br = b_row_of<KIND>(n0, r);
+    const int br = b_row_of(n0, r);
     b_src[i] = b_row_ptr<KIND>(g.b0, g.b1, g.b2, br) + lchunk * 8;
   }
 
@@ -243,84 +246,200 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     }
   }
 
-  // epilogue: acc[i][j][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
-  //                             [tile col wn*64 + j*16 + (lane&15)]
-  // The region (Q, K or V features) is uniform over the workgroup's n-tile,
-  // so each region gets its own small, fully unrolled loop nest and the
-  // accumulators stay in registers.
+  // epilogue: acc[i][2u+s][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
+  //                               [feature n0 + wn*64 + 32u + 2*(lane&15) + s].
+  // Once every wave is done with the last stage, wave w stages its 128 x 64
+  // block through its own 16 KiB of LDS, 64 rows at a time, and writes it
+  // with 16-byte stores.  The region (Q, K or V features) is uniform over
+  // the workgroup's n-tile.
+  __syncthreads();
+  char* st = smem + w * 16384;
+  const int mw = m0 + wm * 128, fw = n0 + 64 * wn;
   if (KIND == GEMM_QKV) {
-    if (n0 < D)
-      qkv_epilogue<0>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
-    else if (n0 < D + KVH * HD)
-      qkv_epilogue<1>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
-    else
-      qkv_epilogue<2>(g, acc, m0 + wm * 128, n0 + 64 * wn, lane);
+    if (n0 < D) {
+      qkv_epilogue<0, 0>(g, acc, st, mw, fw, lane);
+      qkv_epilogue<0, 1>(g, acc, st, mw, fw, lane);
+    } else if (n0 < D + KVH * HD) {
+      qkv_epilogue<1, 0>(g, acc, st, mw, fw, lane);
+      qkv_epilogue<1, 1>(g, acc, st, mw, fw, lane);
+    } else {
+      qkv_epilogue<2, 0>(g, acc, st, mw, fw, lane);
+      qkv_epilogue<2, 1>(g, acc, st, mw, fw, lane);
+    }
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + wm * 128 + i * 16 + (lane >> 4) * 4 + e;
-          if (m < g.M) g.p.out[(size_t)m * D + n] = acc[i][j][e];
-        }
-      }
+    out_epilogue<0>(g, acc, st, mw, fw, lane);
+    out_epilogue<1>(g, acc, st, mw, fw, lane);
   }
 }
 
-// QKV epilogue over a wave's 128 x 128 block (rows from mw, features from fw).
-// REGION 0: Q (rotate, scale by log2(e)/sqrt(128), fp16 to the workspace);
-// REGION 1: K (rotate, bf16 to the cache, fp16 copy); REGION 2: V (bf16 to the
-// dimension-major cache, fp16 copy).  Column pair (acc[i][2u], acc[i][2u+1])
-// of lane l holds features (f, f+1) with f = fw + 32u + 2*(l & 15).
-template <int REGION>
-__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], int mw,
-                                             int fw, int lane) {
-  const PrefillParams& p = g.p;
+// Epilogue staging.  Rows [64*HALF, 64*HALF + 64) of a wave's block go to
+// its 16 KiB of LDS as fp32, either row-major (row r: 64 features in 16
+// units of 16 bytes, unit u at u ^ (r & 15)) or, for V, feature-major
+// (feature c: 64 rows in 16 units, unit u at u ^ (c & 15)).
+__device__ __forceinline__ int stage_off(int line, int unit) {
+  return line * 256 + ((unit ^ (line & 15)) << 4);
+}
+
+template <int HALF>
+__device__ __forceinline__ void stage_rows(char* st, const f32x4 (&acc)[8][4], int lane) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = mw + i * 16 + (lane >> 4) * 4 + e;
-      if (m >= g.M) continue;
-      const int b = m / p.T, t = m - b * p.T;
-      const float2* rope_row = reinterpret_cast<const float2*>(p.rope) + (size_t)t * PAIRS;
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int f = fw + 32 * u + 2 * (lane & 15);
-        float a = acc[i][2 * u][e], c = acc[i][2 * u + 1][e];
-        if (REGION < 2) {
-          const float2 cs = rope_row[(f & (HD - 1)) >> 1];
-          const float ra = a * cs.x - c * cs.y;
-          const float rc = a * cs.y + c * cs.x;
-          a = ra;
-          c = rc;
+        const int r = i * 16 + (lane >> 4) * 4 + e;
+        const int c = 32 * u + 2 * (lane & 15);
+        *reinterpret_cast<float2*>(st + stage_off(r, c >> 2) + (c & 3) * 4) =
+            make_float2(acc[4 * HALF + i][2 * u][e], acc[4 * HALF + i][2 * u + 1][e]);
+      }
+}
+
+template <int HALF>
+__device__ __forceinline__ void stage_cols(char* st, const f32x4 (&acc)[8][4], int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 32 * (j >> 1) + 2 * (lane & 15) + (j & 1);
+      *reinterpret_cast<f32x4*>(st + stage_off(c, i * 4 + (lane >> 4))) = acc[4 * HALF + i][j];
+    }
+}
+
+__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// QKV epilogue over rows [mw + 64*HALF, +64) and features [fw, fw + 64).
+// REGION 0: Q (rotate, scale by log2(e)/sqrt(128), fp16 to the workspace);
+// REGION 1: K (rotate, bf16 to the cache, fp16 copy); REGION 2: V (bf16 to the
+// blocked dimension-major cache, fp16 copy).  For Q and K a lane owns 8
+// consecutive features of one row (4 rotation pairs, one 32-byte RoPE load);
+// for V it owns 8 consecutive positions of one feature, which are 16
+// contiguous bytes of both value layouts when T is a multiple of 8.
+template <int REGION, int HALF>
+__device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
+                                             int mw, int fw, int lane) {
+  const PrefillParams& p = g.p;
+  const int T = p.T;
+  const int mh = mw + 64 * HALF;
+  if (HALF) lds_drain();            // the previous half's reads have returned
+  if (REGION < 2) {
+    const int k = lane & 7;         // 8-feature chunk of the row
+    stage_rows<HALF>(st, acc, lane);
+    f32x4 cs[8][2];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int m = mh + it * 8 + (lane >> 3);
+      const int t = m - (m / T) * T;  // in range for padding rows too
+      const float* rr = p.rope + (size_t)t * HD + (fw & (HD - 1)) + 8 * k;
+      cs[it][0] = *reinterpret_cast<const f32x4*>(rr);
+      cs[it][1] = *reinterpret_cast<const f32x4*>(rr + 4);
+    }
+    lds_drain();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 8 + (lane >> 3);
+      const int m = mh + r;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(st + stage_off(r, 2 * k));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(st + stage_off(r, 2 * k + 1));
+      if (m >= g.M) continue;
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const float c8[8] = {cs[it][0][0], cs[it][0][1], cs[it][0][2], cs[it][0][3],
+                           cs[it][1][0], cs[it][1][1], cs[it][1][2], cs[it][1][3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = v[2 * j], c = v[2 * j + 1];
+        const float co = c8[2 * j], si = c8[2 * j + 1];
+        v[2 * j] = a * co - c * si;
+        v[2 * j + 1] = a * si + c * co;
+      }
+      const int f = fw + 8 * k;
+      if (p.probe) {
+        float* pr = p.probe + (size_t)m * NQKV + f;
+        *reinterpret_cast<f32x4*>(pr) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(pr + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
+      if (REGION == 0) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * kScoreLog2, v[2 * j + 1] * kScoreLog2);
+        *reinterpret_cast<u32x4*>(p.q16 + (size_t)m * D + f) = o;
+      } else {
+        const int b = m / T, t = m - b * T;
+        const int ff = f - D, gg = ff / HD, d = ff % HD;
+        u32x4 kb, kh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+          kh[j] = pack_f16x2(bf16_bits_to_f32(kb[j] & 0xffffu), bf16_bits_to_f32(kb[j] >> 16));
         }
-        if (p.probe) *reinterpret_cast<float2*>(p.probe + (size_t)m * NQKV + f) = make_float2(a, c);
-        if (REGION == 0) {
-          *reinterpret_cast<uint32_t*>(p.q16 + (size_t)m * D + f) =
-              pack_f16x2(a * kScoreLog2, c * kScoreLog2);
-        } else if (REGION == 1) {
-          const int ff = f - D, gg = ff / HD, d = ff % HD;
-          const uint32_t kb = pack_bf16x2(a, c);
-          *reinterpret_cast<uint32_t*>(p.kcache + ((size_t)(b * KVH + gg) * p.T_max + t) * HD + d) = kb;
-          *reinterpret_cast<uint32_t*>(p.k16 + ((size_t)(b * KVH + gg) * p.Tp + t) * HD + d) =
-              pack_f16x2(bf16_bits_to_f32(kb & 0xffffu), bf16_bits_to_f32(kb >> 16));
-        } else {
-          const int ff = f - D - KVH * HD, gg = ff / HD, d = ff % HD;
-          const uint32_t v0 = f32_to_bf16_bits(a), v1 = f32_to_bf16_bits(c);
-          uint16_t* vc = p.vcache + vcache_index(b, gg, t, d, p.T_max);
-          vc[0] = (uint16_t)v0;
-          vc[VB] = (uint16_t)v1;
-          uint16_t* vt = p.v16t + (((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK;
-          const _Float16 h0 = (_Float16)bf16_bits_to_f32(v0), h1 = (_Float16)bf16_bits_to_f32(v1);
-          vt[0] = __builtin_bit_cast(uint16_t, h0);
-          vt[AK] = __builtin_bit_cast(uint16_t, h1);
+        *reinterpret_cast<u32x4*>(p.kcache + ((size_t)(b * KVH + gg) * p.T_max + t) * HD + d) = kb;
+        *reinterpret_cast<u32x4*>(p.k16 + ((size_t)(b * KVH + gg) * p.Tp + t) * HD + d) = kh;
+      }
+    }
+  } else {
+    stage_cols<HALF>(st, acc, lane);
+    lds_drain();
+    const int q = lane & 7;         // 8-row group of the half
+    const bool vec = (T & 7) == 0;  // then a group is 8 aligned positions of one sequence
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int c = (lane >> 3) + 8 * it;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(st + stage_off(c, 2 * q));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(st + stage_off(c, 2 * q + 1));
+      const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int f = fw + c;
+      const int ff = f - D - KVH * HD, gg = ff / HD, d = ff % HD;
+      const int m0 = mh + 8 * q;
+      if (p.probe) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (m0 + e < g.M) p.probe[(size_t)(m0 + e) * NQKV + f] = v[e];
+      }
+      if (vec) {
+        if (m0 >= g.M) continue;
+        const int b = m0 / T, t = m0 - b * T;
+        u32x4 vb, vh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+          vh[j] = pack_f16x2(bf16_bits_to_f32(vb[j] & 0xffffu), bf16_bits_to_f32(vb[j] >> 16));
+        }
+        *reinterpret_cast<u32x4*>(p.vcache + vcache_index(b, gg, t, d, p.T_max)) = vb;
+        *reinterpret_cast<u32x4*>(
+            p.v16t + (((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK) = vh;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int m = m0 + e;
+          if (m >= g.M) break;
+          const int b = m / T, t = m - b * T;
+          const uint32_t vb = f32_to_bf16_bits(v[e]);
+          p.vcache[vcache_index(b, gg, t, d, p.T_max)] = (uint16_t)vb;
+          const _Float16 h = (_Float16)bf16_bits_to_f32(vb);
+          p.v16t[(((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] =
+              __builtin_bit_cast(uint16_t, h);
         }
       }
     }
+  }
+}
+
+// wo epilogue: fp32 rows of Delta, one 16-byte unit per lane, 4 rows of 256
+// bytes per store instruction.
+template <int HALF>
+__device__ __forceinline__ void out_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
+                                             int mw, int fw, int lane) {
+  if (HALF) lds_drain();
+  stage_rows<HALF>(st, acc, lane);
+  lds_drain();
+  const int mh = mw + 64 * HALF;
+  const int u = lane & 15;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = it * 4 + (lane >> 4);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(st + stage_off(r, u));
+    const int m = mh + r;
+    if (m < g.M) *reinterpret_cast<f32x4*>(g.p.out + (size_t)m * D + fw + 4 * u) = v;
   }
 }
 
