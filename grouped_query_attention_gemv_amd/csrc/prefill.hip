@@ -481,17 +481,22 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 // Causal flash attention (prefill)
 // ---------------------------------------------------------------------------
 //
-// Workgroup = (sequence b, kv head g, query tile of 64 positions); wave w
-// handles query head 4g + w.  Per 64-key tile, in fp16 on the matrix cores:
-//   S^T[64 keys x 64 q] = K . Q^T      (A = K tile from LDS, B = Q in VGPRs)
-//   O^T[128 dims x 64 q] += V^T . P^T  (A = V^T tile from LDS, B = P in VGPRs)
+// Workgroup = (sequence b, kv head g, query tile of 64 positions), 8 waves:
+// wave w handles query head 4g + (w & 3) for the 32 queries 32*(w >> 2) ..
+// of the tile, so all 8 waves share every K/V tile in LDS and two waves run
+// on each SIMD (one's softmax overlaps the other's matrix-core work).  Per
+// 64-key tile, in fp16 on the matrix cores:
+//   S^T[64 keys x 32 q] = K . Q^T      (A = K tile from LDS, B = Q in VGPRs)
+//   O^T[128 dims x 32 q] += V^T . P^T  (A = V^T tile from LDS, B = P in VGPRs)
 // Within each 32-key half, A-operand row r of score tile "sub" holds key
 // (r >> 2)*8 + sub*4 + (r & 3); each lane then owns 8 consecutive keys of
 // its query column, which is exactly its B operand for the P.V step.
 
-__global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
-  // two stages of [64 keys][128 dims] K and [128 dims][64 keys] V^T, fp16
-  __shared__ __attribute__((aligned(16))) char sKV[2][2][AK * HD * 2];    // 64 KiB
+constexpr int kAttnStage = 2 * AK * HD * 2;      // K and V^T tiles, fp16: 32 KiB
+constexpr int kAttnLds = 2 * kAttnStage;         // double-buffered: 64 KiB
+
+__global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
@@ -500,7 +505,8 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
   const int bg = blockIdx.x % pairs;
   const int qt = nqt - 1 - blockIdx.x / pairs;      // longest rows first
   const int b = bg / KVH, g = bg % KVH;
-  const int h = g * REP + w;
+  const int h = g * REP + (w & 3);
+  const int q0 = qt * AQ + 32 * (w >> 2);           // first query of this wave
   const int T = p.T, Tp = p.Tp;
 
   const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
@@ -510,49 +516,49 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
   // consecutive LDS per instruction).  Each lane picks the global chunk that
   // belongs at its LDS slot under the XOR swizzle: K rows (256 B) hold chunk
   // c at c ^ (key & 15), V^T rows (128 B) hold chunk c at c ^ (dim & 7).
-  // Wave w fills K rows w*16 .. +16 and V^T rows w*32 .. +32.  Positions in
+  // Wave w fills K rows w*8 .. +8 and V^T rows w*16 .. +16.  Positions in
   // [T, Tp) of the workspace copies are zero, so no masking is needed here.
-  const uint16_t* k_src[4];
-  const uint16_t* v_src[4];
+  const uint16_t* k_src[2];
+  const uint16_t* v_src[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = w * 16 + i * 4 + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int key = w * 8 + i * 4 + (lane >> 4);
     k_src[i] = kg + (size_t)key * HD + (((lane & 15) ^ (key & 15)) * 8);
-    const int dim = w * 32 + i * 8 + (lane >> 3);
+    const int dim = w * 16 + i * 8 + (lane >> 3);
     v_src[i] = vg + (size_t)dim * AK + (((lane & 7) ^ (dim & 7)) * 8);
   }
   auto issue_tile = [&](int kt, int stage) {
-    char* dk = sKV[stage][0];
-    char* dv = sKV[stage][1];
+    char* dk = smem + stage * kAttnStage;
+    char* dv = dk + AK * HD * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(k_src[i] + (size_t)kt * AK * HD,
-                                       (lds_void*)(dk + (w * 16 + i * 4) * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(v_src[i] + (size_t)kt * (HD * AK),
-                                       (lds_void*)(dv + (w * 32 + i * 8) * 128), 16, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(k_src[i] + (size_t)kt * AK * HD),
+                                       (lds_void*)(dk + (w * 8 + i * 4) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(v_src[i] + (size_t)kt * (HD * AK)),
+                                       (lds_void*)(dv + (w * 16 + i * 8) * 128), 16, 0, 0);
     }
   };
   issue_tile(0, 0);
 
-  // Q^T fragments: query qt*64 + nt*16 + col, dims rg*8 + 32*ks
-  u32x4 qf[4][4];
+  // Q^T fragments: query q0 + nt*16 + col, dims rg*8 + 32*ks
+  u32x4 qf[2][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int t = qt * AQ + nt * 16 + col;
+  for (int nt = 0; nt < 2; ++nt) {
+    const int t = q0 + nt * 16 + col;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       qf[nt][ks] = (t < T) ? ld_u32x4(p.q16 + ((size_t)b * T + t) * D + h * HD + rg * 8 + 32 * ks)
                            : u32x4{0u, 0u, 0u, 0u};
   }
 
-  f32x4 oacc[8][4];
+  f32x4 oacc[8][2];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
+    for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2], l_run[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     m_run[nt] = -INFINITY;
     l_run[nt] = 0.f;
   }
@@ -563,15 +569,15 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt < qt) issue_tile(kt + 1, (kt + 1) & 1);
-    const char* sK = sKV[kt & 1][0];
-    const char* sV = sKV[kt & 1][1];
+    const char* sK = smem + (kt & 1) * kAttnStage;
+    const char* sV = sK + AK * HD * 2;
 
     // ---- scores ----
-    f32x4 sacc[4][4];
+    f32x4 sacc[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -580,16 +586,16 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
         const int c = ks * 4 + rg;
         const u32x4 kf = *reinterpret_cast<const u32x4*>(sK + key * 256 + ((c ^ (key & 15)) << 4));
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) sacc[mt][nt] = mfma_f16(kf, qf[nt][ks], sacc[mt][nt]);
+        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma_f16(kf, qf[nt][ks], sacc[mt][nt]);
       }
     }
 
     // ---- online softmax per query column ----
-    // sacc[mt][nt][e]: key kt*64 + 32*(mt>>1) + rg*8 + (mt&1)*4 + e, query nt*16 + col
+    // sacc[mt][nt][e]: key kt*64 + 32*(mt>>1) + rg*8 + (mt&1)*4 + e, query q0 + nt*16 + col
     if (kt == qt) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int q = qt * AQ + nt * 16 + col;
+      for (int nt = 0; nt < 2; ++nt) {
+        const int q = q0 + nt * 16 + col;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -599,10 +605,10 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
           }
       }
     }
-    float tmax[4];
+    float tmax[2];
     bool grow = false;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       float t = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -619,7 +625,7 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
     // wave-uniform, and most tiles skip the rescale entirely.
     if (__any(grow)) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         const float m_new = fmaxf(m_run[nt], tmax[nt]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
         m_run[nt] = m_new;
@@ -628,9 +634,9 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
         for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
       }
     }
-    u32x4 pf[4][2];
+    u32x4 pf[2][2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       const float m_ref = m_run[nt];
       float psum = 0.f;
       uint32_t pk[2][4];
@@ -661,34 +667,48 @@ __global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillParams p) {
         const int c = half * 4 + rg;
         const u32x4 vf = *reinterpret_cast<const u32x4*>(sV + dim * 128 + ((c ^ (dim & 7)) << 4));
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_f16(vf, pf[nt][half], oacc[dt][nt]);
+        for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = mfma_f16(vf, pf[nt][half], oacc[dt][nt]);
       }
     }
   }
 
-  // ---- normalise and store O (fp16) ----
+  // ---- normalise, stage through LDS, store O (fp16) ----
+  // Wave w's 32 x 128 block goes to its own 8 KiB of LDS, row = query, with
+  // 16-byte chunk c of a row at c ^ (row & 15); each lane then stores 16
+  // bytes, 4 rows of 256 contiguous bytes per instruction.
+  __syncthreads();                                  // every wave is done with the K/V tiles
+  char* so = smem + w * (32 * HD * 2);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     float l = l_run[nt];
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
     const float inv = 1.f / l;
-    const int t = qt * AQ + nt * 16 + col;
-    if (t < T) {
-      uint16_t* orow = p.o16 + ((size_t)b * T + t) * D + h * HD;
+    const int row = nt * 16 + col;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 o = oacc[dt][nt];
-        const u32x2 v = {pack_f16x2(o[0] * inv, o[1] * inv), pack_f16x2(o[2] * inv, o[3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dt * 16 + rg * 4) = v;
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = oacc[dt][nt];
+      const u32x2 v = {pack_f16x2(o[0] * inv, o[1] * inv), pack_f16x2(o[2] * inv, o[3] * inv)};
+      const int c = dt * 2 + (rg >> 1);
+      *reinterpret_cast<u32x2*>(so + row * 256 + ((c ^ (row & 15)) << 4) + (rg & 1) * 8) = v;
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 4 + (lane >> 4), c = lane & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(so + row * 256 + ((c ^ (row & 15)) << 4));
+    const int t = q0 + row;
+    if (t < T) *reinterpret_cast<u32x4*>(p.o16 + ((size_t)b * T + t) * D + h * HD + c * 8) = v;
   }
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_attn_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
+  if (e != hipSuccess) return e;
   const int nqt = p.Tp / AQ;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(p.B * KVH * nqt), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(p.B * KVH * nqt), dim3(512), kAttnLds, s, p);
   return hipGetLastError();
 }
 
