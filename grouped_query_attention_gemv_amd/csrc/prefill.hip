@@ -18,6 +18,8 @@
 // while Q, P and O gain 3 significant bits over bf16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -220,30 +222,42 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     if (kb + 1 < nk) load_stage((kb + 1) & 1, (kb + 1) * GBK);
     const char* sa = smem + (kb & 1) * (GBM + GBN) * GBK * 2;
     const char* sb = sa + GBM * GBK * 2;
+    // Both 32-deep halves' fragments are read up front; the second half's
+    // reads are interleaved with the first half's matrix-core ops, so only
+    // the first reads' latency is exposed per stage.
+    u32x4 af[2][8], bf[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int chunk = ks * 4 + (lane >> 4);
-      u32x4 af[8], bf[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ra = wm * 128 + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const u32x4*>(sa + ra * 128 + ((chunk ^ (ra & 7)) << 4));
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rb = wn * 64 + j * 16 + (lane & 15);
-        bf[j] = *reinterpret_cast<const u32x4*>(sb + rb * 128 + ((chunk ^ (rb & 7)) << 4));
+        bf[ks][j] = *reinterpret_cast<const u32x4*>(sb + rb * 128 + ((chunk ^ (rb & 7)) << 4));
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ra = wm * 128 + i * 16 + (lane & 15);
+        af[ks][i] = *reinterpret_cast<const u32x4*>(sa + ra * 128 + ((chunk ^ (ra & 7)) << 4));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (KIND == GEMM_QKV)
-            acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+            acc[i][j] = mfma_bf16(af[ks][i], bf[ks][j], acc[i][j]);
           else
-            acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
+            acc[i][j] = mfma_f16(af[ks][i], bf[ks][j], acc[i][j]);
         }
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);    // first half's LDS reads
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix-core ops
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one read of the second half
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
   }
 
   // epilogue: acc[i][2u+s][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
@@ -493,6 +507,13 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 // its query column, which is exactly its B operand for the P.V step.
 
 constexpr int kAttnStage = 2 * AK * HD * 2;      // K and V^T tiles, fp16: 32 KiB
+
+// LDS swizzles of the K and V^T tiles.  One fragment read touches 16 K rows
+// (keys whose bits 0, 1, 3, 4 vary) or 16 consecutive V^T rows; both maps
+// send those rows to distinct 16-byte slots of a 256-byte bank window, and
+// any 8 consecutive of them to distinct slots of a 128-byte window.
+__device__ __forceinline__ int attn_kswz(int key) { return (key & 3) | ((key >> 1) & 12); }
+__device__ __forceinline__ int attn_vswz(int dim) { return (dim & 7) ^ ((dim >> 3) & 1); }
 constexpr int kAttnLds = 2 * kAttnStage;         // double-buffered: 64 KiB
 
 __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
@@ -515,30 +536,40 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   // Tile loads go straight to LDS (16 bytes a lane, a wave writes 1 KiB of
   // consecutive LDS per instruction).  Each lane picks the global chunk that
   // belongs at its LDS slot under the XOR swizzle: K rows (256 B) hold chunk
-  // c at c ^ (key & 15), V^T rows (128 B) hold chunk c at c ^ (dim & 7).
-  // Wave w fills K rows w*8 .. +8 and V^T rows w*16 .. +16.  Positions in
-  // [T, Tp) of the workspace copies are zero, so no masking is needed here.
+  // c at c ^ attn_kswz(key), V^T rows (128 B) hold chunk c at
+  // c ^ attn_vswz(dim).  Wave w fills K rows w*8 .. +8 and V^T rows
+  // w*16 .. +16.  Positions in [T, Tp) of the workspace copies are zero, so
+  // no masking is needed here.
   const uint16_t* k_src[2];
   const uint16_t* v_src[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int key = w * 8 + i * 4 + (lane >> 4);
-    k_src[i] = kg + (size_t)key * HD + (((lane & 15) ^ (key & 15)) * 8);
+    k_src[i] = kg + (size_t)key * HD + (((lane & 15) ^ attn_kswz(key)) * 8);
     const int dim = w * 16 + i * 8 + (lane >> 3);
-    v_src[i] = vg + (size_t)dim * AK + (((lane & 7) ^ (dim & 7)) * 8);
+    v_src[i] = vg + (size_t)dim * AK + (((lane & 7) ^ attn_vswz(dim)) * 8);
   }
-  auto issue_tile = [&](int kt, int stage) {
-    char* dk = smem + stage * kAttnStage;
-    char* dv = dk + AK * HD * 2;
+  // K tile kt lives in K buffer kt & 1 and V^T tile kt in V buffer kt & 1.
+  // Iteration kt reads K tile kt+1 (the next scores) and V tile kt, so at
+  // its start K tile kt+2 and V tile kt+1 can be fetched into the buffers
+  // iteration kt-1 has finished with.
+  auto sK = [&](int kt) { return smem + (kt & 1) * (AK * HD * 2); };
+  auto sV = [&](int kt) { return smem + 2 * (AK * HD * 2) + (kt & 1) * (AK * HD * 2); };
+  auto issue_k = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(k_src[i] + (size_t)kt * AK * HD),
-                                       (lds_void*)(dk + (w * 8 + i * 4) * 256), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(v_src[i] + (size_t)kt * (HD * AK)),
-                                       (lds_void*)(dv + (w * 16 + i * 8) * 128), 16, 0, 0);
-    }
+                                       (lds_void*)(sK(kt) + (w * 8 + i * 4) * 256), 16, 0, 0);
   };
-  issue_tile(0, 0);
+  auto issue_v = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(v_src[i] + (size_t)kt * (HD * AK)),
+                                       (lds_void*)(sV(kt) + (w * 16 + i * 8) * 128), 16, 0, 0);
+  };
+  issue_k(0);
+  issue_v(0);
+  if (qt > 0) issue_k(1);
 
   // Q^T fragments: query q0 + nt*16 + col, dims rg*8 + 32*ks
   u32x4 qf[2][4];
@@ -563,17 +594,9 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
     l_run[nt] = 0.f;
   }
 
-  for (int kt = 0; kt <= qt; ++kt) {
-    // this tile has landed for every wave, and every wave is done reading
-    // the other stage, which the next tile's loads now overwrite
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt < qt) issue_tile(kt + 1, (kt + 1) & 1);
-    const char* sK = smem + (kt & 1) * kAttnStage;
-    const char* sV = sK + AK * HD * 2;
-
-    // ---- scores ----
-    f32x4 sacc[4][2];
+  // S^T = K . Q^T for the K tile at k_lds.
+  // sacc[mt][nt][e]: key 32*(mt>>1) + rg*8 + (mt&1)*4 + e of the tile, query q0 + nt*16 + col
+  auto scores = [&](const char* k_lds, f32x4 (&sacc)[4][2]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -584,15 +607,31 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
       for (int mt = 0; mt < 4; ++mt) {
         const int key = 32 * (mt >> 1) + (col >> 2) * 8 + (mt & 1) * 4 + (col & 3);
         const int c = ks * 4 + rg;
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(sK + key * 256 + ((c ^ (key & 15)) << 4));
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(k_lds + key * 256 + ((c ^ attn_kswz(key)) << 4));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma_f16(kf, qf[nt][ks], sacc[mt][nt]);
       }
     }
+  };
 
-    // ---- online softmax per query column ----
-    // sacc[mt][nt][e]: key kt*64 + 32*(mt>>1) + rg*8 + (mt&1)*4 + e, query q0 + nt*16 + col
-    if (kt == qt) {
+  // One key tile: softmax of the scores s (tile kt) and O += V P, with the
+  // next tile's scores computed in between (not on the diagonal tile, which
+  // is the last), so matrix-core and vector work of one wave interleave.
+  f32x4 s[4][2];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  scores(sK(0), s);
+  auto step = [&](auto last_tag, int kt) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    // K tile kt+1 and V tile kt have landed for every wave, and every wave
+    // is done with K tile kt and V tile kt-1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!LAST) {
+      if (kt + 2 <= qt) issue_k(kt + 2);
+      issue_v(kt + 1);
+    }
+    if (LAST) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int q = q0 + nt * 16 + col;
@@ -601,11 +640,15 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
-            if (key > q) sacc[mt][nt][e] = -INFINITY;
+            if (key > q) s[mt][nt][e] = -INFINITY;
           }
       }
     }
-    float tmax[2];
+    // Lazy rescaling: the reference maximum only moves (and O, l are only
+    // rescaled) when a column's maximum grows by more than 2^8 over it, so
+    // p = exp2(s - m) <= 256 (exact in range for fp16).  The decision is
+    // wave-uniform, and most tiles skip the rescale entirely.
+    float m_new[2];
     bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -613,64 +656,80 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t = fmaxf(t, sacc[mt][nt][e]);
+        for (int e = 0; e < 4; ++e) t = fmaxf(t, s[mt][nt][e]);
       t = fmaxf(t, shfl_xor(t, 16));
       t = fmaxf(t, shfl_xor(t, 32));
-      tmax[nt] = t;
+      m_new[nt] = fmaxf(m_run[nt], t);
       grow |= t > m_run[nt] + kLazyRescale;
     }
-    // Lazy rescaling: the reference maximum only moves (and O, l are only
-    // rescaled) when a column's maximum grows by more than 2^8 over it, so
-    // p = exp2(s - m) <= 256 (exact in range for fp16).  The decision is
-    // wave-uniform, and most tiles skip the rescale entirely.
-    if (__any(grow)) {
+    const bool rescale = __any(grow);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) m_new[nt] = rescale ? m_new[nt] : m_run[nt];
+    if (rescale) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float m_new = fmaxf(m_run[nt], tmax[nt]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-        m_run[nt] = m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
         l_run[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
       }
     }
+
+    f32x4 sn[4][2];
+    if (!LAST) scores(sK(kt + 1), sn);
+
     u32x4 pf[2][2];
+    float psum[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const float m_ref = m_run[nt];
-      float psum = 0.f;
+      const float m_ref = m_new[nt];
+      float ps = 0.f;
       uint32_t pk[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const int mt = half * 2 + sub;
-          const float p0 = __builtin_amdgcn_exp2f(sacc[mt][nt][0] - m_ref);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[mt][nt][1] - m_ref);
-          const float p2 = __builtin_amdgcn_exp2f(sacc[mt][nt][2] - m_ref);
-          const float p3 = __builtin_amdgcn_exp2f(sacc[mt][nt][3] - m_ref);
-          psum += (p0 + p1) + (p2 + p3);
+          const float p0 = __builtin_amdgcn_exp2f(s[mt][nt][0] - m_ref);
+          const float p1 = __builtin_amdgcn_exp2f(s[mt][nt][1] - m_ref);
+          const float p2 = __builtin_amdgcn_exp2f(s[mt][nt][2] - m_ref);
+          const float p3 = __builtin_amdgcn_exp2f(s[mt][nt][3] - m_ref);
+          ps += (p0 + p1) + (p2 + p3);
           pk[half][sub * 2] = pack_f16x2(p0, p1);
           pk[half][sub * 2 + 1] = pack_f16x2(p2, p3);
         }
-      l_run[nt] += psum;
+      psum[nt] = ps;
       pf[nt][0] = u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
       pf[nt][1] = u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
     }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      m_run[nt] = m_new[nt];
+      l_run[nt] += psum[nt];
+    }
 
     // ---- O^T += V^T P^T ----
+    const char* v_lds = sV(kt);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int dim = dt * 16 + col;
         const int c = half * 4 + rg;
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(sV + dim * 128 + ((c ^ (dim & 7)) << 4));
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_lds + dim * 128 + ((c ^ attn_vswz(dim)) << 4));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = mfma_f16(vf, pf[nt][half], oacc[dt][nt]);
       }
     }
-  }
+    if (!LAST) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s[mt][nt] = sn[mt][nt];
+    }
+  };
+  for (int kt = 0; kt < qt; ++kt) step(std::false_type{}, kt);
+  step(std::true_type{}, qt);
 
   // ---- normalise, stage through LDS, store O (fp16) ----
   // Wave w's 32 x 128 block goes to its own 8 KiB of LDS, row = query, with
