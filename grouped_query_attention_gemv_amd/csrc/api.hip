@@ -77,14 +77,14 @@ inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
 
 int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
                  const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                 const float* rope, int B, int T, float* out, void* ws, size_t ws_bytes,
-                 float* probe, hipStream_t stream, hipEvent_t* events) {
+                 const float* rope, int start_pos, int B, int T, float* out, void* ws,
+                 size_t ws_bytes, float* probe, hipStream_t stream, hipEvent_t* events) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
   if (T < 1 || (long)B * T > (1L << 24)) return GQA_ERR_SHAPE;
-  if (T > T_max) return GQA_ERR_RANGE;
+  if (start_pos < 0 || (long)start_pos + T > T_max) return GQA_ERR_RANGE;
   if (probe && !aligned16(probe)) return GQA_ERR_ALIGN;
-  if (ws_bytes < gqa_workspace_bytes(B, T, T_max)) return GQA_ERR_WORKSPACE;
+  if (ws_bytes < gqa_workspace_bytes_from(B, start_pos, T, T_max)) return GQA_ERR_WORKSPACE;
   const size_t M = (size_t)B * T;
   const Range outs[] = {span(out, M * D * 4), span(kcache, cache_bytes(B, T_max)),
                         span(vcache, cache_bytes(B, T_max)), span(ws, ws_bytes),
@@ -98,9 +98,9 @@ int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, cons
   memset(&p, 0, sizeof(p));
   p.x = x; p.wq = wq; p.wk = wk; p.wv = wv; p.wo = wo;
   p.kcache = kcache; p.vcache = vcache; p.rope = rope; p.out = out; p.probe = probe;
-  p.T_max = T_max; p.B = B; p.T = T;
-  p.Tp = (T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
-  prefill_ws_carve(ws, B, T, &p);
+  p.T_max = T_max; p.B = B; p.T = T; p.start_pos = start_pos;
+  p.Tp = (start_pos + T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+  prefill_ws_carve(ws, &p);
 
   (void)hipGetLastError();
   hipError_t e;
@@ -214,10 +214,18 @@ int gqa_decode_schedule(int B, int start_pos, int T_max) {
   return sched < 0 ? GQA_ERR_ARG : sched;
 }
 
+size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max) {
+  if (B < 1 || B > GQA_MAX_BATCH || T < 1 || T_max < 1 || T_max > GQA_MAX_T_MAX) return 0;
+  if ((long)B * T > (1L << 24) || start_pos < 0 || (long)start_pos + T > T_max) return 0;
+  const size_t a = prefill_ws_bytes(B, start_pos, T);
+  const size_t b = decode_ws_bytes(B);
+  return a > b ? a : b;
+}
+
 size_t gqa_workspace_bytes(int B, int T, int T_max) {
   if (B < 1 || B > GQA_MAX_BATCH || T < 1 || T_max < 1 || T_max > GQA_MAX_T_MAX) return 0;
   if ((long)B * T > (1L << 24)) return 0;
-  const size_t a = prefill_ws_bytes(B, T);
+  const size_t a = prefill_ws_bytes(B, 0, T);
   const size_t b = decode_ws_bytes(B);
   return a > b ? a : b;
 }
@@ -226,8 +234,17 @@ int gqa_block_prefill(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
                       const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
                       gqa_bf16* vcache, int T_max, const float* rope, int B, int T, float* out,
                       void* ws, size_t ws_bytes, float* probe, hipStream_t stream) {
-  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, T, out, ws, ws_bytes,
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, 0, B, T, out, ws, ws_bytes,
                       probe, stream, nullptr);
+}
+
+int gqa_block_prefill_from(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                           const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                           gqa_bf16* vcache, int T_max, const float* rope, int start_pos, int B,
+                           int T, float* out, void* ws, size_t ws_bytes, float* probe,
+                           hipStream_t stream) {
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, out, ws,
+                      ws_bytes, probe, stream, nullptr);
 }
 
 int gqa_block_prefill_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
@@ -236,7 +253,7 @@ int gqa_block_prefill_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_
                                float* out, void* ws, size_t ws_bytes, float* probe,
                                hipStream_t stream, hipEvent_t* events) {
   if (!events) return GQA_ERR_NULL;
-  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, T, out, ws, ws_bytes,
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, 0, B, T, out, ws, ws_bytes,
                       probe, stream, events);
 }
 

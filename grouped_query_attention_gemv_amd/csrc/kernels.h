@@ -92,19 +92,21 @@ struct PrefillParams {
   const float* rope;
   float* out;               // [M][4096]
   float* probe;             // optional [M][6144]
-  int T_max, B, T, Tp;      // Tp = T rounded up to the attention tile
+  int T_max, B, T;          // T new tokens per sequence, at positions start_pos ..
+  int start_pos;            // cached rows 0 .. start_pos-1 precede them
+  int Tp;                   // start_pos + T rounded up to the attention tile
   // workspace
   uint16_t* wo16;           // [4096][4096] fp16 copy of wo
   uint16_t* q16;            // [M][4096] fp16 Q * log2(e)/sqrt(128)
-  uint16_t* k16;            // [B][8][Tp][128] fp16 copy of the appended keys
-  uint16_t* v16t;           // [B][8][Tp/64][128][64] fp16 copy of the appended values
+  uint16_t* k16;            // [B][8][Tp][128] fp16 copy of keys 0 .. start_pos+T-1
+  uint16_t* v16t;           // [B][8][Tp/64][128][64] fp16 copy of the values
   uint16_t* o16;            // [M][4096] fp16 attention output
 };
 
 constexpr int kPrefillTile = 64;     // query and key tile of the prefill attention
 
-size_t prefill_ws_bytes(int B, int T);
-void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p);
+size_t prefill_ws_bytes(int B, int start_pos, int T);
+void prefill_ws_carve(void* ws, PrefillParams* p);   // reads B, T, Tp
 
 hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s);

@@ -1,8 +1,13 @@
-// Prefill path of the attention block: T new tokens per sequence from
-// position 0, causal mask (page "Llama 3.1 8B . Grouped-query attention",
-// evidence "scores": key j hidden from query row i iff j > i here).
+// Prefill path of the attention block: T new tokens per sequence at
+// positions start_pos .. start_pos+T-1, after start_pos cached rows, with the
+// causal mask of the page "Llama 3.1 8B . Grouped-query attention" (evidence
+// "scores" and the mask listing of its code section: new token i sits at
+// position start_pos + i and sees every key j <= start_pos + i).
+// start_pos = 0 is the plain prefill; start_pos > 0 continues a prefix
+// (chunked prefill).
 //
-//   convert_wo_kernel    wo bf16 -> fp16 copy in the workspace
+//   prefill_prep_kernel  wo bf16 -> fp16 copy in the workspace; cached K/V
+//                        rows 0 .. start_pos-1 -> the fp16 attention copies
 //   gemm_kernel<QKV>     [Q|K|V] = x [Wq;Wk;Wv]^T on bf16 matrix cores; the
 //                        epilogue rotates Q/K pairs (RoPE), appends K/V to
 //                        the bf16 cache and writes fp16 copies of Q (scaled
@@ -35,9 +40,13 @@ constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V
 // Workspace
 // ---------------------------------------------------------------------------
 
-size_t prefill_ws_bytes(int B, int T) {
+static size_t prefill_key_rows(int start_pos, int T) {
+  return (size_t)(start_pos + T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+}
+
+size_t prefill_ws_bytes(int B, int start_pos, int T) {
   const size_t M = (size_t)B * T;
-  const size_t Tp = (size_t)(T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+  const size_t Tp = prefill_key_rows(start_pos, T);
   size_t n = kSyncBytes;                            // decode's synchronisation words, untouched
   n += align256((size_t)D * D * 2);                 // wo16
   n += align256(M * D * 2);                         // q16
@@ -47,8 +56,8 @@ size_t prefill_ws_bytes(int B, int T) {
   return n;
 }
 
-void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
-  const size_t M = (size_t)B * T;
+void prefill_ws_carve(void* ws, PrefillParams* p) {
+  const size_t M = (size_t)p->B * p->T;
   const size_t Tp = (size_t)p->Tp;
   char* c = static_cast<char*>(ws) + kSyncBytes;
   p->wo16 = reinterpret_cast<uint16_t*>(c);
@@ -56,9 +65,9 @@ void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
   p->q16 = reinterpret_cast<uint16_t*>(c);
   c += align256(M * D * 2);
   p->k16 = reinterpret_cast<uint16_t*>(c);
-  c += align256((size_t)B * KVH * Tp * HD * 2);
+  c += align256((size_t)p->B * KVH * Tp * HD * 2);
   p->v16t = reinterpret_cast<uint16_t*>(c);
-  c += align256((size_t)B * KVH * HD * Tp * 2);
+  c += align256((size_t)p->B * KVH * HD * Tp * 2);
   p->o16 = reinterpret_cast<uint16_t*>(c);
 }
 
@@ -66,11 +75,15 @@ void prefill_ws_carve(void* ws, int B, int T, PrefillParams* p) {
 // wo -> fp16
 // ---------------------------------------------------------------------------
 
-// Converts wo to fp16 and clears the positions [T, Tp) of the fp16 K and
-// V^T workspace copies (the attention tiles read them; they must be finite).
+// Converts wo to fp16, copies the cached rows 0 .. start_pos-1 of K and V
+// into the fp16 attention copies (bf16 -> fp16 is exact but for magnitudes
+// below fp16's normal range), and clears the positions [start_pos+T, Tp) of
+// both copies (the attention tiles read them; they must be finite).
 __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
+  const long stride = (long)gridDim.x * 256;
+  const long tid0 = (long)blockIdx.x * 256 + threadIdx.x;
   const int n8 = D * D / 8;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n8; i += gridDim.x * 256) {
+  for (long i = tid0; i < n8; i += stride) {
     const u32x4 v = ld_nt_u32x4(p.wo + (size_t)i * 8);
     u32x4 o;
 #pragma unroll
@@ -80,22 +93,63 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
     }
     *reinterpret_cast<u32x4*>(p.wo16 + (size_t)i * 8) = o;
   }
-  const int pad = p.Tp - p.T;
-  if (pad == 0) return;
   const int pairs = p.B * KVH;
+  const int nblk = p.Tp / AK;
+  // cached prefix: 8 elements per item (a K row segment, or 8 positions of
+  // one V dimension; the V items of an unaligned tail are element-wise)
+  const int sp = p.start_pos;
+  if (sp > 0) {
+    const long nk = (long)pairs * sp * (HD / 8);
+    for (long i = tid0; i < nk; i += stride) {
+      const int pair = (int)(i / ((long)sp * (HD / 8)));
+      const int r = (int)(i % ((long)sp * (HD / 8)));
+      const int t = r / (HD / 8), d = (r % (HD / 8)) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p.kcache + ((size_t)pair * p.T_max + t) * HD + d);
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_f16x2(bf16_bits_to_f32(v[q] & 0xffffu), bf16_bits_to_f32(v[q] >> 16));
+      *reinterpret_cast<u32x4*>(p.k16 + ((size_t)pair * p.Tp + t) * HD + d) = o;
+    }
+    const int groups = (sp + 7) / 8;
+    const long nv = (long)pairs * HD * groups;
+    for (long i = tid0; i < nv; i += stride) {
+      const int pair = (int)(i / ((long)HD * groups));
+      const int r = (int)(i % ((long)HD * groups));
+      const int d = r / groups, t0 = (r % groups) * 8;
+      const int b = pair / KVH, g = pair % KVH;
+      uint16_t* dst = p.v16t + (((size_t)pair * nblk + t0 / AK) * HD + d) * AK + t0 % AK;
+      if (t0 + 8 <= sp) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p.vcache + vcache_index(b, g, t0, d, p.T_max));
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = pack_f16x2(bf16_bits_to_f32(v[q] & 0xffffu), bf16_bits_to_f32(v[q] >> 16));
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        for (int t = t0; t < sp; ++t) {
+          const _Float16 h = (_Float16)bf16_bits_to_f32(p.vcache[vcache_index(b, g, t, d, p.T_max)]);
+          dst[t - t0] = __builtin_bit_cast(uint16_t, h);
+        }
+      }
+    }
+  }
+  const int lo = sp + p.T;
+  const int pad = p.Tp - lo;
+  if (pad == 0) return;
   // K rows: pairs * pad rows of 128; V^T: pairs * 128 dims of pad positions
   const long nk = (long)pairs * pad * HD;
   const long total = 2 * nk;
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+  for (long i = tid0; i < total; i += stride) {
     const long e = i < nk ? i : i - nk;
     const int pair = (int)(e / ((long)pad * HD));
     const int r = (int)(e % ((long)pad * HD));
     if (i < nk) {
-      const int t = p.T + r / HD, d = r % HD;
+      const int t = lo + r / HD, d = r % HD;
       p.k16[((size_t)pair * p.Tp + t) * HD + d] = 0;
     } else {
-      const int d = r / pad, t = p.T + r % pad;
-      p.v16t[(((size_t)pair * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] = 0;
+      const int d = r / pad, t = lo + r % pad;
+      p.v16t[(((size_t)pair * nblk + t / AK) * HD + d) * AK + t % AK] = 0;
     }
   }
 }
@@ -323,12 +377,14 @@ __device__ __forceinline__ void stage_cols(char* st, const f32x4 (&acc)[8][4], i
 __device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // QKV epilogue over rows [mw + 64*HALF, +64) and features [fw, fw + 64).
+// Row m is token t = m mod T of sequence m / T, at position start_pos + t.
 // REGION 0: Q (rotate, scale by log2(e)/sqrt(128), fp16 to the workspace);
 // REGION 1: K (rotate, bf16 to the cache, fp16 copy); REGION 2: V (bf16 to the
 // blocked dimension-major cache, fp16 copy).  For Q and K a lane owns 8
 // consecutive features of one row (4 rotation pairs, one 32-byte RoPE load);
 // for V it owns 8 consecutive positions of one feature, which are 16
-// contiguous bytes of both value layouts when T is a multiple of 8.
+// contiguous bytes of both value layouts when T and start_pos are multiples
+// of 8.
 template <int REGION, int HALF>
 __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
                                              int mw, int fw, int lane) {
@@ -343,8 +399,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int m = mh + it * 8 + (lane >> 3);
-      const int t = m - (m / T) * T;  // in range for padding rows too
-      const float* rr = p.rope + (size_t)t * HD + (fw & (HD - 1)) + 8 * k;
+      const int pos = p.start_pos + m - (m / T) * T;  // in range for padding rows too
+      const float* rr = p.rope + (size_t)pos * HD + (fw & (HD - 1)) + 8 * k;
       cs[it][0] = *reinterpret_cast<const f32x4*>(rr);
       cs[it][1] = *reinterpret_cast<const f32x4*>(rr + 4);
     }
@@ -378,7 +434,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
         for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * kScoreLog2, v[2 * j + 1] * kScoreLog2);
         *reinterpret_cast<u32x4*>(p.q16 + (size_t)m * D + f) = o;
       } else {
-        const int b = m / T, t = m - b * T;
+        const int b = m / T, t = p.start_pos + m - b * T;
         const int ff = f - D, gg = ff / HD, d = ff % HD;
         u32x4 kb, kh;
 #pragma unroll
@@ -394,7 +450,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
     stage_cols<HALF>(st, acc, lane);
     lds_drain();
     const int q = lane & 7;         // 8-row group of the half
-    const bool vec = (T & 7) == 0;  // then a group is 8 aligned positions of one sequence
+    // then a group is 8 aligned positions of one sequence
+    const bool vec = ((T | p.start_pos) & 7) == 0;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int c = (lane >> 3) + 8 * it;
@@ -411,7 +468,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
       }
       if (vec) {
         if (m0 >= g.M) continue;
-        const int b = m0 / T, t = m0 - b * T;
+        const int b = m0 / T, t = p.start_pos + m0 - b * T;
         u32x4 vb, vh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -426,7 +483,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
         for (int e = 0; e < 8; ++e) {
           const int m = m0 + e;
           if (m >= g.M) break;
-          const int b = m / T, t = m - b * T;
+          const int b = m / T, t = p.start_pos + m - b * T;
           const uint32_t vb = f32_to_bf16_bits(v[e]);
           p.vcache[vcache_index(b, gg, t, d, p.T_max)] = (uint16_t)vb;
           const _Float16 h = (_Float16)bf16_bits_to_f32(vb);
@@ -521,14 +578,18 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
-  const int nqt = p.Tp / AQ;
+  const int T = p.T, Tp = p.Tp;
+  const int nqt = (T + AQ - 1) / AQ;
   const int pairs = p.B * KVH;
   const int bg = blockIdx.x % pairs;
   const int qt = nqt - 1 - blockIdx.x / pairs;      // longest rows first
   const int b = bg / KVH, g = bg % KVH;
   const int h = g * REP + (w & 3);
-  const int q0 = qt * AQ + 32 * (w >> 2);           // first query of this wave
-  const int T = p.T, Tp = p.Tp;
+  const int q0 = qt * AQ + 32 * (w >> 2);           // first new token of this wave
+  // key tiles 0 .. klast hold the keys of the workgroup's queries (positions
+  // start_pos + t); from tile kmask on, some key lies past one of this wave's
+  const int klast = (p.start_pos + min(qt * AQ + AQ - 1, T - 1)) / AK;
+  const int kmask = (p.start_pos + q0) / AK;
 
   const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
   const uint16_t* vg = p.v16t + (size_t)bg * HD * Tp;
@@ -569,7 +630,7 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   };
   issue_k(0);
   issue_v(0);
-  if (qt > 0) issue_k(1);
+  if (klast > 0) issue_k(1);
 
   // Q^T fragments: query q0 + nt*16 + col, dims rg*8 + 32*ks
   u32x4 qf[2][4];
@@ -615,7 +676,7 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   };
 
   // One key tile: softmax of the scores s (tile kt) and O += V P, with the
-  // next tile's scores computed in between (not on the diagonal tile, which
+  // next tile's scores computed in between (not on the last tile, which
   // is the last), so matrix-core and vector work of one wave interleave.
   f32x4 s[4][2];
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -628,13 +689,13 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (!LAST) {
-      if (kt + 2 <= qt) issue_k(kt + 2);
+      if (kt + 2 <= klast) issue_k(kt + 2);
       issue_v(kt + 1);
     }
-    if (LAST) {
+    if (LAST || kt >= kmask) {                      // causal mask near the diagonal
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int q = q0 + nt * 16 + col;
+        const int q = p.start_pos + q0 + nt * 16 + col;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -728,8 +789,8 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
         for (int nt = 0; nt < 2; ++nt) s[mt][nt] = sn[mt][nt];
     }
   };
-  for (int kt = 0; kt < qt; ++kt) step(std::false_type{}, kt);
-  step(std::true_type{}, qt);
+  for (int kt = 0; kt < klast; ++kt) step(std::false_type{}, kt);
+  step(std::true_type{}, klast);
 
   // ---- normalise, stage through LDS, store O (fp16) ----
   // Wave w's 32 x 128 block goes to its own 8 KiB of LDS, row = query, with
@@ -766,7 +827,7 @@ hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_attn_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
   if (e != hipSuccess) return e;
-  const int nqt = p.Tp / AQ;
+  const int nqt = (p.T + AQ - 1) / AQ;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3(p.B * KVH * nqt), dim3(512), kAttnLds, s, p);
   return hipGetLastError();
 }

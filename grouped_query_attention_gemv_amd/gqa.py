@@ -41,6 +41,7 @@ _SIGS = {
     "gqa_status_string": (ctypes.c_char_p, [_I]),
     "gqa_rope_table": (_I, [_I, ctypes.c_double, _I, _P, _P]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "gqa_workspace_bytes_from": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "gqa_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
     "gqa_set_decode_schedule": (_I, [_I]),
     "gqa_decode_schedule": (_I, [_I, _I, _I]),
@@ -48,6 +49,8 @@ _SIGS = {
                                ctypes.c_size_t, _P, _P]),
     "gqa_block_prefill_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
                                         ctypes.c_size_t, _P, _P, _P]),
+    "gqa_block_prefill_from": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
+                                    ctypes.c_size_t, _P, _P]),
     "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
                               ctypes.c_size_t, _P, _P]),
     "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
@@ -116,16 +119,19 @@ def _need(t, name, dtype, shape, device):
 # Allocation helpers (layouts of include/gqa.h)
 # ----------------------------------------------------------------------------
 
-def workspace_bytes(B: int, T: int, T_max: int) -> int:
+def workspace_bytes(B: int, T: int, T_max: int, start_pos: int = 0) -> int:
+    if start_pos:
+        return int(lib().gqa_workspace_bytes_from(int(B), int(start_pos), int(T), int(T_max)))
     return int(lib().gqa_workspace_bytes(int(B), int(T), int(T_max)))
 
 
-def workspace(B: int, T: int, T_max: int, device) -> torch.Tensor:
-    """A workspace for these arguments, initialised (gqa_workspace_init) on
-    the current stream."""
-    n = workspace_bytes(B, T, T_max)
+def workspace(B: int, T: int, T_max: int, device, start_pos: int = 0) -> torch.Tensor:
+    """A workspace for these arguments (prefill of T tokens from start_pos,
+    and decode), initialised (gqa_workspace_init) on the current stream."""
+    n = workspace_bytes(B, T, T_max, start_pos)
     if n == 0:
-        raise ValueError(f"no workspace size for B={B}, T={T}, T_max={T_max}")
+        raise ValueError(f"no workspace size for B={B}, start_pos={start_pos}, T={T}, "
+                         f"T_max={T_max}")
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     _check(lib().gqa_workspace_init(_ptr(ws), n, _stream(ws.device)), "gqa_workspace_init")
     return ws
@@ -290,9 +296,10 @@ def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope):
 
 
 def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, probe=None,
-                  events: HipEvents | None = None) -> torch.Tensor:
-    """Delta_attn [B, T, 4096] fp32 for x [B, T, 4096] bf16 from position 0;
-    writes cache rows 0..T-1."""
+                  events: HipEvents | None = None, start_pos: int = 0) -> torch.Tensor:
+    """Delta_attn [B, T, 4096] fp32 for x [B, T, 4096] bf16 at positions
+    start_pos..start_pos+T-1; reads cache rows 0..start_pos-1 and writes rows
+    start_pos..start_pos+T-1 (start_pos > 0: gqa_block_prefill_from)."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, 4096]")
     dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
@@ -304,7 +311,15 @@ def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, pr
     if probe is not None:
         _need(probe, "probe", torch.float32, (B, T, QKV_DIM), dev)
     if ws is None:
-        ws = workspace(B, T, T_max, dev)
+        ws = workspace(B, T, T_max, dev, start_pos)
+    if start_pos:
+        if events is not None:
+            raise ValueError("per-stage events are recorded for start_pos = 0 only")
+        _check(lib().gqa_block_prefill_from(
+            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
+            int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(out), _ptr(ws),
+            ws.numel(), _ptr(probe), _stream(dev)), "gqa_block_prefill_from")
+        return out
     args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
             int(T_max), _ptr(rope), int(B), int(T), _ptr(out), _ptr(ws), ws.numel(),
             _ptr(probe), _stream(dev)]

@@ -90,3 +90,13 @@ def prefill_workload(seed: int, B: int, T: int, device="cpu"):
     x = randn_bf16(gen, (B, T, D_MODEL), 1.0, device)
     w = block_weights(gen, device)
     return x, w
+
+
+def chunked_prefill_workload(seed: int, B: int, start_pos: int, T: int, device="cpu"):
+    """x [B, T, 4096], weights, and cached rows [B, start_pos, 8, 128] for K
+    and V (the keys and values of the earlier chunk)."""
+    gen = generator(seed, device)
+    x = randn_bf16(gen, (B, T, D_MODEL), 1.0, device)
+    w = block_weights(gen, device)
+    k, v = cache_rows(gen, B, start_pos, device)
+    return x, w, k, v

@@ -132,6 +132,14 @@ int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t
 size_t gqa_workspace_bytes(int B, int T, int T_max);
 
 /*
+ * gqa_workspace_bytes_from -- the same for gqa_block_prefill_from(start_pos,
+ * B, T) (and decode); its fp16 K/V copies hold all start_pos + T keys.  0 when
+ * the arguments are out of range (start_pos < 0 or start_pos + T > T_max
+ * included).  gqa_workspace_bytes(B, T, T_max) equals the start_pos = 0 value.
+ */
+size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max);
+
+/*
  * gqa_workspace_init -- zero the synchronisation words of a workspace of
  * ws_bytes bytes (one hipMemsetAsync on stream, not to be captured in a graph).
  * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (< GQA_SYNC_BYTES),
@@ -181,6 +189,30 @@ int gqa_block_prefill(const gqa_bf16* x,
                       const float* rope, int B, int T,
                       float* out, void* ws, size_t ws_bytes, float* probe,
                       hipStream_t stream);
+
+/*
+ * gqa_block_prefill_from -- the block over T new tokens of B sequences at
+ * positions start_pos .. start_pos+T-1, after start_pos rows already in the
+ * caches (chunked prefill).  The page "Llama 3.1 8B . Grouped-query
+ * attention" states the rule in the mask listing of its code section: with
+ * start_pos cached positions, new token i sits at position start_pos + i and
+ * attends to every key j <= start_pos + i, the cached rows included; RoPE
+ * uses the same absolute positions.  start_pos = 0 is gqa_block_prefill.
+ *   start_pos  0 .. T_max-T; rows 0 .. start_pos-1 of every sequence must
+ *              hold the earlier tokens' keys and values; they are read, not
+ *              written, and rows start_pos .. start_pos+T-1 are written
+ *   ws         ws_bytes >= gqa_workspace_bytes_from(B, start_pos, T, T_max)
+ *   other arguments as for gqa_block_prefill
+ * Errors: as gqa_block_prefill; GQA_ERR_RANGE for start_pos < 0 or
+ * start_pos + T > T_max.
+ */
+int gqa_block_prefill_from(const gqa_bf16* x,
+                           const gqa_bf16* wq, const gqa_bf16* wk,
+                           const gqa_bf16* wv, const gqa_bf16* wo,
+                           gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                           const float* rope, int start_pos, int B, int T,
+                           float* out, void* ws, size_t ws_bytes, float* probe,
+                           hipStream_t stream);
 
 /*
  * gqa_block_decode -- one new token per sequence at position start_pos (the

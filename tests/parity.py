@@ -178,14 +178,25 @@ class DecodeCase:
 
 
 class PrefillCase:
+    """Seeded prefill of T tokens per sequence at positions start_pos.. (cache
+    rows 0..start_pos-1 from the generator, sentinel NaN everywhere else)."""
+
     def __init__(self, B: int, T: int, T_max: int, seed: int = 0, dev="cuda", theta=5e5,
-                 scaled=True):
+                 scaled=True, start_pos: int = 0):
         self.B, self.T, self.T_max, self.dev = B, T, T_max, torch.device(dev)
-        self.theta, self.scaled = theta, scaled
-        self.x, self.w = synth.prefill_workload(seed, B, T)
+        self.theta, self.scaled, self.start_pos = theta, scaled, start_pos
+        if start_pos:
+            self.x, self.w, self.kc_rows, self.vc_rows = synth.chunked_prefill_workload(
+                seed, B, start_pos, T)
+        else:
+            self.x, self.w = synth.prefill_workload(seed, B, T)
+            self.kc_rows = self.vc_rows = None
         self.kcache, self.vcache = G.empty_caches(B, T_max, self.dev)
         self.kcache.copy_(synth.sentinel_like(self.kcache.shape, self.dev))
         self.vcache.copy_(synth.sentinel_like(self.vcache.shape, self.dev))
+        if start_pos:
+            G.kcache_by_position(self.kcache)[:, :start_pos] = self.kc_rows.to(self.dev)
+            G.vcache_write(self.vcache, 0, self.vc_rows.to(self.dev))
         self.k_before = self.kcache.clone()
         self.v_before = self.vcache.clone()
         self.rope = G.rope_table(T_max, theta, scaled, device=self.dev)
@@ -196,18 +207,21 @@ class PrefillCase:
         self.probe = torch.empty((self.B, self.T, G.QKV_DIM), dtype=torch.float32,
                                  device=self.dev) if probe else None
         self.out = G.block_prefill(self.xd, *self.wd, self.kcache, self.vcache, self.rope,
-                                   probe=self.probe)
+                                   probe=self.probe, start_pos=self.start_pos)
         torch.cuda.synchronize()
         return self.out
 
     def oracle(self, seqs=None):
         seqs = list(range(self.B)) if seqs is None else list(seqs)
         w = [f64(t) for t in self.w]
-        return O.gqa_block(f64(self.x[seqs]), *w, None, None, 0, self.theta, self.scaled)
+        kc = f64(self.kc_rows[seqs]) if self.start_pos else None
+        vc = f64(self.vc_rows[seqs]) if self.start_pos else None
+        return O.gqa_block(f64(self.x[seqs]), *w, kc, vc, self.start_pos, self.theta,
+                           self.scaled)
 
     def check(self, res, seqs=None):
         seqs = list(range(self.B)) if seqs is None else list(seqs)
-        B, T = len(seqs), self.T
+        B, T, sp = len(seqs), self.T, self.start_pos
         errs = {}
         errs["delta"] = assert_close("delta", f64(self.out[seqs]), res.delta)
         if self.probe is not None:
@@ -216,24 +230,32 @@ class PrefillCase:
             errs["k"] = assert_close("K", pr[..., 4096:5120], res.k.reshape(B, T, 1024))
             errs["v"] = assert_close("V", pr[..., 5120:], res.v.reshape(B, T, 1024))
         kpos = G.kcache_by_position(self.kcache)
-        vrows = G.vcache_read(self.vcache[seqs], 0, T)
+        vrows = G.vcache_read(self.vcache[seqs], sp, sp + T)
         kp = vp = None
         if self.probe is not None:
             kp = pr[..., 4096:5120].reshape(B, T, 8, 128)
             vp = pr[..., 5120:].reshape(B, T, 8, 128)
-        errs["k_flips"] = assert_bf16_rows("kcache rows", bits(kpos[seqs, :T]), res.k_bits, kp)
+        errs["k_flips"] = assert_bf16_rows("kcache rows", bits(kpos[seqs, sp:sp + T]), res.k_bits,
+                                           kp)
         errs["v_flips"] = assert_bf16_rows("vcache rows", bits(vrows), res.v_bits, vp)
-        log_errs(f"prefill B={self.B} T={T}", errs)
+        log_errs(f"prefill B={self.B} start_pos={sp} T={T}", errs)
         return errs
 
     def check_untouched(self):
-        """Rows T.. of every sequence keep their bits (the sentinel)."""
-        T, T_max = self.T, self.T_max
-        if T == T_max:
-            return
-        a = G.kcache_by_position(self.kcache)[:, T:].contiguous().view(torch.int16)
-        b = G.kcache_by_position(self.k_before)[:, T:].contiguous().view(torch.int16)
-        assert torch.equal(a, b) and bool((b == synth.SENTINEL_BITS).all()), "key rows >= T changed"
-        a = G.vcache_read(self.vcache, T, T_max).view(torch.int16)
-        b = G.vcache_read(self.v_before, T, T_max).view(torch.int16)
-        assert torch.equal(a, b) and bool((b == synth.SENTINEL_BITS).all()), "value rows >= T changed"
+        """Rows 0..start_pos-1 keep the cached prefix and rows start_pos+T..
+        the sentinel, bit for bit."""
+        sp, end, T_max = self.start_pos, self.start_pos + self.T, self.T_max
+        kb = lambda c: G.kcache_by_position(c).contiguous().view(torch.int16)
+        a, b = kb(self.kcache), kb(self.k_before)
+        assert torch.equal(a[:, :sp], b[:, :sp]), "cached key rows changed"
+        assert torch.equal(a[:, end:], b[:, end:]), "key rows past the chunk changed"
+        assert bool((b[:, end:] == synth.SENTINEL_BITS).all())
+        if sp:
+            assert torch.equal(G.vcache_read(self.vcache, 0, sp).view(torch.int16),
+                               G.vcache_read(self.v_before, 0, sp).view(torch.int16)), \
+                "cached value rows changed"
+        if end < T_max:
+            a = G.vcache_read(self.vcache, end, T_max).view(torch.int16)
+            b = G.vcache_read(self.v_before, end, T_max).view(torch.int16)
+            assert torch.equal(a, b) and bool((b == synth.SENTINEL_BITS).all()), \
+                "value rows past the chunk changed"

@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     for n in ("gqa_rope_table", "gqa_workspace_bytes", "gqa_block_prefill", "gqa_block_decode",
-              "gqa_status_string", "gqa_block_prefill_profiled", "gqa_block_decode_profiled"):
+              "gqa_status_string", "gqa_block_prefill_profiled", "gqa_block_decode_profiled",
+              "gqa_block_prefill_from", "gqa_workspace_bytes_from"):
         assert n in names
 
 
@@ -115,6 +116,39 @@ def test_decode_rejects_bad_arguments(kw, code):
 ])
 def test_prefill_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_block_prefill(*_prefill_args(**kw)) == code
+
+
+def _prefill_from_args(**kw):
+    a = dict(x=_fake(0), wq=_fake(1), wk=_fake(2), wv=_fake(3), wo=_fake(4), kc=_fake(5),
+             vc=_fake(6), T_max=1024, rope=_fake(7), start_pos=100, B=1, T=16, out=_fake(8),
+             ws=_fake(9), ws_bytes=1 << 40, probe=None, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("x", "wq", "wk", "wv", "wo", "kc", "vc", "T_max", "rope", "start_pos",
+                           "B", "T", "out", "ws", "ws_bytes", "probe", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), ENULL), (dict(rope=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(T=0), ESHAPE),
+    (dict(start_pos=-1), ERANGE), (dict(start_pos=1009), ERANGE), (dict(T=925), ERANGE),
+    (dict(ws_bytes=4096), EWS),
+    (dict(out=_fake(3)), EALIAS), (dict(vc=_fake(5)), EALIAS),
+])
+def test_prefill_from_rejects_bad_arguments(kw, code):
+    assert G.lib().gqa_block_prefill_from(*_prefill_from_args(**kw)) == code
+
+
+def test_workspace_bytes_from():
+    lib = G.lib()
+    assert lib.gqa_workspace_bytes_from(1, -1, 16, 1024) == 0
+    assert lib.gqa_workspace_bytes_from(1, 1009, 16, 1024) == 0
+    assert lib.gqa_workspace_bytes_from(1, 1008, 16, 1024) > 0
+    assert lib.gqa_workspace_bytes_from(4, 0, 2048, 4096) == lib.gqa_workspace_bytes(4, 2048, 4096)
+    # the fp16 K and V^T copies hold all start_pos + T keys: 2048 more rows of
+    # 8 heads x 128 fp16 per sequence, twice
+    grow = lib.gqa_workspace_bytes_from(4, 2048, 2048, 4096) - lib.gqa_workspace_bytes(4, 2048, 4096)
+    assert grow == 2 * 4 * 8 * 2048 * 128 * 2
+    assert G.workspace_bytes(4, 2048, 4096, start_pos=2048) == grow + lib.gqa_workspace_bytes(4, 2048, 4096)
 
 
 def test_profiled_variants_need_events():

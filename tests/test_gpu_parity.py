@@ -266,6 +266,48 @@ def test_prefill_is_deterministic():
 
 
 # ----------------------------------------------------------------------------
+# Chunked prefill: T new tokens after start_pos cached rows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,start_pos,T", [(1, 1, 1), (1, 64, 64), (2, 37, 70), (1, 130, 5),
+                                           (3, 200, 129), (2, 1000, 48), (1, 960, 300)])
+def test_prefill_chunked_small(B, start_pos, T):
+    T_max = ((start_pos + T + 31) // 32) * 32 + 32
+    c = PrefillCase(B, T, T_max, dev=DEV, start_pos=start_pos)
+    c.run()
+    c.check(c.oracle())
+    c.check_untouched()
+
+
+def test_prefill_chunked_b2_p1024_t1024():
+    """1,024 new tokens after 1,024 cached rows; the oracle checks sequence 1."""
+    c = PrefillCase(2, 1024, 2048, dev=DEV, start_pos=1024)
+    c.run()
+    print("chunked prefill B=2 P=1024 T=1024 errors", c.check(c.oracle([1]), [1]))
+    c.check_untouched()
+
+
+def test_chunked_prefill_continues_a_prefill():
+    """Prefill 300 tokens, then the next 200 from start_pos 300 on the same
+    cache.  The cache rows equal those of one 500-token prefill bit for bit
+    (same GEMM rows, same positions); the chunk's Delta matches the oracle of
+    the 500-token prefill."""
+    P, T = 300, 200
+    full = PrefillCase(1, P + T, 512, dev=DEV)
+    full.run(probe=False)
+    ref = full.oracle()
+    kc, vc = G.empty_caches(1, 512, DEV)
+    G.block_prefill(full.xd[:, :P].contiguous(), *full.wd, kc, vc, full.rope)
+    out = G.block_prefill(full.xd[:, P:].contiguous(), *full.wd, kc, vc, full.rope, start_pos=P)
+    torch.cuda.synchronize()
+    assert_close("chunk vs oracle", f64(out), ref.delta[:, P:])
+    assert_close("chunk vs one prefill", f64(out), f64(full.out[:, P:]))
+    assert np.array_equal(bits(G.kcache_by_position(kc)[:, :P + T]),
+                          bits(G.kcache_by_position(full.kcache)[:, :P + T]))
+    assert np.array_equal(bits(G.vcache_read(vc, 0, P + T)), bits(G.vcache_read(full.vcache, 0, P + T)))
+
+
+# ----------------------------------------------------------------------------
 # Decode after prefill
 # ----------------------------------------------------------------------------
 
