@@ -55,10 +55,10 @@ def decode_bytes(B: int, P: int) -> dict:
     return {"qkv": qkv, "attn": attn, "wo": wo, "step": step}
 
 
-def prefill_flops(B: int, T: int) -> dict:
+def prefill_flops(B: int, T: int, start_pos: int = 0) -> dict:
     M = B * T
     qkv = 2.0 * M * NQKV * D
-    causal_pairs = B * T * (T + 1) / 2
+    causal_pairs = B * (T * start_pos + T * (T + 1) / 2)   # token i sees start_pos + i + 1 keys
     attn = 4.0 * causal_pairs * 32 * HD             # QK^T and PV over visible pairs, 32 heads
     wo = 2.0 * M * D * D
     return {"qkv": qkv, "attn": attn, "wo": wo, "total": qkv + attn + wo}
@@ -212,6 +212,36 @@ def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
                 kern_tflops={k: fl[k] / (kern[k] * 1e-6) / 1e12 for k in ("qkv", "attn", "wo")})
 
 
+def bench_chunked_prefill(G, synth, steps: int, warmup: int, B=4, P=2048, T=2048):
+    """Whole-call timing of a prefill of T tokens after P cached rows per
+    sequence (gqa_block_prefill_from), HIP events on the current stream."""
+    dev = torch.device("cuda:0")
+    x, w, kc_rows, vc_rows = synth.chunked_prefill_workload(0, B, P, T)
+    x = x.to(dev)
+    w = [t.to(dev) for t in w]
+    T_max = P + T
+    kc, vc = G.empty_caches(B, T_max, dev)
+    G.kcache_by_position(kc)[:, :P] = kc_rows.to(dev)
+    G.vcache_write(vc, 0, vc_rows.to(dev))
+    del kc_rows, vc_rows
+    rope = G.rope_table(T_max, device=dev)
+    ws = G.workspace(B, T, T_max, dev, start_pos=P)
+    out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        G.block_prefill(x, *w, kc, vc, rope, out=out, ws=ws, start_pos=P)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        G.block_prefill(x, *w, kc, vc, rope, out=out, ws=ws, start_pos=P)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1000.0 / steps
+    fl = prefill_flops(B, T, P)
+    return us, fl
+
+
 def _timed_steps(step, steps, warmup, use_graph):
     """Median-free whole-loop timing of `steps` calls of step(i) (graph replay
     of the whole loop when use_graph), HIP events on the current stream."""
@@ -354,7 +384,8 @@ def main():
                     help="decode schedule of the headline workloads (auto: the library's "
                          "choice, which is the one-launch schedule where it applies)")
     ap.add_argument("--workload", default="decode_p1000",
-                    choices=["decode_p1000", "decode_p128", "batched", "stacked_long"],
+                    choices=["decode_p1000", "decode_p128", "batched", "stacked_long",
+                             "chunked_prefill"],
                     help="decode_p1000 (headline), batched (B=64, P=8192) or "
                          "stacked_long (32 blocks, B=8, P=131071)")
     args = ap.parse_args()
@@ -397,6 +428,25 @@ def main():
                          "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes": nb["attn"]}}), flush=True)
+        return
+    if args.workload == "chunked_prefill":
+        B, P, T = 4, 2048, 2048
+        steps = args.steps if args.steps != 400 else 10
+        us, fl = bench_chunked_prefill(G, synth, steps, min(args.warmup, 3), B, P, T)
+        tfs = fl["total"] / (us * 1e-6) / 1e12
+        print(json.dumps({
+            "metric": METRIC, "value": round(B * T / (us * 1e-6), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 3),
+            "ms_per_step": round(us / 1000, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "Llama-3.1-8B GQA block chunked prefill: B=4 sequences, "
+                                   "2,048 new tokens after 2,048 cached rows each",
+                       "B": B, "start_pos": P, "T": T, "T_max": P + T},
+            "algorithmic_gflop": round(fl["total"] / 1e9, 3),
+            "roofline": {"kernel": "whole call (prep, QKV GEMM, attention, wo GEMM)",
+                         "bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None}}), flush=True)
         return
     if args.workload == "stacked_long":
         us, nb, finite = bench_stacked(G, synth, args.steps if args.steps != 400 else 5,
