@@ -212,6 +212,38 @@ def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
                 kern_tflops={k: fl[k] / (kern[k] * 1e-6) / 1e12 for k in ("qkv", "attn", "wo")})
 
 
+def bench_layer_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024):
+    """Graph-replay time per step of the layer (RMSNorm, block, residual:
+    gqa_layer_decode) and of the bare block on the same rotated inputs."""
+    dev = torch.device("cuda:0")
+    sets = []
+    for s_ in range(N_SETS):
+        x, w, kc_rows, vc_rows = synth.decode_workload(s_, B, P)
+        kc, vc = G.empty_caches(B, T_max, dev)
+        kc.zero_()
+        vc.zero_()
+        G.kcache_by_position(kc)[:, :P] = kc_rows.to(dev)
+        G.vcache_write(vc, 0, vc_rows.to(dev))
+        sets.append(dict(x=x.to(dev), w=[t.to(dev) for t in w], kc=kc, vc=vc,
+                         g=synth.norm_gain(100 + s_).to(dev)))
+    rope = G.rope_table(T_max, device=dev)
+    ws = G.layer_workspace(B, 1, T_max, dev)
+    h = torch.empty((B, D), dtype=torch.float32, device=dev)
+    h16 = torch.empty((B, D), dtype=torch.bfloat16, device=dev)
+
+    def layer(i):
+        st = sets[i % N_SETS]
+        G.layer_decode(st["x"], st["g"], *st["w"], st["kc"], st["vc"], rope, P, h=h, h_bf16=h16,
+                       ws=ws)
+
+    def block(i):
+        st = sets[i % N_SETS]
+        G.block_decode(st["x"], *st["w"], st["kc"], st["vc"], rope, P, out=h, ws=ws)
+
+    n = max(N_SETS, steps // N_SETS * N_SETS)
+    return _timed_steps(layer, n, warmup, True), _timed_steps(block, n, warmup, True)
+
+
 def bench_chunked_prefill(G, synth, steps: int, warmup: int, B=4, P=2048, T=2048):
     """Whole-call timing of a prefill of T tokens after P cached rows per
     sequence (gqa_block_prefill_from), HIP events on the current stream."""
@@ -385,7 +417,7 @@ def main():
                          "choice, which is the one-launch schedule where it applies)")
     ap.add_argument("--workload", default="decode_p1000",
                     choices=["decode_p1000", "decode_p128", "batched", "stacked_long",
-                             "chunked_prefill"],
+                             "chunked_prefill", "layer_decode_p1000"],
                     help="decode_p1000 (headline), batched (B=64, P=8192) or "
                          "stacked_long (32 blocks, B=8, P=131071)")
     args = ap.parse_args()
@@ -428,6 +460,23 @@ def main():
                          "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes": nb["attn"]}}), flush=True)
+        return
+    if args.workload == "layer_decode_p1000":
+        steps = args.steps if args.steps != 400 else 200
+        lay, blk = bench_layer_decode(G, synth, steps, min(args.warmup, 20))
+        nb = decode_bytes(1, 1000)["step"] + 2 * 4096 * 2 + 2 * 4096 * 4   # + x, gain, h, h_bf16
+        tbs = nb / (lay * 1e-6) / 1e12
+        print(json.dumps({
+            "metric": METRIC, "value": round(lay, 3), "unit": "us/layer-step", "n_gpus": 1,
+            "steps": steps, "warmup": min(args.warmup, 20), "ms_per_step": round(lay / 1000, 5),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "Llama-3.1-8B attention layer decode (RMSNorm, block, residual), "
+                                   "B=1, P=1000", "B": 1, "P": 1000, "T_max": 1024,
+                       "hip_graph": True},
+            "block_only_us": round(blk, 3), "norm_residual_overhead_us": round(lay - blk, 3),
+            "hbm_tbs": round(tbs, 4), "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4)}),
+            flush=True)
         return
     if args.workload == "chunked_prefill":
         B, P, T = 4, 2048, 2048

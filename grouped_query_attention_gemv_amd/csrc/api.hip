@@ -78,7 +78,8 @@ inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
 int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
                  const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
                  const float* rope, int start_pos, int B, int T, float* out, void* ws,
-                 size_t ws_bytes, float* probe, hipStream_t stream, hipEvent_t* events) {
+                 size_t ws_bytes, float* probe, hipStream_t stream, hipEvent_t* events,
+                 int accumulate = 0, bool dry = false) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
   if (T < 1 || (long)B * T > (1L << 24)) return GQA_ERR_SHAPE;
@@ -98,9 +99,10 @@ int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, cons
   memset(&p, 0, sizeof(p));
   p.x = x; p.wq = wq; p.wk = wk; p.wv = wv; p.wo = wo;
   p.kcache = kcache; p.vcache = vcache; p.rope = rope; p.out = out; p.probe = probe;
-  p.T_max = T_max; p.B = B; p.T = T; p.start_pos = start_pos;
+  p.T_max = T_max; p.B = B; p.T = T; p.start_pos = start_pos; p.accumulate = accumulate;
   p.Tp = (start_pos + T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
   prefill_ws_carve(ws, &p);
+  if (dry) return GQA_OK;
 
   (void)hipGetLastError();
   hipError_t e;
@@ -120,7 +122,8 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
                 const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
                 const float* rope, int start_pos, int B, float* out, gqa_bf16* out_bf16,
                 int accumulate, void* ws, size_t ws_bytes, float* probe, hipStream_t stream,
-                hipEvent_t* events) {
+                hipEvent_t* events, bool dry = false, const gqa_bf16* norm_w = nullptr,
+                float norm_eps = 0.f, const gqa_bf16* resid = nullptr) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
@@ -142,10 +145,13 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   p.kcache = kcache; p.vcache = vcache; p.rope = rope;
   p.out = out; p.out_bf16 = out_bf16; p.probe = probe;
   p.T_max = T_max; p.start_pos = start_pos; p.B = B; p.accumulate = accumulate;
+  p.norm_w = norm_w; p.norm_eps = norm_eps; p.resid = resid;
+  if ((norm_w || resid) && (B > kGemvMaxB || accumulate)) return GQA_ERR_ARG;
   decode_ws_carve(ws, B, &p);
   decode_split(B, start_pos + 1, &p.nsplit, &p.chunk);
   const int sched = pick_schedule(B, start_pos);
   if (sched < 0) return GQA_ERR_ARG;
+  if (dry) return GQA_OK;
 
   (void)hipGetLastError();
   hipError_t e;
@@ -162,6 +168,25 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   if ((e = mark(events, 2, stream)) != hipSuccess) return GQA_ERR_HIP;
   if ((e = launch_decode_wo(p, stream)) != hipSuccess) return hip_status(e);
   if ((e = mark(events, 3, stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+// Checks shared by the layer entry points; on success *xn points at the
+// normalised input inside ws, after the block's own block_bytes.
+int layer_prologue(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, const void* h,
+                   void* ws, size_t ws_bytes, size_t block_bytes, gqa_bf16** xn) {
+  if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(norm_w) || !aligned16(h) || !aligned16(ws)) return GQA_ERR_ALIGN;
+  if (!(eps > 0.f) || !(eps < 1.f)) return GQA_ERR_ARG;
+  if (block_bytes == 0) return GQA_ERR_SHAPE;
+  const size_t base = (block_bytes + 255) & ~(size_t)255;
+  if (ws_bytes < base + (size_t)M * D * 2) return GQA_ERR_WORKSPACE;
+  // the residual h must not overlap the input, the gain or the workspace
+  const Range ins[] = {span(x, (size_t)M * D * 2), span(norm_w, (size_t)D * 2),
+                       span(ws, ws_bytes)};
+  const Range outs[] = {span(h, (size_t)M * D * 4)};
+  if (any_alias(outs, 1, ins, 3)) return GQA_ERR_ALIAS;
+  *xn = reinterpret_cast<gqa_bf16*>(static_cast<char*>(ws) + base);
   return GQA_OK;
 }
 
@@ -236,6 +261,62 @@ int gqa_block_prefill(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
                       void* ws, size_t ws_bytes, float* probe, hipStream_t stream) {
   return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, 0, B, T, out, ws, ws_bytes,
                       probe, stream, nullptr);
+}
+
+size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max) {
+  const size_t n = gqa_workspace_bytes_from(B, start_pos, T, T_max);
+  if (n == 0) return 0;
+  return ((n + 255) & ~(size_t)255) + (size_t)B * T * D * 2;
+}
+
+int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                           const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                           const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                           const float* rope, int start_pos, int B, int T, float* h, void* ws,
+                           size_t ws_bytes, float* probe, hipStream_t stream) {
+  if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
+  if (B < 1 || B > GQA_MAX_BATCH || T < 1 || (long)B * T > (1L << 24) || T_max < 1 ||
+      T_max > GQA_MAX_T_MAX)
+    return GQA_ERR_SHAPE;
+  if (start_pos < 0 || (long)start_pos + T > T_max) return GQA_ERR_RANGE;
+  const size_t block = gqa_workspace_bytes_from(B, start_pos, T, T_max);
+  gqa_bf16* xn = nullptr;
+  int st = layer_prologue(x, norm_w, eps, B * T, h, ws, ws_bytes, block, &xn);
+  if (st != GQA_OK) return st;
+  st = prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws, block,
+                    probe, stream, nullptr, 1, true);
+  if (st != GQA_OK) return st;
+  (void)hipGetLastError();
+  if (launch_rmsnorm(x, norm_w, eps, B * T, xn, h, stream) != hipSuccess) return GQA_ERR_HIP;
+  return prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws,
+                      block, probe, stream, nullptr, 1, false);
+}
+
+int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const gqa_bf16* wq,
+                     const gqa_bf16* wk, const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max, const float* rope,
+                     int start_pos, int B, float* h, gqa_bf16* h_bf16, void* ws, size_t ws_bytes,
+                     float* probe, hipStream_t stream) {
+  if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
+  if (B < 1 || B > GQA_MAX_BATCH || T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
+  if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
+  const size_t block = gqa_workspace_bytes(B, 1, T_max);
+  gqa_bf16* xn = nullptr;
+  int st = layer_prologue(x, norm_w, eps, B, h, ws, ws_bytes, block, &xn);
+  if (st != GQA_OK) return st;
+  if (B <= kGemvMaxB) {
+    // GEMV path: the QKV prologue normalises the staged rows and the wo
+    // epilogue adds the residual, no extra launch
+    return decode_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 0,
+                       ws, block, probe, stream, nullptr, false, norm_w, eps, x);
+  }
+  st = decode_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 1, ws,
+                   block, probe, stream, nullptr, true);
+  if (st != GQA_OK) return st;
+  (void)hipGetLastError();
+  if (launch_rmsnorm(x, norm_w, eps, B, xn, h, stream) != hipSuccess) return GQA_ERR_HIP;
+  return decode_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 1,
+                     ws, block, probe, stream, nullptr, false);
 }
 
 int gqa_block_prefill_from(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,

@@ -80,6 +80,48 @@ __device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restr
 // QKV projection + RoPE + cache append
 // ---------------------------------------------------------------------------
 
+// Layer pre-norm of the NB staged rows, in place: x -> bf16(x * r * g) with
+// r = 1 / sqrt(mean(x^2) + eps) per row (page "Llama 3.1 8B . Grouped-query
+// attention", code section: the block receives attention_norm(x); the norm
+// is read as the standard RMSNorm with a per-feature gain).  Thread i owns
+// bf16 pairs i + 256*j, j < 8, of every row; the row sums combine the four
+// waves in a fixed order.
+template <int NB>
+__device__ __forceinline__ void norm_rows(uint32_t* xs, const uint16_t* __restrict__ g, float eps) {
+  __shared__ float red[4 * NB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float ss[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = xs[t * (D / 2) + tid + 256 * j];
+      const float a = bf16_bits_to_f32(u & 0xffffu), b = bf16_bits_to_f32(u >> 16);
+      ss[t] += a * a + b * b;
+    }
+    ss[t] = wave_sum(ss[t]);
+    if (lane == 0) red[w * NB + t] = ss[t];
+  }
+  uint32_t gp[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gp[j] = reinterpret_cast<const uint32_t*>(g)[tid + 256 * j];
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const float tot = (red[t] + red[NB + t]) + (red[2 * NB + t] + red[3 * NB + t]);
+    const float r = 1.f / sqrtf(tot * (1.f / D) + eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t* q = xs + t * (D / 2) + tid + 256 * j;
+      const uint32_t u = *q;
+      *q = pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * r * bf16_bits_to_f32(gp[j] & 0xffffu),
+                       bf16_bits_to_f32(u >> 16) * r * bf16_bits_to_f32(gp[j] >> 16));
+    }
+  }
+  __syncthreads();
+}
+
 // Output features of QKV workgroup `blk`: 8 consecutive features, 2 per wave.
 // The three-launch schedule takes them in feature order.  The fused schedule
 // takes them kv head by kv head (Q of its 4 query heads: 64 workgroups, then
@@ -122,6 +164,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
     for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
   }
   __syncthreads();
+  if (p.norm_w) norm_rows<NB>(xs, p.norm_w, p.norm_eps);
 
   float acc[2][NB];
   gemv_rows2<NB, 1>(wa, wb, xs, lane, acc);
@@ -639,6 +682,10 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
     const float2 prev = *o;
     r.x += prev.x;
     r.y += prev.y;
+  } else if (p.resid) {
+    const uint32_t xr = *reinterpret_cast<const uint32_t*>(p.resid + (size_t)b * D + r0);
+    r.x += bf16_bits_to_f32(xr & 0xffffu);
+    r.y += bf16_bits_to_f32(xr >> 16);
   }
   *o = r;
   if (p.out_bf16)

@@ -60,6 +60,12 @@ struct DecodeParams {
   uint32_t* kv_new;         // [B][2][8][64] appended K, V rows as packed bf16 pairs
   int* sync;                // the workspace's synchronisation words
   int nsplit, chunk;        // positions split over nsplit workgroups of chunk keys
+  // layer mode of the GEMV path (B <= kGemvMaxB): the QKV prologue replaces
+  // x by RMSNorm(x) * norm_w (rounded to bf16), and the wo epilogue writes
+  // out = resid + Delta
+  const uint16_t* norm_w;   // optional [4096] bf16 gain
+  float norm_eps;
+  const uint16_t* resid;    // optional [B][4096] bf16 residual
 };
 
 // Split of the L = start_pos + 1 visible positions over workgroups.
@@ -94,6 +100,7 @@ struct PrefillParams {
   float* probe;             // optional [M][6144]
   int T_max, B, T;          // T new tokens per sequence, at positions start_pos ..
   int start_pos;            // cached rows 0 .. start_pos-1 precede them
+  int accumulate;           // out += Delta instead of out = Delta
   int Tp;                   // start_pos + T rounded up to the attention tile
   // workspace
   uint16_t* wo16;           // [4096][4096] fp16 copy of wo
@@ -112,5 +119,14 @@ hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Pre-norm of a layer
+// ---------------------------------------------------------------------------
+
+// xn[m] = bf16(RMSNorm(x[m]) * g) for M rows of 4096; h[m] = x[m] in fp32
+// when h is non-null (the residual the block's update is added to).
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* g, float eps, int M, uint16_t* xn,
+                          float* h, hipStream_t s);
 
 }  // namespace gqa

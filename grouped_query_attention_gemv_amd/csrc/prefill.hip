@@ -495,8 +495,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
   }
 }
 
-// wo epilogue: fp32 rows of Delta, one 16-byte unit per lane, 4 rows of 256
-// bytes per store instruction.
+// wo epilogue: fp32 rows of Delta (added to out when accumulating), one
+// 16-byte unit per lane, 4 rows of 256 bytes per store instruction.
 template <int HALF>
 __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const f32x4 (&acc)[8][4], char* st,
                                              int mw, int fw, int lane) {
@@ -510,7 +510,9 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const f32x4 (&ac
     const int r = it * 4 + (lane >> 4);
     const f32x4 v = *reinterpret_cast<const f32x4*>(st + stage_off(r, u));
     const int m = mh + r;
-    if (m < g.M) *reinterpret_cast<f32x4*>(g.p.out + (size_t)m * D + fw + 4 * u) = v;
+    if (m >= g.M) continue;
+    f32x4* dst = reinterpret_cast<f32x4*>(g.p.out + (size_t)m * D + fw + 4 * u);
+    *dst = g.p.accumulate ? *dst + v : v;
   }
 }
 

@@ -53,6 +53,11 @@ _SIGS = {
                                     ctypes.c_size_t, _P, _P]),
     "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
                               ctypes.c_size_t, _P, _P]),
+    "gqa_layer_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "gqa_layer_prefill_from": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I,
+                                    _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
+    "gqa_layer_decode": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I,
+                              _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
                                        _P, ctypes.c_size_t, _P, _P, _P]),
 }
@@ -328,6 +333,71 @@ def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, pr
     else:
         _check(lib().gqa_block_prefill_profiled(*args, events.events), "gqa_block_prefill_profiled")
     return out
+
+
+NORM_EPS = 1e-5   # norm_eps of the Llama 3.1 8B catalogue entry
+
+
+def layer_workspace(B: int, T: int, T_max: int, device, start_pos: int = 0) -> torch.Tensor:
+    """An initialised workspace for layer_prefill(B, T, start_pos) (or, with
+    T = 1 and start_pos = 0, for layer_decode)."""
+    n = int(lib().gqa_layer_workspace_bytes(int(B), int(start_pos), int(T), int(T_max)))
+    if n == 0:
+        raise ValueError(f"no layer workspace size for B={B}, start_pos={start_pos}, T={T}, "
+                         f"T_max={T_max}")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().gqa_workspace_init(_ptr(ws), n, _stream(ws.device)), "gqa_workspace_init")
+    return ws
+
+
+def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int = 0,
+                  eps: float = NORM_EPS, h=None, ws=None, probe=None) -> torch.Tensor:
+    """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, T, 4096] fp32 for x
+    [B, T, 4096] bf16 at positions start_pos..; the block's cache rows as in
+    block_prefill."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, 4096]")
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    T = x.shape[1]
+    _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
+    _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
+    if h is None:
+        h = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=dev)
+    _need(h, "h", torch.float32, (B, T, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, T, QKV_DIM), dev)
+    if ws is None:
+        ws = layer_workspace(B, T, T_max, dev, start_pos)
+    _check(lib().gqa_layer_prefill_from(
+        _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
+        _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(h), _ptr(ws),
+        ws.numel(), _ptr(probe), _stream(dev)), "gqa_layer_prefill_from")
+    return h
+
+
+def layer_decode(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int,
+                 eps: float = NORM_EPS, h=None, h_bf16=None, ws=None, probe=None) -> torch.Tensor:
+    """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, 4096] fp32 for one token per
+    sequence at start_pos; h_bf16 (optional) receives its bf16 rounding."""
+    if x.dim() != 2:
+        raise ValueError("x must be [B, 4096]")
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
+    _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
+    if h is None:
+        h = torch.empty((B, D_MODEL), dtype=torch.float32, device=dev)
+    _need(h, "h", torch.float32, (B, D_MODEL), dev)
+    if h_bf16 is not None:
+        _need(h_bf16, "h_bf16", torch.bfloat16, (B, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, QKV_DIM), dev)
+    if ws is None:
+        ws = layer_workspace(B, 1, T_max, dev)
+    _check(lib().gqa_layer_decode(
+        _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
+        _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(h), _ptr(h_bf16),
+        _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)), "gqa_layer_decode")
+    return h
 
 
 def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=None,

@@ -100,3 +100,10 @@ def chunked_prefill_workload(seed: int, B: int, start_pos: int, T: int, device="
     w = block_weights(gen, device)
     k, v = cache_rows(gen, B, start_pos, device)
     return x, w, k, v
+
+
+def norm_gain(seed: int, device="cpu") -> torch.Tensor:
+    """bf16 [4096] gain of a pre-norm: 1 + N(0, 0.1^2)."""
+    gen = generator(seed, device)
+    g = 1.0 + 0.1 * torch.randn((D_MODEL,), generator=gen, dtype=torch.float32, device=device)
+    return g.to(torch.bfloat16)

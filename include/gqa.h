@@ -215,6 +215,47 @@ int gqa_block_prefill_from(const gqa_bf16* x,
                            hipStream_t stream);
 
 /*
+ * Layer entry points: the block inside its residual branch, as the page
+ * "Llama 3.1 8B . Grouped-query attention" shows it in its code section
+ * (h = x + attention(attention_norm(x), ...), attention_norm an RMSNorm over
+ * the 4096 features with eps = norm_eps, 1e-5 in the catalogue entry).  The
+ * pages do not print the norm's body; it is taken as
+ *   xn = x / sqrt(mean(x^2) + eps) * norm_w,
+ * computed in fp32 and rounded once to bf16, the block's input dtype.
+ * Outputs: h = x + Delta_attn(xn) in fp32, and for decode optionally its bf16
+ * rounding (the next layer's input).
+ *   x        bf16, [B][T][4096] (prefill) or [B][4096] (decode), the residual
+ *            stream before the layer
+ *   norm_w   bf16 [4096], the norm's gain
+ *   eps      0 < eps < 1
+ *   h        fp32, same shape as x; written, never read
+ *   ws       ws_bytes >= gqa_layer_workspace_bytes(B, start_pos, T, T_max)
+ *            for prefill, gqa_layer_workspace_bytes(B, 0, 1, T_max) for
+ *            decode; the normalised input lives at its end
+ *   other arguments as for gqa_block_prefill_from / gqa_block_decode
+ * Errors: those of the block calls; GQA_ERR_ARG for eps; GQA_ERR_ALIAS when h
+ * overlaps x, norm_w or ws.
+ */
+size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max);
+
+int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                           const gqa_bf16* wq, const gqa_bf16* wk,
+                           const gqa_bf16* wv, const gqa_bf16* wo,
+                           gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                           const float* rope, int start_pos, int B, int T,
+                           float* h, void* ws, size_t ws_bytes, float* probe,
+                           hipStream_t stream);
+
+int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                     const gqa_bf16* wq, const gqa_bf16* wk,
+                     const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
+                     const float* rope, int start_pos, int B,
+                     float* h, gqa_bf16* h_bf16,
+                     void* ws, size_t ws_bytes, float* probe,
+                     hipStream_t stream);
+
+/*
  * gqa_block_decode -- one new token per sequence at position start_pos (the
  * page's decode mode): writes cache row start_pos and attends over rows
  * 0..start_pos of each of the B sequences (one start_pos for all of them).

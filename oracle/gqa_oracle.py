@@ -36,6 +36,12 @@ notes of the repository):
     factor 1, high-frequency factor 4, original context 8192).  The pages cite
     but do not print that rule, so its constants are "parity unpinned";
     only its shape (continuity, limits) is pinned by the tests.
+  * Pre-norm (``rms_norm``, ``gqa_layer``): the page constructs
+    attention_norm = RMSNorm(dim, eps=norm_eps) (norm_eps 1e-5 in the
+    catalogue entry) and adds the attention's update to x, but does not print
+    the norm's body.  It is read as the standard root-mean-square norm with a
+    per-feature gain, x / sqrt(mean(x^2) + eps) * g, and its output is
+    rounded once to bf16 because the block consumes bf16 input.
   * Cache layout: the oracle's logical cache is [B][position][kv_head][dim]
     (the keys comment in evidence "gqa" indexes keys by batch, position,
     head, dim).  How the GPU lays it out in memory is not the oracle's concern.
@@ -310,3 +316,27 @@ def stacked_decode(x_bits_first, weights, k_cached_list, v_cached_list, start_po
         deltas.append(d)
         h = h + d
     return h, deltas
+
+
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """Root-mean-square norm over the last axis with gain g:
+    x / sqrt(mean(x^2) + eps) * g (the reading of attention_norm above)."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def gqa_layer(x, norm_w, eps: float, wq, wk, wv, wo, k_cached, v_cached, start_pos: int,
+              theta: float = ROPE_THETA, scaled: bool = True):
+    """The block inside its residual branch (page "Llama 3.1 8B . Grouped-query
+    attention", code section: h = x + attention(attention_norm(x), ...)).
+
+    x: [B, T, d] bf16 values; norm_w: [d] bf16 values.  The normalised input
+    is rounded to bf16 (the block's input dtype) before the block.
+    Returns (h [B, T, d] fp64, the block's BlockResult).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xn = f64_from_bf16_bits(bf16_bits_from_f64(rms_norm(x, norm_w, eps)))
+    res = gqa_block(xn, wq, wk, wv, wo, k_cached, v_cached, start_pos, theta, scaled)
+    return x + res.delta, res

@@ -151,6 +151,37 @@ def test_workspace_bytes_from():
     assert G.workspace_bytes(4, 2048, 4096, start_pos=2048) == grow + lib.gqa_workspace_bytes(4, 2048, 4096)
 
 
+def test_layer_workspace_bytes():
+    lib = G.lib()
+    for (B, sp, T, Tm) in [(1, 0, 1, 1024), (4, 2048, 2048, 4096), (2, 0, 70, 128)]:
+        base = lib.gqa_workspace_bytes_from(B, sp, T, Tm)
+        assert lib.gqa_layer_workspace_bytes(B, sp, T, Tm) == ((base + 255) // 256) * 256 + B * T * 4096 * 2
+    assert lib.gqa_layer_workspace_bytes(1, 1020, 8, 1024) == 0
+
+
+def _layer_decode_args(**kw):
+    a = dict(x=_fake(0), g=_fake(10), eps=ctypes.c_float(1e-5), wq=_fake(1), wk=_fake(2),
+             wv=_fake(3), wo=_fake(4), kc=_fake(5), vc=_fake(6), T_max=1024, rope=_fake(7),
+             start_pos=10, B=1, h=_fake(8), h_bf16=None, ws=_fake(9), ws_bytes=1 << 40,
+             probe=None, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("x", "g", "eps", "wq", "wk", "wv", "wo", "kc", "vc", "T_max", "rope",
+                           "start_pos", "B", "h", "h_bf16", "ws", "ws_bytes", "probe", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), ENULL), (dict(h=None), ENULL), (dict(wq=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(start_pos=1024), ERANGE), (dict(start_pos=-3), ERANGE),
+    (dict(eps=ctypes.c_float(0.0)), EARG), (dict(eps=ctypes.c_float(float("nan"))), EARG),
+    (dict(g=ctypes.c_void_p(BASE + (10 << 32) + 2)), EALIGN),
+    (dict(ws_bytes=4096), EWS),
+    (dict(h=_fake(0)), EALIAS), (dict(h=_fake(10)), EALIAS), (dict(h=_fake(9)), EALIAS),
+    (dict(h_bf16=_fake(5)), EALIAS),
+])
+def test_layer_decode_rejects_bad_arguments(kw, code):
+    assert G.lib().gqa_layer_decode(*_layer_decode_args(**kw)) == code
+
+
 def test_profiled_variants_need_events():
     l = G.lib()
     assert l.gqa_block_decode_profiled(*_decode_args(), None) == ENULL

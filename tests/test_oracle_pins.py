@@ -377,3 +377,43 @@ def test_stacked_decode_residual():
     x1 = O.f64_from_bf16_bits(O.bf16_bits_from_f64(h1))
     r1 = O.gqa_block(x1[:, None], *ws[1], kcs[1], vcs[1], sp)
     assert np.max(np.abs(h - (h1 + r1.delta[:, 0]))) < 1e-12
+
+
+def test_rms_norm_matches_torch_rms_norm():
+    """The pre-norm reading against the library routine, in fp64."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 5, 4096)) * 3.0
+    g = rng.standard_normal(4096)
+    for eps in (1e-5, 0.3):
+        want = F.rms_norm(torch.from_numpy(x), (4096,), weight=torch.from_numpy(g), eps=eps).numpy()
+        assert np.max(np.abs(O.rms_norm(x, g, eps) - want)) < 1e-12
+
+
+def test_rms_norm_closed_forms():
+    d, eps = 4096, 1e-5
+    g = np.linspace(-2.0, 2.0, d)
+    c = 0.75
+    y = O.rms_norm(np.full((1, d), c), np.ones(d), eps)
+    assert np.allclose(y, c / math.sqrt(c * c + eps), rtol=0, atol=1e-15)
+    x = np.zeros((1, d))
+    x[0, 17] = 5.0                                    # one nonzero feature: mean = 25 / d
+    y = O.rms_norm(x, g, eps)
+    assert abs(y[0, 17] - 5.0 / math.sqrt(25.0 / d + eps) * g[17]) < 1e-12
+    assert np.count_nonzero(y) == 1
+    # scale equivariance: norm(s x, s^2 eps) == norm(x, eps)
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((2, d))
+    assert np.max(np.abs(O.rms_norm(7.0 * x, g, 49.0 * eps) - O.rms_norm(x, g, eps))) < 1e-12
+
+
+def test_layer_with_zero_gain_is_the_identity():
+    """norm_w = 0 makes the block's input zero: every q, k, v is zero, the
+    attention averages zero values, Delta = 0 and h == x bit for bit."""
+    rng = np.random.default_rng(23)
+    d, KV, hd = 4096, 8, 128
+    x = _bf16_vals(rng, (2, 3, d), 1.0)
+    w = (_bf16_vals(rng, (d, d), 0.02), _bf16_vals(rng, (KV * hd, d), 0.02),
+         _bf16_vals(rng, (KV * hd, d), 0.02), _bf16_vals(rng, (d, d), 0.02))
+    h, res = O.gqa_layer(x, np.zeros(d), 1e-5, *w, None, None, 0)
+    assert np.array_equal(h, x)
+    assert not np.any(res.delta)
