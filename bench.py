@@ -417,7 +417,7 @@ def main():
                          "choice, which is the one-launch schedule where it applies)")
     ap.add_argument("--workload", default="decode_p1000",
                     choices=["decode_p1000", "decode_p128", "batched", "stacked_long",
-                             "chunked_prefill", "layer_decode_p1000"],
+                             "chunked_prefill", "layer_decode_p1000", "vocab_b1"],
                     help="decode_p1000 (headline), batched (B=64, P=8192) or "
                          "stacked_long (32 blocks, B=8, P=131071)")
     args = ap.parse_args()
@@ -460,6 +460,32 @@ def main():
                          "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes": nb["attn"]}}), flush=True)
+        return
+    if args.workload == "vocab_b1":
+        dev = torch.device("cuda:0")
+        V, B = G.VOCAB, 1
+        w = torch.empty((V, D), dtype=torch.bfloat16, device=dev)
+        synth.fill_randn_bf16_(w, synth.generator(60, dev), 0.02)
+        h = synth.randn_bf16(synth.generator(61), (B, D)).to(dev)
+        g = synth.norm_gain(62).to(dev)
+        L = torch.empty((B, V), dtype=torch.float32, device=dev)
+        steps = args.steps if args.steps != 400 else 50
+        us = _timed_steps(lambda i: G.vocab_logits(h, w, g, logits=L), steps,
+                          min(args.warmup, 5), True)
+        nb = V * D * 2 + B * D * 2 + D * 2 + B * V * 4
+        gbs = nb / (us * 1e-6) / 1e9
+        print(json.dumps({
+            "metric": METRIC, "value": round(us, 3), "unit": "us/call", "n_gpus": 1,
+            "steps": steps, "warmup": min(args.warmup, 5), "ms_per_step": round(us / 1000, 5),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "Llama-3.1 vocabulary projection with final RMSNorm, "
+                                   "B=1, 4096 x 128256 bf16 weights", "B": B, "V": V,
+                       "hip_graph": True},
+            "roofline": {"kernel": "vocab_gemv_kernel<1>", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": nb}}), flush=True)
         return
     if args.workload == "layer_decode_p1000":
         steps = args.steps if args.steps != 400 else 200

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "rope.hip", "decode.hip", "prefill.hip", "norm.hip"]
+SOURCES = ["api.hip", "rope.hip", "decode.hip", "prefill.hip", "norm.hip", "vocab.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -263,6 +263,23 @@ int gqa_block_prefill(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
                       probe, stream, nullptr);
 }
 
+int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps, const gqa_bf16* w_out,
+                     int V, int B, float* logits, hipStream_t stream) {
+  if (!h || !w_out || !logits) return GQA_ERR_NULL;
+  if (B < 1 || B > GQA_MAX_BATCH || V < 1 || V > GQA_MAX_VOCAB) return GQA_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_out) || !aligned16(logits) || (norm_w && !aligned16(norm_w)))
+    return GQA_ERR_ALIGN;
+  if (norm_w && !(eps > 0.f && eps < 1.f)) return GQA_ERR_ARG;
+  const Range outs[] = {span(logits, (size_t)B * V * 4)};
+  const Range ins[] = {span(h, (size_t)B * D * 2), span(w_out, (size_t)V * D * 2),
+                       span(norm_w, norm_w ? (size_t)D * 2 : 0)};
+  if (any_alias(outs, 1, ins, 3)) return GQA_ERR_ALIAS;
+  VocabParams p;
+  p.z = h; p.norm_w = norm_w; p.norm_eps = eps; p.w = w_out; p.logits = logits; p.V = V; p.B = B;
+  (void)hipGetLastError();
+  return hip_status(launch_vocab_gemv(p, stream));
+}
+
 size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max) {
   const size_t n = gqa_workspace_bytes_from(B, start_pos, T, T_max);
   if (n == 0) return 0;

@@ -121,6 +121,21 @@ hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Vocabulary projection
+// ---------------------------------------------------------------------------
+
+struct VocabParams {
+  const uint16_t* z;        // [B][4096] bf16 (normalised here when norm_w is set)
+  const uint16_t* norm_w;   // optional [4096] bf16 gain of the final norm
+  float norm_eps;
+  const uint16_t* w;        // [V][4096] bf16, [out, in]
+  float* logits;            // [B][V] fp32 (bf16-rounded values)
+  int V, B;
+};
+
+hipError_t launch_vocab_gemv(const VocabParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Pre-norm of a layer
 // ---------------------------------------------------------------------------
 

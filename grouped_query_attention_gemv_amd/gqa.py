@@ -54,6 +54,7 @@ _SIGS = {
     "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
                               ctypes.c_size_t, _P, _P]),
     "gqa_layer_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "gqa_vocab_logits": (_I, [_P, _P, ctypes.c_float, _P, _I, _I, _P, _P]),
     "gqa_layer_prefill_from": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                     _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
     "gqa_layer_decode": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I,
@@ -336,6 +337,28 @@ def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, pr
 
 
 NORM_EPS = 1e-5   # norm_eps of the Llama 3.1 8B catalogue entry
+VOCAB = 128256    # vocabulary size of Llama 3
+
+
+def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None) -> torch.Tensor:
+    """Logits [B, V] fp32 (bf16-rounded values) = z W_out^T for h [B, 4096]
+    bf16, z = RMSNorm(h) * norm_w when norm_w is given, else h."""
+    if h.dim() != 2 or w_out.dim() != 2:
+        raise ValueError("h must be [B, 4096] and w_out [V, 4096]")
+    dev = h.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, V = h.shape[0], w_out.shape[0]
+    _need(h, "h", torch.bfloat16, (B, D_MODEL), dev)
+    _need(w_out, "w_out", torch.bfloat16, (V, D_MODEL), dev)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
+    if logits is None:
+        logits = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, (B, V), dev)
+    _check(lib().gqa_vocab_logits(_ptr(h), _ptr(norm_w), float(eps), _ptr(w_out), int(V), int(B),
+                                  _ptr(logits), _stream(dev)), "gqa_vocab_logits")
+    return logits
 
 
 def layer_workspace(B: int, T: int, T_max: int, device, start_pos: int = 0) -> torch.Tensor:

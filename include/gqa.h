@@ -68,6 +68,7 @@ extern "C" {
 #define GQA_ROPE_PAIRS  64
 #define GQA_V_BLOCK     32              /* positions per value-cache block */
 #define GQA_MAX_BATCH   1024
+#define GQA_MAX_VOCAB  (1 << 20)   /* rows of the vocabulary projection */
 #define GQA_MAX_T_MAX   (1 << 20)
 
 /* Leading bytes of every workspace that hold the decode synchronisation words. */
@@ -236,6 +237,27 @@ int gqa_block_prefill_from(const gqa_bf16* x,
  * Errors: those of the block calls; GQA_ERR_ARG for eps; GQA_ERR_ALIAS when h
  * overlaps x, norm_w or ws.
  */
+/*
+ * gqa_vocab_logits -- the vocabulary projection of the page "Llama 3.1 8B .
+ * Vocabulary projection": L = z W_out for one position of each of B
+ * sequences, the weight stored [out, in] = [V][4096], no bias.  The page
+ * casts the projection's output to float32 before returning it, so each
+ * logit is the bf16 rounding (nearest even) of its fp32-accumulated dot
+ * product, returned as fp32.  With norm_w non-NULL, z is the final norm of
+ * the page's code (self.norm, an RMSNorm with norm_eps) applied to h, read as
+ * in the layer pre-norm above; with NULL, z = h.
+ *   h       [B][4096] bf16
+ *   norm_w  NULL or [4096] bf16; eps as for the layers (ignored when NULL)
+ *   w_out   [V][4096] bf16; V = 128256 for Llama 3.1 (1 .. GQA_MAX_VOCAB)
+ *   logits  [B][V] fp32, written
+ * One weight pass per 8 sequences.  No workspace.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_ALIGN, GQA_ERR_ARG (eps),
+ * GQA_ERR_ALIAS (logits overlapping an input), GQA_ERR_HIP.
+ */
+int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps,
+                     const gqa_bf16* w_out, int V, int B, float* logits,
+                     hipStream_t stream);
+
 size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max);
 
 int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,

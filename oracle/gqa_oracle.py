@@ -340,3 +340,19 @@ def gqa_layer(x, norm_w, eps: float, wq, wk, wv, wo, k_cached, v_cached, start_p
     xn = f64_from_bf16_bits(bf16_bits_from_f64(rms_norm(x, norm_w, eps)))
     res = gqa_block(xn, wq, wk, wv, wo, k_cached, v_cached, start_pos, theta, scaled)
     return x + res.delta, res
+
+
+def vocab_logits(h, w_out, norm_w=None, eps: float = 1e-5) -> np.ndarray:
+    """Page "Llama 3.1 8B . Vocabulary projection": L = z W_out with the
+    weight stored [out, in] (F.linear, no bias), z the final norm of h (the
+    page's code applies self.norm first; read as ``rms_norm`` with its output
+    rounded to bf16) or h itself when no gain is given.  The projection's
+    output is in the model's bf16 and is cast to float32 on return, so each
+    logit is the bf16 rounding of the exact dot product.
+
+    h: [B, d] bf16 values; w_out: [V, d] bf16 values.  Returns [B, V] fp64
+    holding bf16 values.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    z = h if norm_w is None else f64_from_bf16_bits(bf16_bits_from_f64(rms_norm(h, norm_w, eps)))
+    return f64_from_bf16_bits(bf16_bits_from_f64(z @ np.asarray(w_out, dtype=np.float64).T))

@@ -182,6 +182,24 @@ def test_layer_decode_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_layer_decode(*_layer_decode_args(**kw)) == code
 
 
+def _vocab_args(**kw):
+    a = dict(h=_fake(0), g=None, eps=ctypes.c_float(1e-5), w=_fake(1), V=128256, B=1,
+             logits=_fake(2), stream=None)
+    a.update(kw)
+    return [a[k] for k in ("h", "g", "eps", "w", "V", "B", "logits", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), ENULL), (dict(w=None), ENULL), (dict(logits=None), ENULL),
+    (dict(B=0), ESHAPE), (dict(V=0), ESHAPE), (dict(V=(1 << 20) + 1), ESHAPE),
+    (dict(logits=ctypes.c_void_p(BASE + (2 << 32) + 4)), EALIGN),
+    (dict(g=_fake(3), eps=ctypes.c_float(-1.0)), EARG),
+    (dict(logits=_fake(1)), EALIAS), (dict(logits=_fake(0)), EALIAS),
+])
+def test_vocab_logits_rejects_bad_arguments(kw, code):
+    assert G.lib().gqa_vocab_logits(*_vocab_args(**kw)) == code
+
+
 def test_profiled_variants_need_events():
     l = G.lib()
     assert l.gqa_block_decode_profiled(*_decode_args(), None) == ENULL

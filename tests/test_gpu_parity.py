@@ -398,6 +398,54 @@ def test_layer_prefill(B, start_pos, T):
 
 
 # ----------------------------------------------------------------------------
+# Vocabulary projection
+# ----------------------------------------------------------------------------
+
+def _check_logits(got, ref, name):
+    """Logits are bf16 values: within the tolerance of the oracle and rarely
+    a different rounding of it."""
+    g = f64(got)
+    assert np.array_equal(O.f64_from_bf16_bits(O.bf16_bits_from_f64(g)), g), f"{name}: not bf16 values"
+    errs = {"logits": assert_close(name, g, ref)}
+    flips = float(np.mean(O.bf16_bits_from_f64(g) != O.bf16_bits_from_f64(ref)))
+    assert flips <= 1e-3, f"{name}: {flips:.2e} of the logits round differently from the oracle"
+    errs["flips"] = flips
+    return errs
+
+
+@pytest.mark.parametrize("B,V,norm", [(3, 1001, True), (11, 4096, False), (8, 130, True)])
+def test_vocab_logits_small(B, V, norm):
+    from grouped_query_attention_gemv_amd import synth
+    gen = synth.generator(40 + B)
+    h = synth.randn_bf16(gen, (B, G.D_MODEL))
+    w = synth.randn_bf16(gen, (V, G.D_MODEL), 0.02)
+    g = synth.norm_gain(41) if norm else None
+    L = G.vocab_logits(h.to(DEV), w.to(DEV), g.to(DEV) if norm else None)
+    torch.cuda.synchronize()
+    ref = O.vocab_logits(f64(h), f64(w), f64(g) if norm else None, G.NORM_EPS)
+    print(f"vocab B={B} V={V} norm={norm}", _check_logits(L, ref, "logits"))
+
+
+def test_vocab_logits_llama31_size():
+    """V = 128,256 (the Llama 3 vocabulary), B = 2, final norm on: weights drawn
+    on the device, 4,096 sampled rows checked against the oracle."""
+    from grouped_query_attention_gemv_amd import synth
+    B, V = 2, G.VOCAB
+    gen = synth.generator(50)
+    h = synth.randn_bf16(gen, (B, G.D_MODEL))
+    g = synth.norm_gain(51)
+    w = torch.empty((V, G.D_MODEL), dtype=torch.bfloat16, device=DEV)
+    synth.fill_randn_bf16_(w, synth.generator(52, DEV), 0.02)
+    L = G.vocab_logits(h.to(DEV), w, g.to(DEV))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(53).choice(V, 4096, replace=False))
+    rows[-1] = V - 1
+    ref = O.vocab_logits(f64(h), f64(w[torch.from_numpy(rows).to(DEV)]), f64(g), G.NORM_EPS)
+    print("vocab B=2 V=128256", _check_logits(L[:, torch.from_numpy(rows).to(DEV)], ref, "logits"))
+    assert bool(torch.isfinite(L).all())
+
+
+# ----------------------------------------------------------------------------
 # Decode after prefill
 # ----------------------------------------------------------------------------
 

@@ -417,3 +417,22 @@ def test_layer_with_zero_gain_is_the_identity():
     h, res = O.gqa_layer(x, np.zeros(d), 1e-5, *w, None, None, 0)
     assert np.array_equal(h, x)
     assert not np.any(res.delta)
+
+
+def test_vocab_logits_one_hot_and_library():
+    """A one-hot h picks a weight column exactly (W holds bf16 values); a
+    general h matches F.linear in fp64 rounded to bf16."""
+    rng = np.random.default_rng(31)
+    V, d = 257, 4096
+    w = _bf16_vals(rng, (V, d), 0.02)
+    h = np.zeros((2, d))
+    h[0, 5] = 1.0
+    h[1, 4095] = -1.0
+    L = O.vocab_logits(h, w)
+    assert np.array_equal(L[0], w[:, 5]) and np.array_equal(L[1], -w[:, 4095])
+    h = _bf16_vals(rng, (3, d), 1.0)
+    want = F.linear(torch.from_numpy(h), torch.from_numpy(w)).numpy()
+    assert np.array_equal(O.vocab_logits(h, w), O.f64_from_bf16_bits(O.bf16_bits_from_f64(want)))
+    g = _bf16_vals(rng, (d,), 1.0)
+    z = O.f64_from_bf16_bits(O.bf16_bits_from_f64(O.rms_norm(h, g, 1e-5)))
+    assert np.array_equal(O.vocab_logits(h, w, g, 1e-5), O.vocab_logits(z, w))
