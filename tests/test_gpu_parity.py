@@ -258,6 +258,17 @@ def test_prefill_b4_t2048():
     print("prefill B=4 T=2048 errors", errs)
 
 
+def test_prefill_unscaled_rope():
+    """Llama 3 setting (use_scaled_rope False): prefill and a chunk after it."""
+    c = PrefillCase(1, 300, 640, dev=DEV, scaled=False)
+    c.run()
+    c.check(c.oracle())
+    c = PrefillCase(1, 200, 640, dev=DEV, scaled=False, start_pos=300)
+    c.run()
+    c.check(c.oracle())
+    c.check_untouched()
+
+
 def test_prefill_is_deterministic():
     c = PrefillCase(2, 200, 256, dev=DEV)
     a = c.run().clone()
