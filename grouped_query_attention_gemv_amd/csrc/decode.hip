@@ -524,6 +524,11 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = (blk * 4 + wave) * 2;
   u32x4 wa[8], wb[8];
+  if (FUSED) {
+    // hold the weight stream back while QKV finishes (kWoHoldTicks)
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < kWoHoldTicks) __builtin_amdgcn_s_sleep(8);
+  }
   load_rows2(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, lane, wa, wb);
   if (FUSED) {
     // wave 0 waits until every (b, g) has published O, one word per lane

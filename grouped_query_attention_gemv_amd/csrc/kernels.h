@@ -35,6 +35,13 @@ constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused s
 constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
 constexpr int kFusedWoWG = 512;      // 8 wo rows each
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
+// The fused schedule's wo workgroups start streaming their weights this many
+// real-time ticks (100 MHz: 5 us) after they start.  They are dispatched as
+// the QKV workgroups retire and do not need the weights until O is complete;
+// starting at once, their 32 MiB competed with the tail of the QKV stream
+// that the attention chain waits on.  Measured at B = 1: P = 128, 1000, 2000
+// take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
+constexpr unsigned kWoHoldTicks = 500;
 static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
 static_assert(kSyncProj + 32 * (6144 / 128) <= kSyncBytes / 4, "sync region too small");
 
