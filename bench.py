@@ -41,17 +41,18 @@ N_SETS = 8
 D, NQKV, KVH, HD = 4096, 6144, 8, 128
 
 
-def decode_bytes(B: int, P: int) -> dict:
-    """Algorithmic HBM bytes of one decode block-step and of each kernel."""
-    w_qkv = NQKV * D * 2
+def decode_bytes(B: int, P: int, kvh: int = KVH) -> dict:
+    """Algorithmic HBM bytes of one decode block-step and of each kernel
+    (kvh key/value heads; 8 for Llama 3.1 8B)."""
+    w_qkv = (D + 2 * kvh * HD) * D * 2
     w_o = D * D * 2
-    kv_read = B * (P + 1) * KVH * HD * 2 * 2      # rows 0..P of K and V (row P just written)
-    kv_write = B * KVH * HD * 2 * 2
+    kv_read = B * (P + 1) * kvh * HD * 2 * 2      # rows 0..P of K and V (row P just written)
+    kv_write = B * kvh * HD * 2 * 2
     qkv = w_qkv + B * D * 2 + kv_write + B * D * 4 + 64 * 8      # x in, Q fp32 out, rope row
     attn = kv_read + B * D * 4 + B * D * 2 * 2                     # K/V, Q in, O hi/lo out
     wo = w_o + B * D * 2 * 2 + B * D * 4                           # Wo, O hi/lo in, out fp32
     # whole step as the pages count it: weights + cache read + cache write + x + out + rope
-    step = w_qkv + w_o + B * P * KVH * HD * 2 * 2 + kv_write + B * D * 2 + B * D * 4 + 64 * 8
+    step = w_qkv + w_o + B * P * kvh * HD * 2 * 2 + kv_write + B * D * 2 + B * D * 4 + 64 * 8
     return {"qkv": qkv, "attn": attn, "wo": wo, "step": step}
 
 
@@ -86,21 +87,22 @@ def counter_traffic(summary: str, kernel: str, source: str):
 
 
 def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use_graph=True,
-                 schedule=None):
+                 schedule=None, kvh=KVH):
     """Eager, graph-replay and per-kernel timings of decode steps under the
     given decode schedule (the library's choice when None)."""
     if schedule is not None:
         prev = G.set_decode_schedule(schedule)
         try:
-            return bench_decode(G, synth, steps, warmup, B, P, T_max, use_graph, None)
+            return bench_decode(G, synth, steps, warmup, B, P, T_max, use_graph, None, kvh)
         finally:
             G.set_decode_schedule(prev)
     dev = torch.device("cuda:0")
-    fused = G.decode_schedule(B, P, T_max) == G.DECODE_FUSED
+    # the one-launch schedule exists for 8 key/value heads only
+    fused = kvh == KVH and G.decode_schedule(B, P, T_max) == G.DECODE_FUSED
     sets = []
     for s in range(N_SETS):
-        x, w, kc_rows, vc_rows = synth.decode_workload(s, B, P)
-        kc, vc = G.empty_caches(B, T_max, dev)
+        x, w, kc_rows, vc_rows = synth.decode_workload(s, B, P, n_kv_heads=kvh)
+        kc, vc = G.empty_caches(B, T_max, dev, kvh)
         kc.zero_()
         vc.zero_()
         G.kcache_by_position(kc)[:, :P] = kc_rows.to(dev)
@@ -417,7 +419,8 @@ def main():
                          "choice, which is the one-launch schedule where it applies)")
     ap.add_argument("--workload", default="decode_p1000",
                     choices=["decode_p1000", "decode_p128", "batched", "stacked_long",
-                             "chunked_prefill", "layer_decode_p1000", "vocab_b1"],
+                             "chunked_prefill", "layer_decode_p1000", "vocab_b1",
+                             "mha_decode_p1000", "kv16_decode_p1000"],
                     help="decode_p1000 (headline), batched (B=64, P=8192) or "
                          "stacked_long (32 blocks, B=8, P=131071)")
     args = ap.parse_args()
@@ -537,6 +540,37 @@ def main():
             "ms_per_32_block_step": round(us / 1000, 4), "hbm_tbs": round(tbs, 4),
             "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4),
             "tokens_per_s": 8 / (us * 1e-6), "outputs_finite": finite}), flush=True)
+        return
+
+    if args.workload in ("mha_decode_p1000", "kv16_decode_p1000"):
+        kvh = 32 if args.workload.startswith("mha") else 16
+        B, P, T_max = 1, 1000, 1024
+        dec = bench_decode(G, synth, args.steps, args.warmup, B, P, T_max,
+                           use_graph=not args.no_graph, kvh=kvh)
+        us = dec["graph_us_step"] if dec["graph_us_step"] is not None else dec["us_step"]
+        nb = decode_bytes(B, P, kvh)
+        step_tbs = nb["step"] / (us * 1e-6) / 1e12
+        qkv_gbs = nb["qkv"] / (dec["kern_us"]["qkv"] * 1e-6) / 1e9
+        kind = "multi-head (n_kv = 32)" if kvh == 32 else "GQA with n_kv = 16"
+        print(json.dumps({
+            "metric": METRIC, "value": round(us, 3), "unit": "us/block-step", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": us / 1000.0,
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded bf16 N(0,1) x and cache, N(0,0.02) weights; 8 sets)",
+            "config": {"workload": f"Llama-3.1-8B-shaped attention block decode, {kind}, "
+                                   f"B=1, P={P}",
+                       "B": B, "P": P, "T_max": T_max, "kv_heads": kvh,
+                       "hip_graph": dec["graph_us_step"] is not None,
+                       "schedule": dec["schedule"]},
+            "hbm_tbs": round(step_tbs, 4),
+            "hbm_frac_of_peak": round(step_tbs * 1000.0 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": nb["step"],
+            "eager_us_step": round(dec["us_step"], 3),
+            "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
+            "roofline": {"kernel": f"decode_qkv_kernel<1, {kvh}> (QKV GEMV + RoPE + append)",
+                         "bound": "hbm", "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(qkv_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "algorithmic_bytes": nb["qkv"]}}), flush=True)
         return
 
     B, P, T_max = (1, 128, 256) if args.workload == "decode_p128" else (1, 1000, 1024)

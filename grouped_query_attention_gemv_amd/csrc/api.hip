@@ -18,10 +18,10 @@ std::atomic<int> g_decode_schedule{GQA_DECODE_AUTO};
 
 // Schedule a decode call of this shape runs with under the current setting;
 // -1 when the setting demands the fused schedule and the shape does not admit it.
-int pick_schedule(int B, int start_pos) {
+int pick_schedule(int B, int start_pos, int kv = KVH) {
   int nsplit = 0, chunk = 0;
-  decode_split(B, start_pos + 1, &nsplit, &chunk);
-  const bool ok = decode_fused_eligible(B, nsplit);
+  decode_split(B, start_pos + 1, kv, &nsplit, &chunk);
+  const bool ok = kv == KVH && decode_fused_eligible(B, nsplit);
   switch (g_decode_schedule.load()) {
     case GQA_DECODE_SPLIT: return GQA_DECODE_SPLIT;
     case GQA_DECODE_FUSED: return ok ? GQA_DECODE_FUSED : -1;
@@ -68,7 +68,7 @@ int check_common(const void* x, const void* wq, const void* wk, const void* wv, 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
-size_t cache_bytes(int B, int T_max) { return (size_t)B * KVH * T_max * HD * 2; }
+size_t cache_bytes(int B, int T_max, int kv = KVH) { return (size_t)B * kv * T_max * HD * 2; }
 
 // Record events[i] when events is non-NULL.
 inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
@@ -123,19 +123,23 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
                 const float* rope, int start_pos, int B, float* out, gqa_bf16* out_bf16,
                 int accumulate, void* ws, size_t ws_bytes, float* probe, hipStream_t stream,
                 hipEvent_t* events, bool dry = false, const gqa_bf16* norm_w = nullptr,
-                float norm_eps = 0.f, const gqa_bf16* resid = nullptr) {
+                float norm_eps = 0.f, const gqa_bf16* resid = nullptr, int kv = KVH) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
+  if (kv != KVH && kv != 16 && kv != 32) return GQA_ERR_ARG;
+  if (kv != KVH && B > kGemvMaxB) return GQA_ERR_SHAPE;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
   if ((probe && !aligned16(probe)) || (out_bf16 && !aligned16(out_bf16))) return GQA_ERR_ALIGN;
   if (accumulate != 0 && accumulate != 1) return GQA_ERR_ARG;
   if (ws_bytes < gqa_workspace_bytes(B, 1, T_max)) return GQA_ERR_WORKSPACE;
   const size_t Bz = (size_t)B;
+  const size_t nqkv = (size_t)D + 2 * kv * HD;
   const Range outs[] = {span(out, Bz * D * 4), span(out_bf16, out_bf16 ? Bz * D * 2 : 0),
-                        span(kcache, cache_bytes(B, T_max)), span(vcache, cache_bytes(B, T_max)),
-                        span(ws, ws_bytes), span(probe, probe ? Bz * NQKV * 4 : 0)};
+                        span(kcache, cache_bytes(B, T_max, kv)),
+                        span(vcache, cache_bytes(B, T_max, kv)),
+                        span(ws, ws_bytes), span(probe, probe ? Bz * nqkv * 4 : 0)};
   const Range ins[] = {span(x, Bz * D * 2), span(wq, (size_t)D * D * 2),
-                       span(wk, (size_t)KVH * HD * D * 2), span(wv, (size_t)KVH * HD * D * 2),
+                       span(wk, (size_t)kv * HD * D * 2), span(wv, (size_t)kv * HD * D * 2),
                        span(wo, (size_t)D * D * 2), span(rope, (size_t)T_max * PAIRS * 8)};
   if (any_alias(outs, 6, ins, 6)) return GQA_ERR_ALIAS;
 
@@ -145,11 +149,11 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   p.kcache = kcache; p.vcache = vcache; p.rope = rope;
   p.out = out; p.out_bf16 = out_bf16; p.probe = probe;
   p.T_max = T_max; p.start_pos = start_pos; p.B = B; p.accumulate = accumulate;
-  p.norm_w = norm_w; p.norm_eps = norm_eps; p.resid = resid;
+  p.norm_w = norm_w; p.norm_eps = norm_eps; p.resid = resid; p.kv = kv;
   if ((norm_w || resid) && (B > kGemvMaxB || accumulate)) return GQA_ERR_ARG;
   decode_ws_carve(ws, B, &p);
-  decode_split(B, start_pos + 1, &p.nsplit, &p.chunk);
-  const int sched = pick_schedule(B, start_pos);
+  decode_split(B, start_pos + 1, kv, &p.nsplit, &p.chunk);
+  const int sched = pick_schedule(B, start_pos, kv);
   if (sched < 0) return GQA_ERR_ARG;
   if (dry) return GQA_OK;
 
@@ -353,6 +357,17 @@ int gqa_block_prefill_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_
   if (!events) return GQA_ERR_NULL;
   return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, 0, B, T, out, ws, ws_bytes,
                       probe, stream, events);
+}
+
+int gqa_block_decode_kv(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                        const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                        gqa_bf16* vcache, int n_kv_heads, int T_max, const float* rope,
+                        int start_pos, int B, float* out, gqa_bf16* out_bf16, int accumulate,
+                        void* ws, size_t ws_bytes, float* probe, hipStream_t stream,
+                        hipEvent_t* events) {
+  return decode_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, out, out_bf16,
+                     accumulate, ws, ws_bytes, probe, stream, events, false, nullptr, 0.f, nullptr,
+                     n_kv_heads);
 }
 
 int gqa_block_decode(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,

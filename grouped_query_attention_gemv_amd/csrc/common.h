@@ -17,9 +17,10 @@ constexpr int REP = H / KVH;            // 4 query heads per KV head
 constexpr int PAIRS = GQA_ROPE_PAIRS;   // 64
 constexpr int VB = GQA_V_BLOCK;         // 32 positions per value-cache block
 
-// Element offset of value (b, g, t, d) in the blocked value cache.
-__device__ __forceinline__ size_t vcache_index(int b, int g, int t, int d, int T_max) {
-  return ((size_t)(b * KVH + g) * (T_max / VB) + t / VB) * (HD * VB) + d * VB + (t % VB);
+// Element offset of value (b, g, t, d) in the blocked value cache of kv
+// kv heads (8 for Llama 3.1 8B).
+__device__ __forceinline__ size_t vcache_index(int b, int g, int t, int d, int T_max, int kv = KVH) {
+  return ((size_t)(b * kv + g) * (T_max / VB) + t / VB) * (HD * VB) + d * VB + (t % VB);
 }
 
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale into exp2.

@@ -39,8 +39,11 @@ __device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
   return D + KVH * HD + g * HD + (r - 80) * 8;
 }
 
-template <int NB, bool FUSED>
+// KV: kv heads of the projection (the fused schedule runs KV = 8 only).
+template <int NB, bool FUSED, int KV = KVH>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
+  static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
+  constexpr int kNqkv = D + 2 * KV * HD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int grp;
   const int r0 = qkv_first_feature<FUSED>(blk, &grp) + wave * 2;   // even feature, 0..6142
@@ -48,10 +51,10 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   int rr;
   if (r0 < D) {
     wbase = p.wq; rr = r0;
-  } else if (r0 < D + KVH * HD) {
+  } else if (r0 < D + KV * HD) {
     wbase = p.wk; rr = r0 - D;
   } else {
-    wbase = p.wv; rr = r0 - D - KVH * HD;
+    wbase = p.wv; rr = r0 - D - KV * HD;
   }
   // the weight stream does not depend on x: start it before staging x
   u32x4 wa[8], wb[8];
@@ -60,7 +63,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   stage_rows<NB>(xs, p.x + (size_t)b0 * D);
   if (!FUSED && blk == 0 && b0 == 0) {
     // the attention kernel that follows counts split arrivals from zero
-    for (int i = threadIdx.x; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+    for (int i = threadIdx.x; i < p.B * KV; i += blockDim.x) p.counters[i] = 0;
   }
   __syncthreads();
   if (p.norm_w) norm_rows<NB>(xs, p.norm_w, p.norm_eps);
@@ -79,7 +82,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   if (lane < NB) {
     const int b = b0 + lane;
     const int pos = p.start_pos;
-    const bool is_v = r0 >= D + KVH * HD;
+    const bool is_v = r0 >= D + KV * HD;
     if (!is_v) {
       // rotate the pair (2i, 2i+1) of this head by position * f_i
       const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * PAIRS + ((rr & (HD - 1)) >> 1)];
@@ -89,7 +92,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
       v1 = c;
     }
     if (p.probe) {
-      *reinterpret_cast<float2*>(p.probe + (size_t)b * NQKV + r0) = make_float2(v0, v1);
+      *reinterpret_cast<float2*>(p.probe + (size_t)b * kNqkv + r0) = make_float2(v0, v1);
     }
     if (r0 < D) {
       float* qd = p.q + (size_t)b * D + r0;
@@ -103,10 +106,10 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
       const int g = rr / HD, d = rr % HD;
       const uint32_t pair = pack_bf16x2(v0, v1);
       if (!is_v) {
-        uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+        uint16_t* dst = p.kcache + ((size_t)(b * KV + g) * p.T_max + pos) * HD + d;
         *reinterpret_cast<uint32_t*>(dst) = pair;
       } else {
-        uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
+        uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max, KV);
         dst[0] = (uint16_t)(pair & 0xffffu);
         dst[VB] = (uint16_t)(pair >> 16);
       }
@@ -126,10 +129,10 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   }
 }
 
-template <int NB>
+template <int NB, int KV>
 __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[NB * (D / 2)];
-  qkv_body<NB, false>(p, b0, blockIdx.x, xs);
+  qkv_body<NB, false, KV>(p, b0, blockIdx.x, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,34 +156,44 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // In the fused schedule the workgroup loads its first tiles before Q exists,
 // waits for its kv head's release, then replaces the row of position
 // start_pos (which the same launch writes) with the copy in kv_new.
-constexpr int kAttnLdsWords = kAttnWaves * REP * HD + 2 * kAttnWaves * REP + 1;
+// LDS of the 4-wave merge for n_rep query heads per kv head
+constexpr int attn_lds_words(int rep) { return kAttnWaves * rep * HD + 2 * kAttnWaves * rep + 1; }
+constexpr int kAttnLdsWords = attn_lds_words(REP);
 
 // FUSED: Q, K and V come from the same launch.  The workgroup waits on its kv
 // head's counter, reads Q and the appended row with device-scope loads, and
 // hands O to the wo workgroups of the launch.
-template <bool FUSED>
+// KV kv heads serve NR = 32 / KV query heads each (NR = 4 for Llama 3.1 8B;
+// 2 and 1, the last being multi-head attention, on the three-launch path).
+// The MFMA operand columns are the NR heads' hi parts, then their lo parts.
+template <bool FUSED, int KV = KVH>
 __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float* lds) {
+  constexpr int NR = H / KV;
+  static_assert(NR == 1 || NR == 2 || NR == 4, "the wave merge maps one 64-thread slice per head");
+  static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
+  constexpr int kShlNr = 0x100 + NR;             // DPP row_shl:NR, lane i <- lane i + NR
+  constexpr int kShrNr = 0x110 + NR;             // DPP row_shr:NR, lane i <- lane i - NR
   const int split = blk % p.nsplit;
-  const int g = (blk / p.nsplit) % KVH;
-  const int b = blk / (p.nsplit * KVH);
+  const int g = (blk / p.nsplit) % KV;
+  const int b = blk / (p.nsplit * KV);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
-  const int head = col & 3;
-  const bool valid_col = col < 8;
-  const bool is_lo = (col & 4) != 0;
+  const int head = col % NR;
+  const bool valid_col = col < 2 * NR;
+  const bool is_lo = (col / NR) == 1;
   const int L = p.start_pos + 1;
   const int P = p.start_pos;
   const int j_begin = split * p.chunk;
   const int j_end = min(L, j_begin + p.chunk);
   const int T_max = p.T_max;
 
-  float (*sm_o)[REP][HD] = reinterpret_cast<float (*)[REP][HD]>(lds);
-  float (*sm_m)[REP] = reinterpret_cast<float (*)[REP]>(lds + kAttnWaves * REP * HD);
-  float (*sm_l)[REP] = reinterpret_cast<float (*)[REP]>(lds + kAttnWaves * REP * HD + kAttnWaves * REP);
-  int* sm_last = reinterpret_cast<int*>(lds + kAttnWaves * REP * HD + 2 * kAttnWaves * REP);
+  float (*sm_o)[NR][HD] = reinterpret_cast<float (*)[NR][HD]>(lds);
+  float (*sm_m)[NR] = reinterpret_cast<float (*)[NR]>(lds + kAttnWaves * NR * HD);
+  float (*sm_l)[NR] = reinterpret_cast<float (*)[NR]>(lds + kAttnWaves * NR * HD + kAttnWaves * NR);
+  int* sm_last = reinterpret_cast<int*>(lds + kAttnWaves * NR * HD + 2 * kAttnWaves * NR);
 
-  const uint16_t* kbase = p.kcache + (size_t)(b * KVH + g) * T_max * HD;
-  const uint16_t* vbase = p.vcache + (size_t)(b * KVH + g) * (T_max / VB) * (HD * VB);
+  const uint16_t* kbase = p.kcache + (size_t)(b * KV + g) * T_max * HD;
+  const uint16_t* vbase = p.vcache + (size_t)(b * KV + g) * (T_max / VB) * (HD * VB);
 
   // Loads of one 32-position tile (tiles start at multiples of 32, so a tile
   // is one value-cache block).  Key rows past the last visible position are
@@ -269,7 +282,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // Q fragments, pre-scaled by log2(e)/sqrt(128)
   u32x4 qf[4];
   {
-    const float* qrow = p.q + (size_t)b * D + (g * REP + head) * HD;
+    const float* qrow = p.q + (size_t)b * D + (g * NR + head) * HD;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int d0 = rg * 8 + 32 * ks;
@@ -336,9 +349,9 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float v = s[mt][i];
-        const float sum = v + dpp<DPP_ROW_SHL4>(v);      // hi + lo, valid in cols 0-3
-        const float bc = dpp<DPP_ROW_SHR4>(sum);          // copy to cols 4-7
-        const float full = (col < 4) ? sum : bc;
+        const float sum = v + dpp<kShlNr>(v);            // hi + lo, valid in cols 0 .. NR-1
+        const float bc = dpp<kShrNr>(sum);               // copy to cols NR .. 2NR-1
+        const float full = (col < NR) ? sum : bc;
         const int j = jv + mt * 4 + i;
         sv[mt * 4 + i] = (j < j_end) ? full : -INFINITY;
         tmax = fmaxf(tmax, sv[mt * 4 + i]);
@@ -391,31 +404,34 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float v = oacc[dt][i];
-      const float o = v + dpp<DPP_ROW_SHL4>(v);
-      if (col < 4) sm_o[w][col][rg * 4 + i + 16 * dt] = o;
+      const float o = v + dpp<kShlNr>(v);
+      if (col < NR) sm_o[w][col][rg * 4 + i + 16 * dt] = o;
     }
   }
-  if (lane < 4) {
+  if (lane < NR) {
     sm_m[w][lane] = m_run;
     sm_l[w][lane] = l_run;
   }
   __syncthreads();
 
-  // merge the 4 waves: thread -> (head, two dims); wave w holds head w
+  // merge the 4 waves: thread -> (head, two dims); wave w takes head w (the
+  // waves past NR only join the barriers)
   const int mh = tid >> 6, d2 = (tid & 63) * 2;
+  const bool merges = mh < NR;
+  const int mhc = merges ? mh : 0;
   float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][mh]);
+  for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][mhc]);
   float lsum = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int ww = 0; ww < kAttnWaves; ++ww) {
-    const float f = __builtin_amdgcn_exp2f(sm_m[ww][mh] - M);
-    lsum += sm_l[ww][mh] * f;
-    o0 += sm_o[ww][mh][d2] * f;
-    o1 += sm_o[ww][mh][d2 + 1] * f;
+    const float f = __builtin_amdgcn_exp2f(sm_m[ww][mhc] - M);
+    lsum += sm_l[ww][mhc] * f;
+    o0 += sm_o[ww][mhc][d2] * f;
+    o1 += sm_o[ww][mhc][d2 + 1] * f;
   }
 
-  const size_t out_off = (size_t)b * D + (g * REP + mh) * HD + d2;
+  const size_t out_off = (size_t)b * D + (g * NR + mhc) * HD + d2;
   // O of (b, g) leaves as bf16 hi/lo parts; in the fused schedule through
   // device-scope stores, after which every wo workgroup is told
   auto emit = [&](float r0, float r1) {
@@ -424,6 +440,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
     uint32_t* ph = reinterpret_cast<uint32_t*>(p.o_hi + out_off);
     uint32_t* pl = reinterpret_cast<uint32_t*>(p.o_lo + out_off);
+    if (!merges) return;
     if (FUSED) {
       st_dev(ph, h0 | (h1 << 16));
       st_dev(pl, lo0 | (lo1 << 16));
@@ -451,16 +468,18 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // stores go through to the coherence point shared by all XCDs, the wait
   // makes sure they have landed, then a relaxed device-scope count.  The
   // last workgroup to arrive merges every partial.
-  const size_t split_stride = (size_t)REP * kPartStride;
-  float* part0 = p.part + ((size_t)(b * KVH + g) * p.nsplit) * split_stride + (size_t)mh * kPartStride;
+  const size_t split_stride = (size_t)NR * kPartStride;
+  float* part0 = p.part + ((size_t)(b * KV + g) * p.nsplit) * split_stride + (size_t)mhc * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
-  int* split_cnt = p.counters + b * KVH + g;
-  if (d2 == 0) {
-    st_dev(mine, M);
-    st_dev(mine + 1, lsum);
+  int* split_cnt = p.counters + b * KV + g;
+  if (merges) {
+    if (d2 == 0) {
+      st_dev(mine, M);
+      st_dev(mine + 1, lsum);
+    }
+    st_dev(mine + 4 + d2, o0);
+    st_dev(mine + 5 + d2, o1);
   }
-  st_dev(mine + 4 + d2, o0);
-  st_dev(mine + 5 + d2, o1);
   wait_vm();
   __syncthreads();
   if (tid == 0) {
@@ -510,9 +529,10 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   emit(g0 / gl, g1 / gl);
 }
 
+template <int KV>
 __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
-  __shared__ float lds[kAttnLdsWords];
-  attn_body<false>(p, blockIdx.x, lds);
+  __shared__ float lds[attn_lds_words(H / KV)];
+  attn_body<false, KV>(p, blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -907,16 +927,16 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 // Host side
 // ---------------------------------------------------------------------------
 
-int decode_max_split(int B) {
-  const int pairs = B * KVH;
+int decode_max_split(int B, int kv) {
+  const int pairs = B * kv;
   const int want = (1024 + pairs - 1) / pairs;
   return max(1, min(kMaxSplit, want));
 }
 
-void decode_split(int B, int L, int* nsplit, int* chunk) {
+void decode_split(int B, int L, int kv, int* nsplit, int* chunk) {
   const int per_wg = kAttnWaves * kAttnTile;
   const int by_len = (L + per_wg - 1) / per_wg;
-  int n = max(1, min(by_len, decode_max_split(B)));
+  int n = max(1, min(by_len, decode_max_split(B, kv)));
   int c = (L + n - 1) / n;
   c = (c + kAttnTile - 1) / kAttnTile * kAttnTile;
   n = (L + c - 1) / c;
@@ -929,7 +949,8 @@ static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Partials: the attention splits' (m, l, o), and for B > 8 also the split-K
 // partials of the projections (the two never live at the same time).
 static size_t decode_part_bytes(int B) {
-  size_t n = (size_t)B * KVH * decode_max_split(B) * REP * kPartStride * 4;
+  // the largest over the kv-head counts is the GQA one (more heads per split)
+  size_t n = (size_t)B * KVH * decode_max_split(B, KVH) * REP * kPartStride * 4;
   if (B > kGemvMaxB) {
     const size_t qkv = (size_t)NQKV * p2_splits<0>() * kP2Cols * 4;
     const size_t wo = (size_t)D * p2_splits<1>() * kP2Cols * 4;
@@ -942,7 +963,7 @@ size_t decode_ws_bytes(int B) {
   size_t n = kSyncBytes;
   n += align256((size_t)B * D * 4);                       // q
   n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
-  n += align256((size_t)B * KVH * 4);                     // counters
+  n += align256((size_t)B * kMaxKv * 4);                  // counters
   n += align256(decode_part_bytes(B));                   // partials
   n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new
   return n;
@@ -959,7 +980,7 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   p->o_lo = reinterpret_cast<uint16_t*>(c);
   c += align256((size_t)B * D * 2);
   p->counters = reinterpret_cast<int*>(c);
-  c += align256((size_t)B * KVH * 4);
+  c += align256((size_t)B * kMaxKv * 4);
   p->part = reinterpret_cast<float*>(c);
   c += align256(decode_part_bytes(B));
   p->kv_new = reinterpret_cast<uint32_t*>(c);
@@ -984,19 +1005,31 @@ hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
                          kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
     return hipGetLastError();
   }
-  const int blocks = NQKV / 2 / 4;    // one wave per row pair, 4 waves per workgroup
+  const int blocks = (D + 2 * p.kv * HD) / 2 / 4;    // one wave per row pair, 4 waves per workgroup
   for (int b0 = 0; b0 < p.B; b0 += kGemvMaxNB) {
     const int nb = min(kGemvMaxNB, p.B - b0);
-#define GQA_LAUNCH_QKV(N) \
-    hipLaunchKernelGGL(decode_qkv_kernel<N>, dim3(blocks), dim3(256), 0, s, p, b0)
+#define GQA_LAUNCH_QKV_KV(N, KV) \
+    hipLaunchKernelGGL((decode_qkv_kernel<N, KV>), dim3(blocks), dim3(256), 0, s, p, b0)
+#define GQA_LAUNCH_QKV(N)                                     \
+    switch (p.kv) {                                           \
+      case 16: GQA_LAUNCH_QKV_KV(N, 16); break;               \
+      case 32: GQA_LAUNCH_QKV_KV(N, 32); break;               \
+      default: GQA_LAUNCH_QKV_KV(N, KVH); break;              \
+    }
     GQA_NB_SWITCH(nb, GQA_LAUNCH_QKV)
 #undef GQA_LAUNCH_QKV
+#undef GQA_LAUNCH_QKV_KV
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(p.nsplit * KVH * p.B), dim3(256), 0, s, p);
+  const dim3 grid(p.nsplit * p.kv * p.B);
+  switch (p.kv) {
+    case 16: hipLaunchKernelGGL(decode_attn_kernel<16>, grid, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL(decode_attn_kernel<32>, grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL(decode_attn_kernel<KVH>, grid, dim3(256), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 

@@ -66,6 +66,8 @@ struct DecodeParams {
   float* part;              // [B][8][nsplit][4][kPartStride]
   uint32_t* kv_new;         // [B][2][8][64] appended K, V rows as packed bf16 pairs
   int* sync;                // the workspace's synchronisation words
+  int kv;                   // kv heads: 8 (Llama 3.1 8B), or 16 / 32 (n_rep 2, 1) on the
+                            // GEMV path (B <= kGemvMaxB) with the three-launch schedule
   int nsplit, chunk;        // positions split over nsplit workgroups of chunk keys
   // layer mode of the GEMV path (B <= kGemvMaxB): the QKV prologue replaces
   // x by RMSNorm(x) * norm_w (rounded to bf16), and the wo epilogue writes
@@ -76,8 +78,9 @@ struct DecodeParams {
 };
 
 // Split of the L = start_pos + 1 visible positions over workgroups.
-void decode_split(int B, int L, int* nsplit, int* chunk);
-int decode_max_split(int B);
+constexpr int kMaxKv = 32;           // most kv heads (n_rep 1)
+void decode_split(int B, int L, int kv, int* nsplit, int* chunk);
+int decode_max_split(int B, int kv);
 size_t decode_ws_bytes(int B);
 void decode_ws_carve(void* ws, int B, DecodeParams* p);
 

@@ -16,6 +16,7 @@ import torch
 D_MODEL = 4096
 N_HEADS = 32
 N_KV_HEADS = 8
+DECODE_KV_HEADS = (8, 16, 32)   # key/value head counts the decode path takes
 HEAD_DIM = 128
 QKV_DIM = 6144
 ROPE_PAIRS = 64
@@ -59,6 +60,8 @@ _SIGS = {
                                     _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
     "gqa_layer_decode": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I,
                               _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "gqa_block_decode_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I,
+                                 _P, ctypes.c_size_t, _P, _P, _P]),
     "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
                                        _P, ctypes.c_size_t, _P, _P, _P]),
 }
@@ -167,24 +170,25 @@ def decode_schedule(B: int, start_pos: int, T_max: int) -> int:
     return r
 
 
-def empty_caches(B: int, T_max: int, device):
-    """(kcache [B, 8, T_max, 128], vcache [B, 8, T_max/32, 128, 32]) bf16,
-    uninitialised; T_max must be a multiple of 32."""
+def empty_caches(B: int, T_max: int, device, n_kv_heads: int = N_KV_HEADS):
+    """(kcache [B, n_kv, T_max, 128], vcache [B, n_kv, T_max/32, 128, 32])
+    bf16, uninitialised; T_max must be a multiple of 32; n_kv defaults to
+    Llama 3.1 8B's 8 key/value heads."""
     if T_max % V_BLOCK:
         raise ValueError(f"T_max must be a multiple of {V_BLOCK}")
-    k = torch.empty((B, N_KV_HEADS, T_max, HEAD_DIM), dtype=torch.bfloat16, device=device)
-    v = torch.empty((B, N_KV_HEADS, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dtype=torch.bfloat16,
+    k = torch.empty((B, n_kv_heads, T_max, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, n_kv_heads, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dtype=torch.bfloat16,
                     device=device)
     return k, v
 
 
 def kcache_by_position(kcache: torch.Tensor) -> torch.Tensor:
-    """View [B, T_max, 8, 128] of the head-major key cache."""
+    """View [B, T_max, n_kv, 128] of the head-major key cache."""
     return kcache.permute(0, 2, 1, 3)
 
 
 def vcache_blocks(vcache: torch.Tensor) -> torch.Tensor:
-    """View [B, T_max/32, 32, 8, 128] of the blocked value cache: block,
+    """View [B, T_max/32, 32, n_kv, 128] of the blocked value cache: block,
     position within the block, kv head, dim."""
     return vcache.permute(0, 2, 4, 1, 3)
 
@@ -200,13 +204,13 @@ def _block_pieces(lo: int, hi: int):
 
 
 def vcache_read(vcache: torch.Tensor, lo: int, hi: int) -> torch.Tensor:
-    """Copy of value rows [lo, hi) as [B, hi - lo, 8, 128]."""
+    """Copy of value rows [lo, hi) as [B, hi - lo, n_kv, 128]."""
     v5 = vcache_blocks(vcache)
     return torch.cat([v5[:, b, r0:r1] for b, r0, r1 in _block_pieces(lo, hi)], dim=1)
 
 
 def vcache_write(vcache: torch.Tensor, lo: int, rows: torch.Tensor) -> None:
-    """Store rows [B, n, 8, 128] at positions lo .. lo + n - 1."""
+    """Store rows [B, n, n_kv, 128] at positions lo .. lo + n - 1."""
     v5 = vcache_blocks(vcache)
     off = 0
     n = rows.shape[1]
@@ -217,7 +221,7 @@ def vcache_write(vcache: torch.Tensor, lo: int, rows: torch.Tensor) -> None:
             if b == first_full:   # all full blocks in one strided copy
                 nb = last_full - first_full
                 v5[:, b:b + nb] = rows[:, off:off + nb * V_BLOCK].reshape(
-                    rows.shape[0], nb, V_BLOCK, N_KV_HEADS, HEAD_DIM)
+                    rows.shape[0], nb, V_BLOCK, rows.shape[2], HEAD_DIM)
                 off += nb * V_BLOCK
             continue
         v5[:, b, r0:r1] = rows[:, off:off + r1 - r0]
@@ -281,20 +285,25 @@ def rope_table(T_max: int, theta: float = 500000.0, scaled: bool = True, device=
     return out
 
 
-def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope):
+def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope, kv_heads=(N_KV_HEADS,)):
+    """Validate the weights, caches and rope table; the number of key/value
+    heads comes from wk's rows and must be one of kv_heads."""
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
+    if wk.dim() != 2 or wk.shape[0] % HEAD_DIM or wk.shape[0] // HEAD_DIM not in kv_heads:
+        raise ValueError(f"wk must be [n_kv*128, 4096] with n_kv in {tuple(kv_heads)}")
+    n_kv = wk.shape[0] // HEAD_DIM
     _need(wq, "wq", torch.bfloat16, (D_MODEL, D_MODEL), dev)
-    _need(wk, "wk", torch.bfloat16, (N_KV_HEADS * HEAD_DIM, D_MODEL), dev)
-    _need(wv, "wv", torch.bfloat16, (N_KV_HEADS * HEAD_DIM, D_MODEL), dev)
+    _need(wk, "wk", torch.bfloat16, (n_kv * HEAD_DIM, D_MODEL), dev)
+    _need(wv, "wv", torch.bfloat16, (n_kv * HEAD_DIM, D_MODEL), dev)
     _need(wo, "wo", torch.bfloat16, (D_MODEL, D_MODEL), dev)
     if kcache.dim() != 4:
-        raise ValueError("kcache must be [B, 8, T_max, 128]")
+        raise ValueError(f"kcache must be [B, {n_kv}, T_max, 128]")
     B, T_max = kcache.shape[0], kcache.shape[2]
-    _need(kcache, "kcache", torch.bfloat16, (B, N_KV_HEADS, T_max, HEAD_DIM), dev)
+    _need(kcache, "kcache", torch.bfloat16, (B, n_kv, T_max, HEAD_DIM), dev)
     _need(vcache, "vcache", torch.bfloat16,
-          (B, N_KV_HEADS, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dev)
+          (B, n_kv, T_max // V_BLOCK, HEAD_DIM, V_BLOCK), dev)
     if rope.dim() != 3 or rope.shape[0] < T_max:
         raise ValueError("rope must be [>= T_max, 64, 2]")
     _need(rope, "rope", torch.float32, (rope.shape[0], ROPE_PAIRS, 2), dev)
@@ -427,10 +436,14 @@ def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=No
                  out_bf16=None, accumulate: bool = False, ws=None, probe=None,
                  events: HipEvents | None = None) -> torch.Tensor:
     """One token per sequence at position start_pos: x [B, 4096] bf16 ->
-    out [B, 4096] fp32 (= Delta, or += Delta with accumulate)."""
+    out [B, 4096] fp32 (= Delta, or += Delta with accumulate).  The number of
+    key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), or 16 / 32
+    (gqa_block_decode_kv, B <= 8)."""
     if x.dim() != 2:
         raise ValueError("x must be [B, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
+                                 kv_heads=DECODE_KV_HEADS)
+    n_kv = wk.shape[0] // HEAD_DIM
     _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
     if out is None:
         if accumulate:
@@ -440,9 +453,16 @@ def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=No
     if out_bf16 is not None:
         _need(out_bf16, "out_bf16", torch.bfloat16, (B, D_MODEL), dev)
     if probe is not None:
-        _need(probe, "probe", torch.float32, (B, QKV_DIM), dev)
+        _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
         ws = workspace(B, 1, T_max, dev)
+    if n_kv != N_KV_HEADS:
+        _check(lib().gqa_block_decode_kv(
+            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
+            int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
+            int(bool(accumulate)), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev),
+            None if events is None else events.events), "gqa_block_decode_kv")
+        return out
     args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
             int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
             int(bool(accumulate)), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)]

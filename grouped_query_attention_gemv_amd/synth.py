@@ -53,12 +53,12 @@ def fill_randn_bf16_(dst: torch.Tensor, gen: torch.Generator, scale: float = 1.0
     return dst
 
 
-def block_weights(gen: torch.Generator, device="cpu"):
+def block_weights(gen: torch.Generator, device="cpu", n_kv_heads: int = N_KV_HEADS):
     """(Wq, Wk, Wv, Wo), [out, in] bf16, N(0, 0.02^2), drawn on ``device``
     (which must be the generator's device)."""
     wq = randn_bf16(gen, (N_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
-    wk = randn_bf16(gen, (N_KV_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
-    wv = randn_bf16(gen, (N_KV_HEADS * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
+    wk = randn_bf16(gen, (n_kv_heads * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
+    wv = randn_bf16(gen, (n_kv_heads * HEAD_DIM, D_MODEL), WEIGHT_STD, device)
     wo = randn_bf16(gen, (D_MODEL, N_HEADS * HEAD_DIM), WEIGHT_STD, device)
     return wq, wk, wv, wo
 
@@ -68,19 +68,20 @@ def sentinel_like(shape, device="cpu") -> torch.Tensor:
     return torch.full(shape, SENTINEL_BITS, dtype=torch.int16, device=device).view(torch.bfloat16)
 
 
-def cache_rows(gen: torch.Generator, B: int, P: int, device="cpu"):
-    """Logical cache rows [B, P, 8, 128] for K then V, bf16 N(0, 1)."""
-    k = randn_bf16(gen, (B, P, N_KV_HEADS, HEAD_DIM), 1.0, device)
-    v = randn_bf16(gen, (B, P, N_KV_HEADS, HEAD_DIM), 1.0, device)
+def cache_rows(gen: torch.Generator, B: int, P: int, device="cpu", n_kv_heads: int = N_KV_HEADS):
+    """Logical cache rows [B, P, n_kv, 128] for K then V, bf16 N(0, 1)."""
+    k = randn_bf16(gen, (B, P, n_kv_heads, HEAD_DIM), 1.0, device)
+    v = randn_bf16(gen, (B, P, n_kv_heads, HEAD_DIM), 1.0, device)
     return k, v
 
 
-def decode_workload(seed: int, B: int, P: int, device="cpu"):
-    """x [B, 4096], weights, and cached rows [B, P, 8, 128] for K and V."""
+def decode_workload(seed: int, B: int, P: int, device="cpu", n_kv_heads: int = N_KV_HEADS):
+    """x [B, 4096], weights, and cached rows [B, P, n_kv, 128] for K and V
+    (n_kv key/value heads, 8 for Llama 3.1 8B)."""
     gen = generator(seed, device)
     x = randn_bf16(gen, (B, D_MODEL), 1.0, device)
-    w = block_weights(gen, device)
-    k, v = cache_rows(gen, B, P, device)
+    w = block_weights(gen, device, n_kv_heads)
+    k, v = cache_rows(gen, B, P, device, n_kv_heads)
     return x, w, k, v
 
 

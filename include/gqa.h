@@ -304,6 +304,35 @@ int gqa_block_decode(const gqa_bf16* x,
                      hipStream_t stream);
 
 /*
+ * gqa_block_decode_kv -- gqa_block_decode for a model with n_kv_heads key /
+ * value heads shared by 32 / n_kv_heads query heads each (the n_rep of the
+ * page "Llama 3.1 8B . Grouped-query attention", evidence "gqa": KV head g
+ * serves query heads g*n_rep .. g*n_rep + n_rep - 1; n_rep = 1 is the
+ * multi-head attention the page sizes beside GQA).  Llama 3.1 8B is
+ * n_kv_heads = 8, where this equals gqa_block_decode.
+ *   n_kv_heads  8, 16 or 32; other than 8 only for B <= 8, and with the
+ *               three-launch schedule (GQA_ERR_ARG if GQA_DECODE_FUSED is
+ *               forced)
+ *   wk, wv      [n_kv_heads*128][4096] bf16
+ *   kcache      [B][n_kv_heads][T_max][128] bf16
+ *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
+ *   probe       NULL or [B][4096 + 2*n_kv_heads*128] fp32
+ *   events      NULL, or GQA_DECODE_STAGES + 1 events recorded as by
+ *               gqa_block_decode_profiled
+ *   other arguments, ownership and workspace as for gqa_block_decode
+ * Errors: as gqa_block_decode; GQA_ERR_ARG for another n_kv_heads,
+ * GQA_ERR_SHAPE for n_kv_heads != 8 with B > 8.
+ */
+int gqa_block_decode_kv(const gqa_bf16* x,
+                        const gqa_bf16* wq, const gqa_bf16* wk,
+                        const gqa_bf16* wv, const gqa_bf16* wo,
+                        gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                        int T_max, const float* rope, int start_pos, int B,
+                        float* out, gqa_bf16* out_bf16, int accumulate,
+                        void* ws, size_t ws_bytes, float* probe,
+                        hipStream_t stream, hipEvent_t* events);
+
+/*
  * Same as gqa_block_prefill / gqa_block_decode, and additionally records
  * events[0] on `stream` before the first kernel and events[i] after stage i
  * (GQA_PREFILL_STAGES / GQA_DECODE_STAGES stages), so that a caller can time

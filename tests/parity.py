@@ -90,12 +90,13 @@ class DecodeCase:
     generator, sentinel NaN everywhere else)."""
 
     def __init__(self, B: int, P: int, T_max: int, seed: int = 0, dev="cuda", theta=5e5,
-                 scaled=True, cache_on_device=False):
+                 scaled=True, cache_on_device=False, n_kv=8):
         self.B, self.P, self.T_max, self.dev = B, P, T_max, torch.device(dev)
-        self.theta, self.scaled = theta, scaled
-        self.kcache, self.vcache = G.empty_caches(B, T_max, self.dev)
+        self.theta, self.scaled, self.n_kv = theta, scaled, n_kv
+        self.kcache, self.vcache = G.empty_caches(B, T_max, self.dev, n_kv)
         if not cache_on_device:
-            self.x, self.w, self.kc_rows, self.vc_rows = synth.decode_workload(seed, B, P)
+            self.x, self.w, self.kc_rows, self.vc_rows = synth.decode_workload(seed, B, P,
+                                                                                n_kv_heads=n_kv)
             self.kcache.copy_(synth.sentinel_like(self.kcache.shape, self.dev))
             self.vcache.copy_(synth.sentinel_like(self.vcache.shape, self.dev))
             G.kcache_by_position(self.kcache)[:, :P] = self.kc_rows.to(self.dev)
@@ -105,13 +106,14 @@ class DecodeCase:
             # drawn on the device straight into the cache buffers
             gen = synth.generator(seed)
             self.x = synth.randn_bf16(gen, (B, synth.D_MODEL))
-            self.w = synth.block_weights(gen)
+            self.w = synth.block_weights(gen, n_kv_heads=n_kv)
             dgen = synth.generator(seed + 1, self.dev)
             synth.fill_randn_bf16_(self.kcache, dgen)
             synth.fill_randn_bf16_(self.vcache, dgen)
             n = T_max - P
-            G.kcache_by_position(self.kcache)[:, P:] = synth.sentinel_like((B, n, 8, 128), self.dev)
-            G.vcache_write(self.vcache, P, synth.sentinel_like((B, n, 8, 128), self.dev))
+            G.kcache_by_position(self.kcache)[:, P:] = synth.sentinel_like((B, n, n_kv, 128),
+                                                                            self.dev)
+            G.vcache_write(self.vcache, P, synth.sentinel_like((B, n, n_kv, 128), self.dev))
             self.kc_rows = self.vc_rows = None
         self.k_before = self.kcache.clone()
         self.v_before = self.vcache.clone()
@@ -120,7 +122,8 @@ class DecodeCase:
         self.xd = self.x.to(self.dev)
 
     def run(self, probe=True):
-        self.probe = torch.empty((self.B, G.QKV_DIM), dtype=torch.float32, device=self.dev) \
+        nqkv = G.D_MODEL + 2 * self.n_kv * G.HEAD_DIM
+        self.probe = torch.empty((self.B, nqkv), dtype=torch.float32, device=self.dev) \
             if probe else None
         self.ws = G.workspace(self.B, 1, self.T_max, self.dev)
         self.out = G.block_decode(self.xd, *self.wd, self.kcache, self.vcache, self.rope,
@@ -138,26 +141,28 @@ class DecodeCase:
         else:   # the generator's values, as staged before the call
             kc = f64(G.kcache_by_position(self.k_before)[seqs, :self.P])
             vc = f64(G.vcache_read(self.v_before[seqs], 0, self.P))
-        return O.gqa_block(x, *w, kc, vc, self.P, self.theta, self.scaled)
+        return O.gqa_block(x, *w, kc, vc, self.P, self.theta, self.scaled,
+                           n_kv_heads=self.n_kv)
 
     def check(self, res, seqs=None):
         """Compare the GPU results of sequences ``seqs`` with oracle result res."""
         seqs = list(range(self.B)) if seqs is None else list(seqs)
         B = len(seqs)
         P = self.P
+        nk = self.n_kv * 128
         errs = {}
         errs["delta"] = assert_close("delta", f64(self.out[seqs]), res.delta[:, 0])
         if self.probe is not None:
             pr = f64(self.probe[seqs])
             errs["q"] = assert_close("Q", pr[:, :4096], res.q.reshape(B, 4096))
-            errs["k"] = assert_close("K", pr[:, 4096:5120], res.k.reshape(B, 1024))
-            errs["v"] = assert_close("V", pr[:, 5120:], res.v.reshape(B, 1024))
+            errs["k"] = assert_close("K", pr[:, 4096:4096 + nk], res.k.reshape(B, nk))
+            errs["v"] = assert_close("V", pr[:, 4096 + nk:], res.v.reshape(B, nk))
         kpos = G.kcache_by_position(self.kcache)
         vrow = G.vcache_read(self.vcache[seqs], P, P + 1)[:, 0]
         kp = vp = None
         if self.probe is not None:
-            kp = pr[:, 4096:5120].reshape(B, 8, 128)
-            vp = pr[:, 5120:].reshape(B, 8, 128)
+            kp = pr[:, 4096:4096 + nk].reshape(B, self.n_kv, 128)
+            vp = pr[:, 4096 + nk:].reshape(B, self.n_kv, 128)
         errs["k_flips"] = assert_bf16_rows("kcache row", bits(kpos[seqs, P]), res.k_bits[:, 0], kp)
         errs["v_flips"] = assert_bf16_rows("vcache row", bits(vrow), res.v_bits[:, 0], vp)
         log_errs(f"decode B={self.B} P={P} seqs={seqs if len(seqs) < self.B else 'all'}", errs)

@@ -82,6 +82,32 @@ def _decode_args(**kw):
                            "stream")]
 
 
+def _decode_kv_args(n_kv, **kw):
+    a = _decode_args(**kw)
+    return a[:7] + [n_kv] + a[7:] + [None]
+
+
+@pytest.mark.parametrize("n_kv,kw,code", [
+    (4, {}, EARG), (24, {}, EARG), (0, {}, EARG), (-8, {}, EARG),
+    (16, dict(B=9), ESHAPE), (32, dict(B=64), ESHAPE),
+    (32, dict(x=None), ENULL), (16, dict(start_pos=1024), ERANGE), (32, dict(ws_bytes=1024), EWS),
+    (32, dict(out=_fake(0)), EALIAS), (16, dict(probe=_fake(8)), EALIAS),
+])
+def test_decode_kv_rejects_bad_arguments(n_kv, kw, code):
+    assert G.lib().gqa_block_decode_kv(*_decode_kv_args(n_kv, **kw)) == code
+
+
+def test_decode_kv_fused_schedule_is_rejected_off_eight_heads():
+    """The one-launch schedule is built for 8 key/value heads; forcing it
+    makes the other head counts fail before any launch."""
+    prev = G.set_decode_schedule(G.DECODE_FUSED)
+    try:
+        assert G.lib().gqa_block_decode_kv(*_decode_kv_args(16)) == EARG
+        assert G.lib().gqa_block_decode_kv(*_decode_kv_args(32)) == EARG
+    finally:
+        G.set_decode_schedule(prev)
+
+
 def _prefill_args(**kw):
     a = dict(x=_fake(0), wq=_fake(1), wk=_fake(2), wv=_fake(3), wo=_fake(4), kc=_fake(5),
              vc=_fake(6), T_max=1024, rope=_fake(7), B=1, T=16, out=_fake(8), ws=_fake(9),

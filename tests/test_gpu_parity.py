@@ -87,6 +87,15 @@ def test_decode_unscaled_rope():
     _decode_full(1, 5000, 5024, scaled=False)
 
 
+@pytest.mark.parametrize("n_kv,B,P", [(32, 1, 1000), (32, 3, 777), (16, 1, 1000), (16, 2, 100),
+                                      (32, 8, 129), (16, 5, 0)])
+def test_decode_other_kv_head_counts(n_kv, B, P):
+    """n_rep = 32 / n_kv query heads per key/value head: 1 is multi-head
+    attention, 2 a wider GQA; the same kernels templated on the head count."""
+    _, errs = _decode_full(B, P, 1024, n_kv=n_kv)
+    assert errs["delta"][0] < 1e-3
+
+
 def test_decode_accumulate_and_bf16_out(schedule):
     """out += Delta with the bf16 copy of the updated residual."""
     c = DecodeCase(2, 100, 128, dev=DEV)
