@@ -56,9 +56,9 @@ def decode_bytes(B: int, P: int, kvh: int = KVH) -> dict:
     return {"qkv": qkv, "attn": attn, "wo": wo, "step": step}
 
 
-def prefill_flops(B: int, T: int, start_pos: int = 0) -> dict:
+def prefill_flops(B: int, T: int, start_pos: int = 0, kvh: int = KVH) -> dict:
     M = B * T
-    qkv = 2.0 * M * NQKV * D
+    qkv = 2.0 * M * (D + 2 * kvh * HD) * D
     causal_pairs = B * (T * start_pos + T * (T + 1) / 2)   # token i sees start_pos + i + 1 keys
     attn = 4.0 * causal_pairs * 32 * HD             # QK^T and PV over visible pairs, 32 heads
     wo = 2.0 * M * D * D
@@ -184,14 +184,14 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
                 profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
 
 
-def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
+def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048, kvh=KVH):
     dev = torch.device("cuda:0")
-    x, w = synth.prefill_workload(0, B, T)
+    x, w = synth.prefill_workload(0, B, T, n_kv_heads=kvh)
     x = x.to(dev)
     w = [t.to(dev) for t in w]
-    kc, vc = G.empty_caches(B, T, dev)
+    kc, vc = G.empty_caches(B, T, dev, kvh)
     rope = G.rope_table(T, device=dev)
-    ws = G.workspace(B, T, T, dev)
+    ws = G.workspace(B, T, T, dev, n_kv_heads=kvh)
     out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     for _ in range(warmup):
         G.block_prefill(x, *w, kc, vc, rope, out=out, ws=ws)
@@ -206,7 +206,7 @@ def bench_prefill(G, synth, steps: int, warmup: int, B=4, T=2048):
         tot.append(ev.elapsed_ms(0, G.PREFILL_STAGES))
     ev.close()
     us = float(np.mean(tot) * 1000.0)
-    fl = prefill_flops(B, T)
+    fl = prefill_flops(B, T, kvh=kvh)
     kern = dict(zip(["wo_fp16", "qkv", "attn", "wo"], (per.mean(axis=0) * 1000.0).tolist()))
     return dict(B=B, T=T, us_step=us, tokens_per_s=B * T / (us * 1e-6),
                 mfma_util=fl["total"] / (us * 1e-6) / (MFMA_PEAK_TFLOPS * 1e12),
@@ -459,7 +459,7 @@ def main():
                        "B": 64, "P": 8192, "T_max": 8224, "hip_graph": True},
             "hbm_tbs": round(tbs, 4), "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4),
             "tokens_per_s": 64 / (us * 1e-6), "kernels_us": {k: round(v, 3) for k, v in kern.items()},
-            "roofline": {"kernel": "decode_attn_kernel", "bound": "hbm",
+            "roofline": {"kernel": "decode_attn_kernel<8>", "bound": "hbm",
                          "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes": nb["attn"]}}), flush=True)
@@ -570,7 +570,9 @@ def main():
             "roofline": {"kernel": f"decode_qkv_kernel<1, {kvh}> (QKV GEMV + RoPE + append)",
                          "bound": "hbm", "achieved": round(qkv_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(qkv_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "algorithmic_bytes": nb["qkv"]}}), flush=True)
+                         "traffic": None, "algorithmic_bytes": nb["qkv"]},
+            "prefill": None if args.no_prefill else bench_prefill(G, synth, steps=10, warmup=3,
+                                                                  kvh=kvh)}), flush=True)
         return
 
     B, P, T_max = (1, 128, 256) if args.workload == "decode_p128" else (1, 1000, 1024)
@@ -595,8 +597,8 @@ def main():
     else:
         dom_us = dec["kern_us"]["qkv"]
         dom_bytes = nb["qkv"]
-        roof_kernel = "decode_qkv_kernel<1> (QKV GEMV + RoPE + cache append)"
-        traffic = counter_traffic("decode_p1000_hbm_traffic.md", "decode_qkv_kernel<1>", src)
+        roof_kernel = "decode_qkv_kernel<1, 8> (QKV GEMV + RoPE + cache append)"
+        traffic = counter_traffic("decode_p1000_hbm_traffic.md", "decode_qkv_kernel<1, 8>", src)
     dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     other = None
     if dec["schedule"] == "fused":
