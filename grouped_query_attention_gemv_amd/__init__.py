@@ -9,5 +9,5 @@ from .gqa import (  # noqa: F401
     rope_table, status_string, vcache_blocks, vcache_read, vcache_write, workspace,
     workspace_bytes, V_BLOCK, SYNC_BYTES, DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED,
     decode_schedule, set_decode_schedule, workspace_errors,
-    NORM_EPS, layer_decode, layer_prefill, layer_workspace, VOCAB, vocab_logits, DECODE_KV_HEADS,
+    NORM_EPS, layer_decode, layer_prefill, layer_workspace, VOCAB, vocab_logits, KV_HEAD_COUNTS,
 )

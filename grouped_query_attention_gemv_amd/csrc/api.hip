@@ -70,6 +70,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
 size_t cache_bytes(int B, int T_max, int kv = KVH) { return (size_t)B * kv * T_max * HD * 2; }
 
+// key/value head counts the kernels are instantiated for
+bool kv_supported(int kv) { return kv == KVH || kv == 16 || kv == 32; }
+
 // Record events[i] when events is non-NULL.
 inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
   return events ? hipEventRecord(events[i], s) : hipSuccess;
@@ -79,19 +82,21 @@ int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, cons
                  const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
                  const float* rope, int start_pos, int B, int T, float* out, void* ws,
                  size_t ws_bytes, float* probe, hipStream_t stream, hipEvent_t* events,
-                 int accumulate = 0, bool dry = false) {
+                 int accumulate = 0, bool dry = false, int kv = KVH) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
+  if (!kv_supported(kv)) return GQA_ERR_ARG;
   if (T < 1 || (long)B * T > (1L << 24)) return GQA_ERR_SHAPE;
   if (start_pos < 0 || (long)start_pos + T > T_max) return GQA_ERR_RANGE;
   if (probe && !aligned16(probe)) return GQA_ERR_ALIGN;
-  if (ws_bytes < gqa_workspace_bytes_from(B, start_pos, T, T_max)) return GQA_ERR_WORKSPACE;
+  if (ws_bytes < gqa_workspace_bytes_kv(B, start_pos, T, T_max, kv)) return GQA_ERR_WORKSPACE;
   const size_t M = (size_t)B * T;
-  const Range outs[] = {span(out, M * D * 4), span(kcache, cache_bytes(B, T_max)),
-                        span(vcache, cache_bytes(B, T_max)), span(ws, ws_bytes),
-                        span(probe, probe ? M * NQKV * 4 : 0)};
+  const size_t nqkv = (size_t)D + 2 * kv * HD;
+  const Range outs[] = {span(out, M * D * 4), span(kcache, cache_bytes(B, T_max, kv)),
+                        span(vcache, cache_bytes(B, T_max, kv)), span(ws, ws_bytes),
+                        span(probe, probe ? M * nqkv * 4 : 0)};
   const Range ins[] = {span(x, M * D * 2), span(wq, (size_t)D * D * 2),
-                       span(wk, (size_t)KVH * HD * D * 2), span(wv, (size_t)KVH * HD * D * 2),
+                       span(wk, (size_t)kv * HD * D * 2), span(wv, (size_t)kv * HD * D * 2),
                        span(wo, (size_t)D * D * 2), span(rope, (size_t)T_max * PAIRS * 8)};
   if (any_alias(outs, 5, ins, 6)) return GQA_ERR_ALIAS;
 
@@ -100,6 +105,7 @@ int prefill_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, cons
   p.x = x; p.wq = wq; p.wk = wk; p.wv = wv; p.wo = wo;
   p.kcache = kcache; p.vcache = vcache; p.rope = rope; p.out = out; p.probe = probe;
   p.T_max = T_max; p.B = B; p.T = T; p.start_pos = start_pos; p.accumulate = accumulate;
+  p.kv = kv;
   p.Tp = (start_pos + T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
   prefill_ws_carve(ws, &p);
   if (dry) return GQA_OK;
@@ -126,7 +132,7 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
                 float norm_eps = 0.f, const gqa_bf16* resid = nullptr, int kv = KVH) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
-  if (kv != KVH && kv != 16 && kv != 32) return GQA_ERR_ARG;
+  if (!kv_supported(kv)) return GQA_ERR_ARG;
   if (kv != KVH && B > kGemvMaxB) return GQA_ERR_SHAPE;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
   if ((probe && !aligned16(probe)) || (out_bf16 && !aligned16(out_bf16))) return GQA_ERR_ALIGN;
@@ -243,12 +249,17 @@ int gqa_decode_schedule(int B, int start_pos, int T_max) {
   return sched < 0 ? GQA_ERR_ARG : sched;
 }
 
-size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max) {
+size_t gqa_workspace_bytes_kv(int B, int start_pos, int T, int T_max, int n_kv_heads) {
   if (B < 1 || B > GQA_MAX_BATCH || T < 1 || T_max < 1 || T_max > GQA_MAX_T_MAX) return 0;
   if ((long)B * T > (1L << 24) || start_pos < 0 || (long)start_pos + T > T_max) return 0;
-  const size_t a = prefill_ws_bytes(B, start_pos, T);
+  if (!kv_supported(n_kv_heads)) return 0;
+  const size_t a = prefill_ws_bytes(B, start_pos, T, n_kv_heads);
   const size_t b = decode_ws_bytes(B);
   return a > b ? a : b;
+}
+
+size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max) {
+  return gqa_workspace_bytes_kv(B, start_pos, T, T_max, KVH);
 }
 
 size_t gqa_workspace_bytes(int B, int T, int T_max) {
@@ -357,6 +368,15 @@ int gqa_block_prefill_profiled(const gqa_bf16* x, const gqa_bf16* wq, const gqa_
   if (!events) return GQA_ERR_NULL;
   return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, 0, B, T, out, ws, ws_bytes,
                       probe, stream, events);
+}
+
+int gqa_block_prefill_kv(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                         const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                         gqa_bf16* vcache, int n_kv_heads, int T_max, const float* rope,
+                         int start_pos, int B, int T, float* out, void* ws, size_t ws_bytes,
+                         float* probe, hipStream_t stream, hipEvent_t* events) {
+  return prefill_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, out, ws,
+                      ws_bytes, probe, stream, events, 0, false, n_kv_heads);
 }
 
 int gqa_block_decode_kv(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,

@@ -107,7 +107,8 @@ struct PrefillParams {
   uint16_t* vcache;
   const float* rope;
   float* out;               // [M][4096]
-  float* probe;             // optional [M][6144]
+  float* probe;             // optional [M][4096 + 2*kv*128]
+  int kv;                   // key/value heads (8 for Llama 3.1 8B; 16, 32)
   int T_max, B, T;          // T new tokens per sequence, at positions start_pos ..
   int start_pos;            // cached rows 0 .. start_pos-1 precede them
   int accumulate;           // out += Delta instead of out = Delta
@@ -115,15 +116,15 @@ struct PrefillParams {
   // workspace
   uint16_t* wo16;           // [4096][4096] fp16 copy of wo
   uint16_t* q16;            // [M][4096] fp16 Q * log2(e)/sqrt(128)
-  uint16_t* k16;            // [B][8][Tp][128] fp16 copy of keys 0 .. start_pos+T-1
-  uint16_t* v16t;           // [B][8][Tp/64][128][64] fp16 copy of the values
+  uint16_t* k16;            // [B][kv][Tp][128] fp16 copy of keys 0 .. start_pos+T-1
+  uint16_t* v16t;           // [B][kv][Tp/64][128][64] fp16 copy of the values
   uint16_t* o16;            // [M][4096] fp16 attention output
 };
 
 constexpr int kPrefillTile = 64;     // query and key tile of the prefill attention
 
-size_t prefill_ws_bytes(int B, int start_pos, int T);
-void prefill_ws_carve(void* ws, PrefillParams* p);   // reads B, T, Tp
+size_t prefill_ws_bytes(int B, int start_pos, int T, int kv = KVH);
+void prefill_ws_carve(void* ws, PrefillParams* p);   // reads B, T, Tp, kv
 
 hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s);

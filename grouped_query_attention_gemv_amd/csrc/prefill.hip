@@ -13,8 +13,9 @@
 //                        the bf16 cache and writes fp16 copies of Q (scaled
 //                        by log2(e)/sqrt(128)), K and V^T for attention
 //   prefill_attn_kernel  causal flash attention on fp16 matrix cores, one
-//                        workgroup per (sequence, kv head, 64 queries) with
-//                        the kv head's 4 query heads sharing every K/V tile
+//                        workgroup per (sequence, kv head, query tile) with
+//                        the kv head's n_rep query heads sharing every K/V
+//                        tile (64 queries for Llama 3.1 8B's n_rep = 4)
 //   gemm_kernel<OUT>     Delta = O Wo^T on fp16 matrix cores, fp32 out
 //
 // Precision: the GEMM inputs x and W are bf16 already, products are exact and
@@ -33,7 +34,6 @@ namespace gqa {
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 constexpr float kLazyRescale = 8.f;   // log2 headroom before the softmax reference moves
-constexpr int AQ = kPrefillTile;      // queries per attention workgroup
 constexpr int AK = kPrefillTile;      // keys per attention tile (and per fp16 V^T block)
 
 // ---------------------------------------------------------------------------
@@ -44,14 +44,14 @@ static size_t prefill_key_rows(int start_pos, int T) {
   return (size_t)(start_pos + T + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
 }
 
-size_t prefill_ws_bytes(int B, int start_pos, int T) {
+size_t prefill_ws_bytes(int B, int start_pos, int T, int kv) {
   const size_t M = (size_t)B * T;
   const size_t Tp = prefill_key_rows(start_pos, T);
   size_t n = kSyncBytes;                            // decode's synchronisation words, untouched
   n += align256((size_t)D * D * 2);                 // wo16
   n += align256(M * D * 2);                         // q16
-  n += align256((size_t)B * KVH * Tp * HD * 2);     // k16
-  n += align256((size_t)B * KVH * HD * Tp * 2);     // v16t
+  n += align256((size_t)B * kv * Tp * HD * 2);      // k16
+  n += align256((size_t)B * kv * HD * Tp * 2);      // v16t
   n += align256(M * D * 2);                         // o16
   return n;
 }
@@ -65,9 +65,9 @@ void prefill_ws_carve(void* ws, PrefillParams* p) {
   p->q16 = reinterpret_cast<uint16_t*>(c);
   c += align256(M * D * 2);
   p->k16 = reinterpret_cast<uint16_t*>(c);
-  c += align256((size_t)p->B * KVH * Tp * HD * 2);
+  c += align256((size_t)p->B * p->kv * Tp * HD * 2);
   p->v16t = reinterpret_cast<uint16_t*>(c);
-  c += align256((size_t)p->B * KVH * HD * Tp * 2);
+  c += align256((size_t)p->B * p->kv * HD * Tp * 2);
   p->o16 = reinterpret_cast<uint16_t*>(c);
 }
 
@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
     }
     *reinterpret_cast<u32x4*>(p.wo16 + (size_t)i * 8) = o;
   }
-  const int pairs = p.B * KVH;
+  const int kv = p.kv;
+  const int pairs = p.B * kv;
   const int nblk = p.Tp / AK;
   // cached prefix: 8 elements per item (a K row segment, or 8 positions of
   // one V dimension; the V items of an unaligned tail are element-wise)
@@ -117,10 +118,10 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
       const int pair = (int)(i / ((long)HD * groups));
       const int r = (int)(i % ((long)HD * groups));
       const int d = r / groups, t0 = (r % groups) * 8;
-      const int b = pair / KVH, g = pair % KVH;
+      const int b = pair / kv, g = pair % kv;
       uint16_t* dst = p.v16t + (((size_t)pair * nblk + t0 / AK) * HD + d) * AK + t0 % AK;
       if (t0 + 8 <= sp) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p.vcache + vcache_index(b, g, t0, d, p.T_max));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p.vcache + vcache_index(b, g, t0, d, p.T_max, kv));
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
         *reinterpret_cast<u32x4*>(dst) = o;
       } else {
         for (int t = t0; t < sp; ++t) {
-          const _Float16 h = (_Float16)bf16_bits_to_f32(p.vcache[vcache_index(b, g, t, d, p.T_max)]);
+          const _Float16 h = (_Float16)bf16_bits_to_f32(p.vcache[vcache_index(b, g, t, d, p.T_max, kv)]);
           dst[t - t0] = __builtin_bit_cast(uint16_t, h);
         }
       }
@@ -187,13 +188,14 @@ __device__ __forceinline__ int b_row_of(int n0, int j) {
   return n0 + (j & ~31) + 2 * (j & 15) + ((j >> 4) & 1);
 }
 
+// kvf: K (and V) features of the QKV GEMM, kv heads * 128
 template <int KIND>
 __device__ __forceinline__ const uint16_t* b_row_ptr(const uint16_t* b0, const uint16_t* b1,
-                                                     const uint16_t* b2, int row) {
+                                                     const uint16_t* b2, int row, int kvf) {
   if (KIND == GEMM_QKV) {
     if (row < D) return b0 + (size_t)row * D;
-    if (row < D + KVH * HD) return b1 + (size_t)(row - D) * D;
-    return b2 + (size_t)(row - D - KVH * HD) * D;
+    if (row < D + kvf) return b1 + (size_t)(row - D) * D;
+    return b2 + (size_t)(row - D - kvf) * D;
   }
   return b0 + (size_t)row * D;
 }
@@ -249,7 +251,7 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     const int am = min(m0 + r, g.M - 1);
     a_src[i] = g.a + (size_t)am * D + lchunk * 8;
     const int br = b_row_of(n0, r);
-    b_src[i] = b_row_ptr<KIND>(g.b0, g.b1, g.b2, br) + lchunk * 8;
+    b_src[i] = b_row_ptr<KIND>(g.b0, g.b1, g.b2, br, g.p.kv * HD) + lchunk * 8;
   }
 
   auto load_stage = [&](int stage, int k0) {
@@ -327,7 +329,7 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     if (n0 < D) {
       qkv_epilogue<0, 0>(g, acc, st, mw, fw, lane);
       qkv_epilogue<0, 1>(g, acc, st, mw, fw, lane);
-    } else if (n0 < D + KVH * HD) {
+    } else if (n0 < D + g.p.kv * HD) {
       qkv_epilogue<1, 0>(g, acc, st, mw, fw, lane);
       qkv_epilogue<1, 1>(g, acc, st, mw, fw, lane);
     } else {
@@ -424,7 +426,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
       }
       const int f = fw + 8 * k;
       if (p.probe) {
-        float* pr = p.probe + (size_t)m * NQKV + f;
+        float* pr = p.probe + (size_t)m * g.N + f;
         *reinterpret_cast<f32x4*>(pr) = f32x4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(pr + 4) = f32x4{v[4], v[5], v[6], v[7]};
       }
@@ -442,8 +444,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
           kb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
           kh[j] = pack_f16x2(bf16_bits_to_f32(kb[j] & 0xffffu), bf16_bits_to_f32(kb[j] >> 16));
         }
-        *reinterpret_cast<u32x4*>(p.kcache + ((size_t)(b * KVH + gg) * p.T_max + t) * HD + d) = kb;
-        *reinterpret_cast<u32x4*>(p.k16 + ((size_t)(b * KVH + gg) * p.Tp + t) * HD + d) = kh;
+        *reinterpret_cast<u32x4*>(p.kcache + ((size_t)(b * p.kv + gg) * p.T_max + t) * HD + d) = kb;
+        *reinterpret_cast<u32x4*>(p.k16 + ((size_t)(b * p.kv + gg) * p.Tp + t) * HD + d) = kh;
       }
     }
   } else {
@@ -459,12 +461,12 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
       const f32x4 hi = *reinterpret_cast<const f32x4*>(st + stage_off(c, 2 * q + 1));
       const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const int f = fw + c;
-      const int ff = f - D - KVH * HD, gg = ff / HD, d = ff % HD;
+      const int ff = f - D - p.kv * HD, gg = ff / HD, d = ff % HD;
       const int m0 = mh + 8 * q;
       if (p.probe) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (m0 + e < g.M) p.probe[(size_t)(m0 + e) * NQKV + f] = v[e];
+          if (m0 + e < g.M) p.probe[(size_t)(m0 + e) * g.N + f] = v[e];
       }
       if (vec) {
         if (m0 >= g.M) continue;
@@ -475,9 +477,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
           vb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
           vh[j] = pack_f16x2(bf16_bits_to_f32(vb[j] & 0xffffu), bf16_bits_to_f32(vb[j] >> 16));
         }
-        *reinterpret_cast<u32x4*>(p.vcache + vcache_index(b, gg, t, d, p.T_max)) = vb;
+        *reinterpret_cast<u32x4*>(p.vcache + vcache_index(b, gg, t, d, p.T_max, p.kv)) = vb;
         *reinterpret_cast<u32x4*>(
-            p.v16t + (((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK) = vh;
+            p.v16t + (((size_t)(b * p.kv + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK) = vh;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -485,9 +487,9 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
           if (m >= g.M) break;
           const int b = m / T, t = p.start_pos + m - b * T;
           const uint32_t vb = f32_to_bf16_bits(v[e]);
-          p.vcache[vcache_index(b, gg, t, d, p.T_max)] = (uint16_t)vb;
+          p.vcache[vcache_index(b, gg, t, d, p.T_max, p.kv)] = (uint16_t)vb;
           const _Float16 h = (_Float16)bf16_bits_to_f32(vb);
-          p.v16t[(((size_t)(b * KVH + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] =
+          p.v16t[(((size_t)(b * p.kv + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] =
               __builtin_bit_cast(uint16_t, h);
         }
       }
@@ -533,7 +535,7 @@ hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s) {
   g.b1 = p.wk;
   g.b2 = p.wv;
   g.M = p.B * p.T;
-  g.N = NQKV;
+  g.N = D + 2 * p.kv * HD;
   g.p = p;
   return launch_gemm<GEMM_QKV>(g, s);
 }
@@ -554,9 +556,11 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 // Causal flash attention (prefill)
 // ---------------------------------------------------------------------------
 //
-// Workgroup = (sequence b, kv head g, query tile of 64 positions), 8 waves:
-// wave w handles query head 4g + (w & 3) for the 32 queries 32*(w >> 2) ..
-// of the tile, so all 8 waves share every K/V tile in LDS and two waves run
+// Workgroup = (sequence b, kv head g, query tile), 8 waves: wave w handles
+// query head NR*g + (w % NR) for the 32 queries 32*(w / NR) .. of the tile,
+// NR = 32 / KV query heads per kv head, so the tile spans 256 / NR queries
+// (64 for Llama 3.1 8B's NR = 4; 128 for NR = 2; 256 for multi-head
+// attention).  All 8 waves share every K/V tile in LDS and two waves run
 // on each SIMD (one's softmax overlaps the other's matrix-core work).  Per
 // 64-key tile, in fp16 on the matrix cores:
 //   S^T[64 keys x 32 q] = K . Q^T      (A = K tile from LDS, B = Q in VGPRs)
@@ -575,22 +579,29 @@ __device__ __forceinline__ int attn_kswz(int key) { return (key & 3) | ((key >> 
 __device__ __forceinline__ int attn_vswz(int dim) { return (dim & 7) ^ ((dim >> 3) & 1); }
 constexpr int kAttnLds = 2 * kAttnStage;         // double-buffered: 64 KiB
 
+// queries per workgroup of the attention kernel for kv heads KV
+constexpr int attn_queries(int kv) { return 32 * (8 / (H / kv)); }
+
+template <int KV>
 __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NR = H / KV;
+  constexpr int AQW = attn_queries(KV);
+  static_assert(NR == 1 || NR == 2 || NR == 4, "8 waves split over NR heads");
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
   const int T = p.T, Tp = p.Tp;
-  const int nqt = (T + AQ - 1) / AQ;
-  const int pairs = p.B * KVH;
+  const int nqt = (T + AQW - 1) / AQW;
+  const int pairs = p.B * KV;
   const int bg = blockIdx.x % pairs;
   const int qt = nqt - 1 - blockIdx.x / pairs;      // longest rows first
-  const int b = bg / KVH, g = bg % KVH;
-  const int h = g * REP + (w & 3);
-  const int q0 = qt * AQ + 32 * (w >> 2);           // first new token of this wave
+  const int b = bg / KV, g = bg % KV;
+  const int h = g * NR + (w % NR);
+  const int q0 = qt * AQW + 32 * (w / NR);          // first new token of this wave
   // key tiles 0 .. klast hold the keys of the workgroup's queries (positions
   // start_pos + t); from tile kmask on, some key lies past one of this wave's
-  const int klast = (p.start_pos + min(qt * AQ + AQ - 1, T - 1)) / AK;
+  const int klast = (p.start_pos + min(qt * AQW + AQW - 1, T - 1)) / AK;
   const int kmask = (p.start_pos + q0) / AK;
 
   const uint16_t* kg = p.k16 + (size_t)bg * Tp * HD;
@@ -825,13 +836,22 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   }
 }
 
-hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_attn_kernel),
+template <int KV>
+static hipError_t launch_attn(const PrefillParams& p, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_attn_kernel<KV>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
   if (e != hipSuccess) return e;
-  const int nqt = (p.T + AQ - 1) / AQ;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(p.B * KVH * nqt), dim3(512), kAttnLds, s, p);
+  const int nqt = (p.T + attn_queries(KV) - 1) / attn_queries(KV);
+  hipLaunchKernelGGL(prefill_attn_kernel<KV>, dim3(p.B * KV * nqt), dim3(512), kAttnLds, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+  switch (p.kv) {
+    case 16: return launch_attn<16>(p, s);
+    case 32: return launch_attn<32>(p, s);
+    default: return launch_attn<KVH>(p, s);
+  }
 }
 
 }  // namespace gqa

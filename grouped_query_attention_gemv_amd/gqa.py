@@ -16,7 +16,7 @@ import torch
 D_MODEL = 4096
 N_HEADS = 32
 N_KV_HEADS = 8
-DECODE_KV_HEADS = (8, 16, 32)   # key/value head counts the decode path takes
+KV_HEAD_COUNTS = (8, 16, 32)   # key/value head counts the block entry points take
 HEAD_DIM = 128
 QKV_DIM = 6144
 ROPE_PAIRS = 64
@@ -43,6 +43,9 @@ _SIGS = {
     "gqa_rope_table": (_I, [_I, ctypes.c_double, _I, _P, _P]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "gqa_workspace_bytes_from": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "gqa_workspace_bytes_kv": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "gqa_block_prefill_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P,
+                                  ctypes.c_size_t, _P, _P, _P]),
     "gqa_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
     "gqa_set_decode_schedule": (_I, [_I]),
     "gqa_decode_schedule": (_I, [_I, _I, _I]),
@@ -128,16 +131,22 @@ def _need(t, name, dtype, shape, device):
 # Allocation helpers (layouts of include/gqa.h)
 # ----------------------------------------------------------------------------
 
-def workspace_bytes(B: int, T: int, T_max: int, start_pos: int = 0) -> int:
+def workspace_bytes(B: int, T: int, T_max: int, start_pos: int = 0,
+                    n_kv_heads: int = N_KV_HEADS) -> int:
+    if n_kv_heads != N_KV_HEADS:
+        return int(lib().gqa_workspace_bytes_kv(int(B), int(start_pos), int(T), int(T_max),
+                                                int(n_kv_heads)))
     if start_pos:
         return int(lib().gqa_workspace_bytes_from(int(B), int(start_pos), int(T), int(T_max)))
     return int(lib().gqa_workspace_bytes(int(B), int(T), int(T_max)))
 
 
-def workspace(B: int, T: int, T_max: int, device, start_pos: int = 0) -> torch.Tensor:
+def workspace(B: int, T: int, T_max: int, device, start_pos: int = 0,
+              n_kv_heads: int = N_KV_HEADS) -> torch.Tensor:
     """A workspace for these arguments (prefill of T tokens from start_pos,
-    and decode), initialised (gqa_workspace_init) on the current stream."""
-    n = workspace_bytes(B, T, T_max, start_pos)
+    and decode, with n_kv_heads key/value heads), initialised
+    (gqa_workspace_init) on the current stream."""
+    n = workspace_bytes(B, T, T_max, start_pos, n_kv_heads)
     if n == 0:
         raise ValueError(f"no workspace size for B={B}, start_pos={start_pos}, T={T}, "
                          f"T_max={T_max}")
@@ -314,19 +323,30 @@ def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, pr
                   events: HipEvents | None = None, start_pos: int = 0) -> torch.Tensor:
     """Delta_attn [B, T, 4096] fp32 for x [B, T, 4096] bf16 at positions
     start_pos..start_pos+T-1; reads cache rows 0..start_pos-1 and writes rows
-    start_pos..start_pos+T-1 (start_pos > 0: gqa_block_prefill_from)."""
+    start_pos..start_pos+T-1 (start_pos > 0: gqa_block_prefill_from).  The
+    number of key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), 16 or
+    32 (gqa_block_prefill_kv)."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
+                                 kv_heads=KV_HEAD_COUNTS)
+    n_kv = wk.shape[0] // HEAD_DIM
     T = x.shape[1]
     _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
     if out is None:
         out = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, (B, T, D_MODEL), dev)
     if probe is not None:
-        _need(probe, "probe", torch.float32, (B, T, QKV_DIM), dev)
+        _need(probe, "probe", torch.float32, (B, T, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = workspace(B, T, T_max, dev, start_pos)
+        ws = workspace(B, T, T_max, dev, start_pos, n_kv)
+    if n_kv != N_KV_HEADS:
+        _check(lib().gqa_block_prefill_kv(
+            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
+            int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(out), _ptr(ws),
+            ws.numel(), _ptr(probe), _stream(dev), None if events is None else events.events),
+            "gqa_block_prefill_kv")
+        return out
     if start_pos:
         if events is not None:
             raise ValueError("per-stage events are recorded for start_pos = 0 only")
@@ -442,7 +462,7 @@ def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=No
     if x.dim() != 2:
         raise ValueError("x must be [B, 4096]")
     dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
-                                 kv_heads=DECODE_KV_HEADS)
+                                 kv_heads=KV_HEAD_COUNTS)
     n_kv = wk.shape[0] // HEAD_DIM
     _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
     if out is None:

@@ -85,21 +85,22 @@ def decode_workload(seed: int, B: int, P: int, device="cpu", n_kv_heads: int = N
     return x, w, k, v
 
 
-def prefill_workload(seed: int, B: int, T: int, device="cpu"):
+def prefill_workload(seed: int, B: int, T: int, device="cpu", n_kv_heads: int = N_KV_HEADS):
     """x [B, T, 4096] and weights."""
     gen = generator(seed, device)
     x = randn_bf16(gen, (B, T, D_MODEL), 1.0, device)
-    w = block_weights(gen, device)
+    w = block_weights(gen, device, n_kv_heads)
     return x, w
 
 
-def chunked_prefill_workload(seed: int, B: int, start_pos: int, T: int, device="cpu"):
-    """x [B, T, 4096], weights, and cached rows [B, start_pos, 8, 128] for K
-    and V (the keys and values of the earlier chunk)."""
+def chunked_prefill_workload(seed: int, B: int, start_pos: int, T: int, device="cpu",
+                             n_kv_heads: int = N_KV_HEADS):
+    """x [B, T, 4096], weights, and cached rows [B, start_pos, n_kv, 128] for
+    K and V (the keys and values of the earlier chunk)."""
     gen = generator(seed, device)
     x = randn_bf16(gen, (B, T, D_MODEL), 1.0, device)
-    w = block_weights(gen, device)
-    k, v = cache_rows(gen, B, start_pos, device)
+    w = block_weights(gen, device, n_kv_heads)
+    k, v = cache_rows(gen, B, start_pos, device, n_kv_heads)
     return x, w, k, v
 
 

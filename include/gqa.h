@@ -141,6 +141,14 @@ size_t gqa_workspace_bytes(int B, int T, int T_max);
 size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max);
 
 /*
+ * gqa_workspace_bytes_kv -- gqa_workspace_bytes_from for a model with
+ * n_kv_heads key/value heads (8, 16 or 32; the prefill's fp16 K/V copies grow
+ * with it).  0 for another n_kv_heads or out-of-range arguments; n_kv_heads = 8
+ * equals gqa_workspace_bytes_from.
+ */
+size_t gqa_workspace_bytes_kv(int B, int start_pos, int T, int T_max, int n_kv_heads);
+
+/*
  * gqa_workspace_init -- zero the synchronisation words of a workspace of
  * ws_bytes bytes (one hipMemsetAsync on stream, not to be captured in a graph).
  * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (< GQA_SYNC_BYTES),
@@ -214,6 +222,31 @@ int gqa_block_prefill_from(const gqa_bf16* x,
                            const float* rope, int start_pos, int B, int T,
                            float* out, void* ws, size_t ws_bytes, float* probe,
                            hipStream_t stream);
+
+/*
+ * gqa_block_prefill_kv -- gqa_block_prefill_from for a model with n_kv_heads
+ * key / value heads, each shared by 32 / n_kv_heads query heads (the n_rep of
+ * the page "Llama 3.1 8B . Grouped-query attention", evidence "gqa": query
+ * head h reads kv head h / n_rep; n_kv_heads = 32 is multi-head attention).
+ *   n_kv_heads  8, 16 or 32 (8 behaves as gqa_block_prefill_from)
+ *   wk, wv      [n_kv_heads*128][4096] bf16
+ *   kcache      [B][n_kv_heads][T_max][128] bf16
+ *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
+ *   ws          ws_bytes >= gqa_workspace_bytes_kv(B, start_pos, T, T_max,
+ *               n_kv_heads)
+ *   probe       NULL or [B*T][4096 + 2*n_kv_heads*128] fp32
+ *   events      NULL, or GQA_PREFILL_STAGES + 1 events recorded as by
+ *               gqa_block_prefill_profiled
+ *   other arguments as for gqa_block_prefill_from
+ * Errors: as gqa_block_prefill_from; GQA_ERR_ARG for another n_kv_heads.
+ */
+int gqa_block_prefill_kv(const gqa_bf16* x,
+                         const gqa_bf16* wq, const gqa_bf16* wk,
+                         const gqa_bf16* wv, const gqa_bf16* wo,
+                         gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                         int T_max, const float* rope, int start_pos, int B,
+                         int T, float* out, void* ws, size_t ws_bytes,
+                         float* probe, hipStream_t stream, hipEvent_t* events);
 
 /*
  * Layer entry points: the block inside its residual branch, as the page

@@ -153,6 +153,35 @@ def _prefill_from_args(**kw):
                            "B", "T", "out", "ws", "ws_bytes", "probe", "stream")]
 
 
+def _prefill_kv_args(n_kv, **kw):
+    a = _prefill_from_args(**kw)
+    return a[:7] + [n_kv] + a[7:] + [None]
+
+
+@pytest.mark.parametrize("n_kv,kw,code", [
+    (4, {}, EARG), (12, {}, EARG), (64, {}, EARG), (0, {}, EARG),
+    (32, dict(x=None), ENULL), (16, dict(T=0), ESHAPE), (32, dict(start_pos=1009), ERANGE),
+    (32, dict(ws_bytes=4096), EWS), (16, dict(out=_fake(3)), EALIAS),
+    (32, dict(probe=_fake(8)), EALIAS),
+])
+def test_prefill_kv_rejects_bad_arguments(n_kv, kw, code):
+    assert G.lib().gqa_block_prefill_kv(*_prefill_kv_args(n_kv, **kw)) == code
+
+
+def test_workspace_bytes_kv():
+    L = G.lib()
+    for B, sp, T, T_max in [(1, 0, 1, 32), (4, 0, 2048, 2048), (2, 100, 300, 512)]:
+        assert L.gqa_workspace_bytes_kv(B, sp, T, T_max, 8) == \
+            L.gqa_workspace_bytes_from(B, sp, T, T_max)
+        n8, n16, n32 = (L.gqa_workspace_bytes_kv(B, sp, T, T_max, k) for k in (8, 16, 32))
+        assert 0 < n8 <= n16 <= n32
+    # the fp16 K/V copies: B * n_kv * Tp * 128 * 2 bytes each, Tp = 2048
+    assert L.gqa_workspace_bytes_kv(4, 0, 2048, 2048, 32) - \
+        L.gqa_workspace_bytes_kv(4, 0, 2048, 2048, 8) == 2 * 4 * 24 * 2048 * 128 * 2
+    for k in (0, 4, 24, 33):
+        assert L.gqa_workspace_bytes_kv(1, 0, 16, 64, k) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), ENULL), (dict(rope=None), ENULL),
     (dict(B=0), ESHAPE), (dict(T=0), ESHAPE),

@@ -285,6 +285,47 @@ def test_prefill_is_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("n_kv,B,start_pos,T", [
+    (32, 1, 0, 300), (32, 2, 0, 257), (32, 3, 0, 64), (32, 1, 130, 129), (32, 2, 1000, 48),
+    (16, 2, 0, 130), (16, 1, 37, 200), (16, 1, 0, 1), (16, 3, 64, 256)])
+def test_prefill_other_kv_head_counts(n_kv, B, start_pos, T):
+    """n_rep = 32 / n_kv query heads per key/value head (1: multi-head
+    attention, 256-query tiles; 2: 128-query tiles), from position 0 and after
+    cached rows, with ragged query tiles."""
+    T_max = ((start_pos + T + 31) // 32) * 32 + 32
+    c = PrefillCase(B, T, T_max, dev=DEV, start_pos=start_pos, n_kv=n_kv)
+    c.run()
+    c.check(c.oracle())
+    c.check_untouched()
+
+
+@pytest.mark.parametrize("n_kv", [16, 32])
+def test_kv_variant_decode_after_prefill(n_kv):
+    """Multi-head / n_rep = 2 models: prefill 700 tokens, decode token 700 on
+    the cache it wrote, against a 701-token prefill and its oracle."""
+    T = 700
+    full = PrefillCase(1, T + 1, 704, dev=DEV, n_kv=n_kv)
+    full.run(probe=False)
+    ref = full.oracle()
+    assert_close("prefill 701", f64(full.out), ref.delta)
+    kc, vc = G.empty_caches(1, 704, DEV, n_kv)
+    G.block_prefill(full.xd[:, :T].contiguous(), *full.wd, kc, vc, full.rope)
+    out = G.block_decode(full.xd[:, T].contiguous(), *full.wd, kc, vc, full.rope, T)
+    torch.cuda.synchronize()
+    assert_close("decode vs oracle", f64(out), ref.delta[:, T])
+    assert np.array_equal(bits(G.kcache_by_position(kc)[:, :T]),
+                          bits(G.kcache_by_position(full.kcache)[:, :T]))
+    assert np.array_equal(bits(G.vcache_read(vc, 0, T)), bits(G.vcache_read(full.vcache, 0, T)))
+
+
+def test_prefill_mha_b2_t1024():
+    """Multi-head attention (n_kv = 32) prefill at B=2, T=1024: four full
+    256-query tiles per sequence and head."""
+    c = PrefillCase(2, 1024, 1024, dev=DEV, n_kv=32)
+    c.run()
+    c.check(c.oracle())
+
+
 # ----------------------------------------------------------------------------
 # Chunked prefill: T new tokens after start_pos cached rows
 # ----------------------------------------------------------------------------
