@@ -98,8 +98,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (a + b) + (c + d);
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// op(own value, value of lane l ^ 16) and op(own, lane l ^ 32), the same in
+// both lanes of a pair.  The row-swap permutes of gfx950 exchange 16-lane
+// rows (0 <-> 1 and 2 <-> 3) or wave halves between their two operands in
+// the VALU, with no LDS round trip; with both operands holding v, the two
+// results are v and its partner's v in every lane.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------

@@ -357,8 +357,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
         tmax = fmaxf(tmax, sv[mt * 4 + i]);
       }
     }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    tmax = max_xor32(max_xor16(tmax));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = valid_col ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
     float psum = 0.f;
@@ -397,8 +396,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   }
 
   // wave result: l summed over the 4 lane rows, O = hi column + lo column
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_xor32(sum_xor16(l_run));
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll

@@ -731,8 +731,7 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) t = fmaxf(t, s[mt][nt][e]);
-      t = fmaxf(t, shfl_xor(t, 16));
-      t = fmaxf(t, shfl_xor(t, 32));
+      t = max_xor32(max_xor16(t));
       m_new[nt] = fmaxf(m_run[nt], t);
       grow |= t > m_run[nt] + kLazyRescale;
     }
@@ -814,8 +813,7 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     float l = l_run[nt];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    l = sum_xor32(sum_xor16(l));
     const float inv = 1.f / l;
     const int row = nt * 16 + col;
 #pragma unroll
