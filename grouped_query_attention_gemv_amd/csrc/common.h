@@ -157,6 +157,25 @@ __device__ __forceinline__ u32x4 ld_dev_x4(const void* base, uint32_t byte_off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
 }
 
+// XCD-local loads.  Every CU of an XCD shares that XCD's L2, and a CU's own
+// cache writes stores through to it, so a completed store of one workgroup is
+// visible to any workgroup of the same XCD that reads past its CU cache: a
+// buffer load with the sc0 policy (base wave-uniform).  Workgroups of one
+// launch are placed round-robin, workgroup i on XCD i % 8.
+__device__ __forceinline__ uint32_t ld_xcd(const void* base, uint32_t byte_off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 1);
+}
+__device__ __forceinline__ float ld_xcd_f(const void* base, uint32_t byte_off) {
+  return __uint_as_float(ld_xcd(base, byte_off));
+}
+__device__ __forceinline__ u32x4 ld_xcd_x4(const void* base, uint32_t byte_off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 1));
+}
+
 // Wait until every memory access this wave has issued has completed (stores
 // acknowledged by the memory system).
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -23,16 +23,16 @@ namespace gqa {
 
 // Output features of QKV workgroup `blk`: 8 consecutive features, 2 per wave.
 // The three-launch schedule takes them in feature order.  The fused schedule
-// takes them kv head by kv head (Q of its 4 query heads: 64 workgroups, then
-// K: 16, then V: 16), so that each kv head's inputs to attention complete
-// together and early heads can start attention while later ones stream.
+// gives kv head g the workgroups blk = g (mod 8), which all run on XCD g,
+// where the head's attention workgroups run too (Q of its 4 query heads: 64
+// workgroups, then K: 16, then V: 16).
 template <bool FUSED>
 __device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
   if (!FUSED) {
     *grp = 0;
     return blk * 8;
   }
-  const int g = blk / 96, r = blk % 96;
+  const int g = blk & 7, r = blk >> 3;
   *grp = g;
   if (r < 64) return g * (REP * HD) + r * 8;
   if (r < 80) return D + g * HD + (r - 64) * 8;
@@ -95,13 +95,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
       *reinterpret_cast<float2*>(p.probe + (size_t)b * kNqkv + r0) = make_float2(v0, v1);
     }
     if (r0 < D) {
-      float* qd = p.q + (size_t)b * D + r0;
-      if (FUSED) {
-        st_dev(qd, v0);
-        st_dev(qd + 1, v1);
-      } else {
-        *reinterpret_cast<float2*>(qd) = make_float2(v0, v1);
-      }
+      *reinterpret_cast<float2*>(p.q + (size_t)b * D + r0) = make_float2(v0, v1);
     } else {
       const int g = rr / HD, d = rr % HD;
       const uint32_t pair = pack_bf16x2(v0, v1);
@@ -114,14 +108,15 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
         dst[VB] = (uint16_t)(pair >> 16);
       }
       // the attention workgroups of the same launch read the new row from here
-      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2, pair);
+      if (FUSED) p.kv_new[((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2] = pair;
     }
   }
 
   if (FUSED) {
-    // Count this workgroup towards its kv head once all of its device-scope
-    // stores have landed.  The head's attention workgroups wait for the
-    // count to reach 96; the last of them rearms it.
+    // Count this workgroup towards its kv head once its stores of Q and of
+    // the new row have reached the XCD's L2, where the head's attention
+    // workgroups (same XCD) read them.  They wait for the count to reach 96;
+    // the last of them rearms it.
     wait_vm();
     __syncthreads();
     if (threadIdx.x == 0)
@@ -160,9 +155,11 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 constexpr int attn_lds_words(int rep) { return kAttnWaves * rep * HD + 2 * kAttnWaves * rep + 1; }
 constexpr int kAttnLdsWords = attn_lds_words(REP);
 
-// FUSED: Q, K and V come from the same launch.  The workgroup waits on its kv
-// head's counter, reads Q and the appended row with device-scope loads, and
-// hands O to the wo workgroups of the launch.
+// FUSED: Q, K and V come from the same launch.  The workgroup runs on the XCD
+// of its kv head (blk = g mod 8), waits on the head's counter, reads Q and
+// the appended row from that XCD's L2, merges the head's splits there, and
+// hands O to the wo workgroups of the launch (on every XCD) through
+// device-scope stores.
 // KV kv heads serve NR = 32 / KV query heads each (NR = 4 for Llama 3.1 8B;
 // 2 and 1, the last being multi-head attention, on the three-launch path).
 // The MFMA operand columns are the NR heads' hi parts, then their lo parts.
@@ -173,9 +170,10 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
   constexpr int kShlNr = 0x100 + NR;             // DPP row_shl:NR, lane i <- lane i + NR
   constexpr int kShrNr = 0x110 + NR;             // DPP row_shr:NR, lane i <- lane i - NR
-  const int split = blk % p.nsplit;
-  const int g = (blk / p.nsplit) % KV;
-  const int b = blk / (p.nsplit * KV);
+  // fused: g = blk mod 8 (the XCD of the head's QKV workgroups)
+  const int split = FUSED ? (blk >> 3) % p.nsplit : blk % p.nsplit;
+  const int g = FUSED ? (blk & 7) : (blk / p.nsplit) % KV;
+  const int b = FUSED ? (blk >> 3) / p.nsplit : blk / (p.nsplit * KV);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
   const int head = col % NR;
@@ -224,7 +222,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
       if (j == P) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          kf[mt][ks] = ld_dev_x4(p.kv_new, kn_off + (uint32_t)(rg * 8 + 32 * ks) * 2u);
+          kf[mt][ks] = ld_xcd_x4(p.kv_new, kn_off + (uint32_t)(rg * 8 + 32 * ks) * 2u);
       }
     }
     const int e = P - tile - rg * 8;     // element of this lane's 8 positions
@@ -232,7 +230,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = col + 16 * dt;
-        const uint32_t wv = ld_dev(vn + d / 2);
+        const uint32_t wv = ld_xcd(vn, (uint32_t)(d / 2) * 4u);
         const uint32_t h = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -273,8 +271,8 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     const uint32_t qoff = (uint32_t)((b * D + (g * REP + head) * HD + rg * 8) * 4);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qraw[2 * ks] = ld_dev_x4(p.q, qoff + ks * 128);
-      qraw[2 * ks + 1] = ld_dev_x4(p.q, qoff + ks * 128 + 16);
+      qraw[2 * ks] = ld_xcd_x4(p.q, qoff + ks * 128);
+      qraw[2 * ks + 1] = ld_xcd_x4(p.q, qoff + ks * 128 + 16);
     }
     if (tile < j_end) patch_tile(tile, kf, vf);
   }
@@ -462,21 +460,32 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     return;
   }
 
-  // Publish this split's partial without an L2 write-back: device-scope
-  // stores go through to the coherence point shared by all XCDs, the wait
-  // makes sure they have landed, then a relaxed device-scope count.  The
-  // last workgroup to arrive merges every partial.
+  // Publish this split's partial, wait for the stores to land, then count
+  // it; the last workgroup to arrive merges every partial.  Three-launch
+  // schedule: device-scope stores (through to the coherence point shared by
+  // all XCDs, without an L2 write-back).  Fused: every split of the head runs
+  // on one XCD, so plain stores into its L2 and loads from there.  Counters
+  // always live at the device-wide coherence point (atomics are performed
+  // there, and the waits poll it with device-scope loads).
   const size_t split_stride = (size_t)NR * kPartStride;
   float* part0 = p.part + ((size_t)(b * KV + g) * p.nsplit) * split_stride + (size_t)mhc * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
   int* split_cnt = p.counters + b * KV + g;
   if (merges) {
-    if (d2 == 0) {
-      st_dev(mine, M);
-      st_dev(mine + 1, lsum);
+    if (FUSED) {
+      if (d2 == 0) {
+        mine[0] = M;
+        mine[1] = lsum;
+      }
+      *reinterpret_cast<float2*>(mine + 4 + d2) = make_float2(o0, o1);
+    } else {
+      if (d2 == 0) {
+        st_dev(mine, M);
+        st_dev(mine + 1, lsum);
+      }
+      st_dev(mine + 4 + d2, o0);
+      st_dev(mine + 5 + d2, o1);
     }
-    st_dev(mine + 4 + d2, o0);
-    st_dev(mine + 5 + d2, o1);
   }
   wait_vm();
   __syncthreads();
@@ -502,10 +511,17 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
         continue;
       }
       const float* ps = part0 + (size_t)s * split_stride;
-      mv[u] = ld_dev(ps);
-      lv[u] = ld_dev(ps + 1);
-      ov0[u] = ld_dev(ps + 4 + d2);
-      ov1[u] = ld_dev(ps + 5 + d2);
+      if (FUSED) {
+        mv[u] = ld_xcd_f(ps, 0);
+        lv[u] = ld_xcd_f(ps, 4);
+        ov0[u] = ld_xcd_f(ps, (uint32_t)(4 + d2) * 4u);
+        ov1[u] = ld_xcd_f(ps, (uint32_t)(5 + d2) * 4u);
+      } else {
+        mv[u] = ld_dev(ps);
+        lv[u] = ld_dev(ps + 1);
+        ov0[u] = ld_dev(ps + 4 + d2);
+        ov1[u] = ld_dev(ps + 5 + d2);
+      }
     }
     float cm = GM;
 #pragma unroll
