@@ -157,11 +157,14 @@ __device__ __forceinline__ u32x4 ld_dev_x4(const void* base, uint32_t byte_off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
 }
 
-// XCD-local loads.  Every CU of an XCD shares that XCD's L2, and a CU's own
-// cache writes stores through to it, so a completed store of one workgroup is
-// visible to any workgroup of the same XCD that reads past its CU cache: a
-// buffer load with the sc0 policy (base wave-uniform).  Workgroups of one
-// launch are placed round-robin, workgroup i on XCD i % 8.
+// Loads through the XCD's L2 (sc0 policy, base wave-uniform).  Measured on
+// this chip: plain stores go through to the device-wide coherence point but
+// do not refresh a copy that an L2 already holds, so such a load sees another
+// workgroup's completed store only if its XCD has not cached the line since
+// the kernel started (the caches are invalidated at every kernel start).  The
+// one-launch decode uses them for data that is first read after a
+// device-scope wait on its producers; the other readers of the same XCD then
+// hit the L2 line the first one brought in.
 __device__ __forceinline__ uint32_t ld_xcd(const void* base, uint32_t byte_off) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);

@@ -114,9 +114,9 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
 
   if (FUSED) {
     // Count this workgroup towards its kv head once its stores of Q and of
-    // the new row have reached the XCD's L2, where the head's attention
-    // workgroups (same XCD) read them.  They wait for the count to reach 96;
-    // the last of them rearms it.
+    // the new row have completed.  The head's attention workgroups wait for
+    // the count to reach 96 before they first read those lines; the last of
+    // them rearms it.
     wait_vm();
     __syncthreads();
     if (threadIdx.x == 0)
@@ -156,10 +156,11 @@ constexpr int attn_lds_words(int rep) { return kAttnWaves * rep * HD + 2 * kAttn
 constexpr int kAttnLdsWords = attn_lds_words(REP);
 
 // FUSED: Q, K and V come from the same launch.  The workgroup runs on the XCD
-// of its kv head (blk = g mod 8), waits on the head's counter, reads Q and
-// the appended row from that XCD's L2, merges the head's splits there, and
-// hands O to the wo workgroups of the launch (on every XCD) through
-// device-scope stores.
+// of its kv head (blk = g mod 8), waits on the head's counter (device scope),
+// then reads Q and the appended row through that XCD's L2: the first reader
+// of a line fetches it, the head's other workgroups hit it.  The split merge
+// works the same way, and O goes to the wo workgroups of the launch (on
+// every XCD) through device-scope stores.
 // KV kv heads serve NR = 32 / KV query heads each (NR = 4 for Llama 3.1 8B;
 // 2 and 1, the last being multi-head attention, on the three-launch path).
 // The MFMA operand columns are the NR heads' hi parts, then their lo parts.
@@ -640,17 +641,21 @@ __global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) 
 // Fused schedule: the whole block step in one launch
 // ---------------------------------------------------------------------------
 //
-// Workgroups [0, 768) run the QKV projection (kv head by kv head), the next
-// nsplit*8*B flash-decode, the last 512 wo.  Every QKV workgroup is resident
+// Workgroups [0, 768) run the QKV projection, the next nsplit*8*B flash-decode,
+// the last 512 wo.  Workgroup i runs on XCD i % 8; kv head g takes the QKV and
+// attention workgroups with i = g (mod 8).  Every QKV workgroup is resident
 // from the start; each consumer starts its own HBM reads (K/V tiles, wo rows)
 // before it waits, so the three phases overlap instead of paying a launch
 // boundary each:
 //   QKV -> attention: per-kv-head arrival counter, which the head's attention
-//     workgroups poll until it reaches 96;
-//   attention -> wo: the workgroup that completes O of (b, g) sets word
-//     b*8 + g of every wo workgroup's slot.
-// Producers publish with device-scope stores and wait for them to land before
-// they signal; consumers read with device-scope loads.  Every wait is bounded
+//     workgroups poll until it reaches 96, then Q and the new row read
+//     through XCD g's L2;
+//   split -> merge: per-(b, g) counter, the last split merges the partials
+//     (read through XCD g's L2);
+//   attention -> wo: the workgroup that completes O of (b, g) stores it with
+//     device-scope stores and sets word b*8 + g of every wo workgroup's slot.
+// Producers wait for their stores to complete before they signal; counters
+// and slots are polled with device-scope loads.  Every wait is bounded
 // (kMaxPolls) and only the consumers wait.  The host admits a shape only if
 // all waiting workgroups together fit in less than the chip's resident
 // capacity, so producers always find room to run whatever order the hardware
