@@ -583,14 +583,17 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
       if (lane < nwords) st_dev(slot + lane, 0);
     }
     __syncthreads();
-    // every load goes out before the first LDS write (one round trip)
+    // every load goes out before the first LDS write (one round trip); no
+    // workgroup reads O before all of it is complete, so the first reader on
+    // each XCD fetches a line into its L2 and the rest of the XCD's wo
+    // workgroups hit it
     constexpr int kPer = NB * (D / 8) / 256;       // 16-byte pieces per thread and part
     u32x4 hv[kPer], lv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const uint32_t off = (uint32_t)(((size_t)b0 * D) * 2 + (threadIdx.x + 256 * k) * 16);
-      hv[k] = ld_dev_x4(p.o_hi, off);
-      lv[k] = ld_dev_x4(p.o_lo, off);
+      hv[k] = ld_xcd_x4(p.o_hi, off);
+      lv[k] = ld_xcd_x4(p.o_lo, off);
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
