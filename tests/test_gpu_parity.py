@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import grouped_query_attention_gemv_amd as G
+from grouped_query_attention_gemv_amd import synth
 from oracle import gqa_oracle as O
 from tests.parity import DecodeCase, PrefillCase, assert_bf16_rows, assert_close, bits, f64
 
@@ -231,6 +232,57 @@ def test_decode_in_hip_graph_matches_eager(schedule):
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
     c.check_untouched()
+
+
+def test_fused_decode_reads_this_calls_data():
+    """The one-launch schedule reads Q, the new K/V row and the split
+    partials through the L2 of the kv head's XCD, relying on those lines not
+    being cached there from an earlier kernel.  Calls on one workspace and
+    one set of buffers, each with a new x (so a new Q and new partials at the
+    same addresses), replayed from a graph with the input changed between
+    replays: every replay must equal a fresh three-launch result on that x."""
+    B, P, T_max = 1, 777, 1024
+    c = DecodeCase(B, P, T_max, dev=DEV)
+    ws = G.workspace(B, 1, T_max, DEV)
+    x = c.xd.clone()
+    out = torch.zeros((B, 4096), dtype=torch.float32, device=DEV)
+    k0, v0 = c.kcache.clone(), c.vcache.clone()
+    xs = [synth.randn_bf16(synth.generator(100 + i), (B, 4096)).to(DEV) for i in range(5)]
+
+    def reference(xi):
+        prev = G.set_decode_schedule(G.DECODE_SPLIT)
+        try:
+            kc, vc = k0.clone(), v0.clone()
+            r = G.block_decode(xi, *c.wd, kc, vc, c.rope, P)
+            torch.cuda.synchronize()
+        finally:
+            G.set_decode_schedule(prev)
+        return r
+
+    prev = G.set_decode_schedule(G.DECODE_FUSED)
+    try:
+        for xi in xs[:2]:                       # eager calls, one workspace
+            x.copy_(xi)
+            r = G.block_decode(x, *c.wd, c.kcache, c.vcache, c.rope, P, out=out, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(r, reference(xi))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            G.block_decode(x, *c.wd, c.kcache, c.vcache, c.rope, P, out=out, ws=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            G.block_decode(x, *c.wd, c.kcache, c.vcache, c.rope, P, out=out, ws=ws)
+        for xi in xs[2:] + xs[:2]:              # graph replays, new x each time
+            x.copy_(xi)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, reference(xi))
+        assert G.workspace_errors(ws) == 0
+    finally:
+        G.set_decode_schedule(prev)
 
 
 def test_decode_rejects_small_workspace_without_side_effects():
