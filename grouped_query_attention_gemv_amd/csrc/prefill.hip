@@ -243,15 +243,17 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
   // (l & 7) ^ (l >> 3))
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow;
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
+  // The tile's first A row and first B row are uniform bases (a B tile lies
+  // in one of Wq / Wk / Wv); lanes keep 32-bit byte offsets from them.
+  const char* a_base = reinterpret_cast<const char*>(g.a + (size_t)m0 * D);
+  const char* b_base = reinterpret_cast<const char*>(b_row_ptr<KIND>(g.b0, g.b1, g.b2, n0, g.p.kv * HD));
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = w * 32 + i * 8 + lrow;
-    const int am = min(m0 + r, g.M - 1);
-    a_src[i] = g.a + (size_t)am * D + lchunk * 8;
-    const int br = b_row_of(n0, r);
-    b_src[i] = b_row_ptr<KIND>(g.b0, g.b1, g.b2, br, g.p.kv * HD) + lchunk * 8;
+    const int am = min(m0 + r, g.M - 1) - m0;
+    a_off[i] = (uint32_t)(am * D + lchunk * 8) * 2u;
+    b_off[i] = (uint32_t)((b_row_of(n0, r) - n0) * D + lchunk * 8) * 2u;
   }
 
   auto load_stage = [&](int stage, int k0) {
@@ -259,8 +261,8 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
     char* sb = sa + GBM * GBK * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(a_src[i] + k0, (lds_void*)(sa + (w * 32 + i * 8) * 128), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(b_src[i] + k0, (lds_void*)(sb + (w * 32 + i * 8) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a_base + a_off[i] + k0 * 2, (lds_void*)(sa + (w * 32 + i * 8) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_base + b_off[i] + k0 * 2, (lds_void*)(sb + (w * 32 + i * 8) * 128), 16, 0, 0);
     }
   };
 
@@ -270,17 +272,35 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Two-phase ping-pong.  The waves of rows 0..127 of the tile (waves 0-3,
+  // one per SIMD) and of rows 128..255 (waves 4-7) alternate between a memory
+  // phase (read this stage's operand fragments from LDS, issue tile loads)
+  // and a compute phase (the stage's 64 matrix-core ops), half a stage apart,
+  // so each SIMD's two waves take turns on the matrix core and on LDS.
+  // Workgroup barriers separate the phases; the second group starts one
+  // barrier late and the first ends with one extra.
+  //   group 0 loads its half (A and B rows 0..127) of stage k+1 in its
+  //   memory phase of stage k, and waits for it at the end of compute k;
+  //   group 1 loads its half (rows 128..255) of stage k+2 in its memory
+  //   phase of stage k, into the buffer it has just read (group 0 read it
+  //   one phase earlier), and waits for stage k+1's half at the same point.
+  // Either way a half is complete before the barrier that precedes the first
+  // read of its stage, and no buffer is overwritten before both groups have
+  // read it.
+  const int grp = w >> 2;
   constexpr int nk = D / GBK;
   load_stage(0, 0);
-  for (int kb = 0; kb < nk; ++kb) {
+  if (grp == 1) {
+    load_stage(1, GBK);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 1 < nk) load_stage((kb + 1) & 1, (kb + 1) * GBK);
+  }
+  __builtin_amdgcn_s_barrier();
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  for (int kb = 0; kb < nk; ++kb) {
     const char* sa = smem + (kb & 1) * (GBM + GBN) * GBK * 2;
     const char* sb = sa + GBM * GBK * 2;
-    // Both 32-deep halves' fragments are read up front; the second half's
-    // reads are interleaved with the first half's matrix-core ops, so only
-    // the first reads' latency is exposed per stage.
     u32x4 af[2][8], bf[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -296,6 +316,19 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
         af[ks][i] = *reinterpret_cast<const u32x4*>(sa + ra * 128 + ((chunk ^ (ra & 7)) << 4));
       }
     }
+    // group 0 loads stage kb+1, group 1 stage kb+2 (into the buffer just read)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int kl = kb + 1 + grp;
+    if (kl < nk) {
+      load_stage(kl & 1, kl * GBK);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -307,14 +340,13 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
           else
             acc[i][j] = mfma_f16(af[ks][i], bf[ks][j], acc[i][j]);
         }
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);    // first half's LDS reads
-#pragma unroll
-    for (int r = 0; r < 12; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix-core ops
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one read of the second half
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
 
   // epilogue: acc[i][2u+s][e] is C[row m0 + wm*128 + i*16 + (lane>>4)*4 + e]
   //                               [feature n0 + wn*64 + 32u + 2*(lane&15) + s].
