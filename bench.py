@@ -166,6 +166,14 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
         torch.cuda.synchronize()
         graph_us = t0.elapsed_time(t1) * 1000.0 / steps
 
+    # hot-cache figure (not the headline): every step reuses set 0, so its
+    # weights and cache stay in the 256 MB Infinity Cache between steps
+    hot_us = None
+    if use_graph:
+        def step0(i):
+            step(0)
+        hot_us = _timed_steps(step0, steps, 3, True)
+
     # the same loop through the profiled entry point: HIP events recorded on
     # the library's stream around each kernel
     ev = G.HipEvents(G.DECODE_STAGES + 1)
@@ -179,7 +187,7 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
     # the fused schedule is one kernel: stage 1 covers it, the others are empty
     names = ["decode_step"] if fused else ["qkv", "attn", "wo"]
     return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps, graph_us_step=graph_us,
-                schedule="fused" if fused else "split",
+                hot_cache_us_step=hot_us, schedule="fused" if fused else "split",
                 kern_us=dict(zip(names, kern_us.tolist())),
                 profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
 
@@ -644,6 +652,9 @@ def main():
         "tokens_per_s": B / (headline_us * 1e-6),
         "eager_us_step": round(dec["us_step"], 3),
         "host_us_per_eager_step": round(dec["wall_us_step"], 3),
+        # one set reused every step, held by the Infinity Cache: not the headline
+        "hot_cache_us_step": (round(dec["hot_cache_us_step"], 3)
+                              if dec["hot_cache_us_step"] is not None else None),
         "algorithmic_bytes_per_step": nb["step"],
         "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
         "profiled_us_step": round(dec["profiled_us_step"], 3),
