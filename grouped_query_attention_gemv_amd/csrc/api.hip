@@ -133,7 +133,6 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
   if (!kv_supported(kv)) return GQA_ERR_ARG;
-  if (kv != KVH && B > kGemvMaxB) return GQA_ERR_SHAPE;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
   if ((probe && !aligned16(probe)) || (out_bf16 && !aligned16(out_bf16))) return GQA_ERR_ALIGN;
   if (accumulate != 0 && accumulate != 1) return GQA_ERR_ARG;

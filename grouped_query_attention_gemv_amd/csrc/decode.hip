@@ -702,11 +702,12 @@ __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
 // QKV epilogue of one column (token b) and features f .. f+3 (one head):
 // RoPE on Q/K pairs with the table entries cs0 (pair f/2) and cs1 (pair
 // f/2 + 1), Q to the workspace, K/V rounded into the cache.
+template <int KV>
 __device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, int b, int f,
                                                float2 cs0, float2 cs1) {
   const int pos = p.start_pos;
   float y[4] = {v[0], v[1], v[2], v[3]};
-  if (f < D + KVH * HD) {
+  if (f < D + KV * HD) {
     const float2 cs[2] = {cs0, cs1};
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
@@ -717,16 +718,16 @@ __device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, i
     }
   }
   if (p.probe)
-    *reinterpret_cast<float4*>(p.probe + (size_t)b * NQKV + f) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4*>(p.probe + (size_t)b * (D + 2 * KV * HD) + f) = make_float4(y[0], y[1], y[2], y[3]);
   if (f < D) {
     *reinterpret_cast<float4*>(p.q + (size_t)b * D + f) = make_float4(y[0], y[1], y[2], y[3]);
-  } else if (f < D + KVH * HD) {
+  } else if (f < D + KV * HD) {
     const int ff = f - D, g = ff / HD, d = ff % HD;
-    uint16_t* dst = p.kcache + ((size_t)(b * KVH + g) * p.T_max + pos) * HD + d;
+    uint16_t* dst = p.kcache + ((size_t)(b * KV + g) * p.T_max + pos) * HD + d;
     *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   } else {
-    const int ff = f - D - KVH * HD, g = ff / HD, d = ff % HD;
-    uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max);
+    const int ff = f - D - KV * HD, g = ff / HD, d = ff % HD;
+    uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max, KV);
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
   }
@@ -745,7 +746,8 @@ __device__ __forceinline__ void st_dev_x4(void* base, uint32_t byte_off, u32x4 v
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16);
 }
 
-template <int MODE>   // 0: QKV + RoPE + cache append, 1: wo (+ residual)
+// KV: key/value heads of the QKV projection (MODE 0): 4096 + 2*KV*128 features.
+template <int MODE, int KV = KVH>   // MODE 0: QKV + RoPE + cache append, 1: wo (+ residual)
 __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_base) {
   constexpr int NP = MODE == 0 ? 1 : 2;        // activation parts (wo: hi, lo)
   constexpr int kP2KS = p2_splits<MODE>();
@@ -761,7 +763,7 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
   const int kbase = ks * kP2Kr;
   if (MODE == 0 && blockIdx.x == 0 && c_base == 0) {
     // the attention kernel that follows counts split arrivals from zero
-    for (int i = tid; i < p.B * KVH; i += blockDim.x) p.counters[i] = 0;
+    for (int i = tid; i < p.B * KV; i += blockDim.x) p.counters[i] = 0;
   }
 
   // A operand: weight row of tile ft, k offset (lane >> 4) * 8 in each step
@@ -771,8 +773,8 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     const int f = fb * kP2Feat + 32 * w + 16 * ft + (lane & 15);
     if (MODE == 0)
       wrow[ft] = (f < D ? p.wq + (size_t)f * D
-                        : (f < D + KVH * HD ? p.wk + (size_t)(f - D) * D
-                                            : p.wv + (size_t)(f - D - KVH * HD) * D)) +
+                        : (f < D + KV * HD ? p.wk + (size_t)(f - D) * D
+                                           : p.wv + (size_t)(f - D - KV * HD) * D)) +
                  kbase + (lane >> 4) * 8;
     else
       wrow[ft] = p.wo + (size_t)f * D + kbase + (lane >> 4) * 8;
@@ -929,7 +931,7 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     const int b = c_base + col;
     const int f = fb * kP2Feat + 4 * f4;
     if (MODE == 0) {
-      proj_qkv_store(p, v, b, f, make_float2(aux[it].x, aux[it].y), make_float2(aux[it].z, aux[it].w));
+      proj_qkv_store<KV>(p, v, b, f, make_float2(aux[it].x, aux[it].y), make_float2(aux[it].z, aux[it].w));
     } else {
       float4 y = make_float4(v[0], v[1], v[2], v[3]);
       if (p.accumulate) {
@@ -969,12 +971,13 @@ void decode_split(int B, int L, int kv, int* nsplit, int* chunk) {
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Partials: the attention splits' (m, l, o), and for B > 8 also the split-K
-// partials of the projections (the two never live at the same time).
+// partials of the projections (the two never live at the same time), sized
+// for the most key/value heads.
 static size_t decode_part_bytes(int B) {
   // the largest over the kv-head counts is the GQA one (more heads per split)
   size_t n = (size_t)B * KVH * decode_max_split(B, KVH) * REP * kPartStride * 4;
   if (B > kGemvMaxB) {
-    const size_t qkv = (size_t)NQKV * p2_splits<0>() * kP2Cols * 4;
+    const size_t qkv = (size_t)(D + 2 * kMaxKv * HD) * p2_splits<0>() * kP2Cols * 4;
     const size_t wo = (size_t)D * p2_splits<1>() * kP2Cols * 4;
     n = std::max(n, std::max(qkv, wo));
   }
@@ -1022,9 +1025,15 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
 
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
-    for (int c = 0; c < p.B; c += kP2Cols)
-      hipLaunchKernelGGL(decode_proj_kernel<0>, dim3(NQKV / kP2Feat * p2_splits<0>()), dim3(256),
-                         kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
+    const dim3 grid((D + 2 * p.kv * HD) / kP2Feat * p2_splits<0>());
+    const size_t lds = kP2Ring * kP2Cols * kP2Kc * 2;
+    for (int c = 0; c < p.B; c += kP2Cols) {
+      switch (p.kv) {
+        case 16: hipLaunchKernelGGL((decode_proj_kernel<0, 16>), grid, dim3(256), lds, s, p, c); break;
+        case 32: hipLaunchKernelGGL((decode_proj_kernel<0, 32>), grid, dim3(256), lds, s, p, c); break;
+        default: hipLaunchKernelGGL((decode_proj_kernel<0, KVH>), grid, dim3(256), lds, s, p, c); break;
+      }
+    }
     return hipGetLastError();
   }
   const int blocks = (D + 2 * p.kv * HD) / 2 / 4;    // one wave per row pair, 4 waves per workgroup

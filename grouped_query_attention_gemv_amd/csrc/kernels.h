@@ -43,7 +43,8 @@ constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedul
 // take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
 constexpr unsigned kWoHoldTicks = 500;
 static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
-static_assert(kSyncProj + 32 * (6144 / 128) <= kSyncBytes / 4, "sync region too small");
+static_assert(kSyncProj + 32 * ((4096 + 2 * 32 * 128) / 128) <= kSyncBytes / 4,
+              "sync region too small for the projection counters of 32 kv heads");
 
 struct DecodeParams {
   const uint16_t* x;        // [B][4096] bf16

@@ -343,9 +343,10 @@ int gqa_block_decode(const gqa_bf16* x,
  * serves query heads g*n_rep .. g*n_rep + n_rep - 1; n_rep = 1 is the
  * multi-head attention the page sizes beside GQA).  Llama 3.1 8B is
  * n_kv_heads = 8, where this equals gqa_block_decode.
- *   n_kv_heads  8, 16 or 32; other than 8 only for B <= 8, and with the
- *               three-launch schedule (GQA_ERR_ARG if GQA_DECODE_FUSED is
- *               forced)
+ *   n_kv_heads  8, 16 or 32; other than 8 only with the three-launch
+ *               schedule (GQA_ERR_ARG if GQA_DECODE_FUSED is forced); above 8
+ *               tokens the projections run on the matrix cores for every
+ *               head count
  *   wk, wv      [n_kv_heads*128][4096] bf16
  *   kcache      [B][n_kv_heads][T_max][128] bf16
  *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
@@ -353,8 +354,7 @@ int gqa_block_decode(const gqa_bf16* x,
  *   events      NULL, or GQA_DECODE_STAGES + 1 events recorded as by
  *               gqa_block_decode_profiled
  *   other arguments, ownership and workspace as for gqa_block_decode
- * Errors: as gqa_block_decode; GQA_ERR_ARG for another n_kv_heads,
- * GQA_ERR_SHAPE for n_kv_heads != 8 with B > 8.
+ * Errors: as gqa_block_decode; GQA_ERR_ARG for another n_kv_heads.
  */
 int gqa_block_decode_kv(const gqa_bf16* x,
                         const gqa_bf16* wq, const gqa_bf16* wk,

@@ -89,7 +89,7 @@ def _decode_kv_args(n_kv, **kw):
 
 @pytest.mark.parametrize("n_kv,kw,code", [
     (4, {}, EARG), (24, {}, EARG), (0, {}, EARG), (-8, {}, EARG),
-    (16, dict(B=9), ESHAPE), (32, dict(B=64), ESHAPE),
+    (16, dict(B=0), ESHAPE), (32, dict(B=64, ws_bytes=1024), EWS),
     (32, dict(x=None), ENULL), (16, dict(start_pos=1024), ERANGE), (32, dict(ws_bytes=1024), EWS),
     (32, dict(out=_fake(0)), EALIAS), (16, dict(probe=_fake(8)), EALIAS),
 ])

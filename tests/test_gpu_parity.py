@@ -89,10 +89,13 @@ def test_decode_unscaled_rope():
 
 
 @pytest.mark.parametrize("n_kv,B,P", [(32, 1, 1000), (32, 3, 777), (16, 1, 1000), (16, 2, 100),
-                                      (32, 8, 129), (16, 5, 0)])
+                                      (32, 8, 129), (16, 5, 0), (16, 9, 300), (32, 17, 65),
+                                      (16, 64, 31), (32, 70, 200)])
 def test_decode_other_kv_head_counts(n_kv, B, P):
     """n_rep = 32 / n_kv query heads per key/value head: 1 is multi-head
-    attention, 2 a wider GQA; the same kernels templated on the head count."""
+    attention, 2 a wider GQA; the same kernels templated on the head count.
+    B > 8 takes the matrix-core projections (B = 70: two 64-token launches,
+    the second ragged)."""
     _, errs = _decode_full(B, P, 1024, n_kv=n_kv)
     assert errs["delta"][0] < 1e-3
 
