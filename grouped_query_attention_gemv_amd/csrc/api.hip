@@ -294,10 +294,38 @@ int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps, const
   return hip_status(launch_vocab_gemv(p, stream));
 }
 
-size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max) {
-  const size_t n = gqa_workspace_bytes_from(B, start_pos, T, T_max);
+size_t gqa_layer_workspace_bytes_kv(int B, int start_pos, int T, int T_max, int n_kv_heads) {
+  const size_t n = gqa_workspace_bytes_kv(B, start_pos, T, T_max, n_kv_heads);
   if (n == 0) return 0;
   return ((n + 255) & ~(size_t)255) + (size_t)B * T * D * 2;
+}
+
+size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max) {
+  return gqa_layer_workspace_bytes_kv(B, start_pos, T, T_max, KVH);
+}
+
+int gqa_layer_prefill_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                         const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                         const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                         int T_max, const float* rope, int start_pos, int B, int T, float* h,
+                         void* ws, size_t ws_bytes, float* probe, hipStream_t stream) {
+  if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
+  if (!kv_supported(n_kv_heads)) return GQA_ERR_ARG;
+  if (B < 1 || B > GQA_MAX_BATCH || T < 1 || (long)B * T > (1L << 24) || T_max < 1 ||
+      T_max > GQA_MAX_T_MAX)
+    return GQA_ERR_SHAPE;
+  if (start_pos < 0 || (long)start_pos + T > T_max) return GQA_ERR_RANGE;
+  const size_t block = gqa_workspace_bytes_kv(B, start_pos, T, T_max, n_kv_heads);
+  gqa_bf16* xn = nullptr;
+  int st = layer_prologue(x, norm_w, eps, B * T, h, ws, ws_bytes, block, &xn);
+  if (st != GQA_OK) return st;
+  st = prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws, block,
+                    probe, stream, nullptr, 1, true, n_kv_heads);
+  if (st != GQA_OK) return st;
+  (void)hipGetLastError();
+  if (launch_rmsnorm(x, norm_w, eps, B * T, xn, h, stream) != hipSuccess) return GQA_ERR_HIP;
+  return prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws,
+                      block, probe, stream, nullptr, 1, false, n_kv_heads);
 }
 
 int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
@@ -305,33 +333,21 @@ int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
                            const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
                            const float* rope, int start_pos, int B, int T, float* h, void* ws,
                            size_t ws_bytes, float* probe, hipStream_t stream) {
-  if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
-  if (B < 1 || B > GQA_MAX_BATCH || T < 1 || (long)B * T > (1L << 24) || T_max < 1 ||
-      T_max > GQA_MAX_T_MAX)
-    return GQA_ERR_SHAPE;
-  if (start_pos < 0 || (long)start_pos + T > T_max) return GQA_ERR_RANGE;
-  const size_t block = gqa_workspace_bytes_from(B, start_pos, T, T_max);
-  gqa_bf16* xn = nullptr;
-  int st = layer_prologue(x, norm_w, eps, B * T, h, ws, ws_bytes, block, &xn);
-  if (st != GQA_OK) return st;
-  st = prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws, block,
-                    probe, stream, nullptr, 1, true);
-  if (st != GQA_OK) return st;
-  (void)hipGetLastError();
-  if (launch_rmsnorm(x, norm_w, eps, B * T, xn, h, stream) != hipSuccess) return GQA_ERR_HIP;
-  return prefill_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, T, h, ws,
-                      block, probe, stream, nullptr, 1, false);
+  return gqa_layer_prefill_kv(x, norm_w, eps, wq, wk, wv, wo, kcache, vcache, KVH, T_max, rope,
+                              start_pos, B, T, h, ws, ws_bytes, probe, stream);
 }
 
-int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const gqa_bf16* wq,
-                     const gqa_bf16* wk, const gqa_bf16* wv, const gqa_bf16* wo,
-                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max, const float* rope,
-                     int start_pos, int B, float* h, gqa_bf16* h_bf16, void* ws, size_t ws_bytes,
-                     float* probe, hipStream_t stream) {
+int gqa_layer_decode_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                        const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                        const gqa_bf16* wo, gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                        int T_max, const float* rope, int start_pos, int B, float* h,
+                        gqa_bf16* h_bf16, void* ws, size_t ws_bytes, float* probe,
+                        hipStream_t stream) {
   if (!x || !norm_w || !h || !ws) return GQA_ERR_NULL;
+  if (!kv_supported(n_kv_heads)) return GQA_ERR_ARG;
   if (B < 1 || B > GQA_MAX_BATCH || T_max < 1 || T_max > GQA_MAX_T_MAX) return GQA_ERR_SHAPE;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
-  const size_t block = gqa_workspace_bytes(B, 1, T_max);
+  const size_t block = gqa_workspace_bytes_kv(B, 0, 1, T_max, n_kv_heads);
   gqa_bf16* xn = nullptr;
   int st = layer_prologue(x, norm_w, eps, B, h, ws, ws_bytes, block, &xn);
   if (st != GQA_OK) return st;
@@ -339,15 +355,24 @@ int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const
     // GEMV path: the QKV prologue normalises the staged rows and the wo
     // epilogue adds the residual, no extra launch
     return decode_impl(x, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 0,
-                       ws, block, probe, stream, nullptr, false, norm_w, eps, x);
+                       ws, block, probe, stream, nullptr, false, norm_w, eps, x, n_kv_heads);
   }
   st = decode_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 1, ws,
-                   block, probe, stream, nullptr, true);
+                   block, probe, stream, nullptr, true, nullptr, 0.f, nullptr, n_kv_heads);
   if (st != GQA_OK) return st;
   (void)hipGetLastError();
   if (launch_rmsnorm(x, norm_w, eps, B, xn, h, stream) != hipSuccess) return GQA_ERR_HIP;
   return decode_impl(xn, wq, wk, wv, wo, kcache, vcache, T_max, rope, start_pos, B, h, h_bf16, 1,
-                     ws, block, probe, stream, nullptr, false);
+                     ws, block, probe, stream, nullptr, false, nullptr, 0.f, nullptr, n_kv_heads);
+}
+
+int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const gqa_bf16* wq,
+                     const gqa_bf16* wk, const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max, const float* rope,
+                     int start_pos, int B, float* h, gqa_bf16* h_bf16, void* ws, size_t ws_bytes,
+                     float* probe, hipStream_t stream) {
+  return gqa_layer_decode_kv(x, norm_w, eps, wq, wk, wv, wo, kcache, vcache, KVH, T_max, rope,
+                             start_pos, B, h, h_bf16, ws, ws_bytes, probe, stream);
 }
 
 int gqa_block_prefill_from(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,

@@ -65,6 +65,11 @@ _SIGS = {
                               _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gqa_block_decode_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I,
                                  _P, ctypes.c_size_t, _P, _P, _P]),
+    "gqa_layer_workspace_bytes_kv": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "gqa_layer_prefill_kv": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _I, _P,
+                                  _I, _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
+    "gqa_layer_decode_kv": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _I, _P,
+                                 _I, _I, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
                                        _P, ctypes.c_size_t, _P, _P, _P]),
 }
@@ -390,10 +395,15 @@ def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None) -> t
     return logits
 
 
-def layer_workspace(B: int, T: int, T_max: int, device, start_pos: int = 0) -> torch.Tensor:
+def layer_workspace(B: int, T: int, T_max: int, device, start_pos: int = 0,
+                    n_kv_heads: int = N_KV_HEADS) -> torch.Tensor:
     """An initialised workspace for layer_prefill(B, T, start_pos) (or, with
-    T = 1 and start_pos = 0, for layer_decode)."""
-    n = int(lib().gqa_layer_workspace_bytes(int(B), int(start_pos), int(T), int(T_max)))
+    T = 1 and start_pos = 0, for layer_decode), n_kv_heads key/value heads."""
+    if n_kv_heads != N_KV_HEADS:
+        n = int(lib().gqa_layer_workspace_bytes_kv(int(B), int(start_pos), int(T), int(T_max),
+                                                   int(n_kv_heads)))
+    else:
+        n = int(lib().gqa_layer_workspace_bytes(int(B), int(start_pos), int(T), int(T_max)))
     if n == 0:
         raise ValueError(f"no layer workspace size for B={B}, start_pos={start_pos}, T={T}, "
                          f"T_max={T_max}")
@@ -406,10 +416,13 @@ def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: in
                   eps: float = NORM_EPS, h=None, ws=None, probe=None) -> torch.Tensor:
     """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, T, 4096] fp32 for x
     [B, T, 4096] bf16 at positions start_pos..; the block's cache rows as in
-    block_prefill."""
+    block_prefill.  The number of key/value heads is wk.shape[0] / 128 (8, 16
+    or 32)."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
+                                 kv_heads=KV_HEAD_COUNTS)
+    n_kv = wk.shape[0] // HEAD_DIM
     T = x.shape[1]
     _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
     _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
@@ -417,9 +430,16 @@ def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: in
         h = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=dev)
     _need(h, "h", torch.float32, (B, T, D_MODEL), dev)
     if probe is not None:
-        _need(probe, "probe", torch.float32, (B, T, QKV_DIM), dev)
+        _need(probe, "probe", torch.float32, (B, T, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = layer_workspace(B, T, T_max, dev, start_pos)
+        ws = layer_workspace(B, T, T_max, dev, start_pos, n_kv)
+    if n_kv != N_KV_HEADS:
+        _check(lib().gqa_layer_prefill_kv(
+            _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+            _ptr(kcache), _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B),
+            int(T), _ptr(h), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)),
+            "gqa_layer_prefill_kv")
+        return h
     _check(lib().gqa_layer_prefill_from(
         _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
         _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(h), _ptr(ws),
@@ -430,10 +450,13 @@ def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: in
 def layer_decode(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int,
                  eps: float = NORM_EPS, h=None, h_bf16=None, ws=None, probe=None) -> torch.Tensor:
     """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, 4096] fp32 for one token per
-    sequence at start_pos; h_bf16 (optional) receives its bf16 rounding."""
+    sequence at start_pos; h_bf16 (optional) receives its bf16 rounding.  The
+    number of key/value heads is wk.shape[0] / 128 (8, 16 or 32)."""
     if x.dim() != 2:
         raise ValueError("x must be [B, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
+                                 kv_heads=KV_HEAD_COUNTS)
+    n_kv = wk.shape[0] // HEAD_DIM
     _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
     _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
     if h is None:
@@ -442,9 +465,16 @@ def layer_decode(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int
     if h_bf16 is not None:
         _need(h_bf16, "h_bf16", torch.bfloat16, (B, D_MODEL), dev)
     if probe is not None:
-        _need(probe, "probe", torch.float32, (B, QKV_DIM), dev)
+        _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = layer_workspace(B, 1, T_max, dev)
+        ws = layer_workspace(B, 1, T_max, dev, 0, n_kv)
+    if n_kv != N_KV_HEADS:
+        _check(lib().gqa_layer_decode_kv(
+            _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+            _ptr(kcache), _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B),
+            _ptr(h), _ptr(h_bf16), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)),
+            "gqa_layer_decode_kv")
+        return h
     _check(lib().gqa_layer_decode(
         _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
         _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(h), _ptr(h_bf16),
@@ -458,7 +488,7 @@ def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=No
     """One token per sequence at position start_pos: x [B, 4096] bf16 ->
     out [B, 4096] fp32 (= Delta, or += Delta with accumulate).  The number of
     key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), or 16 / 32
-    (gqa_block_decode_kv, B <= 8)."""
+    (gqa_block_decode_kv)."""
     if x.dim() != 2:
         raise ValueError("x must be [B, 4096]")
     dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,

@@ -311,6 +311,48 @@ int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
                      hipStream_t stream);
 
 /*
+ * gqa_layer_prefill_kv, gqa_layer_decode_kv, gqa_layer_workspace_bytes_kv --
+ * the two layer entry points above for a model with n_kv_heads key/value
+ * heads (the GQA map and the multi-head case of the page "Llama 3.1 8B .
+ * Grouped-query attention", as for gqa_block_prefill_kv and
+ * gqa_block_decode_kv); 8 behaves as gqa_layer_prefill_from /
+ * gqa_layer_decode.
+ *   n_kv_heads  8, 16 or 32
+ *   wk, wv      [n_kv_heads*128][4096] bf16
+ *   kcache      [B][n_kv_heads][T_max][128] bf16
+ *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
+ *   probe       NULL or [B*T][4096 + 2*n_kv_heads*128] fp32
+ *   ws          ws_bytes >= gqa_layer_workspace_bytes_kv(B, start_pos, T,
+ *               T_max, n_kv_heads) for prefill, (B, 0, 1, T_max, n_kv_heads)
+ *               for decode, initialised once by gqa_workspace_init
+ *   other arguments, ownership and asynchrony as for the 8-head entry points;
+ *   decode other than 8 heads runs the three-launch schedule (GQA_ERR_ARG if
+ *   GQA_DECODE_FUSED is forced)
+ * Errors: as gqa_layer_prefill_from / gqa_layer_decode; GQA_ERR_ARG for
+ * another n_kv_heads.  gqa_layer_workspace_bytes_kv returns 0 for shapes or
+ * head counts that are not accepted.
+ */
+size_t gqa_layer_workspace_bytes_kv(int B, int start_pos, int T, int T_max,
+                                    int n_kv_heads);
+
+int gqa_layer_prefill_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                         const gqa_bf16* wq, const gqa_bf16* wk,
+                         const gqa_bf16* wv, const gqa_bf16* wo,
+                         gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                         int T_max, const float* rope, int start_pos, int B,
+                         int T, float* h, void* ws, size_t ws_bytes,
+                         float* probe, hipStream_t stream);
+
+int gqa_layer_decode_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                        const gqa_bf16* wq, const gqa_bf16* wk,
+                        const gqa_bf16* wv, const gqa_bf16* wo,
+                        gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
+                        int T_max, const float* rope, int start_pos, int B,
+                        float* h, gqa_bf16* h_bf16,
+                        void* ws, size_t ws_bytes, float* probe,
+                        hipStream_t stream);
+
+/*
  * gqa_block_decode -- one new token per sequence at position start_pos (the
  * page's decode mode): writes cache row start_pos and attends over rows
  * 0..start_pos of each of the B sequences (one start_pos for all of them).

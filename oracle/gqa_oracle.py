@@ -328,7 +328,8 @@ def rms_norm(x, g, eps: float) -> np.ndarray:
 
 
 def gqa_layer(x, norm_w, eps: float, wq, wk, wv, wo, k_cached, v_cached, start_pos: int,
-              theta: float = ROPE_THETA, scaled: bool = True):
+              theta: float = ROPE_THETA, scaled: bool = True,
+              n_heads: int = N_HEADS, n_kv_heads: int = N_KV_HEADS):
     """The block inside its residual branch (page "Llama 3.1 8B . Grouped-query
     attention", code section: h = x + attention(attention_norm(x), ...)).
 
@@ -338,7 +339,8 @@ def gqa_layer(x, norm_w, eps: float, wq, wk, wv, wo, k_cached, v_cached, start_p
     """
     x = np.asarray(x, dtype=np.float64)
     xn = f64_from_bf16_bits(bf16_bits_from_f64(rms_norm(x, norm_w, eps)))
-    res = gqa_block(xn, wq, wk, wv, wo, k_cached, v_cached, start_pos, theta, scaled)
+    res = gqa_block(xn, wq, wk, wv, wo, k_cached, v_cached, start_pos, theta, scaled,
+                    n_heads, n_kv_heads)
     return x + res.delta, res
 
 

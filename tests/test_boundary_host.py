@@ -237,6 +237,50 @@ def test_layer_decode_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_layer_decode(*_layer_decode_args(**kw)) == code
 
 
+def test_layer_workspace_bytes_kv():
+    lib = G.lib()
+    for (B, sp, T, Tm) in [(1, 0, 1, 1024), (4, 2048, 2048, 4096), (2, 0, 70, 128)]:
+        assert lib.gqa_layer_workspace_bytes_kv(B, sp, T, Tm, 8) == \
+            lib.gqa_layer_workspace_bytes(B, sp, T, Tm)
+        for kv in (16, 32):
+            base = lib.gqa_workspace_bytes_kv(B, sp, T, Tm, kv)
+            assert lib.gqa_layer_workspace_bytes_kv(B, sp, T, Tm, kv) == \
+                ((base + 255) // 256) * 256 + B * T * 4096 * 2
+    assert lib.gqa_layer_workspace_bytes_kv(1, 0, 1, 1024, 24) == 0
+    assert lib.gqa_layer_workspace_bytes_kv(1, 1020, 8, 1024, 16) == 0
+
+
+def _layer_kv_args(n_kv, **kw):
+    a = _layer_decode_args(**kw)
+    return a[:9] + [n_kv] + a[9:]
+
+
+@pytest.mark.parametrize("n_kv,kw,code", [
+    (4, {}, EARG), (24, {}, EARG), (0, {}, EARG),
+    (16, dict(g=None), ENULL), (32, dict(B=0), ESHAPE), (16, dict(start_pos=1024), ERANGE),
+    (32, dict(ws_bytes=4096), EWS), (16, dict(h=_fake(10)), EALIAS),
+])
+def test_layer_decode_kv_rejects_bad_arguments(n_kv, kw, code):
+    assert G.lib().gqa_layer_decode_kv(*_layer_kv_args(n_kv, **kw)) == code
+
+
+@pytest.mark.parametrize("n_kv,kw,code", [
+    (4, {}, EARG), (24, {}, EARG),
+    (16, dict(x=None), ENULL), (32, dict(T=0), ESHAPE), (16, dict(start_pos=1020), ERANGE),
+    (32, dict(ws_bytes=4096), EWS), (16, dict(h=_fake(9)), EALIAS),
+])
+def test_layer_prefill_kv_rejects_bad_arguments(n_kv, kw, code):
+    a = dict(x=_fake(0), g=_fake(10), eps=ctypes.c_float(1e-5), wq=_fake(1), wk=_fake(2),
+             wv=_fake(3), wo=_fake(4), kc=_fake(5), vc=_fake(6), T_max=1024, rope=_fake(7),
+             start_pos=0, B=1, T=8, h=_fake(8), ws=_fake(9), ws_bytes=1 << 40, probe=None,
+             stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("x", "g", "eps", "wq", "wk", "wv", "wo", "kc", "vc")] + [n_kv] + \
+        [a[k] for k in ("T_max", "rope", "start_pos", "B", "T", "h", "ws", "ws_bytes", "probe",
+                        "stream")]
+    assert G.lib().gqa_layer_prefill_kv(*args) == code
+
+
 def _vocab_args(**kw):
     a = dict(h=_fake(0), g=None, eps=ctypes.c_float(1e-5), w=_fake(1), V=128256, B=1,
              logits=_fake(2), stream=None)

@@ -458,6 +458,48 @@ def test_layer_decode(B, P, mode):
     print(f"layer decode B={B} P={P} {mode}", errs)
 
 
+@pytest.mark.parametrize("n_kv,B,P", [(16, 2, 300), (32, 1, 1000), (16, 12, 100), (32, 9, 65)])
+def test_layer_decode_other_kv_head_counts(n_kv, B, P):
+    """The layer (RMSNorm, block, residual) with 16 and 32 key/value heads, on
+    both projection paths (B <= 8 GEMV with the fused norm and residual, and
+    B > 8 with the norm pass and the accumulating block)."""
+    from grouped_query_attention_gemv_amd import synth
+    c = DecodeCase(B, P, ((P + 1 + 31) // 32) * 32 + 32, dev=DEV, n_kv=n_kv)
+    g = synth.norm_gain(7)
+    ws = G.layer_workspace(B, 1, c.T_max, DEV, n_kv_heads=n_kv)
+    h = G.layer_decode(c.xd, g.to(DEV), *c.wd, c.kcache, c.vcache, c.rope, P, ws=ws)
+    torch.cuda.synchronize()
+    w = [f64(t) for t in c.w]
+    ref_h, res = O.gqa_layer(f64(c.x)[:, None, :], f64(g), G.NORM_EPS, *w, f64(c.kc_rows),
+                             f64(c.vc_rows), P, n_kv_heads=n_kv)
+    errs = {"h": assert_close("h", f64(h), ref_h[:, 0]),
+            "delta": assert_close("h - x", f64(h) - f64(c.x), res.delta[:, 0])}
+    c.check_untouched()
+    print(f"layer decode n_kv={n_kv} B={B} P={P}", errs)
+
+
+@pytest.mark.parametrize("n_kv,B,start_pos,T", [(16, 2, 0, 70), (32, 1, 64, 100)])
+def test_layer_prefill_other_kv_head_counts(n_kv, B, start_pos, T):
+    """The prefill layer with 16 and 32 key/value heads (also after cached rows)."""
+    from grouped_query_attention_gemv_amd import synth
+    T_max = ((start_pos + T + 31) // 32) * 32 + 32
+    c = PrefillCase(B, T, T_max, dev=DEV, start_pos=start_pos, n_kv=n_kv)
+    g = synth.norm_gain(8)
+    ws = G.layer_workspace(B, T, T_max, DEV, start_pos, n_kv_heads=n_kv)
+    h = G.layer_prefill(c.xd, g.to(DEV), *c.wd, c.kcache, c.vcache, c.rope, start_pos=start_pos,
+                        ws=ws)
+    torch.cuda.synchronize()
+    w = [f64(t) for t in c.w]
+    kc = f64(c.kc_rows) if start_pos else None
+    vc = f64(c.vc_rows) if start_pos else None
+    ref_h, res = O.gqa_layer(f64(c.x), f64(g), G.NORM_EPS, *w, kc, vc, start_pos,
+                             n_kv_heads=n_kv)
+    errs = {"h": assert_close("h", f64(h), ref_h),
+            "delta": assert_close("h - x", f64(h) - f64(c.x), res.delta)}
+    c.check_untouched()
+    print(f"layer prefill n_kv={n_kv} B={B} start_pos={start_pos} T={T}", errs)
+
+
 # The normalised input is rounded to bf16 on both sides, from fp32 on the GPU
 # and from fp64 in the oracle, so an element at a rounding tie may land one
 # bf16 step apart (measured: under 1 in 10^5).  Such a step moves the K/V of
