@@ -138,6 +138,7 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
     # the same steps replayed from a captured HIP graph (8 steps per graph,
     # one per weight set), which removes the host-side launch cost
     graph_us = None
+    graph_spread = None
     if use_graph:
         def capture(n):
             g = torch.cuda.CUDAGraph()
@@ -165,6 +166,15 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
         t1.record()
         torch.cuda.synchronize()
         graph_us = t0.elapsed_time(t1) * 1000.0 / steps
+        # spread: 20 more timings of one 8-step replay each (one step per set)
+        reps = []
+        for _ in range(20):
+            t0.record()
+            g8.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            reps.append(t0.elapsed_time(t1) * 1000.0 / N_SETS)
+        graph_spread = [float(np.percentile(reps, q)) for q in (10, 50, 90)]
 
     # hot-cache figure (not the headline): every step reuses set 0, so its
     # weights and cache stay in the 256 MB Infinity Cache between steps
@@ -187,7 +197,8 @@ def bench_decode(G, synth, steps: int, warmup: int, B=1, P=1000, T_max=1024, use
     # the fused schedule is one kernel: stage 1 covers it, the others are empty
     names = ["decode_step"] if fused else ["qkv", "attn", "wo"]
     return dict(us_step=us_step, wall_us_step=wall * 1e6 / steps, graph_us_step=graph_us,
-                hot_cache_us_step=hot_us, schedule="fused" if fused else "split",
+                hot_cache_us_step=hot_us, graph_spread_us=graph_spread,
+                schedule="fused" if fused else "split",
                 kern_us=dict(zip(names, kern_us.tolist())),
                 profiled_us_step=float(per.sum(axis=1).mean() * 1000.0))
 
@@ -660,6 +671,9 @@ def main():
         # one set reused every step, held by the Infinity Cache: not the headline
         "hot_cache_us_step": (round(dec["hot_cache_us_step"], 3)
                               if dec["hot_cache_us_step"] is not None else None),
+        # p10 / median / p90 of 20 separately timed 8-step replays (per step)
+        "us_step_p10_p50_p90": ([round(v, 3) for v in dec["graph_spread_us"]]
+                                if dec["graph_spread_us"] is not None else None),
         "algorithmic_bytes_per_step": nb["step"],
         "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
         "profiled_us_step": round(dec["profiled_us_step"], 3),
