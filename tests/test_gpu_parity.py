@@ -127,6 +127,17 @@ def test_decode_batched_b64_p8192_sampled():
     c.check_untouched()
 
 
+def test_decode_batched_mha_b64_p8192_sampled():
+    """The multi-head variant (32 key/value heads) at the batched bench size:
+    B=64, 8,192 cached positions (caches ~8.6 GiB); sampled sequences against
+    the oracle, every cache bit outside row 8,192 unchanged."""
+    c = DecodeCase(64, 8192, 8224, dev=DEV, cache_on_device=True, n_kv=32)
+    c.run()
+    seqs = [0, 31, 63]
+    c.check(c.oracle(seqs), seqs)
+    c.check_untouched()
+
+
 def test_decode_long_context_p131071_sampled():
     """One block at the long-context point: B=8 sequences with 131,071 cached
     positions each (2 GiB per cache tensor), row 131,071 written; sampled
