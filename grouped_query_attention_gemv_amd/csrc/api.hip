@@ -199,6 +199,12 @@ int layer_prologue(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, 
   return GQA_OK;
 }
 
+// Zeroes the GQA_SYNC_BYTES synchronisation region, 16 bytes per thread.
+__global__ void __launch_bounds__(256) zero_sync_kernel(u32x4* sync) {
+  sync[(size_t)blockIdx.x * 256 + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+}
+static_assert(GQA_SYNC_BYTES % (16 * 256) == 0, "sync region is a whole number of fill blocks");
+
 }  // namespace
 
 extern "C" {
@@ -232,7 +238,11 @@ int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!aligned16(ws)) return GQA_ERR_ALIGN;
   if (ws_bytes < (size_t)GQA_SYNC_BYTES) return GQA_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return hip_status(hipMemsetAsync(ws, 0, GQA_SYNC_BYTES, stream));
+  // a fill kernel rather than hipMemsetAsync, so the call can also sit in a
+  // captured graph
+  hipLaunchKernelGGL(zero_sync_kernel, dim3(GQA_SYNC_BYTES / 16 / 256), dim3(256), 0, stream,
+                     static_cast<u32x4*>(ws));
+  return hip_status(hipGetLastError());
 }
 
 int gqa_set_decode_schedule(int schedule) {

@@ -150,7 +150,7 @@ size_t gqa_workspace_bytes_kv(int B, int start_pos, int T, int T_max, int n_kv_h
 
 /*
  * gqa_workspace_init -- zero the synchronisation words of a workspace of
- * ws_bytes bytes (one hipMemsetAsync on stream, not to be captured in a graph).
+ * ws_bytes bytes (one small fill kernel on stream; no host synchronisation).
  * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (< GQA_SYNC_BYTES),
  * GQA_ERR_HIP.
  */
