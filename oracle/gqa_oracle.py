@@ -296,7 +296,8 @@ def gqa_block(x, wq, wk, wv, wo, k_cached, v_cached, start_pos: int,
 
 
 def stacked_decode(x_bits_first, weights, k_cached_list, v_cached_list, start_pos: int,
-                   theta: float = ROPE_THETA, scaled: bool = True):
+                   theta: float = ROPE_THETA, scaled: bool = True,
+                   n_heads: int = N_HEADS, n_kv_heads: int = N_KV_HEADS):
     """Decode one token through a stack of attention blocks with the residual
     stream h_{l+1} = h_l + Delta_l(bf16(h_l)) and no norms or FFN (the layer
     loop of page "Vocabulary projection" and the block residual of evidence
@@ -311,7 +312,8 @@ def stacked_decode(x_bits_first, weights, k_cached_list, v_cached_list, start_po
     deltas = []
     for (wq, wk, wv, wo), kc, vc in zip(weights, k_cached_list, v_cached_list):
         x_in = f64_from_bf16_bits(bf16_bits_from_f64(h))
-        res = gqa_block(x_in[:, None, :], wq, wk, wv, wo, kc, vc, start_pos, theta, scaled)
+        res = gqa_block(x_in[:, None, :], wq, wk, wv, wo, kc, vc, start_pos, theta, scaled,
+                        n_heads, n_kv_heads)
         d = res.delta[:, 0, :]
         deltas.append(d)
         h = h + d

@@ -358,25 +358,77 @@ def test_decode_after_prefill_equals_longer_prefill():
     assert np.max(np.abs(pre.delta - full.delta[:, :T])) < 1e-12       # causal: later tokens unseen
 
 
-def test_stacked_decode_residual():
-    """Two stacked blocks: h2 = h0 + D0(bf16 h0) + D1(bf16 h1), block by block."""
+def test_stacked_decode_hand_computed_chain():
+    """Three stacked blocks at position 0 (one key, so every softmax is [1]
+    and O is the appended V row of the head's kv head), with one-hot input and
+    small-integer weights: every value is exact and the residual stream was
+    worked out by hand.  d = 8, 2 query heads sharing 1 kv head of width 4.
+
+      x0 = e_0
+      block 0: v = (1, 5, -2, 256) from column 0 of wv;  O = (v, v);
+               wo reverses the features: D0 = (256, -2, 5, 1, 256, -2, 5, 1)
+               h1 = (257, -2, 5, 1, 256, -2, 5, 1)
+      block 1 reads bf16(h1) = (256, -2, 5, 1, 256, -2, 5, 1) (257 is a tie
+               of 256 and 258 and goes to even):
+               v = (3*256, 3*5, -1*1, 2*(-2)) = (768, 15, -1, -4)
+               (768, not the 772 that the unrounded 257 would give)
+               D1 = (O[6], -O[0], 0, 0, 0, 2*O[1], 0, O[3])
+                  = (-1, -768, 0, 0, 0, 30, 0, -4)
+               h2 = (256, -770, 5, 1, 256, 28, 5, -3)   (the stream keeps -770)
+      block 2 reads bf16(h2); v = (0, 0, h2[5], 0) = (0, 0, 28, 0); O[6] is
+               head 1's copy of v[2]; D2 = (0, 0, O[6], 0, ...) = 28 at [2]
+               h3 = (256, -770, 33, 1, 256, 28, 5, -3)
+
+    A dropped residual, an unrounded block input, a transposed wv or wo, or a
+    head expanded from the wrong kv head changes h3."""
+    d, H, KV, hd = 8, 2, 1, 4
+    rng = np.random.default_rng(14)
+    x0 = np.zeros((1, d))
+    x0[0, 0] = 1.0
+
+    def block(wv_entries, wo_entries):
+        wq = _bf16_vals(rng, (H * hd, d), 0.5)       # irrelevant with one key
+        wk = _bf16_vals(rng, (KV * hd, d), 0.5)
+        wv = np.zeros((KV * hd, d))
+        for (r, c), val in wv_entries.items():
+            wv[r, c] = val
+        wo = np.zeros((d, H * hd))
+        for (r, c), val in wo_entries.items():
+            wo[r, c] = val
+        return wq, wk, wv, wo
+
+    blocks = [
+        block({(0, 0): 1, (1, 0): 5, (2, 0): -2, (3, 0): 256},
+              {(i, 7 - i): 1 for i in range(8)}),
+        block({(0, 0): 3, (1, 2): 3, (2, 7): -1, (3, 5): 2},
+              {(0, 6): 1, (1, 0): -1, (5, 1): 2, (7, 3): 1}),
+        block({(2, 5): 1}, {(2, 6): 1}),
+    ]
+    empty = [np.zeros((1, 0, KV, hd))] * 3
+    h, deltas = O.stacked_decode(x0, blocks, empty, empty, 0, n_heads=H, n_kv_heads=KV)
+    assert np.array_equal(deltas[0][0], [256, -2, 5, 1, 256, -2, 5, 1])
+    assert np.array_equal(deltas[1][0], [-1, -768, 0, 0, 0, 30, 0, -4])
+    assert np.array_equal(deltas[2][0], [0, 0, 28, 0, 0, 0, 0, 0])
+    assert np.array_equal(h[0], [256, -770, 33, 1, 256, 28, 5, -3])
+
+
+def test_stacked_decode_with_zero_output_projections_keeps_the_input():
+    """Real shapes, cached rows and RoPE at position 3: with every wo = 0 each
+    block's update is exactly zero, so the residual stream leaves the stack
+    bit for bit equal to its input (and every Delta is zero)."""
     rng = np.random.default_rng(13)
-    d, H, KV = 4096, 32, 8
-    hd = 128
-    B, sp = 1, 2
+    d, KV, hd = 4096, 8, 128
+    B, sp = 2, 3
     x = _bf16_vals(rng, (B, d), 1.0)
     ws, kcs, vcs = [], [], []
-    for _ in range(2):
+    for _ in range(3):
         ws.append((_bf16_vals(rng, (d, d), 0.02), _bf16_vals(rng, (KV * hd, d), 0.02),
-                   _bf16_vals(rng, (KV * hd, d), 0.02), _bf16_vals(rng, (d, d), 0.02)))
+                   _bf16_vals(rng, (KV * hd, d), 0.02), np.zeros((d, d))))
         kcs.append(_bf16_vals(rng, (B, sp, KV, hd), 1.0))
         vcs.append(_bf16_vals(rng, (B, sp, KV, hd), 1.0))
     h, deltas = O.stacked_decode(x, ws, kcs, vcs, sp)
-    r0 = O.gqa_block(x[:, None], *ws[0], kcs[0], vcs[0], sp)
-    h1 = x + r0.delta[:, 0]
-    x1 = O.f64_from_bf16_bits(O.bf16_bits_from_f64(h1))
-    r1 = O.gqa_block(x1[:, None], *ws[1], kcs[1], vcs[1], sp)
-    assert np.max(np.abs(h - (h1 + r1.delta[:, 0]))) < 1e-12
+    assert np.array_equal(h, x)
+    assert all(not np.any(dl) for dl in deltas)
 
 
 def test_rms_norm_matches_torch_rms_norm():
