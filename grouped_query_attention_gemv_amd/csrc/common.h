@@ -62,6 +62,23 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// v clamped to fp16's finite range: values that would round to infinity
+// (|v| >= 65520) become +-65504 and set *sat; NaN stays NaN.
+__device__ __forceinline__ float sat_f16(float v, bool& sat) {
+  const bool big = fabsf(v) >= 65520.f;
+  sat |= big;
+  return big ? copysignf(65504.f, v) : v;
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b, bool& sat) {
+  return pack_f16x2(sat_f16(a, sat), sat_f16(b, sat));
+}
+
+// bf16 pair (packed) -> fp16 pair (packed), saturating.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_sat(uint32_t u, bool& sat) {
+  return pack_f16x2_sat(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16), sat);
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane
 // ---------------------------------------------------------------------------
@@ -157,14 +174,13 @@ __device__ __forceinline__ u32x4 ld_dev_x4(const void* base, uint32_t byte_off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
 }
 
-// Loads through the XCD's L2 (sc0 policy, base wave-uniform).  Measured on
-// this chip: plain stores go through to the device-wide coherence point but
-// do not refresh a copy that an L2 already holds, so such a load sees another
-// workgroup's completed store only if its XCD has not cached the line since
-// the kernel started (the caches are invalidated at every kernel start).  The
-// one-launch decode uses them for data that is first read after a
-// device-scope wait on its producers; the other readers of the same XCD then
-// hit the L2 line the first one brought in.
+// Loads through the XCD's L2 (sc0 policy, base wave-uniform).  A store of
+// another XCD does not refresh a copy that this L2 already holds, so such a
+// load sees another workgroup's completed device-scope store only if its XCD
+// has not cached the line since the kernel started (the caches are
+// invalidated at every kernel start).  The one-launch decode uses them for
+// data that is first read after a device-scope wait on its producers; the
+// other readers of the same XCD then hit the L2 line the first one brought in.
 __device__ __forceinline__ uint32_t ld_xcd(const void* base, uint32_t byte_off) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
@@ -177,6 +193,12 @@ __device__ __forceinline__ u32x4 ld_xcd_x4(const void* base, uint32_t byte_off) 
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 1));
+}
+
+// XCD (XCC) the calling wave runs on, read from the hardware register
+// HW_REG_XCC_ID (bits 3:0).
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u);
 }
 
 // Wait until every memory access this wave has issued has completed (stores

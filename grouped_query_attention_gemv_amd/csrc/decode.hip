@@ -95,7 +95,15 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
       *reinterpret_cast<float2*>(p.probe + (size_t)b * kNqkv + r0) = make_float2(v0, v1);
     }
     if (r0 < D) {
-      *reinterpret_cast<float2*>(p.q + (size_t)b * D + r0) = make_float2(v0, v1);
+      float* qd = p.q + (size_t)b * D + r0;
+      if (FUSED) {
+        // read by attention workgroups of this launch: written through to the
+        // device-wide coherence point
+        st_dev(qd, v0);
+        st_dev(qd + 1, v1);
+      } else {
+        *reinterpret_cast<float2*>(qd) = make_float2(v0, v1);
+      }
     } else {
       const int g = rr / HD, d = rr % HD;
       const uint32_t pair = pack_bf16x2(v0, v1);
@@ -108,7 +116,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
         dst[VB] = (uint16_t)(pair >> 16);
       }
       // the attention workgroups of the same launch read the new row from here
-      if (FUSED) p.kv_new[((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2] = pair;
+      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2, pair);
     }
   }
 
@@ -151,6 +159,12 @@ __global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0)
 // In the fused schedule the workgroup loads its first tiles before Q exists,
 // waits for its kv head's release, then replaces the row of position
 // start_pos (which the same launch writes) with the copy in kv_new.
+// Floats of split partials per (sequence, kv head): nsplit splits of nr
+// heads, rounded up to whole 128-byte lines.
+__host__ __device__ constexpr size_t part_region_floats(int nsplit, int nr) {
+  return ((size_t)nsplit * nr * kPartStride + 31) / 32 * 32;
+}
+
 // LDS of the 4-wave merge for n_rep query heads per kv head
 constexpr int attn_lds_words(int rep) { return kAttnWaves * rep * HD + 2 * kAttnWaves * rep + 1; }
 constexpr int kAttnLdsWords = attn_lds_words(REP);
@@ -210,6 +224,16 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
   };
 
+  // Fused schedule: data produced by other workgroups of this launch (Q, the
+  // new row, split partials) is published with device-scope stores that have
+  // completed before the producer signals, and is first read on any XCD only
+  // after the consumer's device-scope wait on that signal (no line holds data
+  // of two kv heads or two (sequence, head) partial sets).  An L2 that never
+  // held the line since the kernel started (L2 lines are invalidated at every
+  // kernel start) fetches the published value, so the reads go through this
+  // XCD's L2 (ld_xcd, sc0) wherever the workgroup runs; when a head's
+  // workgroups share an XCD, the readers after the first hit the line there.
+
   // Fused schedule: replace the appended row (position start_pos, written by
   // this launch) with the device-scope copy in kv_new, for the lanes that
   // hold it.
@@ -253,27 +277,50 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // counted themselves (each after its stores landed), count this workgroup
   // too (the last of the head's nsplit*B attention workgroups rearms the
   // counter at its end), then read Q and the appended row in one round trip.
+  // A workspace without gqa_workspace_init's magic word holds no valid
+  // counters: the workgroup records the error and stops (the wo workgroups
+  // see the same and write NaN).  A wait that times out records its error
+  // and poisons this workgroup's Q with NaN, so that Delta turns NaN.
   int* grp_cnt = p.sync + kSyncGroup + 32 * g;
   int grp_prev = 0;
   u32x4 qraw[8];
   if (FUSED) {
     if (tid == 0) {
-      int polls = 0;
-      while (ld_dev(grp_cnt) < 96) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++polls > kMaxPolls) {
-          __hip_atomic_fetch_or(p.sync + kSyncErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+      int state = 0;
+      if (p.sync[kSyncMagic] != kWsMagic) {
+        __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        state = 2;
+      } else {
+        int polls = 0;
+        while (ld_dev(grp_cnt) < 96) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++polls > kMaxPolls) {
+            __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            state = 1;
+            break;
+          }
         }
+        grp_prev = __hip_atomic_fetch_add(grp_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // placement diagnostic, once per launch: the first attention workgroup
+        // counts the launch if the dispatcher put it away from XCD g (then
+        // the head's workgroups do not share an L2; results are unaffected)
+        if (blk == 0 && xcc_id() != g)
+          __hip_atomic_fetch_add(p.sync + kSyncOffHome, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      grp_prev = __hip_atomic_fetch_add(grp_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *sm_last = state;
     }
     __syncthreads();
+    const int state = *sm_last;
+    if (state == 2) return;
     const uint32_t qoff = (uint32_t)((b * D + (g * REP + head) * HD + rg * 8) * 4);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       qraw[2 * ks] = ld_xcd_x4(p.q, qoff + ks * 128);
       qraw[2 * ks + 1] = ld_xcd_x4(p.q, qoff + ks * 128 + 16);
+    }
+    if (state == 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qraw[i] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     }
     if (tile < j_end) patch_tile(tile, kf, vf);
   }
@@ -461,32 +508,26 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     return;
   }
 
-  // Publish this split's partial, wait for the stores to land, then count
-  // it; the last workgroup to arrive merges every partial.  Three-launch
-  // schedule: device-scope stores (through to the coherence point shared by
-  // all XCDs, without an L2 write-back).  Fused: every split of the head runs
-  // on one XCD, so plain stores into its L2 and loads from there.  Counters
-  // always live at the device-wide coherence point (atomics are performed
-  // there, and the waits poll it with device-scope loads).
+  // Publish this split's partial with device-scope stores (through to the
+  // coherence point shared by all XCDs, without an L2 write-back), wait for
+  // them to land, then count it; the last workgroup to arrive merges every
+  // partial.  Fused: the merging workgroup reads them through its XCD's L2
+  // (first read of those lines after its wait, as for Q above).
+  // Counters always live at the device-wide coherence point (atomics are
+  // performed there, and the waits poll it with device-scope loads).  Each
+  // (sequence, kv head) owns a whole number of 128-byte lines of partials.
   const size_t split_stride = (size_t)NR * kPartStride;
-  float* part0 = p.part + ((size_t)(b * KV + g) * p.nsplit) * split_stride + (size_t)mhc * kPartStride;
+  float* part0 = p.part + (size_t)(b * KV + g) * part_region_floats(p.nsplit, NR) +
+                 (size_t)mhc * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
   int* split_cnt = p.counters + b * KV + g;
   if (merges) {
-    if (FUSED) {
-      if (d2 == 0) {
-        mine[0] = M;
-        mine[1] = lsum;
-      }
-      *reinterpret_cast<float2*>(mine + 4 + d2) = make_float2(o0, o1);
-    } else {
-      if (d2 == 0) {
-        st_dev(mine, M);
-        st_dev(mine + 1, lsum);
-      }
-      st_dev(mine + 4 + d2, o0);
-      st_dev(mine + 5 + d2, o1);
+    if (d2 == 0) {
+      st_dev(mine, M);
+      st_dev(mine + 1, lsum);
     }
+    st_dev(mine + 4 + d2, o0);
+    st_dev(mine + 5 + d2, o1);
   }
   wait_vm();
   __syncthreads();
@@ -565,24 +606,44 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
     while (__builtin_amdgcn_s_memrealtime() - t0 < kWoHoldTicks) __builtin_amdgcn_s_sleep(8);
   }
   load_rows2(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, lane, wa, wb);
+  // fused: 0 normal, 1 the wait timed out, 2 the workspace is uninitialised;
+  // in either error case this workgroup's outputs are NaN
+  __shared__ int wo_state;
   if (FUSED) {
     // wave 0 waits until every (b, g) has published O, one word per lane
     if (wave == 0) {
-      int* slot = p.sync + kSyncWoSlot + 16 * blk;
-      const int nwords = p.B * KVH;
-      int polls = 0;
-      while (true) {
-        const int v = lane < nwords ? ld_dev(slot + lane) : 1;
-        if (__all(v == 1)) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (++polls > kMaxPolls) {
-          if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+      int state = 0;
+      if (p.sync[kSyncMagic] != kWsMagic) {
+        if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        state = 2;
+      } else {
+        int* slot = p.sync + kSyncWoSlot + 16 * blk;
+        const int nwords = p.B * KVH;
+        int polls = 0;
+        while (true) {
+          const int v = lane < nwords ? ld_dev(slot + lane) : 1;
+          if (__all(v == 1)) break;
+          __builtin_amdgcn_s_sleep(1);
+          if (++polls > kMaxPolls) {
+            if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WO_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            state = 1;
+            break;
+          }
         }
+        if (lane < nwords) st_dev(slot + lane, 0);
       }
-      if (lane < nwords) st_dev(slot + lane, 0);
+      if (lane == 0) wo_state = state;
     }
     __syncthreads();
+    if (wo_state == 2) {
+      // no O to read: NaN outputs, the error word says why
+      if (lane < NB) {
+        const float nan = __uint_as_float(0x7fc00000u);
+        *reinterpret_cast<float2*>(p.out + (size_t)(b0 + lane) * D + r0) = make_float2(nan, nan);
+        if (p.out_bf16) *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)(b0 + lane) * D + r0) = 0x7fc07fc0u;
+      }
+      return;
+    }
     // every load goes out before the first LDS write (one round trip); no
     // workgroup reads O before all of it is complete, so the first reader on
     // each XCD fetches a line into its L2 and the rest of the XCD's wo
@@ -629,6 +690,7 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
     r.x += bf16_bits_to_f32(xr & 0xffffu);
     r.y += bf16_bits_to_f32(xr >> 16);
   }
+  if (FUSED && wo_state == 1) r = make_float2(__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u));
   *o = r;
   if (p.out_bf16)
     *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
@@ -761,6 +823,19 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
   const int ks = blockIdx.x % kP2KS, fb = blockIdx.x / kP2KS;
   const int ncols = min(kP2Cols, p.B - c_base);
   const int kbase = ks * kP2Kr;
+  if (p.sync[kSyncMagic] != kWsMagic) {
+    // uninitialised workspace: the split-K counters cannot be trusted; the
+    // error word says so and the output projection writes NaN
+    if (tid == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (MODE == 1 && ks == 0) {
+      for (int i = tid; i < ncols * kP2Feat; i += 256) {
+        const size_t o = (size_t)(c_base + i / kP2Feat) * D + fb * kP2Feat + i % kP2Feat;
+        p.out[o] = __uint_as_float(0x7fc00000u);
+        if (p.out_bf16) p.out_bf16[o] = 0x7fc0u;
+      }
+    }
+    return;
+  }
   if (MODE == 0 && blockIdx.x == 0 && c_base == 0) {
     // the attention kernel that follows counts split arrivals from zero
     for (int i = tid; i < p.B * KV; i += blockDim.x) p.counters[i] = 0;
@@ -973,28 +1048,27 @@ static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Partials: the attention splits' (m, l, o), and for B > 8 also the split-K
 // partials of the projections (the two never live at the same time), sized
 // for the most key/value heads.
-static size_t decode_part_bytes(int B) {
-  // the largest over the kv-head counts is the GQA one (more heads per split)
-  size_t n = (size_t)B * KVH * decode_max_split(B, KVH) * REP * kPartStride * 4;
+static size_t decode_part_bytes(int B, int kv) {
+  size_t n = (size_t)B * kv * part_region_floats(decode_max_split(B, kv), H / kv) * 4;
   if (B > kGemvMaxB) {
-    const size_t qkv = (size_t)(D + 2 * kMaxKv * HD) * p2_splits<0>() * kP2Cols * 4;
+    const size_t qkv = (size_t)(D + 2 * kv * HD) * p2_splits<0>() * kP2Cols * 4;
     const size_t wo = (size_t)D * p2_splits<1>() * kP2Cols * 4;
     n = std::max(n, std::max(qkv, wo));
   }
   return n;
 }
 
-size_t decode_ws_bytes(int B) {
+size_t decode_ws_bytes(int B, int kv) {
   size_t n = kSyncBytes;
   n += align256((size_t)B * D * 4);                       // q
   n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
-  n += align256((size_t)B * kMaxKv * 4);                  // counters
-  n += align256(decode_part_bytes(B));                   // partials
-  n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new
+  n += align256((size_t)B * kv * 4);                      // counters
+  n += align256(decode_part_bytes(B, kv));               // partials
+  n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new (fused schedule, 8 heads)
   return n;
 }
 
-void decode_ws_carve(void* ws, int B, DecodeParams* p) {
+void decode_ws_carve(void* ws, int B, int kv, DecodeParams* p) {
   char* c = static_cast<char*>(ws);
   p->sync = reinterpret_cast<int*>(c);
   c += kSyncBytes;
@@ -1005,9 +1079,9 @@ void decode_ws_carve(void* ws, int B, DecodeParams* p) {
   p->o_lo = reinterpret_cast<uint16_t*>(c);
   c += align256((size_t)B * D * 2);
   p->counters = reinterpret_cast<int*>(c);
-  c += align256((size_t)B * kMaxKv * 4);
+  c += align256((size_t)B * kv * 4);
   p->part = reinterpret_cast<float*>(c);
-  c += align256(decode_part_bytes(B));
+  c += align256(decode_part_bytes(B, kv));
   p->kv_new = reinterpret_cast<uint32_t*>(c);
 }
 

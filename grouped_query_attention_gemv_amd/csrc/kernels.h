@@ -25,7 +25,11 @@ constexpr int kWoMaxNB = 4;          // tokens per pass of the wo GEMV (hi + lo 
 // They must be zero before the first decode call on a workspace; every call
 // leaves them zero, and prefill never touches them.  Offsets are in ints.
 constexpr int kSyncBytes = 64 * 1024;
-constexpr int kSyncErr = 0;          // sticky error bits: 1 attention wait, 2 wo wait timed out
+constexpr int kSyncErr = 0;          // sticky error bits (GQA_WS_ERR_*)
+constexpr int kSyncMagic = 1;        // kWsMagic once gqa_workspace_init has run
+constexpr int kSyncOffHome = 2;      // fused launches whose first attention workgroup ran
+                                     // away from its kv head's XCD (diagnostic)
+constexpr int kWsMagic = 0x31415147; // "GQA1"
 constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups of kv head g
 constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
 constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
@@ -82,8 +86,8 @@ struct DecodeParams {
 constexpr int kMaxKv = 32;           // most kv heads (n_rep 1)
 void decode_split(int B, int L, int kv, int* nsplit, int* chunk);
 int decode_max_split(int B, int kv);
-size_t decode_ws_bytes(int B);
-void decode_ws_carve(void* ws, int B, DecodeParams* p);
+size_t decode_ws_bytes(int B, int kv);
+void decode_ws_carve(void* ws, int B, int kv, DecodeParams* p);
 
 hipError_t launch_rope_table(float* rope, int T_max, double theta, int scaled, hipStream_t s);
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s);
@@ -114,8 +118,10 @@ struct PrefillParams {
   int start_pos;            // cached rows 0 .. start_pos-1 precede them
   int accumulate;           // out += Delta instead of out = Delta
   int Tp;                   // start_pos + T rounded up to the attention tile
+  int convert_wo;           // the prep kernel converts wo into wo16 (no caller copy)
+  int* err;                 // the workspace's error word (GQA_WS_ERR_FP16_RANGE)
   // workspace
-  uint16_t* wo16;           // [4096][4096] fp16 copy of wo
+  uint16_t* wo16;           // [4096][4096] fp16 copy of wo (the workspace's, or the caller's)
   uint16_t* q16;            // [M][4096] fp16 Q * log2(e)/sqrt(128)
   uint16_t* k16;            // [B][kv][Tp][128] fp16 copy of keys 0 .. start_pos+T-1
   uint16_t* v16t;           // [B][kv][Tp/64][128][64] fp16 copy of the values
@@ -127,7 +133,8 @@ constexpr int kPrefillTile = 64;     // query and key tile of the prefill attent
 size_t prefill_ws_bytes(int B, int start_pos, int T, int kv = KVH);
 void prefill_ws_carve(void* ws, PrefillParams* p);   // reads B, T, Tp, kv
 
-hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_prep(const PrefillParams& p, hipStream_t s);
+hipError_t launch_wo_to_fp16(const uint16_t* wo, uint16_t* wo16, hipStream_t s);
 hipError_t launch_prefill_qkv(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s);

@@ -20,8 +20,12 @@
 //
 // Precision: the GEMM inputs x and W are bf16 already, products are exact and
 // sums are fp32.  Attention and wo use fp16 operands: the cached K/V values
-// are bf16 and convert to fp16 exactly (except fp16-subnormal magnitudes),
-// while Q, P and O gain 3 significant bits over bf16.
+// and Wo are bf16 and convert to fp16 exactly inside fp16's normal range
+// (2^-14 <= |v| <= 65504; smaller magnitudes lose low bits as fp16
+// subnormals), while Q, P and O gain 3 significant bits over bf16.  A value
+// beyond 65504, which bf16 can hold, is saturated to +-65504 and flagged in
+// the workspace's error word (GQA_WS_ERR_FP16_RANGE) instead of becoming
+// infinite.
 #include <math.h>
 
 #include <type_traits>
@@ -47,7 +51,7 @@ static size_t prefill_key_rows(int start_pos, int T) {
 size_t prefill_ws_bytes(int B, int start_pos, int T, int kv) {
   const size_t M = (size_t)B * T;
   const size_t Tp = prefill_key_rows(start_pos, T);
-  size_t n = kSyncBytes;                            // decode's synchronisation words, untouched
+  size_t n = kSyncBytes;                            // error word; decode's synchronisation words
   n += align256((size_t)D * D * 2);                 // wo16
   n += align256(M * D * 2);                         // q16
   n += align256((size_t)B * kv * Tp * HD * 2);      // k16
@@ -59,6 +63,7 @@ size_t prefill_ws_bytes(int B, int start_pos, int T, int kv) {
 void prefill_ws_carve(void* ws, PrefillParams* p) {
   const size_t M = (size_t)p->B * p->T;
   const size_t Tp = (size_t)p->Tp;
+  p->err = static_cast<int*>(ws);   // the error word heads the workspace
   char* c = static_cast<char*>(ws) + kSyncBytes;
   p->wo16 = reinterpret_cast<uint16_t*>(c);
   c += align256((size_t)D * D * 2);
@@ -72,27 +77,40 @@ void prefill_ws_carve(void* ws, PrefillParams* p) {
 }
 
 // ---------------------------------------------------------------------------
-// wo -> fp16
+// Operand preparation: wo -> fp16, cached rows -> fp16 copies
 // ---------------------------------------------------------------------------
 
-// Converts wo to fp16, copies the cached rows 0 .. start_pos-1 of K and V
-// into the fp16 attention copies (bf16 -> fp16 is exact but for magnitudes
-// below fp16's normal range), and clears the positions [start_pos+T, Tp) of
-// both copies (the attention tiles read them; they must be finite).
+// wo16 = fp16(wo) over threads tid0, tid0 + stride, ... (8 values each);
+// returns whether any value saturated.
+__device__ __forceinline__ bool convert_wo_part(const uint16_t* __restrict__ wo,
+                                                uint16_t* __restrict__ wo16, long tid0,
+                                                long stride) {
+  bool sat = false;
+  const long n8 = (long)D * D / 8;
+  for (long i = tid0; i < n8; i += stride) {
+    const u32x4 v = ld_nt_u32x4(wo + (size_t)i * 8);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = bf16x2_to_f16x2_sat(v[q], sat);
+    *reinterpret_cast<u32x4*>(wo16 + (size_t)i * 8) = o;
+  }
+  return sat;
+}
+
+__global__ void __launch_bounds__(256) wo_to_fp16_kernel(const uint16_t* wo, uint16_t* wo16) {
+  (void)convert_wo_part(wo, wo16, (long)blockIdx.x * 256 + threadIdx.x, (long)gridDim.x * 256);
+}
+
+// Converts wo to fp16 (unless the caller passed its own copy), copies the
+// cached rows 0 .. start_pos-1 of K and V into the fp16 attention copies
+// (bf16 -> fp16 is exact inside fp16's normal range and saturates beyond
+// it), and clears the positions [start_pos+T, Tp) of both copies (the
+// attention tiles read them; they must be finite).
 __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
   const long stride = (long)gridDim.x * 256;
   const long tid0 = (long)blockIdx.x * 256 + threadIdx.x;
-  const int n8 = D * D / 8;
-  for (long i = tid0; i < n8; i += stride) {
-    const u32x4 v = ld_nt_u32x4(p.wo + (size_t)i * 8);
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t u = v[q];
-      o[q] = pack_f16x2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
-    }
-    *reinterpret_cast<u32x4*>(p.wo16 + (size_t)i * 8) = o;
-  }
+  bool sat = false;
+  if (p.convert_wo) sat = convert_wo_part(p.wo, p.wo16, tid0, stride);
   const int kv = p.kv;
   const int pairs = p.B * kv;
   const int nblk = p.Tp / AK;
@@ -108,8 +126,7 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(p.kcache + ((size_t)pair * p.T_max + t) * HD + d);
       u32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = pack_f16x2(bf16_bits_to_f32(v[q] & 0xffffu), bf16_bits_to_f32(v[q] >> 16));
+      for (int q = 0; q < 4; ++q) o[q] = bf16x2_to_f16x2_sat(v[q], sat);
       *reinterpret_cast<u32x4*>(p.k16 + ((size_t)pair * p.Tp + t) * HD + d) = o;
     }
     const int groups = (sp + 7) / 8;
@@ -124,17 +141,17 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(p.vcache + vcache_index(b, g, t0, d, p.T_max, kv));
         u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = pack_f16x2(bf16_bits_to_f32(v[q] & 0xffffu), bf16_bits_to_f32(v[q] >> 16));
+        for (int q = 0; q < 4; ++q) o[q] = bf16x2_to_f16x2_sat(v[q], sat);
         *reinterpret_cast<u32x4*>(dst) = o;
       } else {
         for (int t = t0; t < sp; ++t) {
-          const _Float16 h = (_Float16)bf16_bits_to_f32(p.vcache[vcache_index(b, g, t, d, p.T_max, kv)]);
-          dst[t - t0] = __builtin_bit_cast(uint16_t, h);
+          const float f = sat_f16(bf16_bits_to_f32(p.vcache[vcache_index(b, g, t, d, p.T_max, kv)]), sat);
+          dst[t - t0] = __builtin_bit_cast(uint16_t, (_Float16)f);
         }
       }
     }
   }
+  if (sat) __hip_atomic_fetch_or(p.err, GQA_WS_ERR_FP16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int lo = sp + p.T;
   const int pad = p.Tp - lo;
   if (pad == 0) return;
@@ -155,8 +172,13 @@ __global__ void __launch_bounds__(256) prefill_prep_kernel(PrefillParams p) {
   }
 }
 
-hipError_t launch_convert_wo(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_prefill_prep(const PrefillParams& p, hipStream_t s) {
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(2048), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_wo_to_fp16(const uint16_t* wo, uint16_t* wo16, hipStream_t s) {
+  hipLaunchKernelGGL(wo_to_fp16_kernel, dim3(2048), dim3(256), 0, s, wo, wo16);
   return hipGetLastError();
 }
 
@@ -425,6 +447,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
   const PrefillParams& p = g.p;
   const int T = p.T;
   const int mh = mw + 64 * HALF;
+  bool sat = false;                 // an fp16 copy saturated
   if (HALF) lds_drain();            // the previous half's reads have returned
   if (REGION < 2) {
     const int k = lane & 7;         // 8-feature chunk of the row
@@ -465,7 +488,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
       if (REGION == 0) {
         u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * kScoreLog2, v[2 * j + 1] * kScoreLog2);
+        for (int j = 0; j < 4; ++j)
+          o[j] = pack_f16x2_sat(v[2 * j] * kScoreLog2, v[2 * j + 1] * kScoreLog2, sat);
         *reinterpret_cast<u32x4*>(p.q16 + (size_t)m * D + f) = o;
       } else {
         const int b = m / T, t = p.start_pos + m - b * T;
@@ -474,7 +498,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-          kh[j] = pack_f16x2(bf16_bits_to_f32(kb[j] & 0xffffu), bf16_bits_to_f32(kb[j] >> 16));
+          kh[j] = bf16x2_to_f16x2_sat(kb[j], sat);
         }
         *reinterpret_cast<u32x4*>(p.kcache + ((size_t)(b * p.kv + gg) * p.T_max + t) * HD + d) = kb;
         *reinterpret_cast<u32x4*>(p.k16 + ((size_t)(b * p.kv + gg) * p.Tp + t) * HD + d) = kh;
@@ -507,7 +531,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           vb[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-          vh[j] = pack_f16x2(bf16_bits_to_f32(vb[j] & 0xffffu), bf16_bits_to_f32(vb[j] >> 16));
+          vh[j] = bf16x2_to_f16x2_sat(vb[j], sat);
         }
         *reinterpret_cast<u32x4*>(p.vcache + vcache_index(b, gg, t, d, p.T_max, p.kv)) = vb;
         *reinterpret_cast<u32x4*>(
@@ -520,13 +544,14 @@ __device__ __forceinline__ void qkv_epilogue(const GemmArgs& g, const f32x4 (&ac
           const int b = m / T, t = p.start_pos + m - b * T;
           const uint32_t vb = f32_to_bf16_bits(v[e]);
           p.vcache[vcache_index(b, gg, t, d, p.T_max, p.kv)] = (uint16_t)vb;
-          const _Float16 h = (_Float16)bf16_bits_to_f32(vb);
+          const _Float16 h = (_Float16)sat_f16(bf16_bits_to_f32(vb), sat);
           p.v16t[(((size_t)(b * p.kv + gg) * (p.Tp / AK) + t / AK) * HD + d) * AK + t % AK] =
               __builtin_bit_cast(uint16_t, h);
         }
       }
     }
   }
+  if (sat) __hip_atomic_fetch_or(p.err, GQA_WS_ERR_FP16_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // wo epilogue: fp32 rows of Delta (added to out when accumulating), one

@@ -25,6 +25,14 @@ DECODE_STAGES = 3
 PREFILL_STAGES = 4
 SYNC_BYTES = 65536
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
+OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE = 0, 1, 2, 3
+# bits of the workspace error word
+WS_ERR_WAIT, WS_ERR_WO_WAIT, WS_ERR_INIT, WS_ERR_FP16_RANGE = 0x1, 0x2, 0x4, 0x100
+WS_MAGIC = 0x31415147
+
+# With GQA_DEBUG=1 in the environment every block and layer call synchronises
+# and raises if its workspace's error word is nonzero.
+DEBUG = os.environ.get("GQA_DEBUG", "") == "1"
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
@@ -38,40 +46,30 @@ STATUS = {
 # exported entry points and their C signatures
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
 _SIGS = {
     "gqa_status_string": (ctypes.c_char_p, [_I]),
     "gqa_rope_table": (_I, [_I, ctypes.c_double, _I, _P, _P]),
-    "gqa_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
-    "gqa_workspace_bytes_from": (ctypes.c_size_t, [_I, _I, _I, _I]),
-    "gqa_workspace_bytes_kv": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
-    "gqa_block_prefill_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P,
-                                  ctypes.c_size_t, _P, _P, _P]),
-    "gqa_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
-    "gqa_set_decode_schedule": (_I, [_I]),
-    "gqa_decode_schedule": (_I, [_I, _I, _I]),
-    "gqa_block_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
-                               ctypes.c_size_t, _P, _P]),
-    "gqa_block_prefill_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
-                                        ctypes.c_size_t, _P, _P, _P]),
-    "gqa_block_prefill_from": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
-                                    ctypes.c_size_t, _P, _P]),
-    "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
-                              ctypes.c_size_t, _P, _P]),
-    "gqa_layer_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
-    "gqa_vocab_logits": (_I, [_P, _P, ctypes.c_float, _P, _I, _I, _P, _P]),
-    "gqa_layer_prefill_from": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I,
-                                    _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
-    "gqa_layer_decode": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I,
-                              _P, _P, _P, ctypes.c_size_t, _P, _P]),
-    "gqa_block_decode_kv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I,
-                                 _P, ctypes.c_size_t, _P, _P, _P]),
-    "gqa_layer_workspace_bytes_kv": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
-    "gqa_layer_prefill_kv": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _I, _P,
-                                  _I, _I, _I, _P, _P, ctypes.c_size_t, _P, _P]),
-    "gqa_layer_decode_kv": (_I, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _I, _I, _P,
-                                 _I, _I, _P, _P, _P, ctypes.c_size_t, _P, _P]),
-    "gqa_block_decode_profiled": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I,
-                                       _P, ctypes.c_size_t, _P, _P, _P]),
+    "gqa_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "gqa_workspace_init": (_I, [_P, _Z, _P]),
+    "gqa_decode_schedule": (_I, [_I, _I, _I, _I, _I]),
+    "gqa_wo_to_fp16": (_I, [_P, _P, _P]),
+    # x wq wk wv wo wo16 kc vc n_kv T_max rope start_pos B T out ws ws_bytes probe events stream
+    "gqa_block_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z,
+                               _P, _P, _P]),
+    # x wq wk wv wo kc vc n_kv T_max rope start_pos B out out_bf16 accumulate schedule ws
+    # ws_bytes probe events stream
+    "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _I, _P,
+                              _Z, _P, _P, _P]),
+    # x norm_w eps wq wk wv wo wo16 kc vc n_kv T_max rope start_pos B T h ws ws_bytes probe stream
+    "gqa_layer_prefill": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
+                               _P, _Z, _P, _P]),
+    # x norm_w eps wq wk wv wo kc vc n_kv T_max rope start_pos B h h_bf16 schedule ws ws_bytes
+    # probe stream
+    "gqa_layer_decode": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I,
+                              _P, _Z, _P, _P]),
+    "gqa_vocab_logits": (_I, [_P, _P, _F, _P, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -136,49 +134,61 @@ def _need(t, name, dtype, shape, device):
 # Allocation helpers (layouts of include/gqa.h)
 # ----------------------------------------------------------------------------
 
-def workspace_bytes(B: int, T: int, T_max: int, start_pos: int = 0,
+def workspace_bytes(op: int, B: int, T_max: int, T: int = 1, start_pos: int = 0,
                     n_kv_heads: int = N_KV_HEADS) -> int:
-    if n_kv_heads != N_KV_HEADS:
-        return int(lib().gqa_workspace_bytes_kv(int(B), int(start_pos), int(T), int(T_max),
-                                                int(n_kv_heads)))
-    if start_pos:
-        return int(lib().gqa_workspace_bytes_from(int(B), int(start_pos), int(T), int(T_max)))
-    return int(lib().gqa_workspace_bytes(int(B), int(T), int(T_max)))
+    """Scratch bytes of one call of operation ``op`` (OP_PREFILL, OP_DECODE,
+    OP_LAYER_PREFILL, OP_LAYER_DECODE); 0 for arguments out of range."""
+    return int(lib().gqa_workspace_bytes(int(op), int(n_kv_heads), int(B), int(start_pos),
+                                         int(T), int(T_max)))
 
 
-def workspace(B: int, T: int, T_max: int, device, start_pos: int = 0,
+def workspace(op: int, B: int, T_max: int, device, T: int = 1, start_pos: int = 0,
               n_kv_heads: int = N_KV_HEADS) -> torch.Tensor:
-    """A workspace for these arguments (prefill of T tokens from start_pos,
-    and decode, with n_kv_heads key/value heads), initialised
-    (gqa_workspace_init) on the current stream."""
-    n = workspace_bytes(B, T, T_max, start_pos, n_kv_heads)
+    """A workspace for one call of operation ``op`` with these arguments,
+    initialised (gqa_workspace_init) on the current stream."""
+    n = workspace_bytes(op, B, T_max, T, start_pos, n_kv_heads)
     if n == 0:
-        raise ValueError(f"no workspace size for B={B}, start_pos={start_pos}, T={T}, "
-                         f"T_max={T_max}")
+        raise ValueError(f"no workspace size for op={op}, B={B}, start_pos={start_pos}, T={T}, "
+                         f"T_max={T_max}, n_kv_heads={n_kv_heads}")
     ws = torch.empty(n, dtype=torch.uint8, device=device)
-    _check(lib().gqa_workspace_init(_ptr(ws), n, _stream(ws.device)), "gqa_workspace_init")
+    workspace_init(ws)
     return ws
 
 
+def workspace_init(ws: torch.Tensor) -> None:
+    """Zero the synchronisation words and write the magic word (again, e.g.
+    after the error word turned nonzero)."""
+    _check(lib().gqa_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)),
+           "gqa_workspace_init")
+
+
 def workspace_errors(ws: torch.Tensor) -> int:
-    """The workspace's sticky error word (nonzero after a fused decode whose
-    bounded waits timed out).  Synchronises with the device."""
+    """The workspace's sticky error word (WS_ERR_* bits).  Synchronises with
+    the device."""
     return int(ws[:4].view(torch.int32).item())
 
 
-def set_decode_schedule(schedule: int) -> int:
-    """Process-wide decode schedule (DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED);
-    returns the previous one."""
-    prev = int(lib().gqa_set_decode_schedule(int(schedule)))
-    if prev < 0:
-        raise GQAError(prev, "gqa_set_decode_schedule")
-    return prev
+def workspace_off_home(ws: torch.Tensor) -> int:
+    """One-launch decodes since the workspace was initialised whose
+    workgroups the dispatcher did not place on their kv head's XCD (their
+    hand-off reads then miss the shared L2 line; results are unaffected: a
+    performance diagnostic, not an error).  Synchronises."""
+    return int(ws[8:12].view(torch.int32).item())
 
 
-def decode_schedule(B: int, start_pos: int, T_max: int) -> int:
-    """The schedule a decode call of this shape runs (DECODE_SPLIT or
-    DECODE_FUSED) under the current setting."""
-    r = int(lib().gqa_decode_schedule(int(B), int(start_pos), int(T_max)))
+def _debug_check(ws: torch.Tensor, where: str):
+    if DEBUG:
+        err = workspace_errors(ws)
+        if err:
+            raise RuntimeError(f"{where}: workspace error word {err:#x}")
+
+
+def decode_schedule(B: int, start_pos: int, T_max: int, n_kv_heads: int = N_KV_HEADS,
+                    schedule: int = DECODE_AUTO) -> int:
+    """The schedule (DECODE_SPLIT or DECODE_FUSED) a decode call of this shape
+    runs when it asks for ``schedule``."""
+    r = int(lib().gqa_decode_schedule(int(n_kv_heads), int(B), int(start_pos), int(T_max),
+                                      int(schedule)))
     if r < 0:
         raise GQAError(r, "gqa_decode_schedule")
     return r
@@ -299,9 +309,10 @@ def rope_table(T_max: int, theta: float = 500000.0, scaled: bool = True, device=
     return out
 
 
-def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope, kv_heads=(N_KV_HEADS,)):
+def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope, kv_heads=KV_HEAD_COUNTS):
     """Validate the weights, caches and rope table; the number of key/value
-    heads comes from wk's rows and must be one of kv_heads."""
+    heads comes from wk's rows and must be one of kv_heads.  wo may be None
+    when a prefill gets its fp16 copy instead."""
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
@@ -311,7 +322,8 @@ def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope, kv_heads=(N_KV_HEADS,)
     _need(wq, "wq", torch.bfloat16, (D_MODEL, D_MODEL), dev)
     _need(wk, "wk", torch.bfloat16, (n_kv * HEAD_DIM, D_MODEL), dev)
     _need(wv, "wv", torch.bfloat16, (n_kv * HEAD_DIM, D_MODEL), dev)
-    _need(wo, "wo", torch.bfloat16, (D_MODEL, D_MODEL), dev)
+    if wo is not None:
+        _need(wo, "wo", torch.bfloat16, (D_MODEL, D_MODEL), dev)
     if kcache.dim() != 4:
         raise ValueError(f"kcache must be [B, {n_kv}, T_max, 128]")
     B, T_max = kcache.shape[0], kcache.shape[2]
@@ -321,21 +333,39 @@ def _check_block(x, wq, wk, wv, wo, kcache, vcache, rope, kv_heads=(N_KV_HEADS,)
     if rope.dim() != 3 or rope.shape[0] < T_max:
         raise ValueError("rope must be [>= T_max, 64, 2]")
     _need(rope, "rope", torch.float32, (rope.shape[0], ROPE_PAIRS, 2), dev)
-    return dev, B, T_max
+    return dev, B, T_max, n_kv
+
+
+def _events(events):
+    return None if events is None else events.events
+
+
+def wo_to_fp16(wo, out=None) -> torch.Tensor:
+    """fp16 copy [4096, 4096] of wo for the prefill's output projection
+    (gqa_wo_to_fp16; entries beyond +-65504 saturate)."""
+    _need(wo, "wo", torch.bfloat16, (D_MODEL, D_MODEL), wo.device)
+    if out is None:
+        out = torch.empty((D_MODEL, D_MODEL), dtype=torch.float16, device=wo.device)
+    _need(out, "wo16", torch.float16, (D_MODEL, D_MODEL), wo.device)
+    _check(lib().gqa_wo_to_fp16(_ptr(wo), _ptr(out), _stream(wo.device)), "gqa_wo_to_fp16")
+    return out
 
 
 def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, probe=None,
-                  events: HipEvents | None = None, start_pos: int = 0) -> torch.Tensor:
+                  events: HipEvents | None = None, start_pos: int = 0,
+                  wo16=None) -> torch.Tensor:
     """Delta_attn [B, T, 4096] fp32 for x [B, T, 4096] bf16 at positions
     start_pos..start_pos+T-1; reads cache rows 0..start_pos-1 and writes rows
-    start_pos..start_pos+T-1 (start_pos > 0: gqa_block_prefill_from).  The
-    number of key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), 16 or
-    32 (gqa_block_prefill_kv)."""
+    start_pos..start_pos+T-1.  The number of key/value heads is
+    wk.shape[0] / 128: 8 (Llama 3.1 8B), 16 or 32.  wo16: optional fp16 copy
+    of wo from wo_to_fp16 (then wo may be None)."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
-                                 kv_heads=KV_HEAD_COUNTS)
-    n_kv = wk.shape[0] // HEAD_DIM
+    dev, B, T_max, n_kv = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    if wo is None and wo16 is None:
+        raise ValueError("wo or wo16 is needed")
+    if wo16 is not None:
+        _need(wo16, "wo16", torch.float16, (D_MODEL, D_MODEL), dev)
     T = x.shape[1]
     _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
     if out is None:
@@ -344,29 +374,45 @@ def block_prefill(x, wq, wk, wv, wo, kcache, vcache, rope, out=None, ws=None, pr
     if probe is not None:
         _need(probe, "probe", torch.float32, (B, T, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = workspace(B, T, T_max, dev, start_pos, n_kv)
-    if n_kv != N_KV_HEADS:
-        _check(lib().gqa_block_prefill_kv(
-            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
-            int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(out), _ptr(ws),
-            ws.numel(), _ptr(probe), _stream(dev), None if events is None else events.events),
-            "gqa_block_prefill_kv")
-        return out
-    if start_pos:
-        if events is not None:
-            raise ValueError("per-stage events are recorded for start_pos = 0 only")
-        _check(lib().gqa_block_prefill_from(
-            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
-            int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(out), _ptr(ws),
-            ws.numel(), _ptr(probe), _stream(dev)), "gqa_block_prefill_from")
-        return out
-    args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
-            int(T_max), _ptr(rope), int(B), int(T), _ptr(out), _ptr(ws), ws.numel(),
-            _ptr(probe), _stream(dev)]
-    if events is None:
-        _check(lib().gqa_block_prefill(*args), "gqa_block_prefill")
-    else:
-        _check(lib().gqa_block_prefill_profiled(*args, events.events), "gqa_block_prefill_profiled")
+        ws = workspace(OP_PREFILL, B, T_max, dev, T, start_pos, n_kv)
+    _check(lib().gqa_block_prefill(
+        _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(wo16), _ptr(kcache), _ptr(vcache),
+        n_kv, int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(out), _ptr(ws),
+        ws.numel(), _ptr(probe), _events(events), _stream(dev)), "gqa_block_prefill")
+    _debug_check(ws, "gqa_block_prefill")
+    return out
+
+
+def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=None,
+                 out_bf16=None, accumulate: bool = False, ws=None, probe=None,
+                 events: HipEvents | None = None, schedule: int = DECODE_AUTO) -> torch.Tensor:
+    """One token per sequence at position start_pos: x [B, 4096] bf16 ->
+    out [B, 4096] fp32 (= Delta, or += Delta with accumulate).  The number of
+    key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), 16 or 32.
+    schedule: DECODE_AUTO, DECODE_SPLIT or DECODE_FUSED."""
+    if x.dim() != 2:
+        raise ValueError("x must be [B, 4096]")
+    if wo is None:
+        raise ValueError("decode needs wo")
+    dev, B, T_max, n_kv = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, D_MODEL), dev)
+    if out_bf16 is not None:
+        _need(out_bf16, "out_bf16", torch.bfloat16, (B, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
+    if ws is None:
+        ws = workspace(OP_DECODE, B, T_max, dev, n_kv_heads=n_kv)
+    _check(lib().gqa_block_decode(
+        _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
+        int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
+        int(bool(accumulate)), int(schedule), _ptr(ws), ws.numel(), _ptr(probe), _events(events),
+        _stream(dev)), "gqa_block_decode")
+    _debug_check(ws, "gqa_block_decode")
     return out
 
 
@@ -395,34 +441,18 @@ def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None) -> t
     return logits
 
 
-def layer_workspace(B: int, T: int, T_max: int, device, start_pos: int = 0,
-                    n_kv_heads: int = N_KV_HEADS) -> torch.Tensor:
-    """An initialised workspace for layer_prefill(B, T, start_pos) (or, with
-    T = 1 and start_pos = 0, for layer_decode), n_kv_heads key/value heads."""
-    if n_kv_heads != N_KV_HEADS:
-        n = int(lib().gqa_layer_workspace_bytes_kv(int(B), int(start_pos), int(T), int(T_max),
-                                                   int(n_kv_heads)))
-    else:
-        n = int(lib().gqa_layer_workspace_bytes(int(B), int(start_pos), int(T), int(T_max)))
-    if n == 0:
-        raise ValueError(f"no layer workspace size for B={B}, start_pos={start_pos}, T={T}, "
-                         f"T_max={T_max}")
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    _check(lib().gqa_workspace_init(_ptr(ws), n, _stream(ws.device)), "gqa_workspace_init")
-    return ws
-
-
 def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int = 0,
-                  eps: float = NORM_EPS, h=None, ws=None, probe=None) -> torch.Tensor:
+                  eps: float = NORM_EPS, h=None, ws=None, probe=None, wo16=None) -> torch.Tensor:
     """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, T, 4096] fp32 for x
     [B, T, 4096] bf16 at positions start_pos..; the block's cache rows as in
-    block_prefill.  The number of key/value heads is wk.shape[0] / 128 (8, 16
-    or 32)."""
+    block_prefill.  The number of key/value heads is wk.shape[0] / 128."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
-                                 kv_heads=KV_HEAD_COUNTS)
-    n_kv = wk.shape[0] // HEAD_DIM
+    dev, B, T_max, n_kv = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    if wo is None and wo16 is None:
+        raise ValueError("wo or wo16 is needed")
+    if wo16 is not None:
+        _need(wo16, "wo16", torch.float16, (D_MODEL, D_MODEL), dev)
     T = x.shape[1]
     _need(x, "x", torch.bfloat16, (B, T, D_MODEL), dev)
     _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
@@ -432,31 +462,26 @@ def layer_prefill(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: in
     if probe is not None:
         _need(probe, "probe", torch.float32, (B, T, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = layer_workspace(B, T, T_max, dev, start_pos, n_kv)
-    if n_kv != N_KV_HEADS:
-        _check(lib().gqa_layer_prefill_kv(
-            _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
-            _ptr(kcache), _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B),
-            int(T), _ptr(h), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)),
-            "gqa_layer_prefill_kv")
-        return h
-    _check(lib().gqa_layer_prefill_from(
-        _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
-        _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), int(T), _ptr(h), _ptr(ws),
-        ws.numel(), _ptr(probe), _stream(dev)), "gqa_layer_prefill_from")
+        ws = workspace(OP_LAYER_PREFILL, B, T_max, dev, T, start_pos, n_kv)
+    _check(lib().gqa_layer_prefill(
+        _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(wo16),
+        _ptr(kcache), _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B), int(T),
+        _ptr(h), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)), "gqa_layer_prefill")
+    _debug_check(ws, "gqa_layer_prefill")
     return h
 
 
 def layer_decode(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int,
-                 eps: float = NORM_EPS, h=None, h_bf16=None, ws=None, probe=None) -> torch.Tensor:
+                 eps: float = NORM_EPS, h=None, h_bf16=None, ws=None, probe=None,
+                 schedule: int = DECODE_AUTO) -> torch.Tensor:
     """h = x + Delta_attn(RMSNorm(x) * norm_w) [B, 4096] fp32 for one token per
     sequence at start_pos; h_bf16 (optional) receives its bf16 rounding.  The
     number of key/value heads is wk.shape[0] / 128 (8, 16 or 32)."""
     if x.dim() != 2:
         raise ValueError("x must be [B, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
-                                 kv_heads=KV_HEAD_COUNTS)
-    n_kv = wk.shape[0] // HEAD_DIM
+    if wo is None:
+        raise ValueError("decode needs wo")
+    dev, B, T_max, n_kv = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
     _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
     _need(norm_w, "norm_w", torch.bfloat16, (D_MODEL,), dev)
     if h is None:
@@ -467,57 +492,11 @@ def layer_decode(x, norm_w, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int
     if probe is not None:
         _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
     if ws is None:
-        ws = layer_workspace(B, 1, T_max, dev, 0, n_kv)
-    if n_kv != N_KV_HEADS:
-        _check(lib().gqa_layer_decode_kv(
-            _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
-            _ptr(kcache), _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B),
-            _ptr(h), _ptr(h_bf16), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)),
-            "gqa_layer_decode_kv")
-        return h
+        ws = workspace(OP_LAYER_DECODE, B, T_max, dev, n_kv_heads=n_kv)
     _check(lib().gqa_layer_decode(
         _ptr(x), _ptr(norm_w), float(eps), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache),
-        _ptr(vcache), int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(h), _ptr(h_bf16),
-        _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)), "gqa_layer_decode")
+        _ptr(vcache), n_kv, int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(h),
+        _ptr(h_bf16), int(schedule), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)),
+        "gqa_layer_decode")
+    _debug_check(ws, "gqa_layer_decode")
     return h
-
-
-def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=None,
-                 out_bf16=None, accumulate: bool = False, ws=None, probe=None,
-                 events: HipEvents | None = None) -> torch.Tensor:
-    """One token per sequence at position start_pos: x [B, 4096] bf16 ->
-    out [B, 4096] fp32 (= Delta, or += Delta with accumulate).  The number of
-    key/value heads is wk.shape[0] / 128: 8 (Llama 3.1 8B), or 16 / 32
-    (gqa_block_decode_kv)."""
-    if x.dim() != 2:
-        raise ValueError("x must be [B, 4096]")
-    dev, B, T_max = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope,
-                                 kv_heads=KV_HEAD_COUNTS)
-    n_kv = wk.shape[0] // HEAD_DIM
-    _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
-    if out is None:
-        if accumulate:
-            raise ValueError("accumulate needs an existing out tensor")
-        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, (B, D_MODEL), dev)
-    if out_bf16 is not None:
-        _need(out_bf16, "out_bf16", torch.bfloat16, (B, D_MODEL), dev)
-    if probe is not None:
-        _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
-    if ws is None:
-        ws = workspace(B, 1, T_max, dev)
-    if n_kv != N_KV_HEADS:
-        _check(lib().gqa_block_decode_kv(
-            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
-            int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
-            int(bool(accumulate)), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev),
-            None if events is None else events.events), "gqa_block_decode_kv")
-        return out
-    args = [_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache),
-            int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
-            int(bool(accumulate)), _ptr(ws), ws.numel(), _ptr(probe), _stream(dev)]
-    if events is None:
-        _check(lib().gqa_block_decode(*args), "gqa_block_decode")
-    else:
-        _check(lib().gqa_block_decode_profiled(*args, events.events), "gqa_block_decode_profiled")
-    return out

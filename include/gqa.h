@@ -12,7 +12,9 @@
  *             page "Llama 3.1 8B . Query projection"), viewed as heads of 128;
  *   rope      adjacent pairs (2i, 2i+1) of each Q and K head rotated by the
  *             angle position * f_i;
- *   gqa       KV head g serves query heads 4g .. 4g+3;
+ *   gqa       KV head g serves query heads n_rep*g .. n_rep*g + n_rep-1,
+ *             n_rep = 32 / n_kv_heads (4 for Llama 3.1 8B; n_kv_heads = 32 is
+ *             the multi-head attention the page sizes beside it);
  *   scores    softmax over keys of Q K^T / sqrt(128), causal: query at
  *             position p sees keys 0..p;
  *   retrieval P V, heads merged to feature h*128 + d, Delta = O Wo^T.
@@ -20,32 +22,39 @@
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller, contiguous, and
  *     16-byte aligned.  bf16 values are passed as their 16-bit patterns
- *     (gqa_bf16).
+ *     (gqa_bf16).  The library allocates no memory.
  *   - Work is enqueued on `stream` (NULL = the null stream); calls return
  *     without synchronising.  Calls on different streams are safe when their
- *     buffers are disjoint.  The library holds no mutable global state.
+ *     buffers are disjoint.  The library holds no mutable global state: every
+ *     choice (head count, decode schedule, events) is an argument of the call.
  *   - Every argument is validated on the host before any HIP call.  On an
  *     error nothing is launched and no buffer is modified.  No C++ exception
  *     crosses this interface.
  *   - Returns GQA_OK (0) or a negative gqa_status.
  *
- * KV cache layout (bf16, updated in place; T_max = rows per sequence, a
- * multiple of 32):
- *   kcache [B][8][T_max][128]        key of position t, kv head g, dim d at
- *                                    ((b*8 + g)*T_max + t)*128 + d
- *   vcache [B][8][T_max/32][128][32] value of position t, kv head g, dim d at
- *                                    ((b*8 + g)*(T_max/32) + t/32)*4096
- *                                      + d*32 + t%32
+ * KV cache layout (bf16, updated in place; n_kv = n_kv_heads; T_max = rows
+ * per sequence, a multiple of 32):
+ *   kcache [B][n_kv][T_max][128]        key of position t, kv head g, dim d at
+ *                                       ((b*n_kv + g)*T_max + t)*128 + d
+ *   vcache [B][n_kv][T_max/32][128][32] value of position t, kv head g, dim d at
+ *                                       ((b*n_kv + g)*(T_max/32) + t/32)*4096
+ *                                         + d*32 + t%32
  * Keys are head-major so that a run of positions of one head is contiguous.
  * Values come in blocks of 32 positions stored dimension-major, so the
  * positions that one probability multiplies are contiguous for the matrix
- * cores while a 32-position block stays one contiguous 8 KiB piece.  A call writes exactly the
- * rows start_pos .. start_pos+T-1 of sequences 0..B-1 and leaves every other
- * element bit-for-bit unchanged.  The appended values are the post-RoPE keys
- * and the values rounded to bf16 (nearest, ties to even); attention reads the
- * appended rows back in that rounded form.
+ * cores while a 32-position block stays one contiguous 8 KiB piece.  A call
+ * writes exactly the rows start_pos .. start_pos+T-1 of sequences 0..B-1 and
+ * leaves every other element bit-for-bit unchanged.  The appended values are
+ * the post-RoPE keys and the values rounded to bf16 (nearest, ties to even);
+ * attention reads the appended rows back in that rounded form.
  *
  * RoPE table layout: rope[T_max][64][2] fp32, (cos, sin) of position * f_i.
+ *
+ * Value range of prefill: its attention and output projection run on fp16
+ * matrix-core operands (keys, values, Wo, and Q, P, O).  A key, value or Wo
+ * entry beyond fp16's range (|v| > 65504, which bf16 can hold) is saturated
+ * to +-65504, and the call sets GQA_WS_ERR_FP16_RANGE in its workspace's
+ * error word; Delta is then not the exact block.  Decode has no such limit.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -71,17 +80,31 @@ extern "C" {
 #define GQA_MAX_VOCAB  (1 << 20)   /* rows of the vocabulary projection */
 #define GQA_MAX_T_MAX   (1 << 20)
 
-/* Leading bytes of every workspace that hold the decode synchronisation words. */
+/* Leading bytes of every workspace: the synchronisation words of the decode
+ * kernels, headed by an error word and a magic word (gqa_workspace_init). */
 #define GQA_SYNC_BYTES  65536
 
-/* Decode schedules (gqa_set_decode_schedule). */
-#define GQA_DECODE_AUTO   0             /* fused where the shape admits it, else split */
+/* Bits of the workspace error word (its first int). */
+#define GQA_WS_ERR_WAIT        0x1   /* a bounded wait of the one-launch decode timed out */
+#define GQA_WS_ERR_WO_WAIT     0x2   /* the same, in its output projection */
+#define GQA_WS_ERR_INIT        0x4   /* a decode found the workspace uninitialised */
+#define GQA_WS_ERR_FP16_RANGE  0x100 /* a prefill saturated an operand to +-65504 */
+
+/* Decode schedules (the `schedule` argument of the decode calls). */
+#define GQA_DECODE_AUTO   0             /* one launch where the shape admits it, else three */
 #define GQA_DECODE_SPLIT  1             /* three launches: QKV, attention, wo */
 #define GQA_DECODE_FUSED  2             /* one launch; shapes it does not admit fail */
 
-/* Number of stages whose boundaries the *_profiled entry points record. */
+/* Operations whose workspace gqa_workspace_bytes sizes. */
+#define GQA_OP_PREFILL        0
+#define GQA_OP_DECODE         1
+#define GQA_OP_LAYER_PREFILL  2
+#define GQA_OP_LAYER_DECODE   3
+
+/* Number of stages whose boundaries the `events` arguments record. */
 #define GQA_DECODE_STAGES   3           /* QKV+RoPE+append, attention, wo */
-#define GQA_PREFILL_STAGES  4           /* wo to fp16, QKV+RoPE+append, attention, wo */
+#define GQA_PREFILL_STAGES  4           /* prep (wo to fp16, cached rows), QKV+RoPE+append,
+                                           attention, wo */
 
 typedef uint16_t gqa_bf16;
 
@@ -91,10 +114,11 @@ typedef enum {
     GQA_ERR_SHAPE     = -2,  /* B, T or T_max outside the supported range */
     GQA_ERR_RANGE     = -3,  /* start_pos < 0 or start_pos + T > T_max */
     GQA_ERR_ALIGN     = -4,  /* a pointer is not 16-byte aligned, or T_max % 32 != 0 */
-    GQA_ERR_WORKSPACE = -5,  /* ws_bytes < gqa_workspace_bytes(...) */
+    GQA_ERR_WORKSPACE = -5,  /* ws_bytes below gqa_workspace_bytes(...) */
     GQA_ERR_HIP       = -6,  /* a HIP call or kernel launch failed */
     GQA_ERR_ALIAS     = -7,  /* an output overlaps an input or another output */
-    GQA_ERR_ARG       = -8   /* any other invalid argument (theta <= 0, flags) */
+    GQA_ERR_ARG       = -8   /* any other invalid argument (n_kv_heads, theta, flags,
+                                schedule, or a schedule the shape does not admit) */
 } gqa_status;
 
 /* Readable name of a status code; never NULL. */
@@ -118,135 +142,143 @@ const char* gqa_status_string(int status);
 int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t stream);
 
 /*
- * gqa_workspace_bytes -- device scratch needed by gqa_block_prefill(B, T) and
- * by gqa_block_decode(B, start_pos < T_max) with these arguments; 0 when the
- * arguments are out of range.  Calls that share a workspace must be ordered
- * (one stream, or events): they reuse its contents.
- *
- * The first GQA_SYNC_BYTES bytes hold the synchronisation words of the fused
- * decode schedule.  They must be zero before the first call on a workspace
- * (gqa_workspace_init); every call leaves them zero and prefill never writes
- * them.  Their first int is a sticky error word: nonzero after a fused decode
- * whose bounded waits timed out (that call's outputs are invalid; initialise
- * the workspace again).  The rest holds nothing the caller reads.
+ * gqa_workspace_bytes -- device scratch needed by one call of operation `op`
+ * with these arguments; 0 when they are out of range.
+ *   op          GQA_OP_PREFILL (gqa_block_prefill), GQA_OP_DECODE
+ *               (gqa_block_decode), GQA_OP_LAYER_PREFILL, GQA_OP_LAYER_DECODE
+ *   n_kv_heads  8, 16 or 32
+ *   B, T        sequences and new tokens per sequence (T = 1 for decode)
+ *   start_pos   cached rows before the new tokens (prefill's fp16 key/value
+ *               copies hold all start_pos + T keys; decode's scratch does not
+ *               depend on it)
+ *   T_max       rows per sequence of the caches
+ * Decode needs the synchronisation words, Q, O and the attention partials
+ * (about 1.2 MiB at B = 1); prefill adds fp16 copies of Q, O, the keys and
+ * values and of Wo.  A workspace sized for one operation serves any smaller
+ * one.  Calls that share a workspace must be ordered (one stream, or
+ * events): they reuse its contents.
  */
-size_t gqa_workspace_bytes(int B, int T, int T_max);
+size_t gqa_workspace_bytes(int op, int n_kv_heads, int B, int start_pos, int T, int T_max);
 
 /*
- * gqa_workspace_bytes_from -- the same for gqa_block_prefill_from(start_pos,
- * B, T) (and decode); its fp16 K/V copies hold all start_pos + T keys.  0 when
- * the arguments are out of range (start_pos < 0 or start_pos + T > T_max
- * included).  gqa_workspace_bytes(B, T, T_max) equals the start_pos = 0 value.
- */
-size_t gqa_workspace_bytes_from(int B, int start_pos, int T, int T_max);
-
-/*
- * gqa_workspace_bytes_kv -- gqa_workspace_bytes_from for a model with
- * n_kv_heads key/value heads (8, 16 or 32; the prefill's fp16 K/V copies grow
- * with it).  0 for another n_kv_heads or out-of-range arguments; n_kv_heads = 8
- * equals gqa_workspace_bytes_from.
- */
-size_t gqa_workspace_bytes_kv(int B, int start_pos, int T, int T_max, int n_kv_heads);
-
-/*
- * gqa_workspace_init -- zero the synchronisation words of a workspace of
- * ws_bytes bytes (one small fill kernel on stream; no host synchronisation).
- * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (< GQA_SYNC_BYTES),
- * GQA_ERR_HIP.
+ * gqa_workspace_init -- prepare a workspace of ws_bytes bytes (at least
+ * GQA_SYNC_BYTES): zero its synchronisation words and write the magic word
+ * that the decode kernels check (one small fill kernel on stream, no host
+ * synchronisation, no memset, so it can also sit in a captured graph).  Call
+ * it once per workspace before its first decode, and again after the error
+ * word turned nonzero.  Every decode leaves the synchronisation words as it
+ * found them; prefill writes only GQA_WS_ERR_FP16_RANGE into the error word.
+ * A decode on a workspace without the magic word writes NaN into its output
+ * and sets GQA_WS_ERR_INIT.  The error word is the workspace's first int.
+ * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE, GQA_ERR_HIP.
  */
 int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Decode schedule.  GQA_DECODE_SPLIT runs the three stages as three kernels.
- * GQA_DECODE_FUSED runs the whole step as one kernel whose workgroups pass
- * results to each other through the workspace (Q/K/V -> attention -> wo), so
- * that each consumer's HBM reads overlap its producer's; it admits B <= 2 and
- * contexts short enough for at most 128 attention workgroups (start_pos + 1
- * <= 2048 at B = 1, <= 1024 at B = 2).  GQA_DECODE_AUTO (the default) takes
- * the fused schedule where it is admitted.  Results agree between schedules
- * to rounding; each schedule is deterministic.
+ * gqa_decode_schedule -- the schedule a decode call with these arguments runs
+ * when it asks for `schedule`: GQA_DECODE_SPLIT or GQA_DECODE_FUSED, or
+ * GQA_ERR_ARG when the request is not one of the three schedules or is
+ * GQA_DECODE_FUSED for a shape the one-launch schedule does not admit (the
+ * decode call would fail with that code); GQA_ERR_SHAPE / GQA_ERR_RANGE for
+ * invalid shapes.
  *
- * gqa_set_decode_schedule sets the process-wide choice and returns the
- * previous one (GQA_ERR_ARG for an unknown value); gqa_decode_schedule
- * returns the schedule a decode call of this shape would run
- * (GQA_DECODE_SPLIT or GQA_DECODE_FUSED), or GQA_ERR_ARG when the setting is
- * GQA_DECODE_FUSED and the shape is not admitted (the call would fail with
- * that code), GQA_ERR_SHAPE / GQA_ERR_RANGE for invalid arguments.
+ * GQA_DECODE_SPLIT runs the three stages as three kernels.  GQA_DECODE_FUSED
+ * runs the whole step as one kernel whose workgroups pass results to each
+ * other through the workspace (Q/K/V -> attention -> wo), so that each
+ * consumer's HBM reads overlap its producer's; it admits n_kv_heads = 8,
+ * B <= 2 and contexts short enough for at most 128 attention workgroups
+ * (start_pos + 1 <= 2048 at B = 1, <= 1024 at B = 2).  GQA_DECODE_AUTO takes
+ * the one-launch schedule where it is admitted.  Results agree between the
+ * schedules bit for bit; each is deterministic.
  */
-int gqa_set_decode_schedule(int schedule);
-int gqa_decode_schedule(int B, int start_pos, int T_max);
+int gqa_decode_schedule(int n_kv_heads, int B, int start_pos, int T_max, int schedule);
 
 /*
- * gqa_block_prefill -- the block over T new tokens of B sequences starting
- * at position 0 (the "Prefill" mode of the pages), with a causal mask.
- *   x        [B][T][4096] bf16, the block input
- *   wq       [4096][4096] bf16 [out, in];  wk, wv [1024][4096];  wo [4096][4096]
- *   kcache, vcache   layouts above; rows 0..T-1 of each sequence are written
- *   T_max    rows per sequence in the caches and the table; T <= T_max
- *   rope     [T_max][64][2] fp32 from gqa_rope_table
- *   out      [B][T][4096] fp32, Delta_attn
- *   ws       workspace of ws_bytes >= gqa_workspace_bytes(B, T, T_max)
- *   probe    NULL, or [B][T][6144] fp32 receiving the post-RoPE Q | K and the V
- *            features exactly as computed before any rounding (for checking)
+ * gqa_wo_to_fp16 -- convert Wo [4096][4096] bf16 once into the fp16 copy that
+ * prefill's output projection reads (entries beyond +-65504 saturate), so
+ * that a caller running many prefills with one Wo does not pay the 32 MiB
+ * conversion in every call.
+ *   wo    [4096][4096] bf16 [out, in]
+ *   wo16  [4096][4096] fp16, written (must not overlap wo)
+ * Errors: GQA_ERR_NULL, GQA_ERR_ALIGN, GQA_ERR_ALIAS, GQA_ERR_HIP.
+ */
+int gqa_wo_to_fp16(const gqa_bf16* wo, uint16_t* wo16, hipStream_t stream);
+
+/*
+ * gqa_block_prefill -- the block over T new tokens of B sequences at
+ * positions start_pos .. start_pos+T-1, with a causal mask.  start_pos = 0 is
+ * the plain prefill; start_pos > 0 continues after start_pos rows already in
+ * the caches (chunked prefill).  The page "Llama 3.1 8B . Grouped-query
+ * attention" states the rule in the mask listing of its code section: new
+ * token i sits at position start_pos + i and attends to every key
+ * j <= start_pos + i, the cached rows included; RoPE uses the same absolute
+ * positions.
+ *   x          [B][T][4096] bf16, the block input
+ *   wq         [4096][4096] bf16 [out, in]; wk, wv [n_kv_heads*128][4096];
+ *              wo [4096][4096]
+ *   wo16       NULL, or the fp16 copy of wo from gqa_wo_to_fp16 (then wo is
+ *              not read; with NULL the call converts wo into the workspace)
+ *   kcache, vcache   layouts above; rows 0 .. start_pos-1 of every sequence
+ *              must hold the earlier tokens' keys and values (read, not
+ *              written); rows start_pos .. start_pos+T-1 are written
+ *   n_kv_heads 8, 16 or 32
+ *   T_max      rows per sequence in the caches and the table
+ *   rope       [T_max][64][2] fp32 from gqa_rope_table
+ *   start_pos  0 .. T_max-T
+ *   out        [B][T][4096] fp32, Delta_attn
+ *   ws         workspace of ws_bytes >= gqa_workspace_bytes(GQA_OP_PREFILL,
+ *              n_kv_heads, B, start_pos, T, T_max)
+ *   probe      NULL, or [B][T][4096 + 2*n_kv_heads*128] fp32 receiving the
+ *              post-RoPE Q | K and the V features exactly as computed before
+ *              any rounding (for checking)
+ *   events     NULL, or GQA_PREFILL_STAGES + 1 created hipEvent_t handles:
+ *              events[0] is recorded on stream before the first kernel and
+ *              events[i] after stage i, for timing each kernel
  * Aliasing: out, probe, ws and the caches must not overlap each other or the
  * inputs.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_RANGE, GQA_ERR_ALIGN,
+ * GQA_ERR_WORKSPACE, GQA_ERR_ALIAS, GQA_ERR_ARG (n_kv_heads), GQA_ERR_HIP.
  */
 int gqa_block_prefill(const gqa_bf16* x,
                       const gqa_bf16* wq, const gqa_bf16* wk,
-                      const gqa_bf16* wv, const gqa_bf16* wo,
-                      gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                      const float* rope, int B, int T,
+                      const gqa_bf16* wv, const gqa_bf16* wo, const uint16_t* wo16,
+                      gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads, int T_max,
+                      const float* rope, int start_pos, int B, int T,
                       float* out, void* ws, size_t ws_bytes, float* probe,
-                      hipStream_t stream);
+                      hipEvent_t* events, hipStream_t stream);
 
 /*
- * gqa_block_prefill_from -- the block over T new tokens of B sequences at
- * positions start_pos .. start_pos+T-1, after start_pos rows already in the
- * caches (chunked prefill).  The page "Llama 3.1 8B . Grouped-query
- * attention" states the rule in the mask listing of its code section: with
- * start_pos cached positions, new token i sits at position start_pos + i and
- * attends to every key j <= start_pos + i, the cached rows included; RoPE
- * uses the same absolute positions.  start_pos = 0 is gqa_block_prefill.
- *   start_pos  0 .. T_max-T; rows 0 .. start_pos-1 of every sequence must
- *              hold the earlier tokens' keys and values; they are read, not
- *              written, and rows start_pos .. start_pos+T-1 are written
- *   ws         ws_bytes >= gqa_workspace_bytes_from(B, start_pos, T, T_max)
- *   other arguments as for gqa_block_prefill
- * Errors: as gqa_block_prefill; GQA_ERR_RANGE for start_pos < 0 or
- * start_pos + T > T_max.
+ * gqa_block_decode -- one new token per sequence at position start_pos (the
+ * page's decode mode): writes cache row start_pos and attends over rows
+ * 0..start_pos of each of the B sequences (one start_pos for all of them).
+ *   x          [B][4096] bf16
+ *   weights, caches, n_kv_heads, T_max, rope, probe ([B][4096 +
+ *              2*n_kv_heads*128]) and events (GQA_DECODE_STAGES + 1; under
+ *              the one-launch schedule events[1] follows its one kernel and
+ *              the later events are recorded right after) as for prefill
+ *   start_pos  0 .. T_max-1
+ *   out        [B][4096] fp32: out = Delta when accumulate == 0,
+ *              out += Delta when accumulate == 1 (the block residual
+ *              h = x + attention(...), with the caller's fp32 residual in out)
+ *   out_bf16   NULL, or [B][4096] bf16 receiving the bf16 rounding of out
+ *              after the update (the next block's input in a stack of blocks)
+ *   schedule   GQA_DECODE_AUTO, GQA_DECODE_SPLIT or GQA_DECODE_FUSED (see
+ *              gqa_decode_schedule)
+ *   ws         ws_bytes >= gqa_workspace_bytes(GQA_OP_DECODE, n_kv_heads, B,
+ *              start_pos, 1, T_max), initialised once by gqa_workspace_init
+ * Aliasing: out, out_bf16, probe, ws and the caches must not overlap each
+ * other or the inputs.
+ * Errors: as gqa_block_prefill; GQA_ERR_ARG for accumulate not 0/1 or a
+ * schedule gqa_decode_schedule rejects.
  */
-int gqa_block_prefill_from(const gqa_bf16* x,
-                           const gqa_bf16* wq, const gqa_bf16* wk,
-                           const gqa_bf16* wv, const gqa_bf16* wo,
-                           gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                           const float* rope, int start_pos, int B, int T,
-                           float* out, void* ws, size_t ws_bytes, float* probe,
-                           hipStream_t stream);
-
-/*
- * gqa_block_prefill_kv -- gqa_block_prefill_from for a model with n_kv_heads
- * key / value heads, each shared by 32 / n_kv_heads query heads (the n_rep of
- * the page "Llama 3.1 8B . Grouped-query attention", evidence "gqa": query
- * head h reads kv head h / n_rep; n_kv_heads = 32 is multi-head attention).
- *   n_kv_heads  8, 16 or 32 (8 behaves as gqa_block_prefill_from)
- *   wk, wv      [n_kv_heads*128][4096] bf16
- *   kcache      [B][n_kv_heads][T_max][128] bf16
- *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
- *   ws          ws_bytes >= gqa_workspace_bytes_kv(B, start_pos, T, T_max,
- *               n_kv_heads)
- *   probe       NULL or [B*T][4096 + 2*n_kv_heads*128] fp32
- *   events      NULL, or GQA_PREFILL_STAGES + 1 events recorded as by
- *               gqa_block_prefill_profiled
- *   other arguments as for gqa_block_prefill_from
- * Errors: as gqa_block_prefill_from; GQA_ERR_ARG for another n_kv_heads.
- */
-int gqa_block_prefill_kv(const gqa_bf16* x,
-                         const gqa_bf16* wq, const gqa_bf16* wk,
-                         const gqa_bf16* wv, const gqa_bf16* wo,
-                         gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
-                         int T_max, const float* rope, int start_pos, int B,
-                         int T, float* out, void* ws, size_t ws_bytes,
-                         float* probe, hipStream_t stream, hipEvent_t* events);
+int gqa_block_decode(const gqa_bf16* x,
+                     const gqa_bf16* wq, const gqa_bf16* wk,
+                     const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads, int T_max,
+                     const float* rope, int start_pos, int B,
+                     float* out, gqa_bf16* out_bf16, int accumulate, int schedule,
+                     void* ws, size_t ws_bytes, float* probe,
+                     hipEvent_t* events, hipStream_t stream);
 
 /*
  * Layer entry points: the block inside its residual branch, as the page
@@ -263,22 +295,38 @@ int gqa_block_prefill_kv(const gqa_bf16* x,
  *   norm_w   bf16 [4096], the norm's gain
  *   eps      0 < eps < 1
  *   h        fp32, same shape as x; written, never read
- *   ws       ws_bytes >= gqa_layer_workspace_bytes(B, start_pos, T, T_max)
- *            for prefill, gqa_layer_workspace_bytes(B, 0, 1, T_max) for
- *            decode; the normalised input lives at its end
- *   other arguments as for gqa_block_prefill_from / gqa_block_decode
+ *   ws       ws_bytes >= gqa_workspace_bytes(GQA_OP_LAYER_PREFILL or
+ *            GQA_OP_LAYER_DECODE, ...); the normalised input lives at its end
+ *   other arguments as for gqa_block_prefill / gqa_block_decode
  * Errors: those of the block calls; GQA_ERR_ARG for eps; GQA_ERR_ALIAS when h
  * overlaps x, norm_w or ws.
  */
+int gqa_layer_prefill(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                      const gqa_bf16* wq, const gqa_bf16* wk,
+                      const gqa_bf16* wv, const gqa_bf16* wo, const uint16_t* wo16,
+                      gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads, int T_max,
+                      const float* rope, int start_pos, int B, int T,
+                      float* h, void* ws, size_t ws_bytes, float* probe,
+                      hipStream_t stream);
+
+int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                     const gqa_bf16* wq, const gqa_bf16* wk,
+                     const gqa_bf16* wv, const gqa_bf16* wo,
+                     gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads, int T_max,
+                     const float* rope, int start_pos, int B,
+                     float* h, gqa_bf16* h_bf16, int schedule,
+                     void* ws, size_t ws_bytes, float* probe,
+                     hipStream_t stream);
+
 /*
  * gqa_vocab_logits -- the vocabulary projection of the page "Llama 3.1 8B .
  * Vocabulary projection": L = z W_out for one position of each of B
- * sequences, the weight stored [out, in] = [V][4096], no bias.  The page
- * casts the projection's output to float32 before returning it, so each
- * logit is the bf16 rounding (nearest even) of its fp32-accumulated dot
- * product, returned as fp32.  With norm_w non-NULL, z is the final norm of
- * the page's code (self.norm, an RMSNorm with norm_eps) applied to h, read as
- * in the layer pre-norm above; with NULL, z = h.
+ * sequences, the weight stored [out, in] = [V][4096], no bias.  The page's
+ * projection runs in the model's bf16 and its result is handed back as
+ * float32, so each logit is the bf16 rounding (nearest even) of its
+ * fp32-accumulated dot product, returned as fp32.  With norm_w non-NULL, z is
+ * the final norm of the page's code (self.norm, an RMSNorm with norm_eps)
+ * applied to h, read as in the layer pre-norm above; with NULL, z = h.
  *   h       [B][4096] bf16
  *   norm_w  NULL or [4096] bf16; eps as for the layers (ignored when NULL)
  *   w_out   [V][4096] bf16; V = 128256 for Llama 3.1 (1 .. GQA_MAX_VOCAB)
@@ -290,148 +338,6 @@ int gqa_block_prefill_kv(const gqa_bf16* x,
 int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps,
                      const gqa_bf16* w_out, int V, int B, float* logits,
                      hipStream_t stream);
-
-size_t gqa_layer_workspace_bytes(int B, int start_pos, int T, int T_max);
-
-int gqa_layer_prefill_from(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
-                           const gqa_bf16* wq, const gqa_bf16* wk,
-                           const gqa_bf16* wv, const gqa_bf16* wo,
-                           gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                           const float* rope, int start_pos, int B, int T,
-                           float* h, void* ws, size_t ws_bytes, float* probe,
-                           hipStream_t stream);
-
-int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
-                     const gqa_bf16* wq, const gqa_bf16* wk,
-                     const gqa_bf16* wv, const gqa_bf16* wo,
-                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                     const float* rope, int start_pos, int B,
-                     float* h, gqa_bf16* h_bf16,
-                     void* ws, size_t ws_bytes, float* probe,
-                     hipStream_t stream);
-
-/*
- * gqa_layer_prefill_kv, gqa_layer_decode_kv, gqa_layer_workspace_bytes_kv --
- * the two layer entry points above for a model with n_kv_heads key/value
- * heads (the GQA map and the multi-head case of the page "Llama 3.1 8B .
- * Grouped-query attention", as for gqa_block_prefill_kv and
- * gqa_block_decode_kv); 8 behaves as gqa_layer_prefill_from /
- * gqa_layer_decode.
- *   n_kv_heads  8, 16 or 32
- *   wk, wv      [n_kv_heads*128][4096] bf16
- *   kcache      [B][n_kv_heads][T_max][128] bf16
- *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
- *   probe       NULL or [B*T][4096 + 2*n_kv_heads*128] fp32
- *   ws          ws_bytes >= gqa_layer_workspace_bytes_kv(B, start_pos, T,
- *               T_max, n_kv_heads) for prefill, (B, 0, 1, T_max, n_kv_heads)
- *               for decode, initialised once by gqa_workspace_init
- *   other arguments, ownership and asynchrony as for the 8-head entry points;
- *   decode other than 8 heads runs the three-launch schedule (GQA_ERR_ARG if
- *   GQA_DECODE_FUSED is forced)
- * Errors: as gqa_layer_prefill_from / gqa_layer_decode; GQA_ERR_ARG for
- * another n_kv_heads.  gqa_layer_workspace_bytes_kv returns 0 for shapes or
- * head counts that are not accepted.
- */
-size_t gqa_layer_workspace_bytes_kv(int B, int start_pos, int T, int T_max,
-                                    int n_kv_heads);
-
-int gqa_layer_prefill_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
-                         const gqa_bf16* wq, const gqa_bf16* wk,
-                         const gqa_bf16* wv, const gqa_bf16* wo,
-                         gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
-                         int T_max, const float* rope, int start_pos, int B,
-                         int T, float* h, void* ws, size_t ws_bytes,
-                         float* probe, hipStream_t stream);
-
-int gqa_layer_decode_kv(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
-                        const gqa_bf16* wq, const gqa_bf16* wk,
-                        const gqa_bf16* wv, const gqa_bf16* wo,
-                        gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
-                        int T_max, const float* rope, int start_pos, int B,
-                        float* h, gqa_bf16* h_bf16,
-                        void* ws, size_t ws_bytes, float* probe,
-                        hipStream_t stream);
-
-/*
- * gqa_block_decode -- one new token per sequence at position start_pos (the
- * page's decode mode): writes cache row start_pos and attends over rows
- * 0..start_pos of each of the B sequences (one start_pos for all of them).
- *   x          [B][4096] bf16
- *   weights, caches, T_max, rope, ws, probe as for prefill (probe [B][6144])
- *   start_pos  0 .. T_max-1
- *   out        [B][4096] fp32: out = Delta when accumulate == 0,
- *              out += Delta when accumulate != 0 (the block residual
- *              h = x + attention(...), with the caller's fp32 residual in out)
- *   out_bf16   NULL, or [B][4096] bf16 receiving the bf16 rounding of out
- *              after the update (the next block's input in a stack of blocks)
- * Aliasing: out, out_bf16, probe, ws and the caches must not overlap each
- * other or the inputs.
- * Runs the schedule gqa_decode_schedule(B, start_pos, T_max) names; returns
- * GQA_ERR_ARG if that is an error.
- */
-int gqa_block_decode(const gqa_bf16* x,
-                     const gqa_bf16* wq, const gqa_bf16* wk,
-                     const gqa_bf16* wv, const gqa_bf16* wo,
-                     gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                     const float* rope, int start_pos, int B,
-                     float* out, gqa_bf16* out_bf16, int accumulate,
-                     void* ws, size_t ws_bytes, float* probe,
-                     hipStream_t stream);
-
-/*
- * gqa_block_decode_kv -- gqa_block_decode for a model with n_kv_heads key /
- * value heads shared by 32 / n_kv_heads query heads each (the n_rep of the
- * page "Llama 3.1 8B . Grouped-query attention", evidence "gqa": KV head g
- * serves query heads g*n_rep .. g*n_rep + n_rep - 1; n_rep = 1 is the
- * multi-head attention the page sizes beside GQA).  Llama 3.1 8B is
- * n_kv_heads = 8, where this equals gqa_block_decode.
- *   n_kv_heads  8, 16 or 32; other than 8 only with the three-launch
- *               schedule (GQA_ERR_ARG if GQA_DECODE_FUSED is forced); above 8
- *               tokens the projections run on the matrix cores for every
- *               head count
- *   wk, wv      [n_kv_heads*128][4096] bf16
- *   kcache      [B][n_kv_heads][T_max][128] bf16
- *   vcache      [B][n_kv_heads][T_max/32][128][32] bf16
- *   probe       NULL or [B][4096 + 2*n_kv_heads*128] fp32
- *   events      NULL, or GQA_DECODE_STAGES + 1 events recorded as by
- *               gqa_block_decode_profiled
- *   other arguments, ownership and workspace as for gqa_block_decode
- * Errors: as gqa_block_decode; GQA_ERR_ARG for another n_kv_heads.
- */
-int gqa_block_decode_kv(const gqa_bf16* x,
-                        const gqa_bf16* wq, const gqa_bf16* wk,
-                        const gqa_bf16* wv, const gqa_bf16* wo,
-                        gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads,
-                        int T_max, const float* rope, int start_pos, int B,
-                        float* out, gqa_bf16* out_bf16, int accumulate,
-                        void* ws, size_t ws_bytes, float* probe,
-                        hipStream_t stream, hipEvent_t* events);
-
-/*
- * Same as gqa_block_prefill / gqa_block_decode, and additionally records
- * events[0] on `stream` before the first kernel and events[i] after stage i
- * (GQA_PREFILL_STAGES / GQA_DECODE_STAGES stages), so that a caller can time
- * each kernel with hipEventElapsedTime.  events must hold that many + 1
- * created hipEvent_t handles.  Under the fused decode schedule the step is
- * one kernel: events[1] follows it and the later events are recorded
- * immediately after.
- */
-int gqa_block_prefill_profiled(const gqa_bf16* x,
-                               const gqa_bf16* wq, const gqa_bf16* wk,
-                               const gqa_bf16* wv, const gqa_bf16* wo,
-                               gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                               const float* rope, int B, int T,
-                               float* out, void* ws, size_t ws_bytes, float* probe,
-                               hipStream_t stream, hipEvent_t* events);
-
-int gqa_block_decode_profiled(const gqa_bf16* x,
-                              const gqa_bf16* wq, const gqa_bf16* wk,
-                              const gqa_bf16* wv, const gqa_bf16* wo,
-                              gqa_bf16* kcache, gqa_bf16* vcache, int T_max,
-                              const float* rope, int start_pos, int B,
-                              float* out, gqa_bf16* out_bf16, int accumulate,
-                              void* ws, size_t ws_bytes, float* probe,
-                              hipStream_t stream, hipEvent_t* events);
 
 #ifdef __cplusplus
 }
