@@ -11,5 +11,5 @@ from .gqa import (  # noqa: F401
     DECODE_FUSED, OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE, WS_ERR_WAIT,
     WS_ERR_WO_WAIT, WS_ERR_INIT, WS_ERR_FP16_RANGE, WS_MAGIC, decode_schedule, workspace_errors,
     workspace_off_home, NORM_EPS, layer_decode, layer_prefill, VOCAB, vocab_logits,
-    KV_HEAD_COUNTS, wo_to_fp16,
+    KV_HEAD_COUNTS, wo_to_fp16, block_decode_noalloc, NOALLOC_SCRATCH_BYTES,
 )

@@ -1,9 +1,13 @@
 // C ABI of libgqa.so (declared in include/gqa.h): argument validation on the
 // host, workspace layout and kernel dispatch.  Every check runs before the
 // first HIP call, so a rejected call launches nothing and changes nothing.
-// The library keeps no state between calls: every choice is an argument.
+// The library keeps no state between calls: every choice is an argument.  The
+// one exception is gqa_block_decode_noalloc's per-device scratch array and
+// the cached device address of it.
 #include <stdint.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "kernels.h"
 
@@ -159,7 +163,7 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
                 int accumulate, int schedule, void* ws, size_t ws_bytes, float* probe,
                 hipEvent_t* events, hipStream_t stream, bool dry = false,
                 const gqa_bf16* norm_w = nullptr, float norm_eps = 0.f,
-                const gqa_bf16* resid = nullptr) {
+                const gqa_bf16* resid = nullptr, bool ws_is_scratch = false) {
   int st = check_common(x, wq, wk, wv, wo, kcache, vcache, kv, T_max, rope, B, out, ws);
   if (st != GQA_OK) return st;
   if (start_pos < 0 || start_pos >= T_max) return GQA_ERR_RANGE;
@@ -173,7 +177,9 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   const Range outs[] = {span(out, Bz * D * 4), span(out_bf16, out_bf16 ? Bz * D * 2 : 0),
                         span(kcache, cache_bytes(B, T_max, kv)),
                         span(vcache, cache_bytes(B, T_max, kv)),
-                        span(ws, ws_bytes), span(probe, probe ? Bz * nqkv * 4 : 0)};
+                        // the library's own scratch array cannot overlap caller memory
+                        span(ws, ws_is_scratch ? 0 : ws_bytes),
+                        span(probe, probe ? Bz * nqkv * 4 : 0)};
   const Range ins[] = {span(x, Bz * D * 2), span(wq, (size_t)D * D * 2),
                        span(wk, (size_t)kv * HD * D * 2), span(wv, (size_t)kv * HD * D * 2),
                        span(wo, (size_t)D * D * 2), span(rope, (size_t)T_max * PAIRS * 8)};
@@ -236,6 +242,33 @@ __global__ void __launch_bounds__(256) init_sync_kernel(u32x4* sync) {
 }
 static_assert(GQA_SYNC_BYTES % (16 * 256) == 0, "sync region is a whole number of fill blocks");
 static_assert(kSyncErr == 0 && kSyncMagic == 1, "the fill kernel writes the magic into int 1");
+
+// Workspace of gqa_block_decode_noalloc: one array per GPU, alive until the
+// process ends.  In host code `scratch` is only a stand-in symbol; its device
+// address is looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr, which is what kernels and fills receive.
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on its
+// first use; nullptr (and *err set) when the HIP calls fail.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 }  // namespace
 
@@ -313,6 +346,36 @@ int gqa_block_decode(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
                      size_t ws_bytes, float* probe, hipEvent_t* events, hipStream_t stream) {
   return decode_impl(x, wq, wk, wv, wo, kcache, vcache, n_kv_heads, T_max, rope, start_pos, B,
                      out, out_bf16, accumulate, schedule, ws, ws_bytes, probe, events, stream);
+}
+
+int gqa_block_decode_noalloc(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk,
+                             const gqa_bf16* wv, const gqa_bf16* wo, gqa_bf16* kcache,
+                             gqa_bf16* vcache, int n_kv_heads, int T_max, const float* rope,
+                             int start_pos, int B, float* out, gqa_bf16* out_bf16,
+                             int accumulate, int schedule, float* probe, hipStream_t stream) {
+  // the scratch holds what a decode workspace of this shape would
+  const size_t need = ws_bytes_for(GQA_OP_DECODE, n_kv_heads, B, start_pos, 1, T_max);
+  if (need > kScratchBytes) return GQA_ERR_WORKSPACE;
+  // full validation first, with an aligned stand-in for the scratch address
+  // (never dereferenced: the dry run launches nothing)
+  alignas(256) static const unsigned char stand_in[16] = {};
+  void* const fake_ws = const_cast<unsigned char*>(stand_in);
+  int st = decode_impl(x, wq, wk, wv, wo, kcache, vcache, n_kv_heads, T_max, rope, start_pos, B,
+                       out, out_bf16, accumulate, schedule, fake_ws, kScratchBytes, probe,
+                       nullptr, stream, true, nullptr, 0.f, nullptr, true);
+  if (st != GQA_OK) return st;
+  hipError_t e;
+  void* ws = scratch_on_current_device(&e);
+  if (!ws) return GQA_ERR_HIP;
+  // every call starts from cleared synchronisation words (a fill kernel, so
+  // the call may sit in a captured graph)
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(init_sync_kernel, dim3(GQA_SYNC_BYTES / 16 / 256), dim3(256), 0, stream,
+                     static_cast<u32x4*>(ws));
+  if ((e = hipGetLastError()) != hipSuccess) return GQA_ERR_HIP;
+  return decode_impl(x, wq, wk, wv, wo, kcache, vcache, n_kv_heads, T_max, rope, start_pos, B,
+                     out, out_bf16, accumulate, schedule, ws, kScratchBytes, probe, nullptr,
+                     stream, false, nullptr, 0.f, nullptr, true);
 }
 
 int gqa_layer_prefill(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const gqa_bf16* wq,

@@ -24,6 +24,7 @@ V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
 SYNC_BYTES = 65536
+NOALLOC_SCRATCH_BYTES = 16 << 20   # the no-allocation decode's scratch array per GPU
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
 OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE = 0, 1, 2, 3
 # bits of the workspace error word
@@ -62,6 +63,10 @@ _SIGS = {
     # ws_bytes probe events stream
     "gqa_block_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _I, _P,
                               _Z, _P, _P, _P]),
+    # x wq wk wv wo kc vc n_kv T_max rope start_pos B out out_bf16 accumulate schedule probe
+    # stream
+    "gqa_block_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P,
+                                      _I, _I, _P, _P]),
     # x norm_w eps wq wk wv wo wo16 kc vc n_kv T_max rope start_pos B T h ws ws_bytes probe stream
     "gqa_layer_prefill": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
                                _P, _Z, _P, _P]),
@@ -413,6 +418,36 @@ def block_decode(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=No
         int(bool(accumulate)), int(schedule), _ptr(ws), ws.numel(), _ptr(probe), _events(events),
         _stream(dev)), "gqa_block_decode")
     _debug_check(ws, "gqa_block_decode")
+    return out
+
+
+def block_decode_noalloc(x, wq, wk, wv, wo, kcache, vcache, rope, start_pos: int, out=None,
+                         out_bf16=None, accumulate: bool = False, probe=None,
+                         schedule: int = DECODE_AUTO) -> torch.Tensor:
+    """block_decode with the library's own per-GPU scratch array as the
+    workspace (gqa_block_decode_noalloc): no workspace argument and no device
+    allocation inside the call when out is given.  Calls that overlap on one
+    GPU race on the shared array."""
+    if x.dim() != 2:
+        raise ValueError("x must be [B, 4096]")
+    if wo is None:
+        raise ValueError("decode needs wo")
+    dev, B, T_max, n_kv = _check_block(x, wq, wk, wv, wo, kcache, vcache, rope)
+    _need(x, "x", torch.bfloat16, (B, D_MODEL), dev)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, D_MODEL), dev)
+    if out_bf16 is not None:
+        _need(out_bf16, "out_bf16", torch.bfloat16, (B, D_MODEL), dev)
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (B, D_MODEL + 2 * n_kv * HEAD_DIM), dev)
+    _check(lib().gqa_block_decode_noalloc(
+        _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(kcache), _ptr(vcache), n_kv,
+        int(T_max), _ptr(rope), int(start_pos), int(B), _ptr(out), _ptr(out_bf16),
+        int(bool(accumulate)), int(schedule), _ptr(probe), _stream(dev)),
+        "gqa_block_decode_noalloc")
     return out
 
 

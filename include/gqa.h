@@ -22,11 +22,13 @@
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller, contiguous, and
  *     16-byte aligned.  bf16 values are passed as their 16-bit patterns
- *     (gqa_bf16).  The library allocates no memory.
+ *     (gqa_bf16).  The library allocates no memory at run time.
  *   - Work is enqueued on `stream` (NULL = the null stream); calls return
  *     without synchronising.  Calls on different streams are safe when their
- *     buffers are disjoint.  The library holds no mutable global state: every
- *     choice (head count, decode schedule, events) is an argument of the call.
+ *     buffers are disjoint.  Every choice (head count, decode schedule,
+ *     events) is an argument of the call; the only state the library keeps
+ *     is gqa_block_decode_noalloc's scratch array per GPU and its cached
+ *     device address.
  *   - Every argument is validated on the host before any HIP call.  On an
  *     error nothing is launched and no buffer is modified.  No C++ exception
  *     crosses this interface.
@@ -279,6 +281,42 @@ int gqa_block_decode(const gqa_bf16* x,
                      float* out, gqa_bf16* out_bf16, int accumulate, int schedule,
                      void* ws, size_t ws_bytes, float* probe,
                      hipEvent_t* events, hipStream_t stream);
+
+/*
+ * gqa_block_decode_noalloc -- gqa_block_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid it): the same kernels, with the workspace taken from
+ * the library's own scratch array instead of a ws argument.
+ *   scratch    one array of GQA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU the
+ *              library runs on, held until the process ends; its device
+ *              address is looked up (hipGetSymbolAddress) on the first call on
+ *              each device.  The call uses the CURRENT device's array, so
+ *              `stream` must belong to the current device.
+ *   limit      shapes whose decode workspace (gqa_workspace_bytes(
+ *              GQA_OP_DECODE, ...)) exceeds the array fail with
+ *              GQA_ERR_WORKSPACE before anything runs (B up to ~200 with 8 kv
+ *              heads, ~64 with 32).
+ *   other arguments as for gqa_block_decode (no ws, ws_bytes or events).
+ * Each call first clears the array's synchronisation words with a small fill
+ * kernel on `stream` (no memset), then runs the decode.  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (different streams without ordering) race and give
+ * undefined results.  A timed-out wait shows only as NaN in `out` (the error
+ * word is cleared by the next call).  Allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.
+ * Errors: as gqa_block_decode; GQA_ERR_WORKSPACE for shapes beyond the
+ * scratch array; GQA_ERR_HIP when the device or the array's address cannot
+ * be obtained.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES  (16u << 20)
+
+int gqa_block_decode_noalloc(const gqa_bf16* x,
+                             const gqa_bf16* wq, const gqa_bf16* wk,
+                             const gqa_bf16* wv, const gqa_bf16* wo,
+                             gqa_bf16* kcache, gqa_bf16* vcache, int n_kv_heads, int T_max,
+                             const float* rope, int start_pos, int B,
+                             float* out, gqa_bf16* out_bf16, int accumulate, int schedule,
+                             float* probe, hipStream_t stream);
 
 /*
  * Layer entry points: the block inside its residual branch, as the page

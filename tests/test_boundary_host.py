@@ -31,7 +31,8 @@ def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     for n in ("gqa_rope_table", "gqa_workspace_bytes", "gqa_workspace_init", "gqa_block_prefill",
               "gqa_block_decode", "gqa_decode_schedule", "gqa_status_string", "gqa_wo_to_fp16",
-              "gqa_layer_prefill", "gqa_layer_decode", "gqa_vocab_logits"):
+              "gqa_layer_prefill", "gqa_layer_decode", "gqa_vocab_logits",
+              "gqa_block_decode_noalloc"):
         assert n in names
 
 
@@ -51,14 +52,18 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_library_has_no_mutable_global_state_symbols():
-    """No writable data of the library's own: every choice is an argument
-    (the old process-wide decode-schedule setting is gone)."""
+    """No writable data of the library's own but the no-allocation decode's
+    scratch array and its per-device address cache: every choice is an
+    argument (the old process-wide decode-schedule setting is gone)."""
     out = subprocess.run(["nm", "-C", "--defined-only", GB.LIB_PATH], capture_output=True,
                          text=True).stdout
     # (kernel launch handles are data symbols too, but carry a signature)
-    mine = [l for l in out.splitlines()
-            if len(l.split()) >= 3 and l.split()[1] in "bBdD" and "gqa" in l and "(" not in l]
-    assert mine == [], mine
+    mine = [l.split(None, 2)[2] for l in out.splitlines()
+            if len(l.split()) >= 3 and l.split()[1] in "bBdD" and
+            ("gqa" in l or "anonymous namespace" in l) and "(" not in l.split(None, 2)[2]
+            .replace("(anonymous namespace)", "")]
+    assert sorted(mine) == ["(anonymous namespace)::g_scratch_ptr",
+                            "(anonymous namespace)::scratch"], mine
 
 
 def test_status_strings():
@@ -187,6 +192,32 @@ def _decode_args(**kw):
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_block_decode(*_decode_args(**kw)) == code
+
+
+_NOALLOC_KEYS = ("x", "wq", "wk", "wv", "wo", "kc", "vc", "n_kv", "T_max", "rope", "start_pos",
+                 "B", "out", "out_bf16", "accumulate", "schedule", "probe", "stream")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), ENULL), (dict(out=None), ENULL), (dict(B=0), ESHAPE), (dict(n_kv=12), EARG),
+    (dict(start_pos=1024), ERANGE), (dict(accumulate=3), EARG), (dict(schedule=7), EARG),
+    (dict(B=3, schedule=FUSED), EARG), (dict(out=_fake(0)), EALIAS),
+    # beyond the 16 MiB scratch array: rejected before anything runs
+    (dict(B=512), EWS), (dict(B=128, n_kv=32), EWS),
+])
+def test_decode_noalloc_rejects_bad_arguments(kw, code):
+    a = dict(zip(_DECODE_KEYS, _decode_args()))
+    a.update(kw)
+    assert G.lib().gqa_block_decode_noalloc(*[a[k] for k in _NOALLOC_KEYS]) == code
+
+
+def test_decode_noalloc_scratch_limit_matches_the_workspace_sizes():
+    """The shapes the scratch array admits are those whose decode workspace
+    fits in GQA_NOALLOC_SCRATCH_BYTES."""
+    assert "#define GQA_NOALLOC_SCRATCH_BYTES  (16u << 20)" in open(HEADER).read()
+    lim = G.NOALLOC_SCRATCH_BYTES
+    assert _wsb(G.OP_DECODE, 200, 1024) <= lim < _wsb(G.OP_DECODE, 512, 1024)
+    assert _wsb(G.OP_DECODE, 64, 1024, n_kv=32) <= lim < _wsb(G.OP_DECODE, 128, 1024, n_kv=32)
 
 
 def test_decode_workspace_check_uses_the_decode_size():
