@@ -57,24 +57,47 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libgqa.so; returns its path."""
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (argument validation, workspace carving, dispatch).  Every
+# sanitizer flag applies to the host compilation only; the gfx950 code is
+# built as usual.  Load it with the clang ASan runtime preloaded, e.g.
+#   LD_PRELOAD=<libclang_rt.asan-x86_64.so> GQA_LIB=_build/asan/libgqa.so python ...
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-shared-libsan"]
+ASAN_LIB = os.path.join(BUILD, "asan", "libgqa.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that hipcc links against."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source for gfx950 and link libgqa.so; returns its path.
+    With sanitize, the host side is instrumented and the library goes to
+    _build/asan/ instead (for the host tests only)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    out_dir = os.path.join(BUILD, "asan") if sanitize else BUILD
+    lib = ASAN_LIB if sanitize else LIB
+    extra = SANITIZE_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    path = build(verbose="--verbose" in sys.argv)
+    path = build(verbose="--verbose" in sys.argv, sanitize="--sanitize" in sys.argv)
     print(path)

@@ -36,7 +36,9 @@ WS_MAGIC = 0x31415147
 DEBUG = os.environ.get("GQA_DEBUG", "") == "1"
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgqa.so")
+# GQA_LIB names another build of the same library (the host-sanitizer build
+# of the tests); by default the in-tree libgqa.so is loaded
+LIB_PATH = os.environ.get("GQA_LIB") or os.path.join(_HERE, "libgqa.so")
 
 STATUS = {
     0: "GQA_OK", -1: "GQA_ERR_NULL", -2: "GQA_ERR_SHAPE", -3: "GQA_ERR_RANGE",

@@ -55,7 +55,9 @@ def test_library_has_no_mutable_global_state_symbols():
     """No writable data of the library's own but the no-allocation decode's
     scratch array and its per-device address cache: every choice is an
     argument (the old process-wide decode-schedule setting is gone)."""
-    out = subprocess.run(["nm", "-C", "--defined-only", GB.LIB_PATH], capture_output=True,
+    # the product library itself (not a sanitizer build named by GQA_LIB)
+    product = os.path.join(os.path.dirname(GB.__file__), "libgqa.so")
+    out = subprocess.run(["nm", "-C", "--defined-only", product], capture_output=True,
                          text=True).stdout
     # (kernel launch handles are data symbols too, but carry a signature)
     mine = [l.split(None, 2)[2] for l in out.splitlines()

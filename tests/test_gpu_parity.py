@@ -184,6 +184,74 @@ def test_decode_stacked_blocks_residual():
     assert torch.equal(xa.cpu(), h.cpu().to(torch.bfloat16))
 
 
+@pytest.mark.timeout(600)
+def test_decode_stacked_blocks_at_full_context():
+    """Three stacked blocks at the long-context point (B = 8, P = 131,071 in
+    every block, 4 GiB of cache per block), h <- h + Delta with bf16(h) as the
+    next block's input; one sampled sequence against the oracle's block by
+    block chain, and every other cache bit of every block unchanged."""
+    B, P, T_max, L = 8, 131071, 131072, 3
+    gen = synth.generator(17)
+    x0 = synth.randn_bf16(gen, (B, 4096))
+    dgen = synth.generator(18, DEV)
+    blocks = []
+    for _ in range(L):
+        w = [t.to(DEV) for t in synth.block_weights(gen)]
+        kc, vc = G.empty_caches(B, T_max, DEV)
+        synth.fill_randn_bf16_(kc, dgen)
+        synth.fill_randn_bf16_(vc, dgen)
+        blocks.append((w, kc, vc, kc.clone(), vc.clone()))
+    rope = G.rope_table(T_max, device=DEV)
+    ws = G.workspace(G.OP_DECODE, B, T_max, DEV)
+    h = x0.to(DEV).float()
+    xa, xb = x0.to(DEV), torch.empty((B, 4096), dtype=torch.bfloat16, device=DEV)
+    for w, kc, vc, _, _ in blocks:
+        G.block_decode(xa, *w, kc, vc, rope, P, out=h, out_bf16=xb, accumulate=True, ws=ws)
+        xa, xb = xb, xa
+    torch.cuda.synchronize()
+    assert G.workspace_errors(ws) == 0
+    seq = [5]
+    ws_ = ([f64(t) for t in w] for w, *_ in blocks)
+    kcs = (f64(G.kcache_by_position(k0[seq])[:, :P]) for *_, k0, _ in blocks)
+    vcs = (f64(G.vcache_read(v0[seq], 0, P)) for *_, v0 in blocks)
+    h_ref, _ = O.stacked_decode(f64(x0[seq]), ws_, kcs, vcs, P)
+    assert_close("stacked residual at P=131071", f64(h[seq]) - f64(x0[seq]), h_ref - f64(x0[seq]))
+    for _, kc, vc, k0, v0 in blocks:           # only row P of each cache changed
+        a, b = kc.clone(), k0.clone()
+        G.kcache_by_position(a)[:, P] = 0
+        G.kcache_by_position(b)[:, P] = 0
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        a, b = vc.clone(), v0.clone()
+        G.vcache_blocks(a)[:, P // 32, P % 32] = 0
+        G.vcache_blocks(b)[:, P // 32, P % 32] = 0
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_resumes_from_copied_caches():
+    """Checkpoint and resume: prefill 300 tokens, copy the caches out (to the
+    host and back into fresh buffers), and decode token 300 from the copy.
+    Delta and the appended rows equal the decode on the original caches bit
+    for bit, and match the oracle of the 301-token prefill's last row."""
+    T = 300
+    full = PrefillCase(2, T + 1, 320, dev=DEV)
+    ref = full.oracle()
+    kc, vc = G.empty_caches(2, 320, DEV)
+    G.block_prefill(full.xd[:, :T].contiguous(), *full.wd, kc, vc, full.rope)
+    torch.cuda.synchronize()
+    k_host, v_host = kc.cpu(), vc.cpu()                 # the checkpoint
+    kc2, vc2 = G.empty_caches(2, 320, DEV)
+    kc2.copy_(k_host)
+    vc2.copy_(v_host)
+    x = full.xd[:, T].contiguous()
+    a = G.block_decode(x, *full.wd, kc, vc, full.rope, T)
+    b = G.block_decode(x, *full.wd, kc2, vc2, full.rope, T)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
+    assert_close("resumed decode vs oracle", f64(b), ref.delta[:, T])
+
+
 def test_decode_fused_largest_admitted_context(schedule):
     """B=1 at start_pos 2,047: 16 splits x 8 kv heads, the most attention
     workgroups the one-launch schedule admits."""
