@@ -794,11 +794,20 @@ __device__ __forceinline__ void proj_qkv_store(const DecodeParams& p, f32x4 v, i
     for (int e = 0; e < 4; ++e) dst[e * VB] = (uint16_t)f32_to_bf16_bits(y[e]);
   }
 }
-constexpr int kP2Feat = 128;                 // features per workgroup
 constexpr int kP2Kc = 128;                   // K per chunk
+// 16-row matrix-core tiles per wave: 2, so a 4-wave workgroup owns 128
+// features.  One tile per wave with twice the workgroups, or twice the K
+// splits, measured no faster at B = 64 (the chunk chain and the split-K
+// tail, not the workgroup count, set the time).
+template <int MODE>
+constexpr int p2_tiles() { return 2; }
+// features per workgroup
+template <int MODE>
+constexpr int p2_feat() { return 64 * p2_tiles<MODE>(); }
 // K splits: 4 for QKV (192 workgroups), 8 for wo (256 workgroups)
 template <int MODE>
 constexpr int p2_splits() { return MODE == 0 ? 4 : 8; }
+constexpr int kP2CntStride = 16;             // ints between split-K counters
 constexpr int kP2Cols = 64;                  // columns per launch
 constexpr int kP2Ring = 4;                   // chunks in flight: loaded 3 ahead
 
@@ -812,6 +821,8 @@ __device__ __forceinline__ void st_dev_x4(void* base, uint32_t byte_off, u32x4 v
 template <int MODE, int KV = KVH>   // MODE 0: QKV + RoPE + cache append, 1: wo (+ residual)
 __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_base) {
   constexpr int NP = MODE == 0 ? 1 : 2;        // activation parts (wo: hi, lo)
+  constexpr int FT = p2_tiles<MODE>();         // 16-row weight tiles per wave
+  constexpr int kP2Feat = p2_feat<MODE>();
   constexpr int kP2KS = p2_splits<MODE>();
   constexpr int kP2Kr = D / kP2KS;             // K range of a workgroup
   constexpr int kP2Chunks = kP2Kr / kP2Kc;
@@ -842,10 +853,10 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
   }
 
   // A operand: weight row of tile ft, k offset (lane >> 4) * 8 in each step
-  const uint16_t* wrow[2];
+  const uint16_t* wrow[FT];
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft) {
-    const int f = fb * kP2Feat + 32 * w + 16 * ft + (lane & 15);
+  for (int ft = 0; ft < FT; ++ft) {
+    const int f = fb * kP2Feat + 16 * FT * w + 16 * ft + (lane & 15);
     if (MODE == 0)
       wrow[ft] = (f < D ? p.wq + (size_t)f * D
                         : (f < D + KV * HD ? p.wk + (size_t)(f - D) * D
@@ -870,10 +881,10 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     }
   }
 
-  u32x4 wb[kP2Ring][2][4];                      // [ring slot][tile][k-step]
-  auto load_w = [&](int chunk, u32x4 (&dst)[2][4]) {
+  u32x4 wb[kP2Ring][FT][4];                     // [ring slot][tile][k-step]
+  auto load_w = [&](int chunk, u32x4 (&dst)[FT][4]) {
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+    for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int s = 0; s < 4; ++s) dst[ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kP2Kc + s * 32);
   };
@@ -886,16 +897,16 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
                                          (lds_void*)(GQA_SX(part, buf) + (4 * w + j) * 4 * kP2Kc), 16, 0, 0);
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[FT][4];
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft)
+  for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Chunks are loaded kP2Ring - 1 ahead, each as W(c) then X(c) (8 + 4 NP
+  // Chunks are loaded kP2Ring - 1 ahead, each as W(c) then X(c) (4 FT + 4 NP
   // loads per wave).  Chunk c has landed once no more than the loads of the
   // chunks issued after it remain in flight.
-  constexpr int kPerChunk = 8 + 4 * NP;
+  constexpr int kPerChunk = 4 * FT + 4 * NP;
 #pragma unroll
   for (int c = 0; c < kP2Ring - 1; ++c) {
     load_w(c, wb[c]);
@@ -939,12 +950,12 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int ft = 0; ft < 2; ++ft) acc[ft][t] = mfma_bf16(wb[c % kP2Ring][ft][s], xb[s][t], acc[ft][t]);
+          for (int ft = 0; ft < FT; ++ft) acc[ft][t] = mfma_bf16(wb[c % kP2Ring][ft][s], xb[s][t], acc[ft][t]);
     }
   }
 
-  // partials [fb][ks][64 columns][128 features] fp32; lane holds features
-  // 32w + 16ft + 4(lane >> 4) + e (e < 4) of column 16t + (lane & 15)
+  // partials [fb][ks][64 columns][kP2Feat features] fp32; lane holds features
+  // 16 FT w + 16ft + 4(lane >> 4) + e (e < 4) of column 16t + (lane & 15)
   float* part_fb = p.part;
   const uint32_t pbase = (uint32_t)((fb * kP2KS + ks) * kP2Cols) * kP2Feat * 4u;
 #pragma unroll
@@ -952,15 +963,15 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     const int col = 16 * t + (lane & 15);
     if (col >= ncols) continue;
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) {
-      const int fl = 32 * w + 16 * ft + 4 * (lane >> 4);
+    for (int ft = 0; ft < FT; ++ft) {
+      const int fl = 16 * FT * w + 16 * ft + 4 * (lane >> 4);
       st_dev_x4(part_fb, pbase + (uint32_t)(col * kP2Feat + fl) * 4u,
                 __builtin_bit_cast(u32x4, acc[ft][t]));
     }
   }
   wait_vm();
   __syncthreads();
-  int* cnt = p.sync + kSyncProj + 32 * fb;
+  int* cnt = p.sync + kSyncProj + kP2CntStride * fb;
   if (tid == 0) {
     const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm_last = prev == kP2KS - 1;
@@ -972,7 +983,7 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
   // last of the feature block: sum the K ranges in order, then the epilogue;
   // all of a thread's loads (partials, RoPE entries, the residual) go out
   // before the first is used
-  constexpr int kItems = kP2Cols * (kP2Feat / 4) / 256;     // 8 per thread
+  constexpr int kItems = kP2Cols * (kP2Feat / 4) / 256;     // 4 FT per thread
   constexpr int kBatch = kP2KS <= 4 ? kItems : kItems / 2;  // items whose loads go out together
   const int nitems = ncols * (kP2Feat / 4);
   const float2* rrow = reinterpret_cast<const float2*>(p.rope) + (size_t)p.start_pos * PAIRS;
@@ -1099,7 +1110,7 @@ void decode_ws_carve(void* ws, int B, int kv, DecodeParams* p) {
 
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
-    const dim3 grid((D + 2 * p.kv * HD) / kP2Feat * p2_splits<0>());
+    const dim3 grid((D + 2 * p.kv * HD) / p2_feat<0>() * p2_splits<0>());
     const size_t lds = kP2Ring * kP2Cols * kP2Kc * 2;
     for (int c = 0; c < p.B; c += kP2Cols) {
       switch (p.kv) {
@@ -1141,7 +1152,7 @@ hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
     for (int c = 0; c < p.B; c += kP2Cols)
-      hipLaunchKernelGGL(decode_proj_kernel<1>, dim3(D / kP2Feat * p2_splits<1>()), dim3(256),
+      hipLaunchKernelGGL(decode_proj_kernel<1>, dim3(D / p2_feat<1>() * p2_splits<1>()), dim3(256),
                          2 * kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
     return hipGetLastError();
   }

@@ -33,7 +33,7 @@ constexpr int kWsMagic = 0x31415147; // "GQA1"
 constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups of kv head g
 constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
 constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
-constexpr int kSyncProj = 10752;     // + 32*fb: K ranges of projection feature block fb summed
+constexpr int kSyncProj = 10752;     // + 16*fb: K ranges of projection feature block fb summed
 constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
 constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
 constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
@@ -47,7 +47,7 @@ constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedul
 // take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
 constexpr unsigned kWoHoldTicks = 500;
 static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
-static_assert(kSyncProj + 32 * ((4096 + 2 * 32 * 128) / 128) <= kSyncBytes / 4,
+static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncBytes / 4,
               "sync region too small for the projection counters of 32 kv heads");
 
 struct DecodeParams {
