@@ -21,16 +21,18 @@ namespace gqa {
 // QKV projection + RoPE + cache append
 // ---------------------------------------------------------------------------
 
-// Output features of QKV workgroup `blk`: 8 consecutive features, 2 per wave.
-// The three-launch schedule takes them in feature order.  The fused schedule
-// gives kv head g the workgroups blk = g (mod 8), which all run on XCD g,
-// where the head's attention workgroups run too (Q of its 4 query heads: 64
+// Output features of QKV workgroup `blk` of W waves: 2W consecutive
+// features, 2 per wave.  The three-launch schedule takes them in feature
+// order.  The fused schedule (W = 4) gives kv head g the workgroups
+// blk = g (mod 8), which the dispatcher usually places on one XCD together
+// with the head's attention workgroups (Q of its 4 query heads: 64
 // workgroups, then K: 16, then V: 16).
-template <bool FUSED>
+template <bool FUSED, int W>
 __device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
+  static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
   if (!FUSED) {
     *grp = 0;
-    return blk * 8;
+    return blk * 2 * W;
   }
   const int g = blk & 7, r = blk >> 3;
   *grp = g;
@@ -39,14 +41,15 @@ __device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
   return D + KVH * HD + g * HD + (r - 80) * 8;
 }
 
-// KV: kv heads of the projection (the fused schedule runs KV = 8 only).
-template <int NB, bool FUSED, int KV = KVH>
+// KV: kv heads of the projection (the fused schedule runs KV = 8 only); W:
+// waves of the workgroup.
+template <int NB, bool FUSED, int KV = KVH, int W = 4>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
   static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
   constexpr int kNqkv = D + 2 * KV * HD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int grp;
-  const int r0 = qkv_first_feature<FUSED>(blk, &grp) + wave * 2;   // even feature, 0..6142
+  const int r0 = qkv_first_feature<FUSED, W>(blk, &grp) + wave * 2;   // even feature, 0..6142
   const uint16_t* wbase;
   int rr;
   if (r0 < D) {
@@ -56,17 +59,20 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   } else {
     wbase = p.wv; rr = r0 - D - KV * HD;
   }
-  // the weight stream does not depend on x: start it before staging x
+  // x goes to LDS by direct loads issued first; the 16 weight loads follow
+  // at once, and x has landed once only they remain in flight
+  stage_rows_async<NB, W>(xs, p.x + (size_t)b0 * D);
+  uint32_t gp[(D / 2) / (64 * W)];
+  if (p.norm_w) load_norm_gain<W>(p.norm_w, gp);
   u32x4 wa[8], wb[8];
   load_rows2(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, lane, wa, wb);
-
-  stage_rows<NB>(xs, p.x + (size_t)b0 * D);
+  wait_loads_except<16>();
   if (!FUSED && blk == 0 && b0 == 0) {
     // the attention kernel that follows counts split arrivals from zero
     for (int i = threadIdx.x; i < p.B * KV; i += blockDim.x) p.counters[i] = 0;
   }
-  __syncthreads();
-  if (p.norm_w) norm_rows<NB>(xs, p.norm_w, p.norm_eps);
+  lds_barrier();
+  if (p.norm_w) norm_rows<NB, W>(xs, gp, p.norm_eps);
 
   float acc[2][NB];
   gemv_rows2<NB, 1>(wa, wb, xs, lane, acc);
@@ -132,10 +138,13 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   }
 }
 
-template <int NB, int KV>
-__global__ void __launch_bounds__(256) decode_qkv_kernel(DecodeParams p, int b0) {
+// W waves a workgroup: 4, or 8 for 7 and 8 tokens, whose 56-64 KiB of staged
+// inputs would otherwise leave room for only 512 resident 4-wave workgroups
+// (the weights would stream in two rounds).
+template <int NB, int KV, int W>
+__global__ void __launch_bounds__(64 * W) decode_qkv_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[NB * (D / 2)];
-  qkv_body<NB, false, KV>(p, b0, blockIdx.x, xs);
+  qkv_body<NB, false, KV, W>(p, b0, blockIdx.x, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -595,17 +604,26 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
 // wo projection (+ residual)
 // ---------------------------------------------------------------------------
 
-template <int NB, bool FUSED>
+template <int NB, bool FUSED, int W = 4>
 __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
+  static_assert(!FUSED || W == 4, "the fused schedule's wo roles are 4-wave workgroups");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = (blk * 4 + wave) * 2;
+  const int r0 = (blk * W + wave) * 2;
   u32x4 wa[8], wb[8];
   if (FUSED) {
     // hold the weight stream back while QKV finishes (kWoHoldTicks)
     const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
     while (__builtin_amdgcn_s_memrealtime() - t0 < kWoHoldTicks) __builtin_amdgcn_s_sleep(8);
+  } else {
+    // O (hi and lo parts) goes to LDS by direct loads ahead of the weights
+    stage_rows_async<NB, W>(xs, p.o_hi + (size_t)b0 * D);
+    stage_rows_async<NB, W>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
   }
   load_rows2(p.wo + (size_t)r0 * D, p.wo + (size_t)(r0 + 1) * D, lane, wa, wb);
+  if (!FUSED) {
+    wait_loads_except<16>();
+    lds_barrier();
+  }
   // fused: 0 normal, 1 the wait timed out, 2 the workspace is uninitialised;
   // in either error case this workgroup's outputs are NaN
   __shared__ int wo_state;
@@ -661,11 +679,8 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
       reinterpret_cast<u32x4*>(xs)[threadIdx.x + 256 * k] = hv[k];
       reinterpret_cast<u32x4*>(xs + NB * (D / 2))[threadIdx.x + 256 * k] = lv[k];
     }
-  } else {
-    stage_rows<NB>(xs, p.o_hi + (size_t)b0 * D);
-    stage_rows<NB>(xs + NB * (D / 2), p.o_lo + (size_t)b0 * D);
+    __syncthreads();
   }
-  __syncthreads();
 
   float acc[2][NB];
   gemv_rows2<NB, 2>(wa, wb, xs, lane, acc);
@@ -696,10 +711,13 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
     *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
 }
 
-template <int NB>
-__global__ void __launch_bounds__(256) decode_wo_kernel(DecodeParams p, int b0) {
+// W waves a workgroup: 4 up to 4 tokens, 8 above, where the staged hi/lo
+// parts (80-128 KiB) allow one workgroup per CU: 256 workgroups of 16 rows
+// then hold the whole weight stream in flight in one pass.
+template <int NB, int W>
+__global__ void __launch_bounds__(64 * W) decode_wo_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[2 * NB * (D / 2)];
-  wo_body<NB, false>(p, b0, blockIdx.x, xs);
+  wo_body<NB, false, W>(p, b0, blockIdx.x, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,11 +1139,15 @@ hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  const int blocks = (D + 2 * p.kv * HD) / 2 / 4;    // one wave per row pair, 4 waves per workgroup
   for (int b0 = 0; b0 < p.B; b0 += kGemvMaxNB) {
     const int nb = min(kGemvMaxNB, p.B - b0);
-#define GQA_LAUNCH_QKV_KV(N, KV) \
-    hipLaunchKernelGGL((decode_qkv_kernel<N, KV>), dim3(blocks), dim3(256), 0, s, p, b0)
+    // one wave per row pair
+#define GQA_LAUNCH_QKV_KV(N, KV)                                                          \
+    {                                                                                     \
+      constexpr int W = (N) >= 7 ? 8 : 4;                                                 \
+      hipLaunchKernelGGL((decode_qkv_kernel<N, KV, W>), dim3((D + 2 * p.kv * HD) / 2 / W), \
+                         dim3(64 * W), 0, s, p, b0);                                      \
+    }
 #define GQA_LAUNCH_QKV(N)                                     \
     switch (p.kv) {                                           \
       case 16: GQA_LAUNCH_QKV_KV(N, 16); break;               \
@@ -1156,11 +1178,13 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
                          2 * kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
     return hipGetLastError();
   }
-  const int blocks = D / 2 / 4;
   for (int b0 = 0; b0 < p.B; b0 += kWoMaxNB) {
     const int nb = min(kWoMaxNB, p.B - b0);
-#define GQA_LAUNCH_WO(N) \
-    hipLaunchKernelGGL(decode_wo_kernel<N>, dim3(blocks), dim3(256), 0, s, p, b0)
+#define GQA_LAUNCH_WO(N)                                                                     \
+    {                                                                                        \
+      constexpr int W = (N) >= 5 ? 8 : 4;                                                    \
+      hipLaunchKernelGGL((decode_wo_kernel<N, W>), dim3(D / 2 / W), dim3(64 * W), 0, s, p, b0); \
+    }
     GQA_NB_SWITCH(nb, GQA_LAUNCH_WO)
 #undef GQA_LAUNCH_WO
   }

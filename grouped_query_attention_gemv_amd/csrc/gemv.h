@@ -57,55 +57,98 @@ __device__ __forceinline__ void load_rows2(const uint16_t* __restrict__ w0,
   }
 }
 
-// Copy NB rows of 4096 bf16 (one part) from global into LDS.
-template <int NB>
-__device__ __forceinline__ void stage_rows(uint32_t* xs, const uint16_t* __restrict__ src) {
-  for (int i = threadIdx.x; i < NB * (D / 8); i += blockDim.x) {
-    const int t = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<u32x4*>(xs + t * (D / 2) + u * 4) = ld_u32x4(src + (size_t)t * D + u * 8);
-  }
+// Start copying NB rows of 4096 bf16 (one part) from global memory into LDS
+// with direct-to-LDS loads (16 bytes a lane, 1 KiB a wave instruction),
+// spread over the W waves of the workgroup.  Issued before a wave's weight
+// loads, the copy is complete once no more than those weight loads remain in
+// flight (wait_loads_except<16>), instead of queueing behind them.
+template <int NB, int W>
+__device__ __forceinline__ void stage_rows_async(uint32_t* xs, const uint16_t* __restrict__ src) {
+  constexpr int kPieces = NB * (D * 2 / 1024);      // 8 KiB a row
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = wave; i < kPieces; i += W)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + (size_t)i * 512 + lane * 8),
+                                     (lds_void*)(reinterpret_cast<char*>(xs) + i * 1024), 16, 0, 0);
+  asm volatile("" ::: "memory");
 }
+
+// Workgroup barrier for LDS data only: this wave's LDS accesses complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// outstanding global loads (the weight stream keeps flowing); data that
+// direct-to-LDS loads wrote must be waited for first (wait_loads_except).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N memory loads of this wave are still in flight.  The
+// builtin (not inline asm) lets the compiler's own counter bookkeeping see
+// the wait, so it inserts no coarser one where earlier loads are used.
+// Encoding of the gfx9 s_waitcnt immediate: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4] and lgkmcnt [11:8] left at their "no wait" maxima.
+template <int N>
+__device__ __forceinline__ void wait_loads_except() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (N & 15) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 
 // Layer pre-norm of the NB staged rows, in place: x -> bf16(x * r * g) with
 // r = 1 / sqrt(mean(x^2) + eps) per row (page "Llama 3.1 8B . Grouped-query
 // attention", code section: the block receives attention_norm(x); the norm
-// is read as the standard RMSNorm with a per-feature gain).  Thread i owns
-// bf16 pairs i + 256*j, j < 8, of every row; the row sums combine the four
-// waves in a fixed order.
-template <int NB>
-__device__ __forceinline__ void norm_rows(uint32_t* xs, const uint16_t* __restrict__ g, float eps) {
-  __shared__ float red[4 * NB];
+// is read as the standard RMSNorm with a per-feature gain).  With W waves,
+// thread i owns bf16 pairs i + 64W*j of every row; the row sums combine the
+// waves pairwise in a fixed order.  The gain pairs gp come from
+// load_norm_gain, issued before the weight stream so that waiting for them
+// does not wait for the weights.
+template <int W>
+__device__ __forceinline__ void load_norm_gain(const uint16_t* __restrict__ g, uint32_t (&gp)[(D / 2) / (64 * W)]) {
+  constexpr int NT = 64 * W, J = (D / 2) / NT;
+#pragma unroll
+  for (int j = 0; j < J; ++j) gp[j] = reinterpret_cast<const uint32_t*>(g)[threadIdx.x + NT * j];
+}
+
+template <int NB, int W = 4>
+__device__ __forceinline__ void norm_rows(uint32_t* xs, const uint32_t (&gp)[(D / 2) / (64 * W)], float eps) {
+  constexpr int NT = 64 * W, J = (D / 2) / NT;
+  __shared__ float red[W * NB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float ss[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     ss[t] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t u = xs[t * (D / 2) + tid + 256 * j];
+    for (int j = 0; j < J; ++j) {
+      const uint32_t u = xs[t * (D / 2) + tid + NT * j];
       const float a = bf16_bits_to_f32(u & 0xffffu), b = bf16_bits_to_f32(u >> 16);
       ss[t] += a * a + b * b;
     }
     ss[t] = wave_sum(ss[t]);
     if (lane == 0) red[w * NB + t] = ss[t];
   }
-  uint32_t gp[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) gp[j] = reinterpret_cast<const uint32_t*>(g)[tid + 256 * j];
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
-    const float tot = (red[t] + red[NB + t]) + (red[2 * NB + t] + red[3 * NB + t]);
-    const float r = 1.f / sqrtf(tot * (1.f / D) + eps);
+    float v[W];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t* q = xs + t * (D / 2) + tid + 256 * j;
+    for (int ww = 0; ww < W; ++ww) v[ww] = red[ww * NB + t];
+#pragma unroll
+    for (int step = 1; step < W; step *= 2)
+#pragma unroll
+      for (int ww = 0; ww + step < W; ww += 2 * step) v[ww] += v[ww + step];
+    const float r = 1.f / sqrtf(v[0] * (1.f / D) + eps);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      uint32_t* q = xs + t * (D / 2) + tid + NT * j;
       const uint32_t u = *q;
       *q = pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * r * bf16_bits_to_f32(gp[j] & 0xffffu),
                        bf16_bits_to_f32(u >> 16) * r * bf16_bits_to_f32(gp[j] >> 16));
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 }  // namespace gqa

@@ -18,7 +18,7 @@ constexpr int kMaxSplit = 64;        // most position splits per (sequence, kv h
 constexpr int kPartStride = 132;     // floats per (split, head) partial: m, l, pad, pad, o[128]
 constexpr int kGemvMaxNB = 8;        // tokens per pass of the QKV bandwidth GEMV
 constexpr int kGemvMaxB = 8;         // larger batches use the matrix-core projections
-constexpr int kWoMaxNB = 4;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
+constexpr int kWoMaxNB = 8;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
 
 // Synchronisation words at the start of every workspace, used by the fused
 // decode schedule (one launch whose workgroups hand results to each other).

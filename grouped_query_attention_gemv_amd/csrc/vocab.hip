@@ -29,15 +29,22 @@ __global__ void __launch_bounds__(256) vocab_gemv_kernel(VocabParams p, int b0) 
     *w0 = p.w + (size_t)r0 * D;
     *w1 = p.w + (size_t)r1 * D;
   };
+  // z (and the norm gain) go out ahead of the first weight pair, so that
+  // waiting for them leaves that pair's 16 loads in flight
+  stage_rows_async<NB, 4>(xs, p.z + (size_t)b0 * D);
+  uint32_t gp[(D / 2) / 256];
+  if (p.norm_w) load_norm_gain<4>(p.norm_w, gp);
   u32x4 wa[2][8], wb[2][8];
   const uint16_t *w0, *w1;
   if (pr < pairs) {
     rows(pr, &w0, &w1);
     load_rows2(w0, w1, lane, wa[0], wb[0]);
+    wait_loads_except<16>();
+  } else {
+    wait_loads_except<0>();
   }
-  stage_rows<NB>(xs, p.z + (size_t)b0 * D);
-  __syncthreads();
-  if (p.norm_w) norm_rows<NB>(xs, p.norm_w, p.norm_eps);
+  lds_barrier();
+  if (p.norm_w) norm_rows<NB>(xs, gp, p.norm_eps);
 
   auto finish = [&](int q, const float (&acc)[2][NB]) {
     float v0 = 0.f, v1 = 0.f;
