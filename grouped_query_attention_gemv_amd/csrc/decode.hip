@@ -767,11 +767,12 @@ __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
 //  - workgroup (fb, ks) owns 128 output features and one of KS equal K
 //    ranges (KS = 4 for QKV, 8 for wo); its 4 waves own 32 features each
 //    (two 16-row A tiles);
-//  - K advances in chunks of 128.  The chunk of the activation columns (up to
-//    64 per launch) is copied once into LDS (global_load_lds) and read by all
-//    4 waves as the B operand, so each activation byte leaves L2 once per
+//  - the activation columns (up to 64 per launch) of the workgroup's whole K
+//    range are copied into LDS first (global_load_lds, 128 KiB) and read by
+//    all 4 waves as the B operand, so each activation byte leaves L2 once per
 //    workgroup.  Each wave's weight rows come straight from HBM into
-//    registers (its A operand).  Both stream three chunks ahead;
+//    registers (its A operand) in chunks of 128 K, three chunks ahead; after
+//    the one barrier for the activations the waves run unsynchronised;
 //  - the KS K ranges of a feature block are summed by the last of its KS
 //    workgroups to finish (device-scope partials and counter, fixed order),
 //    which then runs the epilogue.
@@ -827,7 +828,10 @@ template <int MODE>
 constexpr int p2_splits() { return MODE == 0 ? 4 : 8; }
 constexpr int kP2CntStride = 16;             // ints between split-K counters
 constexpr int kP2Cols = 64;                  // columns per launch
-constexpr int kP2Ring = 4;                   // chunks in flight: loaded 3 ahead
+constexpr int kP2Ring = 4;                   // weight chunks in flight: loaded 3 ahead
+// dynamic LDS of a projection workgroup: the activations' whole K range
+template <int MODE>
+constexpr size_t p2_lds_bytes() { return (size_t)(MODE == 0 ? 1 : 2) * kP2Cols * (D / p2_splits<MODE>()) * 2; }
 
 // 16-byte device-scope store at base + byte_off (base wave-uniform).
 __device__ __forceinline__ void st_dev_x4(void* base, uint32_t byte_off, u32x4 v) {
@@ -844,10 +848,9 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
   constexpr int kP2KS = p2_splits<MODE>();
   constexpr int kP2Kr = D / kP2KS;             // K range of a workgroup
   constexpr int kP2Chunks = kP2Kr / kP2Kc;
-  // [NP][kP2Ring buffers][64 rows][128 K] bf16, dynamic
+  // [NP][64 rows][kP2Kr] bf16, dynamic
   extern __shared__ __attribute__((aligned(16))) uint16_t sx_dyn[];
   __shared__ int sm_last;
-#define GQA_SX(part, buf) (sx_dyn + ((part) * kP2Ring + (buf)) * (kP2Cols * kP2Kc))
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int ks = blockIdx.x % kP2KS, fb = blockIdx.x / kP2KS;
   const int ncols = min(kP2Cols, p.B - c_base);
@@ -883,21 +886,30 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     else
       wrow[ft] = p.wo + (size_t)f * D + kbase + (lane >> 4) * 8;
   }
-  // activation copies: instruction j of this wave fills rows (4w + j) * 4 ..
-  // + 3 of the chunk (256 bytes each); lane i writes row +i/16, LDS chunk
-  // i % 16, which holds logical chunk (i % 16) ^ (row & 7)
-  const uint16_t* xsrc[NP][4];
+
+  // The activation columns' whole K range goes to LDS once, first:
+  // [NP][64 rows][kP2Kr] bf16, 16-byte unit u of row r at physical unit
+  // u ^ (r & 7).  Copy instruction i of a part fills bytes [1 KiB i, 1 KiB
+  // (i+1)); lane l writes the unit l of that KiB.
+  constexpr int kRowUnits = kP2Kr / 8;                      // 16-byte units a row
+  constexpr int kCopies = kP2Cols * kP2Kr * 2 / 1024;       // per part
+  static_assert(kCopies % 4 == 0, "each wave issues the same number of copies");
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (4 * w + j) * 4 + (lane >> 4);
-    const int col = c_base + min(row, ncols - 1);
-    const int lchunk = (lane & 15) ^ (row & 7);
+  for (int part = 0; part < NP; ++part) {
+    const uint16_t* base = MODE == 0 ? p.x : (part == 0 ? p.o_hi : p.o_lo);
 #pragma unroll
-    for (int part = 0; part < NP; ++part) {
-      const uint16_t* base = MODE == 0 ? p.x : (part == 0 ? p.o_hi : p.o_lo);
-      xsrc[part][j] = base + (size_t)col * D + kbase + lchunk * 8;
+    for (int j = 0; j < kCopies / 4; ++j) {
+      const int i = 4 * j + w;
+      const int unit = i * 64 + lane;                       // physical, over the part
+      const int row = unit / kRowUnits;
+      const int lu = (unit % kRowUnits) ^ (row & 7);
+      const int col = c_base + min(row, ncols - 1);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + (size_t)col * D + kbase + lu * 8),
+                                       (lds_void*)(sx_dyn + (part * kP2Cols * kP2Kr) + i * 512), 16, 0, 0);
     }
   }
+  // the wait counts below assume every copy is issued before any weight load
+  asm volatile("" ::: "memory");
 
   u32x4 wb[kP2Ring][FT][4];                     // [ring slot][tile][k-step]
   auto load_w = [&](int chunk, u32x4 (&dst)[FT][4]) {
@@ -906,14 +918,6 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 #pragma unroll
       for (int s = 0; s < 4; ++s) dst[ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kP2Kc + s * 32);
   };
-  auto load_x = [&](int chunk, int buf) {
-#pragma unroll
-    for (int part = 0; part < NP; ++part)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xsrc[part][j] + chunk * kP2Kc),
-                                         (lds_void*)(GQA_SX(part, buf) + (4 * w + j) * 4 * kP2Kc), 16, 0, 0);
-  };
 
   f32x4 acc[FT][4];
 #pragma unroll
@@ -921,32 +925,32 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Chunks are loaded kP2Ring - 1 ahead, each as W(c) then X(c) (4 FT + 4 NP
-  // loads per wave).  Chunk c has landed once no more than the loads of the
-  // chunks issued after it remain in flight.
-  constexpr int kPerChunk = 4 * FT + 4 * NP;
+  // Each wave's weight chunks stream kP2Ring - 1 ahead (4 FT loads each).
+  // Chunk c has landed once no more than the loads of the chunks issued after
+  // it remain in flight; the activations, issued before all of them, have
+  // landed once the first kP2Ring - 1 chunks alone remain.  One barrier (for
+  // the activations) and no other: each wave then runs at its own pace.
+  constexpr int kPerChunk = 4 * FT;
+  constexpr int kAhead = kP2Ring - 1 < kP2Chunks ? kP2Ring - 1 : kP2Chunks;   // chunks loaded first
+  static_assert(kAhead * kPerChunk < 64, "vmcnt counts to 63");
 #pragma unroll
-  for (int c = 0; c < kP2Ring - 1; ++c) {
+  for (int c = 0; c < kAhead; ++c) {
     load_w(c, wb[c]);
-    load_x(c, c);
+    asm volatile("" ::: "memory");            // chunks leave in order
   }
+  wait_loads_except<kAhead * kPerChunk>();
+  lds_barrier();
 #pragma unroll
   for (int c = 0; c < kP2Chunks; ++c) {
     const int later = min(kP2Ring - 2, kP2Chunks - 1 - c);    // chunks issued after c
-    if (later == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerChunk) : "memory");
-    else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerChunk) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // bare barrier: the waits are explicit above; every wave finished reading
-    // the slot refilled below in the previous chunk
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    if (later >= 4) wait_loads_except<4 * kPerChunk>();
+    else if (later == 3) wait_loads_except<3 * kPerChunk>();
+    else if (later == 2) wait_loads_except<2 * kPerChunk>();
+    else if (later == 1) wait_loads_except<kPerChunk>();
+    else wait_loads_except<0>();
     if (c + kP2Ring - 1 < kP2Chunks) {
       load_w(c + kP2Ring - 1, wb[(c + kP2Ring - 1) % kP2Ring]);
-      load_x(c + kP2Ring - 1, (c + kP2Ring - 1) % kP2Ring);
+      asm volatile("" ::: "memory");          // issued before this chunk's matrix work
     }
     // all of the chunk's B fragments of a part are read before its matrix
     // work, so the LDS reads overlap one another (column tiles past ncols
@@ -960,8 +964,9 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int row = 16 * t + (lane & 15);
-          const int off = row * kP2Kc + (((4 * s + (lane >> 4)) ^ (row & 7)) << 3);
-          xb[s][t] = *reinterpret_cast<const u32x4*>(GQA_SX(part, c % kP2Ring) + off);
+          const int lu = c * (kP2Kc / 8) + 4 * s + (lane >> 4);
+          const int off = part * kP2Cols * kP2Kr + row * kP2Kr + ((lu ^ (row & 7)) << 3);
+          xb[s][t] = *reinterpret_cast<const u32x4*>(sx_dyn + off);
         }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -1048,7 +1053,6 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
     }
   }
   }
-#undef GQA_SX
 }
 
 // ---------------------------------------------------------------------------
@@ -1129,7 +1133,7 @@ void decode_ws_carve(void* ws, int B, int kv, DecodeParams* p) {
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
     const dim3 grid((D + 2 * p.kv * HD) / p2_feat<0>() * p2_splits<0>());
-    const size_t lds = kP2Ring * kP2Cols * kP2Kc * 2;
+    const size_t lds = p2_lds_bytes<0>();
     for (int c = 0; c < p.B; c += kP2Cols) {
       switch (p.kv) {
         case 16: hipLaunchKernelGGL((decode_proj_kernel<0, 16>), grid, dim3(256), lds, s, p, c); break;
@@ -1175,7 +1179,7 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
   if (p.B > kGemvMaxB) {
     for (int c = 0; c < p.B; c += kP2Cols)
       hipLaunchKernelGGL(decode_proj_kernel<1>, dim3(D / p2_feat<1>() * p2_splits<1>()), dim3(256),
-                         2 * kP2Ring * kP2Cols * kP2Kc * 2, s, p, c);
+                         p2_lds_bytes<1>(), s, p, c);
     return hipGetLastError();
   }
   for (int b0 = 0; b0 < p.B; b0 += kWoMaxNB) {

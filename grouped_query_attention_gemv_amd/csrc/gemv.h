@@ -65,11 +65,14 @@ __device__ __forceinline__ void load_rows2(const uint16_t* __restrict__ w0,
 template <int NB, int W>
 __device__ __forceinline__ void stage_rows_async(uint32_t* xs, const uint16_t* __restrict__ src) {
   constexpr int kPieces = NB * (D * 2 / 1024);      // 8 KiB a row
+  static_assert(kPieces % W == 0, "every wave copies the same number of pieces");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = wave; i < kPieces; i += W)
+  for (int j = 0; j < kPieces / W; ++j) {
+    const int i = wave + W * j;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + (size_t)i * 512 + lane * 8),
                                      (lds_void*)(reinterpret_cast<char*>(xs) + i * 1024), 16, 0, 0);
+  }
   asm volatile("" ::: "memory");
 }
 
