@@ -235,10 +235,20 @@ int layer_prologue(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, 
 }
 
 // Prepares the GQA_SYNC_BYTES synchronisation region, 16 bytes per thread:
-// zeros, with the magic word after the error word.
+// zeros, with the magic word after the error word, then the one-launch
+// decode's hand-off buffers filled with their "not yet" markers (bf16 pairs
+// for the appended rows, fp32 elsewhere).
 __global__ void __launch_bounds__(256) init_sync_kernel(u32x4* sync) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  sync[i] = i == 0 ? u32x4{0u, (uint32_t)kWsMagic, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+  const size_t byte = i * 16;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (byte >= kSyncWordsBytes) {
+    const uint32_t m = (byte >= kFusedKvOff && byte < kFusedPartOff) ? kNotYetPair : kNotYet;
+    v = u32x4{m, m, m, m};
+  } else if (i == 0) {
+    v = u32x4{0u, (uint32_t)kWsMagic, 0u, 0u};
+  }
+  sync[i] = v;
 }
 static_assert(GQA_SYNC_BYTES % (16 * 256) == 0, "sync region is a whole number of fill blocks");
 static_assert(kSyncErr == 0 && kSyncMagic == 1, "the fill kernel writes the magic into int 1");

@@ -141,6 +141,9 @@ __device__ __forceinline__ float sum_xor32(float v) {
 // Memory
 // ---------------------------------------------------------------------------
 
+// cache-policy operand of a buffer load that streams (non-temporal)
+constexpr int kNtPolicy = 2;
+
 __device__ __forceinline__ u32x4 ld_nt_u32x4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

@@ -28,14 +28,10 @@ namespace gqa {
 // with the head's attention workgroups (Q of its 4 query heads: 64
 // workgroups, then K: 16, then V: 16).
 template <bool FUSED, int W>
-__device__ __forceinline__ int qkv_first_feature(int blk, int* grp) {
+__device__ __forceinline__ int qkv_first_feature(int blk) {
   static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
-  if (!FUSED) {
-    *grp = 0;
-    return blk * 2 * W;
-  }
+  if (!FUSED) return blk * 2 * W;
   const int g = blk & 7, r = blk >> 3;
-  *grp = g;
   if (r < 64) return g * (REP * HD) + r * 8;
   if (r < 80) return D + g * HD + (r - 64) * 8;
   return D + KVH * HD + g * HD + (r - 80) * 8;
@@ -48,8 +44,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
   constexpr int kNqkv = D + 2 * KV * HD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int grp;
-  const int r0 = qkv_first_feature<FUSED, W>(blk, &grp) + wave * 2;   // even feature, 0..6142
+  const int r0 = qkv_first_feature<FUSED, W>(blk) + wave * 2;   // even feature, 0..6142
   const uint16_t* wbase;
   int rr;
   if (r0 < D) {
@@ -59,9 +54,14 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   } else {
     wbase = p.wv; rr = r0 - D - KV * HD;
   }
-  // x goes to LDS by direct loads issued first; the 16 weight loads follow
-  // at once, and x has landed once only they remain in flight
+  // x goes to LDS by direct loads issued first, with the RoPE entry of the
+  // wave's feature pair (one position for the whole batch) and the norm
+  // gain; the 16 weight loads follow at once, and the rest has landed once
+  // only they remain in flight
   stage_rows_async<NB, W>(xs, p.x + (size_t)b0 * D);
+  const bool is_v = r0 >= D + KV * HD;
+  float2 cs = make_float2(1.f, 0.f);
+  if (!is_v) cs = reinterpret_cast<const float2*>(p.rope)[(size_t)p.start_pos * PAIRS + ((rr & (HD - 1)) >> 1)];
   uint32_t gp[(D / 2) / (64 * W)];
   if (p.norm_w) load_norm_gain<W>(p.norm_w, gp);
   u32x4 wa[8], wb[8];
@@ -88,10 +88,8 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   if (lane < NB) {
     const int b = b0 + lane;
     const int pos = p.start_pos;
-    const bool is_v = r0 >= D + KV * HD;
     if (!is_v) {
       // rotate the pair (2i, 2i+1) of this head by position * f_i
-      const float2 cs = reinterpret_cast<const float2*>(p.rope)[(size_t)pos * PAIRS + ((rr & (HD - 1)) >> 1)];
       const float a = v0 * cs.x - v1 * cs.y;
       const float c = v0 * cs.y + v1 * cs.x;
       v0 = a;
@@ -103,8 +101,9 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
     if (r0 < D) {
       float* qd = p.q + (size_t)b * D + r0;
       if (FUSED) {
-        // read by attention workgroups of this launch: written through to the
-        // device-wide coherence point
+        // read by attention workgroups of this launch, which poll these
+        // words until they no longer hold the "not yet" marker: written
+        // through to the device-wide coherence point
         st_dev(qd, v0);
         st_dev(qd + 1, v1);
       } else {
@@ -121,20 +120,9 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
         dst[0] = (uint16_t)(pair & 0xffffu);
         dst[VB] = (uint16_t)(pair >> 16);
       }
-      // the attention workgroups of the same launch read the new row from here
+      // the attention workgroups of the same launch poll the new row here
       if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2, pair);
     }
-  }
-
-  if (FUSED) {
-    // Count this workgroup towards its kv head once its stores of Q and of
-    // the new row have completed.  The head's attention workgroups wait for
-    // the count to reach 96 before they first read those lines; the last of
-    // them rearms it.
-    wait_vm();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(p.sync + kSyncGroup + 32 * grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -213,6 +201,8 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   float (*sm_m)[NR] = reinterpret_cast<float (*)[NR]>(lds + kAttnWaves * NR * HD);
   float (*sm_l)[NR] = reinterpret_cast<float (*)[NR]>(lds + kAttnWaves * NR * HD + kAttnWaves * NR);
   int* sm_last = reinterpret_cast<int*>(lds + kAttnWaves * NR * HD + 2 * kAttnWaves * NR);
+  // fused schedule: Q of the 4 heads, after the merge words
+  float* sm_q = lds + kFusedAttnQWord;
 
   const uint16_t* kbase = p.kcache + (size_t)(b * KV + g) * T_max * HD;
   const uint16_t* vbase = p.vcache + (size_t)(b * KV + g) * (T_max / VB) * (HD * VB);
@@ -221,133 +211,105 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // is one value-cache block).  Key rows past the last visible position are
   // clamped onto it (their scores are masked); value positions past it are
   // cleared after the load, since the cache may hold anything there.
+  // Buffer loads off the (b, g) bases with 32-bit offsets (a 64-bit address
+  // per load would cost registers the fused kernel does not have).
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0, 0x7fffffff, 0x00020000);
   auto load_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
+      const uint32_t off = (uint32_t)(j * HD + rg * 8) * 2u;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = ld_nt_u32x4(kbase + (size_t)j * HD + rg * 8 + 32 * ks);
+      for (int ks = 0; ks < 4; ++ks)
+        kf[mt][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off + 64 * ks, 0, kNtPolicy));
     }
-    const uint16_t* vblk = vbase + (size_t)(tile / VB) * (HD * VB) + rg * 8;
+    // V^T rows col + 16 dt of the tile's block: dt * 1 KiB apart
+    const uint32_t voff = (uint32_t)((tile / VB) * (HD * VB) + rg * 8 + col * VB) * 2u;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vf[dt] = ld_nt_u32x4(vblk + (col + 16 * dt) * VB);
+    for (int dt = 0; dt < 8; ++dt)
+      vf[dt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff + 1024 * (dt & 3), 4096 * (dt >> 2), kNtPolicy));
   };
 
-  // Fused schedule: data produced by other workgroups of this launch (Q, the
-  // new row, split partials) is published with device-scope stores that have
-  // completed before the producer signals, and is first read on any XCD only
-  // after the consumer's device-scope wait on that signal (no line holds data
-  // of two kv heads or two (sequence, head) partial sets).  An L2 that never
-  // held the line since the kernel started (L2 lines are invalidated at every
-  // kernel start) fetches the published value, so the reads go through this
-  // XCD's L2 (ld_xcd, sc0) wherever the workgroup runs; when a head's
-  // workgroups share an XCD, the readers after the first hit the line there.
+  // Fused schedule: Q and the appended row are published with device-scope
+  // stores into words that hold the "not yet" marker, and polled with
+  // device-scope loads (below).  The split partials are published with
+  // device-scope stores that have completed before the producer counts
+  // itself, and are first read on any XCD only after the merging
+  // workgroup's device-scope counter read (no line holds partials of two
+  // (sequence, head) sets).  An L2 that never held the line since the kernel
+  // started (L2 lines are invalidated at every kernel start) fetches the
+  // published value, so those reads go through this XCD's L2 (ld_xcd, sc0).
 
   // Fused schedule: replace the appended row (position start_pos, written by
-  // this launch) with the device-scope copy in kv_new, for the lanes that
-  // hold it.
+  // this launch) with its copy in kv_new, for the lanes that hold it.  The
+  // wave polls those words with device-scope loads until none holds the
+  // "not yet" marker; a poll that runs out leaves the marker (a NaN) in
+  // place and records the error.
   auto patch_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
     if (P < tile || P >= tile + kAttnTile) return;     // wave-uniform
     const uint32_t kn_off = (uint32_t)(((b * 2) * KVH + g) * HD) * 2u;   // bytes into kv_new
     const uint32_t* vn = p.kv_new + ((size_t)(b * 2 + 1) * KVH + g) * (HD / 2);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
-      if (j == P) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[mt][ks] = ld_xcd_x4(p.kv_new, kn_off + (uint32_t)(rg * 8 + 32 * ks) * 2u);
-      }
-    }
     const int e = P - tile - rg * 8;     // element of this lane's 8 positions
-    if (e >= 0 && e < 8) {
+    for (int polls = 0;; ++polls) {
+      bool ok = true;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d = col + 16 * dt;
-        const uint32_t wv = ld_xcd(vn, (uint32_t)(d / 2) * 4u);
-        const uint32_t h = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
+      for (int mt = 0; mt < 2; ++mt) {
+        const int j = min(tile + (col >> 2) * 8 + mt * 4 + (col & 3), j_end - 1);
+        if (j == P) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q == (e >> 1)) {
-            vf[dt][q] = (e & 1) ? ((vf[dt][q] & 0x0000ffffu) | (h << 16))
-                                : ((vf[dt][q] & 0xffff0000u) | h);
+          for (int ks = 0; ks < 4; ++ks) {
+            kf[mt][ks] = ld_dev_x4(p.kv_new, kn_off + (uint32_t)(rg * 8 + 32 * ks) * 2u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ok &= kf[mt][ks][i] != kNotYetPair;
           }
         }
       }
+      if (e >= 0 && e < 8) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int d = col + 16 * dt;
+          const uint32_t wv = ld_dev(vn + d / 2);
+          ok &= wv != kNotYetPair;
+          const uint32_t h = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q == (e >> 1)) {
+              vf[dt][q] = (e & 1) ? ((vf[dt][q] & 0x0000ffffu) | (h << 16))
+                                  : ((vf[dt][q] & 0xffff0000u) | h);
+            }
+          }
+        }
+      }
+      if (__all(ok)) break;
+      if (polls >= kMaxPolls) {
+        if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
   };
 
-  // the first tile's loads go out before the Q loads, so both round trips overlap
-  u32x4 kf[2][4], vf[8];
-  int tile = j_begin + w * kAttnTile;
-  if (tile < j_end) load_tile(tile, kf, vf);
-
-  // Fused schedule: wait until the 96 QKV workgroups of kv head g have
-  // counted themselves (each after its stores landed), count this workgroup
-  // too (the last of the head's nsplit*B attention workgroups rearms the
-  // counter at its end), then read Q and the appended row in one round trip.
-  // A workspace without gqa_workspace_init's magic word holds no valid
-  // counters: the workgroup records the error and stops (the wo workgroups
-  // see the same and write NaN).  A wait that times out records its error
-  // and poisons this workgroup's Q with NaN, so that Delta turns NaN.
+  u32x4 kf[2][4], vf[8];                  // one 32-position tile of K and V
+  const int tile0 = j_begin + w * kAttnTile;
   int* grp_cnt = p.sync + kSyncGroup + 32 * g;
   int grp_prev = 0;
-  u32x4 qraw[8];
-  if (FUSED) {
-    if (tid == 0) {
-      int state = 0;
-      if (p.sync[kSyncMagic] != kWsMagic) {
-        __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        state = 2;
-      } else {
-        int polls = 0;
-        while (ld_dev(grp_cnt) < 96) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++polls > kMaxPolls) {
-            __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            state = 1;
-            break;
-          }
-        }
-        grp_prev = __hip_atomic_fetch_add(grp_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // placement diagnostic, once per launch: the first attention workgroup
-        // counts the launch if the dispatcher put it away from XCD g (then
-        // the head's workgroups do not share an L2; results are unaffected)
-        if (blk == 0 && xcc_id() != g)
-          __hip_atomic_fetch_add(p.sync + kSyncOffHome, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      *sm_last = state;
-    }
-    __syncthreads();
-    const int state = *sm_last;
-    if (state == 2) return;
-    const uint32_t qoff = (uint32_t)((b * D + (g * REP + head) * HD + rg * 8) * 4);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qraw[2 * ks] = ld_xcd_x4(p.q, qoff + ks * 128);
-      qraw[2 * ks + 1] = ld_xcd_x4(p.q, qoff + ks * 128 + 16);
-    }
-    if (state == 1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qraw[i] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-    }
-    if (tile < j_end) patch_tile(tile, kf, vf);
-  }
+  u32x4 qf[4];
+  float m_run, l_run;
+  f32x4 oacc[8];
 
   // Q fragments, pre-scaled by log2(e)/sqrt(128)
-  u32x4 qf[4];
-  {
+  auto build_q = [&]() {
     const float* qrow = p.q + (size_t)b * D + (g * NR + head) * HD;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int d0 = rg * 8 + 32 * ks;
       float qv[8];
       if (FUSED) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[e] = __uint_as_float(qraw[2 * ks][e]);
-          qv[4 + e] = __uint_as_float(qraw[2 * ks + 1][e]);
-        }
+        const float4 qa = *reinterpret_cast<const float4*>(sm_q + head * HD + d0);
+        const float4 qb = *reinterpret_cast<const float4*>(sm_q + head * HD + d0 + 4);
+        qv[0] = qa.x; qv[1] = qa.y; qv[2] = qa.z; qv[3] = qa.w;
+        qv[4] = qb.x; qv[5] = qb.y; qv[6] = qb.z; qv[7] = qb.w;
       } else {
         const float4 qa = *reinterpret_cast<const float4*>(qrow + d0);
         const float4 qb = *reinterpret_cast<const float4*>(qrow + d0 + 4);
@@ -367,12 +329,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
       }
       qf[ks] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 oacc[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
   auto compute_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
     const int jv = tile + rg * 8;
@@ -439,8 +396,65 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     }
   };
 
+  // Fused schedule: the workgroup polls Q of its 4 heads (4 x 128 floats,
+  // written by the head's QKV workgroups of this launch) with device-scope
+  // loads until no word holds the "not yet" marker: the poll that succeeds
+  // is the read.  The head's nsplit*B attention workgroups count themselves once
+  // they have read Q and the appended row; the last writes the markers back
+  // and rearms the counter (release_inputs).  A workspace without
+  // gqa_workspace_init's magic word holds no valid markers: the workgroup
+  // records the error and stops (the wo workgroups see the same and write
+  // NaN).  A poll that runs out records its error and poisons Q with NaN, so
+  // that Delta turns NaN.
+  auto poll_q = [&]() {
+    // thread i polls floats 2i, 2i+1 of the 4 heads' Q (512 floats), then
+    // leaves them in LDS for every wave
+    const float* qsrc = p.q + (size_t)b * D + g * REP * HD + 2 * tid;
+    float2 v = make_float2(0.f, 0.f);
+    for (int polls = 0;; ++polls) {
+      v = make_float2(ld_dev(qsrc), ld_dev(qsrc + 1));
+      if (__float_as_uint(v.x) != kNotYet && __float_as_uint(v.y) != kNotYet) break;
+      if (polls >= kMaxPolls) {
+        __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = make_float2(__uint_as_float(0xffffffffu), __uint_as_float(0xffffffffu));
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    *reinterpret_cast<float2*>(sm_q + 2 * tid) = v;
+    __syncthreads();
+  };
+
+  // the first tile's loads go out before the Q polls, so both round trips overlap
+  if (tile0 < j_end) load_tile(tile0, kf, vf);
+  if (FUSED) {
+    if (tid == 0) {
+      int state = 0;
+      if (p.sync[kSyncMagic] != kWsMagic) {
+        __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        state = 2;
+      } else if (blk == 0 && xcc_id() != g) {
+        // placement diagnostic, once per launch: the first attention
+        // workgroup counts the launch if the dispatcher put it away from XCD
+        // g (results are unaffected)
+        __hip_atomic_fetch_add(p.sync + kSyncOffHome, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      *sm_last = state;
+    }
+    __syncthreads();
+    if (*sm_last == 2) return;
+    poll_q();
+    if (tile0 < j_end) patch_tile(tile0, kf, vf);
+  }
+  build_q();
+  m_run = -INFINITY;
+  l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   // One tile in registers per wave; latency is hidden by the other waves
   // resident on the SIMD (the kernel is sized for 3 waves per SIMD).
+  int tile = tile0;
   while (tile < j_end) {
     compute_tile(tile, kf, vf);
     tile += kAttnWaves * kAttnTile;
@@ -466,6 +480,8 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     sm_l[w][lane] = l_run;
   }
   __syncthreads();
+  // every wave of the workgroup is past its reads of Q and the appended row
+  if (FUSED && tid == 0) grp_prev = __hip_atomic_fetch_add(grp_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // merge the 4 waves: thread -> (head, two dims); wave w takes head w (the
   // waves past NR only join the barriers)
@@ -506,13 +522,26 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     }
   };
 
-  // the head's last attention workgroup to pass its wait rearms the counter
-  auto rearm_group = [&]() {
-    if (FUSED && tid == 0 && grp_prev == 96 + p.nsplit * p.B - 1) st_dev(grp_cnt, 0);
+  // The head's last attention workgroup to count itself (every other one has
+  // read Q and the appended row, so every producer's store has landed) writes
+  // the markers back into Q of the head's query heads and into the appended
+  // rows of every sequence, then rearms the counter; wave 0 does it.
+  auto release_inputs = [&]() {
+    if (!FUSED || w != 0) return;
+    if (__shfl(grp_prev, 0) != p.nsplit * p.B - 1) return;
+    for (int bb = 0; bb < p.B; ++bb) {
+      float* qg = p.q + (size_t)bb * D + g * REP * HD;
+#pragma unroll
+      for (int i = 0; i < REP * HD / 64; ++i) st_dev(qg + i * 64 + lane, __uint_as_float(kNotYet));
+#pragma unroll
+      for (int kvp = 0; kvp < 2; ++kvp)
+        st_dev(p.kv_new + ((size_t)(bb * 2 + kvp) * KVH + g) * (HD / 2) + lane, kNotYetPair);
+    }
+    if (lane == 0) st_dev(grp_cnt, 0);
   };
 
   if (p.nsplit == 1) {
-    rearm_group();
+    release_inputs();
     emit(o0 / lsum, o1 / lsum);
     return;
   }
@@ -545,7 +574,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     *sm_last = (prev == p.nsplit - 1);
   }
   __syncthreads();
-  rearm_group();
+  release_inputs();
   if (!*sm_last) return;
 
   // merge every split in a fixed order, one round trip per 8 splits,
@@ -724,28 +753,33 @@ __global__ void __launch_bounds__(64 * W) decode_wo_kernel(DecodeParams p, int b
 // Fused schedule: the whole block step in one launch
 // ---------------------------------------------------------------------------
 //
-// Workgroups [0, 768) run the QKV projection, the next nsplit*8*B flash-decode,
-// the last 512 wo.  Workgroup i runs on XCD i % 8; kv head g takes the QKV and
-// attention workgroups with i = g (mod 8).  Every QKV workgroup is resident
-// from the start; each consumer starts its own HBM reads (K/V tiles, wo rows)
-// before it waits, so the three phases overlap instead of paying a launch
-// boundary each:
-//   QKV -> attention: per-kv-head arrival counter, which the head's attention
-//     workgroups poll until it reaches 96, then Q and the new row read
-//     through XCD g's L2;
-//   split -> merge: per-(b, g) counter, the last split merges the partials
-//     (read through XCD g's L2);
+// Workgroups [0, 768) run the QKV projection, the next nsplit*8*B the
+// flash-decode, the last 512 wo.  Dispatch follows the workgroup index and
+// the 768 QKV workgroups fill the chip (3 per CU), so every one of them
+// streams its weights from the start; the attention and wo workgroups take
+// the places of retiring QKV ones.  (Attention first measured slower: the
+// QKV workgroups it displaced started late and stretched the QKV stream.)
+// Kv head g takes the QKV and attention workgroups with i = g (mod 8).  Each
+// consumer starts its own HBM reads (K/V tiles, wo rows) before it waits, so
+// the three phases overlap instead of paying a launch boundary each:
+//   QKV -> attention: Q and the new row are stored into words that hold a
+//     "not yet" marker; the head's attention workgroups poll the words
+//     themselves, so arrival and value come in one round trip, and the last
+//     of them writes the markers back;
+//   split -> merge: per-(b, g) counter, the last split merges the partials;
 //   attention -> wo: the workgroup that completes O of (b, g) stores it with
 //     device-scope stores and sets word b*8 + g of every wo workgroup's slot.
-// Producers wait for their stores to complete before they signal; counters
-// and slots are polled with device-scope loads.  Every wait is bounded
-// (kMaxPolls) and only the consumers wait.  The host admits a shape only if
+// Producers that signal through a separate word wait for their stores to
+// complete first; counters, slots and marked words are polled with
+// device-scope loads.  Every wait is bounded (kMaxPolls) and only the
+// consumers wait.  The host admits a shape only if
 // all waiting workgroups together fit in less than the chip's resident
 // capacity, so producers always find room to run whatever order the hardware
 // dispatches in.
 template <int NB>
 __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
   __shared__ uint32_t lds[2 * NB * (D / 2) > kAttnLdsWords ? 2 * NB * (D / 2) : kAttnLdsWords];
+  static_assert(kFusedAttnQWord + REP * HD <= sizeof(lds) / 4, "no LDS for the attention role's Q");
   const int na = p.nsplit * KVH * p.B;
   const int blk = blockIdx.x;
   if (blk < kFusedQkvWG) {
@@ -1097,7 +1131,6 @@ size_t decode_ws_bytes(int B, int kv) {
   n += 2 * align256((size_t)B * D * 2);                   // o_hi, o_lo
   n += align256((size_t)B * kv * 4);                      // counters
   n += align256(decode_part_bytes(B, kv));               // partials
-  n += align256((size_t)B * 2 * KVH * HD * 2);           // kv_new (fused schedule, 8 heads)
   return n;
 }
 
@@ -1114,8 +1147,6 @@ void decode_ws_carve(void* ws, int B, int kv, DecodeParams* p) {
   p->counters = reinterpret_cast<int*>(c);
   c += align256((size_t)B * kv * 4);
   p->part = reinterpret_cast<float*>(c);
-  c += align256(decode_part_bytes(B, kv));
-  p->kv_new = reinterpret_cast<uint32_t*>(c);
 }
 
 #define GQA_NB_SWITCH(NB_VAR, CALL) \
@@ -1206,6 +1237,10 @@ hipError_t launch_decode_fused(const DecodeParams& p0, hipStream_t s) {
   if (!decode_fused_eligible(p0.B, p0.nsplit)) return hipErrorInvalidValue;
   DecodeParams p = p0;
   p.counters = p.sync + kSyncSplit;     // zero at entry, rearmed by the last split
+  // hand-off buffers with "not yet" markers, after the synchronisation words
+  char* region = reinterpret_cast<char*>(p.sync);
+  p.q = reinterpret_cast<float*>(region + kFusedQOff);
+  p.kv_new = reinterpret_cast<uint32_t*>(region + kFusedKvOff);
   const int grid = kFusedQkvWG + p.nsplit * KVH * p.B + kFusedWoWG;
   if (p.B == 1)
     hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(256), 0, s, p);

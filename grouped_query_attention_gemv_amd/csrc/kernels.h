@@ -20,11 +20,30 @@ constexpr int kGemvMaxNB = 8;        // tokens per pass of the QKV bandwidth GEM
 constexpr int kGemvMaxB = 8;         // larger batches use the matrix-core projections
 constexpr int kWoMaxNB = 8;          // tokens per pass of the wo GEMV (hi + lo parts in LDS)
 
-// Synchronisation words at the start of every workspace, used by the fused
-// decode schedule (one launch whose workgroups hand results to each other).
-// They must be zero before the first decode call on a workspace; every call
-// leaves them zero, and prefill never touches them.  Offsets are in ints.
-constexpr int kSyncBytes = 64 * 1024;
+// Synchronisation region at the start of every workspace, used by the
+// decode kernels; prefill never touches it (except for the error word).  It
+// holds two parts:
+//  - 64 KiB of synchronisation words (offsets in ints below): zero before
+//    the first decode on a workspace, and every call leaves them zero;
+//  - the hand-off buffers of the one-launch schedule (Q, the appended rows,
+//    the split partials), whose every word holds a "not yet" marker until
+//    its producer overwrites it.  A consumer polls the words themselves, so
+//    the value and its arrival travel together; the last consumer writes the
+//    marker back.  The marker is a signalling NaN (fp32, or a pair of bf16
+//    ones), which no arithmetic result and no bf16 rounding of one can be.
+// gqa_workspace_init writes both parts.
+constexpr int kSyncWordsBytes = 64 * 1024;
+constexpr uint32_t kNotYet = 0x7f800001u;       // fp32 signalling NaN
+constexpr uint32_t kNotYetPair = 0x7f817f81u;   // two bf16 signalling NaNs
+constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
+constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
+constexpr size_t kFusedQOff = kSyncWordsBytes;                                  // fp32 [kFusedMaxB][4096]
+constexpr size_t kFusedKvOff = kFusedQOff + (size_t)kFusedMaxB * D * 4;        // bf16 pairs [B][K, V][8][64]
+constexpr size_t kFusedPartOff = kFusedKvOff + (size_t)kFusedMaxB * 2 * KVH * HD * 2;
+// partials of at most kFusedMaxAttnWG splits of REP heads, each (b, g)
+// region rounded up to whole 128-byte lines
+constexpr size_t kFusedPartBytes = ((size_t)kFusedMaxAttnWG * REP * kPartStride + kFusedMaxB * KVH * 32) * 4;
+constexpr int kSyncBytes = (int)(((kFusedPartOff + kFusedPartBytes) + 4095) / 4096 * 4096);
 constexpr int kSyncErr = 0;          // sticky error bits (GQA_WS_ERR_*)
 constexpr int kSyncMagic = 1;        // kWsMagic once gqa_workspace_init has run
 constexpr int kSyncOffHome = 2;      // fused launches whose first attention workgroup ran
@@ -34,8 +53,9 @@ constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups 
 constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
 constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
 constexpr int kSyncProj = 10752;     // + 16*fb: K ranges of projection feature block fb summed
-constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
-constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
+// LDS word where an attention workgroup of the fused schedule keeps Q of its
+// 4 heads (after the words of the 4-wave merge, 16-byte aligned)
+constexpr int kFusedAttnQWord = (kAttnWaves * REP * HD + 2 * kAttnWaves * REP + 1 + 3) / 4 * 4;
 constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
 constexpr int kFusedWoWG = 512;      // 8 wo rows each
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
@@ -47,7 +67,7 @@ constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedul
 // take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
 constexpr unsigned kWoHoldTicks = 500;
 static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
-static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncBytes / 4,
+static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncWordsBytes / 4,
               "sync region too small for the projection counters of 32 kv heads");
 
 struct DecodeParams {
@@ -64,12 +84,12 @@ struct DecodeParams {
   float* probe;             // optional [B][6144]
   int T_max, start_pos, B, accumulate;
   // workspace
-  float* q;                 // [B][4096] post-RoPE Q, fp32
+  float* q;                 // [B][4096] post-RoPE Q, fp32 (fused: in the hand-off region)
   uint16_t* o_hi;           // [B][4096] attention output, bf16 high part
   uint16_t* o_lo;           // [B][4096] bf16 low part (o - hi)
   int* counters;            // [B][8] split arrival counters
   float* part;              // [B][8][nsplit][4][kPartStride]
-  uint32_t* kv_new;         // [B][2][8][64] appended K, V rows as packed bf16 pairs
+  uint32_t* kv_new;         // fused: [B][2][8][64] appended K, V rows as packed bf16 pairs
   int* sync;                // the workspace's synchronisation words
   int kv;                   // kv heads: 8 (Llama 3.1 8B), or 16 / 32 (n_rep 2, 1) on the
                             // GEMV path (B <= kGemvMaxB) with the three-launch schedule

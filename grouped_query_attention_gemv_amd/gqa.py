@@ -23,7 +23,7 @@ ROPE_PAIRS = 64
 V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
-SYNC_BYTES = 65536
+SYNC_BYTES = 380928
 NOALLOC_SCRATCH_BYTES = 16 << 20   # the no-allocation decode's scratch array per GPU
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
 OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE = 0, 1, 2, 3
@@ -163,8 +163,9 @@ def workspace(op: int, B: int, T_max: int, device, T: int = 1, start_pos: int = 
 
 
 def workspace_init(ws: torch.Tensor) -> None:
-    """Zero the synchronisation words and write the magic word (again, e.g.
-    after the error word turned nonzero)."""
+    """Zero the synchronisation words, write the magic word and mark the
+    one-launch decode's hand-off buffers empty (again, e.g. after the error
+    word turned nonzero)."""
     _check(lib().gqa_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)),
            "gqa_workspace_init")
 

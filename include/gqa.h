@@ -83,8 +83,9 @@ extern "C" {
 #define GQA_MAX_T_MAX   (1 << 20)
 
 /* Leading bytes of every workspace: the synchronisation words of the decode
- * kernels, headed by an error word and a magic word (gqa_workspace_init). */
-#define GQA_SYNC_BYTES  65536
+ * kernels, headed by an error word and a magic word, then the hand-off
+ * buffers of the one-launch decode (gqa_workspace_init prepares both). */
+#define GQA_SYNC_BYTES  380928
 
 /* Bits of the workspace error word (its first int). */
 #define GQA_WS_ERR_WAIT        0x1   /* a bounded wait of the one-launch decode timed out */
@@ -154,8 +155,8 @@ int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t
  *               copies hold all start_pos + T keys; decode's scratch does not
  *               depend on it)
  *   T_max       rows per sequence of the caches
- * Decode needs the synchronisation words, Q, O and the attention partials
- * (about 1.2 MiB at B = 1); prefill adds fp16 copies of Q, O, the keys and
+ * Decode needs the synchronisation region, Q, O and the attention partials
+ * (about 1.5 MiB at B = 1); prefill adds fp16 copies of Q, O, the keys and
  * values and of Wo.  A workspace sized for one operation serves any smaller
  * one.  Calls that share a workspace must be ordered (one stream, or
  * events): they reuse its contents.
@@ -164,8 +165,9 @@ size_t gqa_workspace_bytes(int op, int n_kv_heads, int B, int start_pos, int T, 
 
 /*
  * gqa_workspace_init -- prepare a workspace of ws_bytes bytes (at least
- * GQA_SYNC_BYTES): zero its synchronisation words and write the magic word
- * that the decode kernels check (one small fill kernel on stream, no host
+ * GQA_SYNC_BYTES): zero its synchronisation words, write the magic word that
+ * the decode kernels check and mark the one-launch decode's hand-off buffers
+ * empty (one small fill kernel on stream, no host
  * synchronisation, no memset, so it can also sit in a captured graph).  Call
  * it once per workspace before its first decode, and again after the error
  * word turned nonzero.  Every decode leaves the synchronisation words as it

@@ -98,7 +98,7 @@ def test_workspace_bytes_rejects_out_of_range():
 
 
 def test_decode_workspace_excludes_prefill_copies():
-    """Decode needs the sync words, Q, O and the partials: about 1.2 MiB at
+    """Decode needs the sync region, Q, O and the partials: about 1.5 MiB at
     B = 1, not the 32 MiB fp16 Wo of prefill, and no dependence on T_max."""
     n = _wsb(G.OP_DECODE, 1, 1024)
     assert G.SYNC_BYTES < n < 2 << 20
@@ -133,12 +133,17 @@ def test_layer_workspace_sizes():
 
 
 def test_workspace_starts_with_the_sync_region():
-    assert G.SYNC_BYTES == 65536
+    # 64 KiB of synchronisation words, then the one-launch decode's hand-off
+    # buffers: Q and the appended rows of 2 sequences, the partials of 128
+    # attention workgroups (4 heads x 132 floats, 128-byte aligned per
+    # (sequence, kv head)), rounded up to whole 4 KiB fill blocks
+    handoff = 2 * 4096 * 4 + 2 * 2 * 8 * 128 * 2 + (128 * 4 * 132 + 2 * 8 * 32) * 4
+    assert G.SYNC_BYTES == (65536 + handoff + 4095) // 4096 * 4096 == 380928
     for op, B, T, Tm in ((G.OP_DECODE, 1, 1, 64), (G.OP_PREFILL, 4, 2048, 2048),
                          (G.OP_DECODE, 64, 1, 8224)):
         assert _wsb(op, B, Tm, T) > G.SYNC_BYTES
     src = open(HEADER).read()
-    assert "#define GQA_SYNC_BYTES  65536" in src
+    assert "#define GQA_SYNC_BYTES  380928" in src
 
 
 def test_workspace_init_rejections():

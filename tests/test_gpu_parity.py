@@ -258,27 +258,24 @@ def test_decode_fused_largest_admitted_context(schedule):
     _decode_full(1, 2047, 2048, schedule)
 
 
-def _sync_words_rest(ws):
-    """The synchronisation words with the magic word taken out (int 1)."""
-    w = ws[:G.SYNC_BYTES].view(torch.int32).clone()
-    assert int(w[1].item()) == G.WS_MAGIC
-    w[1] = 0
-    return w
-
-
 def test_decode_schedules_agree_bitwise():
     """Both schedules run the same arithmetic in the same order: identical
-    outputs and caches; the workspace's synchronisation words (but the magic
-    word) are zero again after every call of either schedule."""
+    outputs and caches.  Every call of either schedule leaves the workspace's
+    synchronisation region as gqa_workspace_init wrote it: zero words but the
+    magic word, and "not yet" markers in every hand-off buffer."""
     outs, caches = [], []
     ws = G.workspace(G.OP_DECODE, 2, 1024, DEV)
+    torch.cuda.synchronize()
+    region = ws[:G.SYNC_BYTES].view(torch.int32).clone()
+    assert int(region[1].item()) == G.WS_MAGIC
+    assert int(region[2:16384].abs().sum().item()) == 0
     for mode in (G.DECODE_FUSED, G.DECODE_SPLIT, G.DECODE_FUSED):
         c = DecodeCase(2, 777, 1024, dev=DEV)
         out = G.block_decode(c.xd, *c.wd, c.kcache, c.vcache, c.rope, c.P, ws=ws, schedule=mode)
         torch.cuda.synchronize()
         outs.append(out.clone())
         caches.append((c.kcache.clone(), c.vcache.clone()))
-        assert int(_sync_words_rest(ws).abs().sum().item()) == 0
+        assert torch.equal(ws[:G.SYNC_BYTES].view(torch.int32), region)
     for o, (k, v) in zip(outs[1:], caches[1:]):
         assert torch.equal(o, outs[0])
         assert torch.equal(k.view(torch.int16), caches[0][0].view(torch.int16))
@@ -377,6 +374,26 @@ def test_decode_rejects_small_workspace_without_side_effects():
     assert bool((out == 7.0).all())
     assert torch.equal(c.kcache.view(torch.int16), c.k_before.view(torch.int16))
     assert torch.equal(c.vcache.view(torch.int16), c.v_before.view(torch.int16))
+
+
+def test_workspace_init_writes_words_and_markers():
+    """gqa_workspace_init on a workspace full of garbage: zero synchronisation
+    words (64 KiB) but the magic word, then the one-launch decode's hand-off
+    buffers holding their "not yet" markers -- an fp32 signalling NaN in Q
+    (2 x 4096 floats) and in the partials, a pair of bf16 signalling NaNs in
+    the appended rows (2 x 2 x 8 x 128 bf16) -- and nothing written past the
+    region."""
+    n = G.SYNC_BYTES + 4096
+    ws = torch.full((n,), 0x5a, dtype=torch.uint8, device=DEV)
+    G.workspace_init(ws)
+    torch.cuda.synchronize()
+    w = ws.view(torch.int32).cpu().numpy().view(np.uint32)
+    assert w[0] == 0 and w[1] == G.WS_MAGIC and not w[2:16384].any()
+    q_end, kv_end = 16384 + 2 * 4096, 16384 + 2 * 4096 + 2 * 2 * 8 * 64
+    assert (w[16384:q_end] == 0x7f800001).all()
+    assert (w[q_end:kv_end] == 0x7f817f81).all()
+    assert (w[kv_end:G.SYNC_BYTES // 4] == 0x7f800001).all()
+    assert (w[G.SYNC_BYTES // 4:] == 0x5a5a5a5a).all()
 
 
 @pytest.mark.parametrize("B,P,schedule", [(1, 300, G.DECODE_FUSED), (16, 300, G.DECODE_SPLIT)])
