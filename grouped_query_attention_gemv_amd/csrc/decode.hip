@@ -546,18 +546,112 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     return;
   }
 
-  // Publish this split's partial with device-scope stores (through to the
-  // coherence point shared by all XCDs, without an L2 write-back), wait for
-  // them to land, then count it; the last workgroup to arrive merges every
-  // partial.  Fused: the merging workgroup reads them through its XCD's L2
-  // (first read of those lines after its wait, as for Q above).
-  // Counters always live at the device-wide coherence point (atomics are
-  // performed there, and the waits poll it with device-scope loads).  Each
-  // (sequence, kv head) owns a whole number of 128-byte lines of partials.
+  // Each (sequence, kv head) owns a whole number of 128-byte lines of
+  // partials: per split and head m, l, two unused words, o[128].
   const size_t split_stride = (size_t)NR * kPartStride;
   float* part0 = p.part + (size_t)(b * KV + g) * part_region_floats(p.nsplit, NR) +
                  (size_t)mhc * kPartStride;
   float* mine = part0 + (size_t)split * split_stride;
+
+  // merge every split in a fixed order, one round trip per 8 splits,
+  // rescaling the running sums as the maximum grows; get(s, mv, lv, ov0, ov1)
+  // supplies split s (false: not there yet, ask again)
+  constexpr int U = 8;
+  auto merge_splits = [&](auto get) {
+    float GM = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
+    for (int s0 = 0; s0 < p.nsplit; s0 += U) {
+      float mv[U], lv[U], ov0[U], ov1[U];
+      for (int polls = 0;; ++polls) {
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int s = s0 + u;
+          if (s >= p.nsplit) {
+            mv[u] = -INFINITY; lv[u] = 0.f; ov0[u] = 0.f; ov1[u] = 0.f;
+          } else {
+            ok &= get(s, mv[u], lv[u], ov0[u], ov1[u]);
+          }
+        }
+        if (ok) break;
+        if (polls >= kMaxPolls) {
+          __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int u = 0; u < U; ++u) mv[u] = __uint_as_float(0x7fc00000u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      float cm = GM;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cm = fmaxf(cm, mv[u]);
+      const float r = __builtin_amdgcn_exp2f(GM - cm);
+      gl *= r;
+      g0 *= r;
+      g1 *= r;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float f = __builtin_amdgcn_exp2f(mv[u] - cm);
+        gl += lv[u] * f;
+        g0 += ov0[u] * f;
+        g1 += ov1[u] * f;
+      }
+      GM = cm;
+    }
+    emit(g0 / gl, g1 / gl);
+  };
+
+  if (FUSED) {
+    // The last split merges.  The others publish their partial with
+    // device-scope stores into words that hold the "not yet" marker and are
+    // done; the merging workgroup polls those words itself (arrival and value
+    // in one round trip), takes its own partial from registers, and writes
+    // the markers back once every thread has read them.
+    release_inputs();
+    if (split != p.nsplit - 1) {
+      if (merges) {
+        if (d2 == 0) {
+          st_dev(mine, M);
+          st_dev(mine + 1, lsum);
+        }
+        st_dev(mine + 4 + d2, o0);
+        st_dev(mine + 5 + d2, o1);
+      }
+      return;
+    }
+    merge_splits([&](int s, float& mv, float& lv, float& ov0, float& ov1) {
+      if (s == split) {
+        mv = M; lv = lsum; ov0 = o0; ov1 = o1;
+        return true;
+      }
+      const float* ps = part0 + (size_t)s * split_stride;
+      mv = ld_dev(ps);
+      lv = ld_dev(ps + 1);
+      ov0 = ld_dev(ps + 4 + d2);
+      ov1 = ld_dev(ps + 5 + d2);
+      return __float_as_uint(mv) != kNotYet && __float_as_uint(lv) != kNotYet &&
+             __float_as_uint(ov0) != kNotYet && __float_as_uint(ov1) != kNotYet;
+    });
+    // emit's barrier: every thread has read every partial
+    if (merges) {
+      for (int s = 0; s < p.nsplit - 1; ++s) {
+        float* ps = part0 + (size_t)s * split_stride;
+        if (d2 == 0) {
+          st_dev(ps, __uint_as_float(kNotYet));
+          st_dev(ps + 1, __uint_as_float(kNotYet));
+        }
+        st_dev(ps + 4 + d2, __uint_as_float(kNotYet));
+        st_dev(ps + 5 + d2, __uint_as_float(kNotYet));
+      }
+    }
+    return;
+  }
+
+  // Three-launch schedule: publish this split's partial with device-scope
+  // stores (through to the coherence point shared by all XCDs, without an L2
+  // write-back), wait for them to land, then count it; the last workgroup to
+  // arrive merges every partial.  The counter lives at the device-wide
+  // coherence point (atomics are performed there, and the partials are read
+  // with device-scope loads).
   int* split_cnt = p.counters + b * KV + g;
   if (merges) {
     if (d2 == 0) {
@@ -574,53 +668,16 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     *sm_last = (prev == p.nsplit - 1);
   }
   __syncthreads();
-  release_inputs();
   if (!*sm_last) return;
-
-  // merge every split in a fixed order, one round trip per 8 splits,
-  // rescaling the running sums as the maximum grows
-  constexpr int U = 8;
-  float GM = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
-  for (int s0 = 0; s0 < p.nsplit; s0 += U) {
-    float mv[U], lv[U], ov0[U], ov1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
-      if (s >= p.nsplit) {
-        mv[u] = -INFINITY; lv[u] = 0.f; ov0[u] = 0.f; ov1[u] = 0.f;
-        continue;
-      }
-      const float* ps = part0 + (size_t)s * split_stride;
-      if (FUSED) {
-        mv[u] = ld_xcd_f(ps, 0);
-        lv[u] = ld_xcd_f(ps, 4);
-        ov0[u] = ld_xcd_f(ps, (uint32_t)(4 + d2) * 4u);
-        ov1[u] = ld_xcd_f(ps, (uint32_t)(5 + d2) * 4u);
-      } else {
-        mv[u] = ld_dev(ps);
-        lv[u] = ld_dev(ps + 1);
-        ov0[u] = ld_dev(ps + 4 + d2);
-        ov1[u] = ld_dev(ps + 5 + d2);
-      }
-    }
-    float cm = GM;
-#pragma unroll
-    for (int u = 0; u < U; ++u) cm = fmaxf(cm, mv[u]);
-    const float r = __builtin_amdgcn_exp2f(GM - cm);
-    gl *= r;
-    g0 *= r;
-    g1 *= r;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float f = __builtin_amdgcn_exp2f(mv[u] - cm);
-      gl += lv[u] * f;
-      g0 += ov0[u] * f;
-      g1 += ov1[u] * f;
-    }
-    GM = cm;
-  }
   if (tid == 0) st_dev(split_cnt, 0);
-  emit(g0 / gl, g1 / gl);
+  merge_splits([&](int s, float& mv, float& lv, float& ov0, float& ov1) {
+    const float* ps = part0 + (size_t)s * split_stride;
+    mv = ld_dev(ps);
+    lv = ld_dev(ps + 1);
+    ov0 = ld_dev(ps + 4 + d2);
+    ov1 = ld_dev(ps + 5 + d2);
+    return true;
+  });
 }
 
 template <int KV>
@@ -1236,11 +1293,11 @@ bool decode_fused_eligible(int B, int nsplit) {
 hipError_t launch_decode_fused(const DecodeParams& p0, hipStream_t s) {
   if (!decode_fused_eligible(p0.B, p0.nsplit)) return hipErrorInvalidValue;
   DecodeParams p = p0;
-  p.counters = p.sync + kSyncSplit;     // zero at entry, rearmed by the last split
   // hand-off buffers with "not yet" markers, after the synchronisation words
   char* region = reinterpret_cast<char*>(p.sync);
   p.q = reinterpret_cast<float*>(region + kFusedQOff);
   p.kv_new = reinterpret_cast<uint32_t*>(region + kFusedKvOff);
+  p.part = reinterpret_cast<float*>(region + kFusedPartOff);
   const int grid = kFusedQkvWG + p.nsplit * KVH * p.B + kFusedWoWG;
   if (p.B == 1)
     hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(256), 0, s, p);

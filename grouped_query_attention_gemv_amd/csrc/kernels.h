@@ -49,8 +49,7 @@ constexpr int kSyncMagic = 1;        // kWsMagic once gqa_workspace_init has run
 constexpr int kSyncOffHome = 2;      // fused launches whose first attention workgroup ran
                                      // away from its kv head's XCD (diagnostic)
 constexpr int kWsMagic = 0x31415147; // "GQA1"
-constexpr int kSyncGroup = 32;       // + 32*g: QKV (then attention) workgroups of kv head g
-constexpr int kSyncSplit = 320;      // + (b*8 + g): splits of (b, g) that have published
+constexpr int kSyncGroup = 32;       // + 32*g: attention workgroups of kv head g done with Q
 constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
 constexpr int kSyncProj = 10752;     // + 16*fb: K ranges of projection feature block fb summed
 // LDS word where an attention workgroup of the fused schedule keeps Q of its
