@@ -91,11 +91,16 @@ inline hipError_t mark(hipEvent_t* events, int i, hipStream_t s) {
 }
 
 // Scratch of one operation; 0 for arguments out of range.
+// workspace of gqa_vocab_logits: the synchronisation region, then the
+// normalised tokens of the matrix-core path
+size_t vocab_ws_bytes(int B) { return kSyncBytes + align256((size_t)B * D * 2); }
+
 size_t ws_bytes_for(int op, int kv, int B, int start_pos, int T, int T_max) {
   if (!kv_supported(kv)) return 0;
   if (B < 1 || B > GQA_MAX_BATCH || T < 1 || T_max < 1 || T_max > GQA_MAX_T_MAX) return 0;
   if ((long)B * T > (1L << 24) || start_pos < 0 || (long)start_pos + T > T_max) return 0;
   switch (op) {
+    case GQA_OP_VOCAB: return vocab_ws_bytes(B);
     case GQA_OP_PREFILL: return prefill_ws_bytes(B, start_pos, T, kv);
     case GQA_OP_DECODE: return T == 1 ? decode_ws_bytes(B, kv) : 0;
     case GQA_OP_LAYER_PREFILL:
@@ -442,20 +447,30 @@ int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, const
 }
 
 int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps, const gqa_bf16* w_out,
-                     int V, int B, float* logits, hipStream_t stream) {
+                     int V, int B, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!h || !w_out || !logits) return GQA_ERR_NULL;
   if (B < 1 || B > GQA_MAX_BATCH || V < 1 || V > GQA_MAX_VOCAB) return GQA_ERR_SHAPE;
   if (!aligned16(h) || !aligned16(w_out) || !aligned16(logits) || (norm_w && !aligned16(norm_w)))
     return GQA_ERR_ALIGN;
   if (norm_w && !(eps > 0.f && eps < 1.f)) return GQA_ERR_ARG;
-  const Range outs[] = {span(logits, (size_t)B * V * 4)};
+  // the matrix-core path normalises into the workspace first
+  const bool mfma = B > kGemvMaxNB;
+  const bool uses_ws = mfma && norm_w;
+  if (uses_ws) {
+    if (!ws || ws_bytes < vocab_ws_bytes(B)) return GQA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return GQA_ERR_ALIGN;
+  }
+  uint16_t* zn = uses_ws ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + kSyncBytes) : nullptr;
+  const Range outs[] = {span(logits, (size_t)B * V * 4), span(zn, zn ? (size_t)B * D * 2 : 0)};
   const Range ins[] = {span(h, (size_t)B * D * 2), span(w_out, (size_t)V * D * 2),
                        span(norm_w, norm_w ? (size_t)D * 2 : 0)};
-  if (any_alias(outs, 1, ins, 3)) return GQA_ERR_ALIAS;
+  if (any_alias(outs, 2, ins, 3)) return GQA_ERR_ALIAS;
   VocabParams p;
   p.z = h; p.norm_w = norm_w; p.norm_eps = eps; p.w = w_out; p.logits = logits; p.V = V; p.B = B;
   (void)hipGetLastError();
-  return hip_status(launch_vocab_gemv(p, stream));
+  if (!mfma) return hip_status(launch_vocab_gemv(p, stream));
+  if (zn && launch_rmsnorm(h, norm_w, eps, B, zn, nullptr, stream) != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(launch_vocab_mfma(p, zn ? zn : h, stream));
 }
 
 }  // extern "C"

@@ -172,6 +172,8 @@ struct VocabParams {
 };
 
 hipError_t launch_vocab_gemv(const VocabParams& p, hipStream_t s);
+// above kGemvMaxNB tokens: the matrix-core path over z (h, or its norm)
+hipError_t launch_vocab_mfma(const VocabParams& p, const uint16_t* z, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Pre-norm of a layer

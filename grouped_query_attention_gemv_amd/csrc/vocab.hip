@@ -11,6 +11,7 @@
 // issued before the current pair's products (two pairs in flight per wave);
 // the B <= 8 token vectors are staged (and normalised) once per workgroup.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemv.h"
 #include "kernels.h"
@@ -79,6 +80,151 @@ __global__ void __launch_bounds__(256) vocab_gemv_kernel(VocabParams p, int b0) 
     gemv_rows2<NB, 1>(wa[1], wb[1], xs, lane, acc);
     finish(q1, acc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Above 8 tokens: the matrix-core projection
+// ---------------------------------------------------------------------------
+//
+// C^T[rows x tokens] = W[rows x 4096] . Z^T[4096 x tokens] on
+// v_mfma_f32_16x16x32_bf16, streaming the weights once per 64 tokens (the
+// GEMV above streams them once per 8).  The vocabulary is long enough to
+// fill the chip without splitting K:
+//  - workgroup fb owns 128 vocabulary rows (its 4 waves two 16-row A tiles
+//    each) and the whole K; the last block's rows past V are clamped loads
+//    whose results are not stored;
+//  - K advances in chunks of 128.  The tokens' chunk is copied into LDS
+//    (global_load_lds, 16 KiB, XOR-swizzled rows) and read by all 4 waves
+//    as the B operand; each wave's weight rows come from HBM straight into
+//    registers (its A operand).  Both run three chunks ahead of the matrix
+//    work through a 4-slot ring;
+//  - the epilogue rounds each logit to bf16 as the GEMV does.
+// Z is the caller's h, or its norm written beforehand by the norm kernel.
+constexpr int kVcCols = 64;        // tokens per launch
+constexpr int kVcFeat = 128;       // vocabulary rows per workgroup
+constexpr int kVcKc = 128;         // K per chunk
+constexpr int kVcRing = 4;         // chunk slots: loaded three ahead
+constexpr int kVcChunks = D / kVcKc;
+
+__global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const uint16_t* __restrict__ z,
+                                                         int c_base) {
+  __shared__ __attribute__((aligned(16))) uint16_t sx[kVcRing][kVcCols * kVcKc];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int fb = blockIdx.x;
+  const int ncols = min(kVcCols, p.B - c_base);
+
+  // A operand: weight row of tile ft, k offset (lane >> 4) * 8 in each step
+  const uint16_t* wrow[2];
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft) {
+    const int f = fb * kVcFeat + 32 * w + 16 * ft + (lane & 15);
+    wrow[ft] = p.w + (size_t)min(f, p.V - 1) * D + (lane >> 4) * 8;
+  }
+  // token copies: instruction j of this wave fills rows (4w + j) * 4 .. + 3
+  // of the chunk (256 bytes each); lane i writes row +i/16, 16-byte slot
+  // i % 16, which holds logical slot (i % 16) ^ (row & 7).  Rows past the
+  // last token copy the last token (their results are not stored).
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * w + j) * 4 + (lane >> 4);
+    const int lchunk = (lane & 15) ^ (row & 7);
+    xsrc[j] = z + (size_t)(c_base + min(row, ncols - 1)) * D + lchunk * 8;
+  }
+
+  u32x4 wb[kVcRing][2][4];                      // [slot][tile][k-step]
+  auto load_chunk = [&](int chunk, int slot) {
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wb[slot][ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kVcKc + s * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(xsrc[j] + chunk * kVcKc),
+                                       (lds_void*)(&sx[slot][(4 * w + j) * 4 * kVcKc]), 16, 0, 0);
+    asm volatile("" ::: "memory");              // chunks leave in order
+  };
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Chunk c has landed once no more than the loads of the chunks issued
+  // after it (12 a chunk: 8 weight, 4 copies) remain in flight.
+  constexpr int kPerChunk = 12;
+  static_assert(kVcChunks % kVcRing == 0, "the ring slot of a chunk is known at compile time");
+  // one chunk: slot u, LATER chunks already issued after it
+  auto step = [&](auto u_tag, auto later_tag, int c) {
+    constexpr int u = decltype(u_tag)::value;
+    constexpr int LATER = decltype(later_tag)::value;
+    wait_loads_except<LATER * kPerChunk>();
+    // every wave's copies of chunk c have landed, and every wave is done
+    // with the slot refilled below (read in the previous chunk)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (LATER == kVcRing - 2) load_chunk(c + kVcRing - 1, (u + kVcRing - 1) % kVcRing);
+    u32x4 xb[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = 16 * t + (lane & 15);
+        const int off = row * kVcKc + (((4 * s + (lane >> 4)) ^ (row & 7)) << 3);
+        xb[s][t] = *reinterpret_cast<const u32x4*>(&sx[u][off]);
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) acc[ft][t] = mfma_bf16(wb[u][ft][s], xb[s][t], acc[ft][t]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+#pragma unroll
+  for (int c = 0; c < kVcRing - 1; ++c) load_chunk(c, c);
+  // all but the last four chunks load the chunk three ahead
+  for (int c0 = 0; c0 < kVcChunks - kVcRing; c0 += kVcRing) {
+    step(I0{}, I2{}, c0);
+    step(I1{}, I2{}, c0 + 1);
+    step(I2{}, I2{}, c0 + 2);
+    step(I3{}, I2{}, c0 + 3);
+  }
+  constexpr int cl = kVcChunks - kVcRing;
+  step(I0{}, I2{}, cl);                          // loads the last chunk
+  step(I1{}, I2{}, cl + 1);                      // (kVcRing - 1 ahead: none left after)
+  step(I2{}, I1{}, cl + 2);
+  step(I3{}, I0{}, cl + 3);
+
+  // lane holds rows 32w + 16ft + 4(lane >> 4) + e of the block for token
+  // 16t + (lane & 15)
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = 16 * t + (lane & 15);
+    if (col >= ncols) continue;
+    float* lrow = p.logits + (size_t)(c_base + col) * p.V;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const int f0 = fb * kVcFeat + 32 * w + 16 * ft + 4 * (lane >> 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (f0 + e < p.V) lrow[f0 + e] = bf16_bits_to_f32(f32_to_bf16_bits(acc[ft][t][e]));
+    }
+  }
+}
+
+hipError_t launch_vocab_mfma(const VocabParams& p, const uint16_t* z, hipStream_t s) {
+  const int nfb = (p.V + kVcFeat - 1) / kVcFeat;
+  for (int c = 0; c < p.B; c += kVcCols) {
+    hipLaunchKernelGGL(vocab_mfma_kernel, dim3(nfb), dim3(256), 0, s, p, z, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_vocab_gemv(const VocabParams& p, hipStream_t s) {

@@ -26,7 +26,7 @@ PREFILL_STAGES = 4
 SYNC_BYTES = 380928
 NOALLOC_SCRATCH_BYTES = 16 << 20   # the no-allocation decode's scratch array per GPU
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
-OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE = 0, 1, 2, 3
+OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE, OP_VOCAB = 0, 1, 2, 3, 4
 # bits of the workspace error word
 WS_ERR_WAIT, WS_ERR_WO_WAIT, WS_ERR_INIT, WS_ERR_FP16_RANGE = 0x1, 0x2, 0x4, 0x100
 WS_MAGIC = 0x31415147
@@ -76,7 +76,7 @@ _SIGS = {
     # probe stream
     "gqa_layer_decode": (_I, [_P, _P, _F, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P, _I,
                               _P, _Z, _P, _P]),
-    "gqa_vocab_logits": (_I, [_P, _P, _F, _P, _I, _I, _P, _P]),
+    "gqa_vocab_logits": (_I, [_P, _P, _F, _P, _I, _I, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -144,7 +144,7 @@ def _need(t, name, dtype, shape, device):
 def workspace_bytes(op: int, B: int, T_max: int, T: int = 1, start_pos: int = 0,
                     n_kv_heads: int = N_KV_HEADS) -> int:
     """Scratch bytes of one call of operation ``op`` (OP_PREFILL, OP_DECODE,
-    OP_LAYER_PREFILL, OP_LAYER_DECODE); 0 for arguments out of range."""
+    OP_LAYER_PREFILL, OP_LAYER_DECODE, OP_VOCAB); 0 for arguments out of range."""
     return int(lib().gqa_workspace_bytes(int(op), int(n_kv_heads), int(B), int(start_pos),
                                          int(T), int(T_max)))
 
@@ -458,9 +458,12 @@ NORM_EPS = 1e-5   # norm_eps of the Llama 3.1 8B catalogue entry
 VOCAB = 128256    # vocabulary size of Llama 3
 
 
-def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None) -> torch.Tensor:
+def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None,
+                 ws=None) -> torch.Tensor:
     """Logits [B, V] fp32 (bf16-rounded values) = z W_out^T for h [B, 4096]
-    bf16, z = RMSNorm(h) * norm_w when norm_w is given, else h."""
+    bf16, z = RMSNorm(h) * norm_w when norm_w is given, else h.  Above 8
+    sequences with a norm the call needs a workspace (allocated here unless
+    ``ws`` is given)."""
     if h.dim() != 2 or w_out.dim() != 2:
         raise ValueError("h must be [B, 4096] and w_out [V, 4096]")
     dev = h.device
@@ -474,8 +477,11 @@ def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None) -> t
     if logits is None:
         logits = torch.empty((B, V), dtype=torch.float32, device=dev)
     _need(logits, "logits", torch.float32, (B, V), dev)
+    if ws is None and B > 8 and norm_w is not None:
+        ws = workspace(OP_VOCAB, B, 1, dev)
     _check(lib().gqa_vocab_logits(_ptr(h), _ptr(norm_w), float(eps), _ptr(w_out), int(V), int(B),
-                                  _ptr(logits), _stream(dev)), "gqa_vocab_logits")
+                                  _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(dev)), "gqa_vocab_logits")
     return logits
 
 

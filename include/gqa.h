@@ -103,6 +103,7 @@ extern "C" {
 #define GQA_OP_DECODE         1
 #define GQA_OP_LAYER_PREFILL  2
 #define GQA_OP_LAYER_DECODE   3
+#define GQA_OP_VOCAB          4
 
 /* Number of stages whose boundaries the `events` arguments record. */
 #define GQA_DECODE_STAGES   3           /* QKV+RoPE+append, attention, wo */
@@ -148,7 +149,9 @@ int gqa_rope_table(int T_max, double theta, int scaled, float* rope, hipStream_t
  * gqa_workspace_bytes -- device scratch needed by one call of operation `op`
  * with these arguments; 0 when they are out of range.
  *   op          GQA_OP_PREFILL (gqa_block_prefill), GQA_OP_DECODE
- *               (gqa_block_decode), GQA_OP_LAYER_PREFILL, GQA_OP_LAYER_DECODE
+ *               (gqa_block_decode), GQA_OP_LAYER_PREFILL, GQA_OP_LAYER_DECODE,
+ *               GQA_OP_VOCAB (gqa_vocab_logits: only B is used; the others
+ *               must still be in range)
  *   n_kv_heads  8, 16 or 32
  *   B, T        sequences and new tokens per sequence (T = 1 for decode)
  *   start_pos   cached rows before the new tokens (prefill's fp16 key/value
@@ -371,13 +374,21 @@ int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
  *   norm_w  NULL or [4096] bf16; eps as for the layers (ignored when NULL)
  *   w_out   [V][4096] bf16; V = 128256 for Llama 3.1 (1 .. GQA_MAX_VOCAB)
  *   logits  [B][V] fp32, written
- * One weight pass per 8 sequences.  No workspace.
+ *   ws      needed only when B > 8 and norm_w is non-NULL (else it may be
+ *           NULL, ws_bytes 0): ws_bytes >= gqa_workspace_bytes(GQA_OP_VOCAB,
+ *           8, B, 0, 1, 1); the normalised z is written after its
+ *           synchronisation region, which is left untouched
+ * Up to 8 sequences: a bandwidth GEMV over the weight with the norm fused,
+ * one weight pass.  Above 8: the norm first (into ws), then the matrix
+ * cores, one weight pass per 64 sequences.
  * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_ALIGN, GQA_ERR_ARG (eps),
- * GQA_ERR_ALIAS (logits overlapping an input), GQA_ERR_HIP.
+ * GQA_ERR_WORKSPACE (ws missing or too small where needed), GQA_ERR_ALIAS
+ * (logits or the used workspace overlapping an input or each other),
+ * GQA_ERR_HIP.
  */
 int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps,
                      const gqa_bf16* w_out, int V, int B, float* logits,
-                     hipStream_t stream);
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -381,9 +381,13 @@ def test_layer_prefill_rejects_bad_arguments(kw, code):
 
 def _vocab_args(**kw):
     a = dict(h=_fake(0), g=None, eps=ctypes.c_float(1e-5), w=_fake(1), V=128256, B=1,
-             logits=_fake(2), stream=None)
+             logits=_fake(2), ws=None, ws_bytes=0, stream=None)
     a.update(kw)
-    return [a[k] for k in ("h", "g", "eps", "w", "V", "B", "logits", "stream")]
+    return [a[k] for k in ("h", "g", "eps", "w", "V", "B", "logits", "ws", "ws_bytes", "stream")]
+
+
+def _vocab_ws(B):
+    return G.workspace_bytes(G.OP_VOCAB, B, 1)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -392,9 +396,24 @@ def _vocab_args(**kw):
     (dict(logits=ctypes.c_void_p(BASE + (2 << 32) + 4)), EALIGN),
     (dict(g=_fake(3), eps=ctypes.c_float(-1.0)), EARG),
     (dict(logits=_fake(1)), EALIAS), (dict(logits=_fake(0)), EALIAS),
+    # above 8 sequences with a norm the normalised tokens need the workspace
+    (dict(B=9, g=_fake(3)), EWS),
+    (dict(B=9, g=_fake(3), ws=_fake(4), ws_bytes=_vocab_ws(9) - 1), EWS),
+    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (4 << 32) + 8), ws_bytes=_vocab_ws(9)), EALIGN),
+    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE - 380928), ws_bytes=_vocab_ws(9)), EALIAS),
+    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (2 << 32) - (380928 + 4096)),
+          ws_bytes=_vocab_ws(9)), EALIAS),
 ])
 def test_vocab_logits_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_vocab_logits(*_vocab_args(**kw)) == code
+
+
+def test_vocab_workspace_size():
+    """The synchronisation region, then the normalised tokens (B x 4096 bf16,
+    256-byte aligned); the size depends on B alone."""
+    for B in (1, 9, 64, 1024):
+        assert _vocab_ws(B) == G.SYNC_BYTES + (B * 4096 * 2 + 255) // 256 * 256
+    assert G.workspace_bytes(G.OP_VOCAB, 9, 1) == G.workspace_bytes(G.OP_VOCAB, 9, 4096, T=7, n_kv_heads=32)
 
 
 def test_rope_table_rejects_bad_arguments():

@@ -13,8 +13,8 @@ import torch
 import grouped_query_attention_gemv_amd as G
 from grouped_query_attention_gemv_amd import synth
 from oracle import gqa_oracle as O
-from tests.parity import (DecodeCase, PrefillCase, assert_bf16_rows, assert_close, bits, f64,
-                          kv_bounds, round_bounds, tie_slack)
+from tests.parity import (MEAN_TOL, DecodeCase, PrefillCase, assert_bf16_rows, assert_close, bits,
+                          f64, kv_bounds, norm_err, round_bounds, tie_slack)
 
 pytestmark = pytest.mark.gpu
 
@@ -742,12 +742,17 @@ def test_layer_prefill(B, start_pos, T):
 # ----------------------------------------------------------------------------
 
 def _check_logits(got, exact, bound, name):
-    """Logits are bf16 values: within the tolerance of the oracle's logits
-    (its rounding of the exact product), and any that round differently from
-    it lie within the fp32 rounding bound of the exact product."""
+    """Logits are bf16 values, each the rounding of an fp32 dot product whose
+    summation order the page leaves open: every logit equals the oracle's
+    (its rounding of the exact product) unless the exact product lies within
+    the fp32 accumulation bound of a rounding midpoint, where another order
+    may round the other way (assert_bf16_rows); the mean difference from the
+    oracle's logits stays at the usual tolerance."""
     g = f64(got)
     assert np.array_equal(O.f64_from_bf16_bits(O.bf16_bits_from_f64(g)), g), f"{name}: not bf16 values"
-    errs = {"logits": assert_close(name, g, O.f64_from_bf16_bits(O.bf16_bits_from_f64(exact)))}
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    errs = {"logits": norm_err(g, O.f64_from_bf16_bits(O.bf16_bits_from_f64(exact)))}
+    assert errs["logits"][1] <= MEAN_TOL, f"{name}: normalised mean {errs['logits'][1]:.3e}"
     errs["flips"] = assert_bf16_rows(name, O.bf16_bits_from_f64(g), exact, bound)
     return errs
 
@@ -762,7 +767,11 @@ def _vocab_exact(h, w, g):
     return z @ w.T, round_bounds(z, w, rotated=False) + tie_slack(zx, w)
 
 
-@pytest.mark.parametrize("B,V,norm", [(3, 1001, True), (11, 4096, False), (8, 130, True)])
+@pytest.mark.parametrize("B,V,norm", [(3, 1001, True), (8, 130, True),
+                                      # above 8 sequences: the matrix-core path (a partial last
+                                      # block of 128 rows; 70: two launches, the second ragged)
+                                      (11, 4096, False), (9, 4096, True), (20, 1001, True),
+                                      (70, 130, True), (64, 257, False)])
 def test_vocab_logits_small(B, V, norm):
     from grouped_query_attention_gemv_amd import synth
     gen = synth.generator(40 + B)
@@ -777,11 +786,13 @@ def test_vocab_logits_small(B, V, norm):
     print(f"vocab B={B} V={V} norm={norm}", _check_logits(L, exact, bound, "logits"))
 
 
-def test_vocab_logits_llama31_size():
-    """V = 128,256 (the Llama 3 vocabulary), B = 2, final norm on: weights drawn
-    on the device, 4,096 sampled rows checked against the oracle."""
+@pytest.mark.parametrize("B", [2, 24])
+def test_vocab_logits_llama31_size(B):
+    """V = 128,256 (the Llama 3 vocabulary), final norm on: weights drawn on
+    the device, 4,096 sampled rows checked against the oracle.  B = 2 runs
+    the GEMV, B = 24 the matrix-core path."""
     from grouped_query_attention_gemv_amd import synth
-    B, V = 2, G.VOCAB
+    V = G.VOCAB
     gen = synth.generator(50)
     h = synth.randn_bf16(gen, (B, G.D_MODEL))
     g = synth.norm_gain(51)
@@ -795,8 +806,8 @@ def test_vocab_logits_llama31_size():
     ref = O.vocab_logits(f64(h), wr, f64(g), G.NORM_EPS)
     exact, bound = _vocab_exact(f64(h), wr, f64(g))
     assert np.array_equal(O.f64_from_bf16_bits(O.bf16_bits_from_f64(exact)), ref)
-    print("vocab B=2 V=128256", _check_logits(L[:, torch.from_numpy(rows).to(DEV)], exact, bound,
-                                              "logits"))
+    print(f"vocab B={B} V=128256", _check_logits(L[:, torch.from_numpy(rows).to(DEV)], exact, bound,
+                                                 "logits"))
     assert bool(torch.isfinite(L).all())
 
 
