@@ -30,8 +30,7 @@ bool schedule_valid(int s) {
 int pick_schedule(int kv, int B, int start_pos, int requested) {
   if (!schedule_valid(requested)) return -1;
   int nsplit = 0, chunk = 0;
-  decode_split(B, start_pos + 1, kv, &nsplit, &chunk);
-  const bool ok = kv == KVH && decode_fused_eligible(B, nsplit);
+  const bool ok = decode_fused_split(B, start_pos + 1, kv, &nsplit, &chunk);
   switch (requested) {
     case GQA_DECODE_SPLIT: return GQA_DECODE_SPLIT;
     case GQA_DECODE_FUSED: return ok ? GQA_DECODE_FUSED : -1;
@@ -199,7 +198,10 @@ int decode_impl(const gqa_bf16* x, const gqa_bf16* wq, const gqa_bf16* wk, const
   p.norm_w = norm_w; p.norm_eps = norm_eps; p.resid = resid; p.kv = kv;
   if ((norm_w || resid) && (B > kGemvMaxB || accumulate)) return GQA_ERR_ARG;
   decode_ws_carve(ws, B, kv, &p);
-  decode_split(B, start_pos + 1, kv, &p.nsplit, &p.chunk);
+  if (sched == GQA_DECODE_FUSED)
+    decode_fused_split(B, start_pos + 1, kv, &p.nsplit, &p.chunk);
+  else
+    decode_split(B, start_pos + 1, kv, &p.nsplit, &p.chunk);
   if (dry) return GQA_OK;
 
   (void)hipGetLastError();
@@ -242,12 +244,12 @@ int layer_prologue(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, 
 // Prepares the GQA_SYNC_BYTES synchronisation region, 16 bytes per thread:
 // zeros, with the magic word after the error word, then the one-launch
 // decode's hand-off buffers filled with their "not yet" markers (bf16 pairs
-// for the appended rows, fp32 elsewhere).
+// for the appended rows, fp32 elsewhere), then its wo slots, zero.
 __global__ void __launch_bounds__(256) init_sync_kernel(u32x4* sync) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t byte = i * 16;
   u32x4 v = {0u, 0u, 0u, 0u};
-  if (byte >= kSyncWordsBytes) {
+  if (byte >= kSyncWordsBytes && byte < kFusedSlotOff) {
     const uint32_t m = (byte >= kFusedKvOff && byte < kFusedPartOff) ? kNotYetPair : kNotYet;
     v = u32x4{m, m, m, m};
   } else if (i == 0) {

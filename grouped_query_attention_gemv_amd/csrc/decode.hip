@@ -27,24 +27,24 @@ namespace gqa {
 // blk = g (mod 8), which the dispatcher usually places on one XCD together
 // with the head's attention workgroups (Q of its 4 query heads: 64
 // workgroups, then K: 16, then V: 16).
-template <bool FUSED, int W>
+template <bool FUSED, int W, int KV>
 __device__ __forceinline__ int qkv_first_feature(int blk) {
   static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
   if (!FUSED) return blk * 2 * W;
-  const int g = blk & 7, r = blk >> 3;
-  if (r < 64) return g * (REP * HD) + r * 8;
-  if (r < 80) return D + g * HD + (r - 64) * 8;
-  return D + KVH * HD + g * HD + (r - 80) * 8;
+  constexpr int NR = H / KV, QW = 16 * NR;       // Q workgroups of a kv head
+  const int g = blk % KV, r = blk / KV;
+  if (r < QW) return g * (NR * HD) + r * 8;
+  if (r < QW + 16) return D + g * HD + (r - QW) * 8;
+  return D + KV * HD + g * HD + (r - QW - 16) * 8;
 }
 
 // KV: kv heads of the projection (the fused schedule runs KV = 8 only); W:
 // waves of the workgroup.
 template <int NB, bool FUSED, int KV = KVH, int W = 4>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
-  static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
   constexpr int kNqkv = D + 2 * KV * HD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = qkv_first_feature<FUSED, W>(blk) + wave * 2;   // even feature, 0..6142
+  const int r0 = qkv_first_feature<FUSED, W, KV>(blk) + wave * 2;   // even feature
   const uint16_t* wbase;
   int rr;
   if (r0 < D) {
@@ -121,7 +121,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
         dst[VB] = (uint16_t)(pair >> 16);
       }
       // the attention workgroups of the same launch poll the new row here
-      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KVH + g) * (HD / 2) + d / 2, pair);
+      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KV + g) * (HD / 2) + d / 2, pair);
     }
   }
 }
@@ -179,13 +179,12 @@ template <bool FUSED, int KV = KVH>
 __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float* lds) {
   constexpr int NR = H / KV;
   static_assert(NR == 1 || NR == 2 || NR == 4, "the wave merge maps one 64-thread slice per head");
-  static_assert(!FUSED || KV == KVH, "the fused schedule is laid out for 8 kv heads");
   constexpr int kShlNr = 0x100 + NR;             // DPP row_shl:NR, lane i <- lane i + NR
   constexpr int kShrNr = 0x110 + NR;             // DPP row_shr:NR, lane i <- lane i - NR
-  // fused: g = blk mod 8 (the XCD of the head's QKV workgroups)
-  const int split = FUSED ? (blk >> 3) % p.nsplit : blk % p.nsplit;
-  const int g = FUSED ? (blk & 7) : (blk / p.nsplit) % KV;
-  const int b = FUSED ? (blk >> 3) / p.nsplit : blk / (p.nsplit * KV);
+  // fused: g = blk mod KV, as for the head's QKV workgroups
+  const int split = FUSED ? (blk / KV) % p.nsplit : blk % p.nsplit;
+  const int g = FUSED ? blk % KV : (blk / p.nsplit) % KV;
+  const int b = FUSED ? (blk / KV) / p.nsplit : blk / (p.nsplit * KV);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 15, rg = lane >> 4;
   const int head = col % NR;
@@ -248,8 +247,8 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // place and records the error.
   auto patch_tile = [&](int tile, u32x4 (&kf)[2][4], u32x4 (&vf)[8]) {
     if (P < tile || P >= tile + kAttnTile) return;     // wave-uniform
-    const uint32_t kn_off = (uint32_t)(((b * 2) * KVH + g) * HD) * 2u;   // bytes into kv_new
-    const uint32_t* vn = p.kv_new + ((size_t)(b * 2 + 1) * KVH + g) * (HD / 2);
+    const uint32_t kn_off = (uint32_t)(((b * 2) * KV + g) * HD) * 2u;   // bytes into kv_new
+    const uint32_t* vn = p.kv_new + ((size_t)(b * 2 + 1) * KV + g) * (HD / 2);
     const int e = P - tile - rg * 8;     // element of this lane's 8 positions
     for (int polls = 0;; ++polls) {
       bool ok = true;
@@ -407,21 +406,23 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   // NaN).  A poll that runs out records its error and poisons Q with NaN, so
   // that Delta turns NaN.
   auto poll_q = [&]() {
-    // thread i polls floats 2i, 2i+1 of the 4 heads' Q (512 floats), then
-    // leaves them in LDS for every wave
-    const float* qsrc = p.q + (size_t)b * D + g * REP * HD + 2 * tid;
-    float2 v = make_float2(0.f, 0.f);
-    for (int polls = 0;; ++polls) {
-      v = make_float2(ld_dev(qsrc), ld_dev(qsrc + 1));
-      if (__float_as_uint(v.x) != kNotYet && __float_as_uint(v.y) != kNotYet) break;
-      if (polls >= kMaxPolls) {
-        __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v = make_float2(__uint_as_float(0xffffffffu), __uint_as_float(0xffffffffu));
-        break;
+    // thread i polls floats 2i, 2i+1 of the NR heads' Q (NR x 128 floats),
+    // then leaves them in LDS for every wave
+    if (2 * tid < NR * HD) {
+      const float* qsrc = p.q + (size_t)b * D + g * NR * HD + 2 * tid;
+      float2 v = make_float2(0.f, 0.f);
+      for (int polls = 0;; ++polls) {
+        v = make_float2(ld_dev(qsrc), ld_dev(qsrc + 1));
+        if (__float_as_uint(v.x) != kNotYet && __float_as_uint(v.y) != kNotYet) break;
+        if (polls >= kMaxPolls) {
+          __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v = make_float2(__uint_as_float(0xffffffffu), __uint_as_float(0xffffffffu));
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_s_sleep(1);
+      *reinterpret_cast<float2*>(sm_q + 2 * tid) = v;
     }
-    *reinterpret_cast<float2*>(sm_q + 2 * tid) = v;
     __syncthreads();
   };
 
@@ -509,14 +510,18 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     const uint32_t lo1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1));
     uint32_t* ph = reinterpret_cast<uint32_t*>(p.o_hi + out_off);
     uint32_t* pl = reinterpret_cast<uint32_t*>(p.o_lo + out_off);
-    if (!merges) return;
     if (FUSED) {
-      st_dev(ph, h0 | (h1 << 16));
-      st_dev(pl, lo0 | (lo1 << 16));
+      // every thread of the workgroup reaches the barrier (the waves past
+      // NR store nothing)
+      if (merges) {
+        st_dev(ph, h0 | (h1 << 16));
+        st_dev(pl, lo0 | (lo1 << 16));
+      }
       wait_vm();
       __syncthreads();
-      for (int wg = tid; wg < kFusedWoWG; wg += blockDim.x) st_dev(p.sync + kSyncWoSlot + 16 * wg + b * KVH + g, 1);
-    } else {
+      for (int wg = tid; wg < kFusedWoWG; wg += blockDim.x)
+        st_dev(p.wo_slots + kFusedSlotWords * wg + b * KV + g, 1);
+    } else if (merges) {
       *ph = h0 | (h1 << 16);
       *pl = lo0 | (lo1 << 16);
     }
@@ -530,12 +535,12 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     if (!FUSED || w != 0) return;
     if (__shfl(grp_prev, 0) != p.nsplit * p.B - 1) return;
     for (int bb = 0; bb < p.B; ++bb) {
-      float* qg = p.q + (size_t)bb * D + g * REP * HD;
+      float* qg = p.q + (size_t)bb * D + g * NR * HD;
 #pragma unroll
-      for (int i = 0; i < REP * HD / 64; ++i) st_dev(qg + i * 64 + lane, __uint_as_float(kNotYet));
+      for (int i = 0; i < NR * HD / 64; ++i) st_dev(qg + i * 64 + lane, __uint_as_float(kNotYet));
 #pragma unroll
       for (int kvp = 0; kvp < 2; ++kvp)
-        st_dev(p.kv_new + ((size_t)(bb * 2 + kvp) * KVH + g) * (HD / 2) + lane, kNotYetPair);
+        st_dev(p.kv_new + ((size_t)(bb * 2 + kvp) * KV + g) * (HD / 2) + lane, kNotYetPair);
     }
     if (lane == 0) st_dev(grp_cnt, 0);
   };
@@ -690,7 +695,9 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
 // wo projection (+ residual)
 // ---------------------------------------------------------------------------
 
-template <int NB, bool FUSED, int W = 4>
+// KV: kv heads of the fused schedule's attention (one O-ready word per
+// (sequence, kv head) in the workgroup's slot).
+template <int NB, bool FUSED, int W = 4, int KV = KVH>
 __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
   static_assert(!FUSED || W == 4, "the fused schedule's wo roles are 4-wave workgroups");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -721,8 +728,9 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
         if (lane == 0) __hip_atomic_fetch_or(p.sync + kSyncErr, GQA_WS_ERR_INIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         state = 2;
       } else {
-        int* slot = p.sync + kSyncWoSlot + 16 * blk;
-        const int nwords = p.B * KVH;
+        int* slot = p.wo_slots + kFusedSlotWords * blk;
+        const int nwords = p.B * KV;
+        static_assert(kFusedSlotWords <= 64, "one word per lane");
         int polls = 0;
         while (true) {
           const int v = lane < nwords ? ld_dev(slot + lane) : 1;
@@ -833,18 +841,19 @@ __global__ void __launch_bounds__(64 * W) decode_wo_kernel(DecodeParams p, int b
 // all waiting workgroups together fit in less than the chip's resident
 // capacity, so producers always find room to run whatever order the hardware
 // dispatches in.
-template <int NB>
+template <int NB, int KV>
 __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
   __shared__ uint32_t lds[2 * NB * (D / 2) > kAttnLdsWords ? 2 * NB * (D / 2) : kAttnLdsWords];
   static_assert(kFusedAttnQWord + REP * HD <= sizeof(lds) / 4, "no LDS for the attention role's Q");
-  const int na = p.nsplit * KVH * p.B;
+  constexpr int nqkv = fused_qkv_wg(KV);
+  const int na = p.nsplit * KV * p.B;
   const int blk = blockIdx.x;
-  if (blk < kFusedQkvWG) {
-    qkv_body<NB, true>(p, 0, blk, lds);
-  } else if (blk < kFusedQkvWG + na) {
-    attn_body<true>(p, blk - kFusedQkvWG, reinterpret_cast<float*>(lds));
+  if (blk < nqkv) {
+    qkv_body<NB, true, KV>(p, 0, blk, lds);
+  } else if (blk < nqkv + na) {
+    attn_body<true, KV>(p, blk - nqkv, reinterpret_cast<float*>(lds));
   } else {
-    wo_body<NB, true>(p, 0, blk - kFusedQkvWG - na, lds);
+    wo_body<NB, true, 4, KV>(p, 0, blk - nqkv - na, lds);
   }
 }
 
@@ -1286,23 +1295,51 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
 // The fused schedule keeps every waiting workgroup (attention and wo) below
 // the resident capacity of the chip: 256 CUs x 3 workgroups of 256 threads at
 // the kernel's register budget, with room left for at least 128 producers.
-bool decode_fused_eligible(int B, int nsplit) {
-  return B >= 1 && B <= kFusedMaxB && nsplit * KVH * B <= kFusedMaxAttnWG;
+// Its split is decode_split's, with fewer splits where that would exceed
+// kFusedMaxAttnWG attention workgroups (n_rep 1 and 2 at longer contexts); a
+// shape whose splits would then cover more than kFusedMaxChunk positions is
+// not admitted.
+bool decode_fused_split(int B, int L, int kv, int* nsplit, int* chunk) {
+  if (B < 1 || B > kFusedMaxB || kv > kFusedMaxKv) return false;
+  int n, c;
+  decode_split(B, L, kv, &n, &c);
+  const int cap = kFusedMaxAttnWG / (kv * B);
+  if (n > cap) {
+    n = cap;
+    c = (L + n - 1) / n;
+    c = (c + kAttnTile - 1) / kAttnTile * kAttnTile;
+    n = (L + c - 1) / c;
+  }
+  if (c > kFusedMaxChunk) return false;
+  *nsplit = n;
+  *chunk = c;
+  return true;
 }
 
 hipError_t launch_decode_fused(const DecodeParams& p0, hipStream_t s) {
-  if (!decode_fused_eligible(p0.B, p0.nsplit)) return hipErrorInvalidValue;
+  int nsplit = 0, chunk = 0;
+  if (!decode_fused_split(p0.B, p0.start_pos + 1, p0.kv, &nsplit, &chunk) || nsplit != p0.nsplit ||
+      chunk != p0.chunk)
+    return hipErrorInvalidValue;
   DecodeParams p = p0;
-  // hand-off buffers with "not yet" markers, after the synchronisation words
+  // hand-off buffers with "not yet" markers, and the wo slots, after the
+  // synchronisation words
   char* region = reinterpret_cast<char*>(p.sync);
   p.q = reinterpret_cast<float*>(region + kFusedQOff);
   p.kv_new = reinterpret_cast<uint32_t*>(region + kFusedKvOff);
   p.part = reinterpret_cast<float*>(region + kFusedPartOff);
-  const int grid = kFusedQkvWG + p.nsplit * KVH * p.B + kFusedWoWG;
-  if (p.B == 1)
-    hipLaunchKernelGGL(decode_step_kernel<1>, dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(decode_step_kernel<2>, dim3(grid), dim3(256), 0, s, p);
+  p.wo_slots = reinterpret_cast<int*>(region + kFusedSlotOff);
+  const int grid = fused_qkv_wg(p.kv) + p.nsplit * p.kv * p.B + kFusedWoWG;
+#define GQA_LAUNCH_STEP(NB, KV) hipLaunchKernelGGL((decode_step_kernel<NB, KV>), dim3(grid), dim3(256), 0, s, p)
+  switch (p.kv * 4 + p.B) {
+    case 16 * 4 + 1: GQA_LAUNCH_STEP(1, 16); break;
+    case 16 * 4 + 2: GQA_LAUNCH_STEP(2, 16); break;
+    case 32 * 4 + 1: GQA_LAUNCH_STEP(1, 32); break;
+    case 32 * 4 + 2: GQA_LAUNCH_STEP(2, 32); break;
+    case KVH * 4 + 1: GQA_LAUNCH_STEP(1, KVH); break;
+    default: GQA_LAUNCH_STEP(2, KVH); break;
+  }
+#undef GQA_LAUNCH_STEP
   return hipGetLastError();
 }
 

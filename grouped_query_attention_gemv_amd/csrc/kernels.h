@@ -37,26 +37,37 @@ constexpr uint32_t kNotYet = 0x7f800001u;       // fp32 signalling NaN
 constexpr uint32_t kNotYetPair = 0x7f817f81u;   // two bf16 signalling NaNs
 constexpr int kFusedMaxB = 2;        // largest batch of the fused schedule
 constexpr int kFusedMaxAttnWG = 128; // most attention workgroups of the fused schedule
+constexpr int kFusedMaxKv = 32;      // most key/value heads of the fused schedule
+constexpr int kFusedWoWG = 512;      // wo workgroups of the fused schedule, 8 rows each
 constexpr size_t kFusedQOff = kSyncWordsBytes;                                  // fp32 [kFusedMaxB][4096]
-constexpr size_t kFusedKvOff = kFusedQOff + (size_t)kFusedMaxB * D * 4;        // bf16 pairs [B][K, V][8][64]
-constexpr size_t kFusedPartOff = kFusedKvOff + (size_t)kFusedMaxB * 2 * KVH * HD * 2;
-// partials of at most kFusedMaxAttnWG splits of REP heads, each (b, g)
-// region rounded up to whole 128-byte lines
-constexpr size_t kFusedPartBytes = ((size_t)kFusedMaxAttnWG * REP * kPartStride + kFusedMaxB * KVH * 32) * 4;
-constexpr int kSyncBytes = (int)(((kFusedPartOff + kFusedPartBytes) + 4095) / 4096 * 4096);
+constexpr size_t kFusedKvOff = kFusedQOff + (size_t)kFusedMaxB * D * 4;        // bf16 pairs [B][K, V][kv][64]
+constexpr size_t kFusedPartOff = kFusedKvOff + (size_t)kFusedMaxB * 2 * kFusedMaxKv * HD * 2;
+// partials of at most kFusedMaxAttnWG splits (each serving 32 / kv <= 4
+// query heads), each (b, g) region rounded up to whole 128-byte lines
+constexpr size_t kFusedPartBytes =
+    ((size_t)kFusedMaxAttnWG * REP * kPartStride + kFusedMaxB * kFusedMaxKv * 32) * 4;
+// the one part that holds zeros, not markers, at rest: one word per (b, g)
+// for each wo workgroup, set once O of (b, g) is complete
+constexpr int kFusedSlotWords = kFusedMaxB * kFusedMaxKv;
+constexpr size_t kFusedSlotOff = kFusedPartOff + kFusedPartBytes;
+constexpr size_t kFusedSlotBytes = (size_t)kFusedWoWG * kFusedSlotWords * 4;
+constexpr int kSyncBytes = (int)(((kFusedSlotOff + kFusedSlotBytes) + 4095) / 4096 * 4096);
 constexpr int kSyncErr = 0;          // sticky error bits (GQA_WS_ERR_*)
 constexpr int kSyncMagic = 1;        // kWsMagic once gqa_workspace_init has run
 constexpr int kSyncOffHome = 2;      // fused launches whose first attention workgroup ran
                                      // away from its kv head's XCD (diagnostic)
 constexpr int kWsMagic = 0x31415147; // "GQA1"
 constexpr int kSyncGroup = 32;       // + 32*g: attention workgroups of kv head g done with Q
-constexpr int kSyncWoSlot = 2048;    // + 16*w + (b*8 + g): O of (b, g) ready, for wo workgroup w
 constexpr int kSyncProj = 10752;     // + 16*fb: K ranges of projection feature block fb summed
 // LDS word where an attention workgroup of the fused schedule keeps Q of its
 // 4 heads (after the words of the 4-wave merge, 16-byte aligned)
 constexpr int kFusedAttnQWord = (kAttnWaves * REP * HD + 2 * kAttnWaves * REP + 1 + 3) / 4 * 4;
-constexpr int kFusedQkvWG = 768;     // 96 per kv head: Q (64), K (16), V (16) workgroups
-constexpr int kFusedWoWG = 512;      // 8 wo rows each
+// QKV workgroups of the fused schedule, 8 features each: per kv head
+// 16 * 32 / kv for Q, 16 for K, 16 for V (768 for 8 kv heads)
+constexpr int fused_qkv_wg(int kv) { return kv * (16 * (H / kv) + 32); }
+// most positions an attention workgroup of the fused schedule covers (two
+// tiles per wave)
+constexpr int kFusedMaxChunk = 2 * kAttnWaves * kAttnTile;
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
 // The fused schedule's wo workgroups start streaming their weights this many
 // real-time ticks (100 MHz: 5 us) after they start.  They are dispatched as
@@ -65,7 +76,7 @@ constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedul
 // that the attention chain waits on.  Measured at B = 1: P = 128, 1000, 2000
 // take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
 constexpr unsigned kWoHoldTicks = 500;
-static_assert(kSyncWoSlot + 16 * kFusedWoWG <= kSyncProj, "wo slots overlap");
+static_assert(kSyncGroup + 32 * kFusedMaxKv <= kSyncProj, "head counters overlap");
 static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncWordsBytes / 4,
               "sync region too small for the projection counters of 32 kv heads");
 
@@ -90,6 +101,7 @@ struct DecodeParams {
   float* part;              // [B][8][nsplit][4][kPartStride]
   uint32_t* kv_new;         // fused: [B][2][8][64] appended K, V rows as packed bf16 pairs
   int* sync;                // the workspace's synchronisation words
+  int* wo_slots;            // fused: [kFusedWoWG][kFusedSlotWords] O-ready words
   int kv;                   // kv heads: 8 (Llama 3.1 8B), or 16 / 32 (n_rep 2, 1) on the
                             // GEMV path (B <= kGemvMaxB) with the three-launch schedule
   int nsplit, chunk;        // positions split over nsplit workgroups of chunk keys
@@ -112,8 +124,9 @@ hipError_t launch_rope_table(float* rope, int T_max, double theta, int scaled, h
 hipError_t launch_decode_qkv(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_attn(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s);
-// Whether the fused one-launch schedule applies to this call's shape.
-bool decode_fused_eligible(int B, int nsplit);
+// Whether the fused one-launch schedule applies to this call's shape, and
+// its split of the L visible positions.
+bool decode_fused_split(int B, int L, int kv, int* nsplit, int* chunk);
 hipError_t launch_decode_fused(const DecodeParams& p, hipStream_t s);
 
 

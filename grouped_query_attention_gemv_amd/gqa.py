@@ -23,7 +23,7 @@ ROPE_PAIRS = 64
 V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
-SYNC_BYTES = 380928
+SYNC_BYTES = 540672
 NOALLOC_SCRATCH_BYTES = 16 << 20   # the no-allocation decode's scratch array per GPU
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
 OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE, OP_VOCAB = 0, 1, 2, 3, 4

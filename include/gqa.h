@@ -85,7 +85,7 @@ extern "C" {
 /* Leading bytes of every workspace: the synchronisation words of the decode
  * kernels, headed by an error word and a magic word, then the hand-off
  * buffers of the one-launch decode (gqa_workspace_init prepares both). */
-#define GQA_SYNC_BYTES  380928
+#define GQA_SYNC_BYTES  540672
 
 /* Bits of the workspace error word (its first int). */
 #define GQA_WS_ERR_WAIT        0x1   /* a bounded wait of the one-launch decode timed out */

@@ -134,16 +134,17 @@ def test_layer_workspace_sizes():
 
 def test_workspace_starts_with_the_sync_region():
     # 64 KiB of synchronisation words, then the one-launch decode's hand-off
-    # buffers: Q and the appended rows of 2 sequences, the partials of 128
-    # attention workgroups (4 heads x 132 floats, 128-byte aligned per
-    # (sequence, kv head)), rounded up to whole 4 KiB fill blocks
-    handoff = 2 * 4096 * 4 + 2 * 2 * 8 * 128 * 2 + (128 * 4 * 132 + 2 * 8 * 32) * 4
-    assert G.SYNC_BYTES == (65536 + handoff + 4095) // 4096 * 4096 == 380928
+    # buffers: Q and the appended rows of 2 sequences at up to 32 kv heads,
+    # the partials of 128 attention workgroups (up to 4 heads x 132 floats,
+    # 128-byte aligned per (sequence, kv head)), then 512 wo workgroups' slots
+    # of 64 words, rounded up to whole 4 KiB fill blocks
+    handoff = 2 * 4096 * 4 + 2 * 2 * 32 * 128 * 2 + (128 * 4 * 132 + 2 * 32 * 32) * 4 + 512 * 64 * 4
+    assert G.SYNC_BYTES == (65536 + handoff + 4095) // 4096 * 4096 == 540672
     for op, B, T, Tm in ((G.OP_DECODE, 1, 1, 64), (G.OP_PREFILL, 4, 2048, 2048),
                          (G.OP_DECODE, 64, 1, 8224)):
         assert _wsb(op, B, Tm, T) > G.SYNC_BYTES
     src = open(HEADER).read()
-    assert "#define GQA_SYNC_BYTES  380928" in src
+    assert "#define GQA_SYNC_BYTES  540672" in src
 
 
 def test_workspace_init_rejections():
@@ -238,35 +239,47 @@ def test_decode_workspace_check_uses_the_decode_size():
 
 
 def test_fused_schedule_is_rejected_where_it_does_not_apply():
-    """The one-launch schedule is built for 8 key/value heads, B <= 2 and at
-    most 128 attention workgroups; asking for it elsewhere fails before any
-    launch.  The request is per call: the next call is unaffected."""
+    """The one-launch schedule takes B <= 2 and at most 128 attention
+    workgroups of at most 256 positions each; asking for it elsewhere fails
+    before any launch.  The request is per call: the next call is
+    unaffected."""
     L = G.lib()
-    assert L.gqa_block_decode(*_decode_args(n_kv=16, schedule=FUSED)) == EARG
-    assert L.gqa_block_decode(*_decode_args(n_kv=32, schedule=FUSED)) == EARG
     assert L.gqa_block_decode(*_decode_args(B=3, schedule=FUSED)) == EARG
-    assert L.gqa_block_decode(*_decode_args(start_pos=4000, T_max=4096, schedule=FUSED)) == EARG
+    assert L.gqa_block_decode(*_decode_args(start_pos=5000, T_max=8192, schedule=FUSED)) == EARG
+    assert L.gqa_block_decode(*_decode_args(n_kv=32, start_pos=1024, T_max=2048, schedule=FUSED)) == EARG
     # the same arguments with AUTO pass validation up to the planted alias
     assert L.gqa_block_decode(*_decode_args(B=3, schedule=AUTO, out=_fake(0))) == EALIAS
+    # 16 and 32 kv heads take the one-launch schedule too
+    assert L.gqa_block_decode(*_decode_args(n_kv=16, schedule=FUSED, out=_fake(0))) == EALIAS
+    assert L.gqa_block_decode(*_decode_args(n_kv=32, schedule=FUSED, out=_fake(0))) == EALIAS
 
 
 def test_decode_schedule_selection():
     sch = G.lib().gqa_decode_schedule
     F, S = FUSED, SPLIT
-    # fused while the attention grid (splits of 128 positions x 8 kv heads x B)
-    # stays within 128 workgroups, and B <= 2, 8 kv heads
+    # fused for B <= 2 while the attention grid (splits x kv heads x B) fits
+    # in 128 workgroups of at most 256 positions: the splits of 128 positions,
+    # fewer and longer where needed
     assert sch(8, 1, 0, 64, AUTO) == F
     assert sch(8, 1, 1000, 1024, AUTO) == F
     assert sch(8, 1, 2047, 4096, AUTO) == F
-    assert sch(8, 1, 2048, 4096, AUTO) == S
+    assert sch(8, 1, 4095, 4096, AUTO) == F          # 16 splits of 256
+    assert sch(8, 1, 4096, 8192, AUTO) == S          # 16 would need 257 each
     assert sch(8, 2, 1023, 2048, AUTO) == F
-    assert sch(8, 2, 1024, 2048, AUTO) == S
+    assert sch(8, 2, 2047, 2048, AUTO) == F          # 8 splits of 256 per sequence
+    assert sch(8, 2, 2048, 4096, AUTO) == S
     assert sch(8, 3, 10, 64, AUTO) == S
     assert sch(8, 64, 8192, 8224, AUTO) == S
-    # the head count decides too
-    assert sch(16, 1, 1000, 1024, AUTO) == S
-    assert sch(32, 1, 0, 64, AUTO) == S
-    assert sch(16, 1, 1000, 1024, FUSED) == EARG
+    # 16 kv heads: 8 splits per sequence at B = 1; 32: 4
+    assert sch(16, 1, 1000, 1024, AUTO) == F
+    assert sch(16, 1, 2047, 4096, AUTO) == F
+    assert sch(16, 1, 2048, 4096, AUTO) == S
+    assert sch(32, 1, 0, 64, AUTO) == F
+    assert sch(32, 1, 1023, 1024, AUTO) == F
+    assert sch(32, 1, 1024, 2048, AUTO) == S
+    assert sch(32, 2, 511, 1024, AUTO) == F
+    assert sch(32, 2, 512, 1024, AUTO) == S
+    assert sch(32, 1, 1024, 2048, FUSED) == EARG
     # explicit requests
     assert sch(8, 1, 1000, 1024, SPLIT) == S
     assert sch(8, 1, 1000, 1024, FUSED) == F
@@ -353,7 +366,7 @@ def _layer_decode_args(**kw):
     (dict(n_kv=4), EARG), (dict(n_kv=24), EARG), (dict(n_kv=16, g=None), ENULL),
     (dict(n_kv=32, B=0), ESHAPE), (dict(n_kv=16, start_pos=1024), ERANGE),
     (dict(n_kv=32, ws_bytes=4096), EWS), (dict(n_kv=16, h=_fake(10)), EALIAS),
-    (dict(n_kv=16, schedule=FUSED), EARG),
+    (dict(n_kv=32, B=2, start_pos=600, schedule=FUSED), EARG),
 ])
 def test_layer_decode_rejects_bad_arguments(kw, code):
     assert G.lib().gqa_layer_decode(*_layer_decode_args(**kw)) == code
@@ -400,8 +413,8 @@ def _vocab_ws(B):
     (dict(B=9, g=_fake(3)), EWS),
     (dict(B=9, g=_fake(3), ws=_fake(4), ws_bytes=_vocab_ws(9) - 1), EWS),
     (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (4 << 32) + 8), ws_bytes=_vocab_ws(9)), EALIGN),
-    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE - 380928), ws_bytes=_vocab_ws(9)), EALIAS),
-    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (2 << 32) - (380928 + 4096)),
+    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE - G.SYNC_BYTES), ws_bytes=_vocab_ws(9)), EALIAS),
+    (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (2 << 32) - (G.SYNC_BYTES + 4096)),
           ws_bytes=_vocab_ws(9)), EALIAS),
 ])
 def test_vocab_logits_rejects_bad_arguments(kw, code):

@@ -86,6 +86,18 @@ def test_decode_unscaled_rope():
     _decode_full(1, 5000, 5024, scaled=False)
 
 
+@pytest.mark.parametrize("n_kv,B,P", [(16, 1, 1000), (32, 1, 1000), (32, 1, 1023), (32, 2, 300),
+                                      (16, 2, 1000), (8, 1, 3000), (8, 2, 1500), (32, 1, 0)])
+def test_decode_fused_head_counts_and_long_splits(n_kv, B, P):
+    """The one-launch schedule at 16 and 32 kv heads, and with splits capped
+    at 128 attention workgroups (two 32-position tiles per wave, the appended
+    row in the second tile for the last split), within the oracle's bounds;
+    the library picks it for these shapes."""
+    c, errs = _decode_full(B, P, ((P + 1 + 31) // 32) * 32 + 32, G.DECODE_FUSED, n_kv=n_kv)
+    assert G.decode_schedule(B, P, c.T_max, n_kv, G.DECODE_AUTO) == G.DECODE_FUSED
+    assert errs["delta"][0] < 1e-3
+
+
 @pytest.mark.parametrize("n_kv,B,P", [(32, 1, 1000), (32, 3, 777), (16, 1, 1000), (16, 2, 100),
                                       (32, 8, 129), (16, 5, 0), (16, 9, 300), (32, 17, 65),
                                       (16, 64, 31), (32, 70, 200)])
@@ -381,18 +393,22 @@ def test_workspace_init_writes_words_and_markers():
     words (64 KiB) but the magic word, then the one-launch decode's hand-off
     buffers holding their "not yet" markers -- an fp32 signalling NaN in Q
     (2 x 4096 floats) and in the partials, a pair of bf16 signalling NaNs in
-    the appended rows (2 x 2 x 8 x 128 bf16) -- and nothing written past the
-    region."""
+    the appended rows (2 x 2 x 32 x 128 bf16) -- then the wo slots (512 x 64
+    words) zero, and nothing written past the region."""
     n = G.SYNC_BYTES + 4096
     ws = torch.full((n,), 0x5a, dtype=torch.uint8, device=DEV)
     G.workspace_init(ws)
     torch.cuda.synchronize()
     w = ws.view(torch.int32).cpu().numpy().view(np.uint32)
     assert w[0] == 0 and w[1] == G.WS_MAGIC and not w[2:16384].any()
-    q_end, kv_end = 16384 + 2 * 4096, 16384 + 2 * 4096 + 2 * 2 * 8 * 64
+    q_end = 16384 + 2 * 4096
+    kv_end = q_end + 2 * 2 * 32 * 64
+    part_end = kv_end + 128 * 4 * 132 + 2 * 32 * 32
     assert (w[16384:q_end] == 0x7f800001).all()
     assert (w[q_end:kv_end] == 0x7f817f81).all()
-    assert (w[kv_end:G.SYNC_BYTES // 4] == 0x7f800001).all()
+    assert (w[kv_end:part_end] == 0x7f800001).all()
+    assert not w[part_end:part_end + 512 * 64].any()
+    assert not w[part_end + 512 * 64:G.SYNC_BYTES // 4].any()
     assert (w[G.SYNC_BYTES // 4:] == 0x5a5a5a5a).all()
 
 
