@@ -629,11 +629,16 @@ hipError_t launch_prefill_wo(const PrefillParams& p, hipStream_t s) {
 constexpr int kAttnStage = 2 * AK * HD * 2;      // K and V^T tiles, fp16: 32 KiB
 
 // LDS swizzles of the K and V^T tiles.  One fragment read touches 16 K rows
-// (keys whose bits 0, 1, 3, 4 vary) or 16 consecutive V^T rows; both maps
-// send those rows to distinct 16-byte slots of a 256-byte bank window, and
-// any 8 consecutive of them to distinct slots of a 128-byte window.
+// (keys whose bits 0, 1, 3, 4 vary) or 16 consecutive V^T rows (128 bytes
+// each, two to a 256-byte bank window), each lane a 16-byte slot.  K rows
+// hold chunk c at c ^ kswz(key), V^T rows chunk c at c ^ (dim & 7).  Both
+// were chosen by the LDS bank-conflict counter: with these maps the
+// fragment reads register no conflicts on gfx950, while folding bit 3 of
+// the dimension into the V^T map as well (a map that also spreads any 8
+// consecutive rows over a 128-byte window) made the V^T reads take twice
+// the LDS cycles.
 __device__ __forceinline__ int attn_kswz(int key) { return (key & 3) | ((key >> 1) & 12); }
-__device__ __forceinline__ int attn_vswz(int dim) { return (dim & 7) ^ ((dim >> 3) & 1); }
+__device__ __forceinline__ int attn_vswz(int dim) { return dim & 7; }
 constexpr int kAttnLds = 2 * kAttnStage;         // double-buffered: 64 KiB
 
 // queries per workgroup of the attention kernel for kv heads KV
