@@ -266,10 +266,10 @@ def record_decode_b1(G, synth, P, T_max, steps, warmup, traffic_summary):
     if dec["fused"]:
         # one kernel per step: the step time over the timed region is that
         # kernel's average duration (HIP events on the stream the graph runs on)
-        kname = "decode_step_kernel<1>"
+        kname = "decode_step_kernel<1, 8>"
         roof = roofline(kname, "hbm", nb["step"], us, counter_traffic(traffic_summary, kname))
     else:
-        kname = "decode_qkv_kernel<1, 8>"
+        kname = "decode_qkv_kernel<1, 8, 4>"
         roof = roofline(kname, "hbm", nb["qkv"], dec["kern_us"]["qkv"],
                         counter_traffic(traffic_summary, kname))
     tbs = nb["step"] / (us * 1e-6) / 1e12
@@ -608,7 +608,11 @@ def extra_workload(G, synth, args):
         nb = decode_bytes(1, 1000, kvh)
         us = dec["us_step"]
         tbs = nb["step"] / (us * 1e-6) / 1e12
-        kname = f"decode_qkv_kernel<1, {kvh}>"
+        if dec["fused"]:
+            # one kernel per step, as for 8 kv heads
+            roof = roofline(f"decode_step_kernel<1, {kvh}>", "hbm", nb["step"], us)
+        else:
+            roof = roofline(f"decode_qkv_kernel<1, {kvh}, 4>", "hbm", nb["qkv"], dec["kern_us"]["qkv"])
         pf = bench_prefill(G, synth, 10, 3, kvh=kvh)
         rec.update({
             "value": round(us, 3), "unit": "us/block-step", "steps": args.steps,
@@ -619,7 +623,7 @@ def extra_workload(G, synth, args):
                        "schedule": "fused" if dec["fused"] else "split", "hip_graph": dec["graph"]},
             "hbm_tbs": round(tbs, 4), "hbm_frac_of_peak": round(tbs * 1000 / HBM_PEAK_GBS, 4),
             "kernels_us": {k: round(v, 3) for k, v in dec["kern_us"].items()},
-            "roofline": roofline(kname, "hbm", nb["qkv"], dec["kern_us"].get("qkv", us)),
+            "roofline": roof,
             "prefill_b4_t2048": {"us_per_call": round(pf["us"], 2),
                                  "mfma_util": round(pf["fl"]["total"] / (pf["us"] * 1e-6) /
                                                     (MFMA_PEAK_TFLOPS * 1e12), 4)},
@@ -739,6 +743,39 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: int, title: str, comma
     print(f"wrote {out}")
 
 
+def trace_summary(stats_csv: str, bench_log: str, title: str, command: str, out: str):
+    """Write a profiles/ summary of a rocprofv3 --kernel-trace --stats run:
+    its per-kernel statistics (run_kernel_stats.csv) and, beside them, the
+    bench.py record the traced command printed (its own HIP-event timings)."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    rec = None
+    for line in open(bench_log):
+        if line.startswith("{"):
+            rec = json.loads(line)
+    lines = [f"# {title} — rocprofv3 kernel trace", "", "Command (repository root):", "",
+             f"    {command}", "",
+             "Per-kernel statistics from `run_kernel_stats.csv` (every dispatch of the run: "
+             "warm-up, timed steps and the per-stage event passes):", "",
+             "| kernel | calls | mean µs | min µs | max µs | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("void gqa::", "").split("(")[0]
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    if rec is not None:
+        keep = {k: rec[k] for k in ("value", "unit", "ms_per_step", "kernels_us", "roofline",
+                                    "hbm_frac_of_peak", "mfma_frac_of_peak", "config")
+                if k in rec}
+        lines += ["", "The bench.py record of the same run (HIP events around the timed "
+                  "steps; `kernels_us` from the per-stage event pass):", "",
+                  "    " + json.dumps(keep)]
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}")
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -763,8 +800,13 @@ def main():
                          "(commands given with --pmc-commands, calibration copy with "
                          "--copy-probe-mib)")
     ap.add_argument("--pmc-commands", nargs="*", default=[])
+    ap.add_argument("--trace-summary", nargs=5, metavar=("STATS_CSV", "BENCH_LOG", "TITLE", "COMMAND", "OUT"),
+                    help="write a profiles/ summary of a kernel-trace run and exit")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.pmc_summary:
         fcsv, wcsv, title, out = args.pmc_summary
         pmc_summary(fcsv, wcsv, args.copy_probe_mib or 256, title, args.pmc_commands, out)

@@ -94,7 +94,7 @@ extern "C" {
 #define GQA_WS_ERR_FP16_RANGE  0x100 /* a prefill saturated an operand to +-65504 */
 
 /* Decode schedules (the `schedule` argument of the decode calls). */
-#define GQA_DECODE_AUTO   0             /* one launch where the shape admits it, else three */
+#define GQA_DECODE_AUTO   0             /* one launch where admitted and faster, else three */
 #define GQA_DECODE_SPLIT  1             /* three launches: QKV, attention, wo */
 #define GQA_DECODE_FUSED  2             /* one launch; shapes it does not admit fail */
 
@@ -192,11 +192,15 @@ int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * GQA_DECODE_SPLIT runs the three stages as three kernels.  GQA_DECODE_FUSED
  * runs the whole step as one kernel whose workgroups pass results to each
  * other through the workspace (Q/K/V -> attention -> wo), so that each
- * consumer's HBM reads overlap its producer's; it admits n_kv_heads = 8,
- * B <= 2 and contexts short enough for at most 128 attention workgroups
- * (start_pos + 1 <= 2048 at B = 1, <= 1024 at B = 2).  GQA_DECODE_AUTO takes
- * the one-launch schedule where it is admitted.  Results agree between the
- * schedules bit for bit; each is deterministic.
+ * consumer's HBM reads overlap its producer's; it admits B <= 2 and
+ * contexts that fit in at most 128 attention workgroups of at most 256
+ * positions (the three-launch schedule's splits of 128 positions, fewer and
+ * longer where they would be too many): start_pos + 1 <= 4096 at 8 kv heads
+ * and B = 1, <= 2048 at B = 2 or 16 kv heads, <= 1024 at 32 kv heads, <= 512
+ * at 32 kv heads and B = 2.  GQA_DECODE_AUTO takes the one-launch schedule
+ * where it is admitted, except at B = 2 with 16 or 32 kv heads.  Where both
+ * schedules split the positions alike (always below those lengths halved)
+ * their results agree bit for bit; each is deterministic.
  */
 int gqa_decode_schedule(int n_kv_heads, int B, int start_pos, int T_max, int schedule);
 

@@ -91,10 +91,11 @@ def test_decode_unscaled_rope():
 def test_decode_fused_head_counts_and_long_splits(n_kv, B, P):
     """The one-launch schedule at 16 and 32 kv heads, and with splits capped
     at 128 attention workgroups (two 32-position tiles per wave, the appended
-    row in the second tile for the last split), within the oracle's bounds;
-    the library picks it for these shapes."""
+    row in the second tile for the last split), within the oracle's bounds.
+    AUTO picks it at 8 kv heads and at B = 1."""
     c, errs = _decode_full(B, P, ((P + 1 + 31) // 32) * 32 + 32, G.DECODE_FUSED, n_kv=n_kv)
-    assert G.decode_schedule(B, P, c.T_max, n_kv, G.DECODE_AUTO) == G.DECODE_FUSED
+    auto = G.DECODE_FUSED if (n_kv == 8 or B == 1) else G.DECODE_SPLIT
+    assert G.decode_schedule(B, P, c.T_max, n_kv, G.DECODE_AUTO) == auto
     assert errs["delta"][0] < 1e-3
 
 
