@@ -24,9 +24,9 @@ namespace gqa {
 // Output features of QKV workgroup `blk` of W waves: 2W consecutive
 // features, 2 per wave.  The three-launch schedule takes them in feature
 // order.  The fused schedule (W = 4) gives kv head g the workgroups
-// blk = g (mod 8), which the dispatcher usually places on one XCD together
-// with the head's attention workgroups (Q of its 4 query heads: 64
-// workgroups, then K: 16, then V: 16).
+// blk = g (mod KV), which the dispatcher places on XCD g mod 8 together with
+// the head's attention workgroups (Q of its 32 / KV query heads: 16 per
+// head, then K: 16, then V: 16).
 template <bool FUSED, int W, int KV>
 __device__ __forceinline__ int qkv_first_feature(int blk) {
   static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
@@ -38,8 +38,8 @@ __device__ __forceinline__ int qkv_first_feature(int blk) {
   return D + KV * HD + g * HD + (r - QW - 16) * 8;
 }
 
-// KV: kv heads of the projection (the fused schedule runs KV = 8 only); W:
-// waves of the workgroup.
+// KV: kv heads of the projection (8, 16 or 32, both schedules); W: waves of
+// the workgroup.
 template <int NB, bool FUSED, int KV = KVH, int W = 4>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
   constexpr int kNqkv = D + 2 * KV * HD;
@@ -166,15 +166,16 @@ __host__ __device__ constexpr size_t part_region_floats(int nsplit, int nr) {
 constexpr int attn_lds_words(int rep) { return kAttnWaves * rep * HD + 2 * kAttnWaves * rep + 1; }
 constexpr int kAttnLdsWords = attn_lds_words(REP);
 
-// FUSED: Q, K and V come from the same launch.  The workgroup runs on the XCD
-// of its kv head (blk = g mod 8), waits on the head's counter (device scope),
-// then reads Q and the appended row through that XCD's L2: the first reader
-// of a line fetches it, the head's other workgroups hit it.  The split merge
-// works the same way, and O goes to the wo workgroups of the launch (on
-// every XCD) through device-scope stores.
+// FUSED: Q, K and V come from the same launch.  The workgroup polls, with
+// device-scope loads, the words of Q and of the appended row themselves
+// (they hold a "not yet" marker until their QKV workgroup stores them), so
+// value and arrival come in one round trip.  Every split but the last
+// publishes its partials into marked words and ends; the last split polls
+// them and merges, and O goes to the wo workgroups of the launch (on every
+// XCD) through device-scope stores and one flag per wo workgroup.
 // KV kv heads serve NR = 32 / KV query heads each (NR = 4 for Llama 3.1 8B;
-// 2 and 1, the last being multi-head attention, on the three-launch path).
-// The MFMA operand columns are the NR heads' hi parts, then their lo parts.
+// 2 and 1, the last being multi-head attention).  The MFMA operand columns
+// are the NR heads' hi parts, then their lo parts.
 template <bool FUSED, int KV = KVH>
 __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float* lds) {
   constexpr int NR = H / KV;
@@ -230,15 +231,11 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
       vf[dt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff + 1024 * (dt & 3), 4096 * (dt >> 2), kNtPolicy));
   };
 
-  // Fused schedule: Q and the appended row are published with device-scope
-  // stores into words that hold the "not yet" marker, and polled with
-  // device-scope loads (below).  The split partials are published with
-  // device-scope stores that have completed before the producer counts
-  // itself, and are first read on any XCD only after the merging
-  // workgroup's device-scope counter read (no line holds partials of two
-  // (sequence, head) sets).  An L2 that never held the line since the kernel
-  // started (L2 lines are invalidated at every kernel start) fetches the
-  // published value, so those reads go through this XCD's L2 (ld_xcd, sc0).
+  // Fused schedule: Q, the appended row and the split partials are all
+  // published with device-scope stores into words that hold the "not yet"
+  // marker, and polled with device-scope loads, which always see the
+  // latest store whichever XCD made it (an L2-cached poll of a line the L2
+  // already holds would not).
 
   // Fused schedule: replace the appended row (position start_pos, written by
   // this launch) with its copy in kv_new, for the lanes that hold it.  The
@@ -818,24 +815,28 @@ __global__ void __launch_bounds__(64 * W) decode_wo_kernel(DecodeParams p, int b
 // Fused schedule: the whole block step in one launch
 // ---------------------------------------------------------------------------
 //
-// Workgroups [0, 768) run the QKV projection, the next nsplit*8*B the
-// flash-decode, the last 512 wo.  Dispatch follows the workgroup index and
-// the 768 QKV workgroups fill the chip (3 per CU), so every one of them
-// streams its weights from the start; the attention and wo workgroups take
-// the places of retiring QKV ones.  (Attention first measured slower: the
-// QKV workgroups it displaced started late and stretched the QKV stream.)
-// Kv head g takes the QKV and attention workgroups with i = g (mod 8).  Each
-// consumer starts its own HBM reads (K/V tiles, wo rows) before it waits, so
-// the three phases overlap instead of paying a launch boundary each:
+// Workgroups [0, fused_qkv_wg(KV)) run the QKV projection (768 at 8 kv
+// heads), the next nsplit*KV*B the flash-decode, the last 512 wo.  Dispatch
+// follows the workgroup index and the QKV workgroups fill the chip (3 per
+// CU at 8 kv heads), so they stream their weights from the start; the
+// attention and wo workgroups take the places of retiring QKV ones.
+// (Attention first measured slower: the QKV workgroups it displaced started
+// late and stretched the QKV stream.)  Kv head g takes the QKV and attention
+// workgroups with i = g (mod KV).  Each consumer starts its own HBM reads
+// (K/V tiles, wo rows) before it waits, so the three phases overlap instead
+// of paying a launch boundary each:
 //   QKV -> attention: Q and the new row are stored into words that hold a
 //     "not yet" marker; the head's attention workgroups poll the words
 //     themselves, so arrival and value come in one round trip, and the last
-//     of them writes the markers back;
-//   split -> merge: per-(b, g) counter, the last split merges the partials;
-//   attention -> wo: the workgroup that completes O of (b, g) stores it with
-//     device-scope stores and sets word b*8 + g of every wo workgroup's slot.
+//     of them (a per-head count) writes the markers back;
+//   split -> merge: the splits but the last store their partials into marked
+//     words and end; the last split polls them, merges in a fixed order and
+//     restores the markers;
+//   attention -> wo: the merging workgroup stores O of (b, g) with
+//     device-scope stores and sets word b*KV + g of every wo workgroup's
+//     slot.
 // Producers that signal through a separate word wait for their stores to
-// complete first; counters, slots and marked words are polled with
+// complete first; slots and marked words are polled with
 // device-scope loads.  Every wait is bounded (kMaxPolls) and only the
 // consumers wait.  The host admits a shape only if
 // all waiting workgroups together fit in less than the chip's resident

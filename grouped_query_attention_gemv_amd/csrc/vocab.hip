@@ -1,15 +1,17 @@
 // Vocabulary projection (page "Llama 3.1 8B . Vocabulary projection"):
 // L = z W_out with the weight stored [out, in] = [V][4096] and z the final
-// norm of the last hidden state, "cast to float32 before it is returned":
-// the projection's output is taken in the model's bf16 and handed back as
-// fp32, so each logit is the bf16 rounding (nearest even) of its fp32 dot
-// product.  The norm in front (the page's code: self.norm, an RMSNorm with
-// norm_eps) is optional here and read as in the layer pre-norm.
+// norm of the last hidden state.  The page computes the projection in the
+// model's bf16 and converts its result to fp32 on return, so each logit is
+// the bf16 rounding (nearest even) of its fp32 dot product.  The norm in
+// front (the page's code: self.norm, an RMSNorm with norm_eps) is optional
+// here and read as in the layer pre-norm.
 //
-// A bandwidth GEMV over 1.05 GB of weights at V = 128,256: each wave takes
-// pairs of weight rows in a grid-strided loop, with the next pair's 16 loads
-// issued before the current pair's products (two pairs in flight per wave);
-// the B <= 8 token vectors are staged (and normalised) once per workgroup.
+// Up to 8 sequences: a bandwidth GEMV over 1.05 GB of weights at V =
+// 128,256: each wave takes pairs of weight rows in a grid-strided loop, with
+// the next pair's 16 loads issued before the current pair's products (two
+// pairs in flight per wave); the token vectors are staged (and normalised)
+// once per workgroup.  Above 8: the matrix-core kernel further down, one
+// weight pass per 64 sequences.
 #include <algorithm>
 #include <type_traits>
 
