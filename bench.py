@@ -100,6 +100,17 @@ def roofline(kernel: str, bound: str, work: float, us: float, traffic=None) -> d
             "algorithmic_flops": work, "kernel_us": round(us, 3)}
 
 
+def code_digest(path: str) -> str:
+    """sha256 of a C++ source with its comments and blank lines removed, so
+    that a counter summary stays valid across edits that change only
+    comments (string literals in these sources hold no comment markers)."""
+    text = open(os.path.join(ROOT, path)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def counter_traffic(summary: str, kernel: str, source: str = DECODE_SRC):
     """HBM bytes per launch of `kernel` measured by rocprofv3 (FETCH_SIZE +
     WRITE_SIZE, calibrated on a known-size copy), as recorded in a profile
@@ -109,11 +120,10 @@ def counter_traffic(summary: str, kernel: str, source: str = DECODE_SRC):
         fields = {}
         for line in open(os.path.join(ROOT, "profiles", summary)).read().splitlines():
             line = line.strip()
-            if line.startswith(("traffic_bytes_per_launch[", "kernel_source_sha256:")):
+            if line.startswith(("traffic_bytes_per_launch[", "kernel_code_sha256:")):
                 k, v = line.split(": ", 1)
                 fields[k] = v
-        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
-        if fields.get("kernel_source_sha256") != digest:
+        if fields.get("kernel_code_sha256") != code_digest(source):
             return None
         return int(fields[f"traffic_bytes_per_launch[{kernel}]"])
     except (OSError, KeyError, ValueError):
@@ -715,7 +725,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: int, title: str, comma
     # the copy probe is the largest copy dispatch of each run
     ffac = kib / max(fcopies)
     wfac = kib / max(wcopies)
-    digest = hashlib.sha256(open(os.path.join(ROOT, DECODE_SRC), "rb").read()).hexdigest()
+    digest = code_digest(DECODE_SRC)
     lines = [f"# {title} — HBM traffic per kernel (rocprofv3 counters)", "",
              "Commands (two passes, one counter each, repository root):", ""]
     lines += [f"    {c}" for c in commands]
@@ -735,9 +745,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: int, title: str, comma
         traffic[k] = t
         lines.append(f"| {k} | {n} | {fb:,.1f} | {wb:,.1f} | {t:,} |")
     lines += ["", "Figures read by bench.py (`roofline.traffic`; it reports null instead when "
-              "decode.hip differs from the source these counters were taken on):", ""]
+              "the code of decode.hip, comments aside, differs from the code these counters "
+              "were taken on):", ""]
     lines += [f"    traffic_bytes_per_launch[{k}]: {v}" for k, v in traffic.items()]
-    lines += [f"    kernel_source_sha256: {digest}", ""]
+    lines += [f"    kernel_code_sha256: {digest}", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {out}")
