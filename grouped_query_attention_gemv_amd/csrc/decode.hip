@@ -24,9 +24,9 @@ namespace gqa {
 // Output features of QKV workgroup `blk` of W waves: 2W consecutive
 // features, 2 per wave.  The three-launch schedule takes them in feature
 // order.  The fused schedule (W = 4) gives kv head g the workgroups
-// blk = g (mod KV), which the dispatcher places on XCD g mod 8 together with
-// the head's attention workgroups (Q of its 32 / KV query heads: 16 per
-// head, then K: 16, then V: 16).
+// blk = g (mod KV), like the head's attention workgroups (Q of its 32 / KV
+// query heads: 16 per head, then K: 16, then V: 16).  No hand-off depends on
+// the XCD a workgroup lands on.
 template <bool FUSED, int W, int KV>
 __device__ __forceinline__ int qkv_first_feature(int blk) {
   static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
