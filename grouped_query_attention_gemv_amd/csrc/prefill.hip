@@ -689,19 +689,19 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   // Iteration kt reads K tile kt+1 (the next scores) and V tile kt, so at
   // its start K tile kt+2 and V tile kt+1 can be fetched into the buffers
   // iteration kt-1 has finished with.
-  auto sK = [&](int kt) { return smem + (kt & 1) * (AK * HD * 2); };
-  auto sV = [&](int kt) { return smem + 2 * (AK * HD * 2) + (kt & 1) * (AK * HD * 2); };
+  auto sK = [&](int buf) { return smem + buf * (AK * HD * 2); };
+  auto sV = [&](int buf) { return smem + 2 * (AK * HD * 2) + buf * (AK * HD * 2); };
   auto issue_k = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(k_src[i] + (size_t)kt * AK * HD),
-                                       (lds_void*)(sK(kt) + (w * 8 + i * 4) * 256), 16, 0, 0);
+                                       (lds_void*)(sK(kt & 1) + (w * 8 + i * 4) * 256), 16, 0, 0);
   };
   auto issue_v = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(v_src[i] + (size_t)kt * (HD * AK)),
-                                       (lds_void*)(sV(kt) + (w * 16 + i * 8) * 128), 16, 0, 0);
+                                       (lds_void*)(sV(kt & 1) + (w * 16 + i * 8) * 128), 16, 0, 0);
   };
   issue_k(0);
   issue_v(0);
@@ -723,6 +723,9 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m_run: the softmax reference of each query column (exp2 units, Q is
+  // pre-scaled), -inf before the first tile; l_run: the column sums of
+  // exp2(s - m_run) so far.
   float m_run[2], l_run[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -730,13 +733,15 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
     l_run[nt] = 0.f;
   }
 
-  // S^T = K . Q^T for the K tile at k_lds.
+  // S^T - r = K . Q^T - r for the K tile at k_lds, where r is the reference
+  // the column's exponentials will use, folded into the accumulators'
+  // initial value so that no subtraction is needed afterwards.
   // sacc[mt][nt][e]: key 32*(mt>>1) + rg*8 + (mt&1)*4 + e of the tile, query q0 + nt*16 + col
-  auto scores = [&](const char* k_lds, f32x4 (&sacc)[4][2]) {
+  auto scores = [&](const char* k_lds, const float (&r)[2], f32x4 (&sacc)[4][2]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{-r[nt], -r[nt], -r[nt], -r[nt]};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -749,16 +754,76 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
       }
     }
   };
+  // causal mask of tile kt: keys past the query get -inf
+  auto mask = [&](int kt, f32x4 (&sc)[4][2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int q = p.start_pos + q0 + nt * 16 + col;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
+          if (key > q) sc[mt][nt][e] = -INFINITY;
+        }
+    }
+  };
+  // Lazy rescaling: the reference only moves (and O, l are only rescaled)
+  // when a column's maximum exceeds it by more than 2^8, so that
+  // p = exp2(s - m_run) <= 256 (in range for fp16).  The decision is
+  // wave-uniform and most tiles skip the rescale.  prepare() takes the
+  // decision for scores sc computed against reference r and returns the
+  // columns' maxima in cand; rescale() then moves the reference, scales O
+  // and l and re-references sc (it must follow every P.V product of the
+  // earlier tiles).  The first tile always rescales (m_run = -inf; its
+  // columns all hold key 0, so their maxima are finite).
+  auto prepare = [&](const f32x4 (&sc)[4][2], const float (&r)[2], float (&cand)[2]) -> bool {
+    bool grow = false;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) t = fmaxf(t, fmaxf(fmaxf(sc[mt][nt][0], sc[mt][nt][1]),
+                                                         fmaxf(sc[mt][nt][2], sc[mt][nt][3])));
+      t = max_xor32(max_xor16(t));
+      cand[nt] = r[nt] + t;
+      grow |= cand[nt] > m_run[nt] + kLazyRescale;
+    }
+    return __any(grow);
+  };
+  auto rescale = [&](f32x4 (&sc)[4][2], const float (&r)[2], const float (&cand)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float m_new = fmaxf(m_run[nt], cand[nt]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+      l_run[nt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
+      const float shift = m_new - r[nt];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) sc[mt][nt] -= shift;
+      m_run[nt] = m_new;
+    }
+  };
 
-  // One key tile: softmax of the scores s (tile kt) and O += V P, with the
-  // next tile's scores computed in between (not on the last tile, which
-  // is the last), so matrix-core and vector work of one wave interleave.
-  f32x4 s[4][2];
+  // One key tile kt (its scores sc already against reference m_run, masked):
+  // P = exp2(sc) and O += V P, with the next tile's scores (into sn), mask
+  // and rescale decision computed in between, so that matrix-core and
+  // vector work interleave.  BUF = kt & 1 is a constant, so every LDS
+  // address is one too.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  scores(sK(0), s);
-  auto step = [&](auto last_tag, int kt) {
+  f32x4 sa[4][2], sb[4][2];
+  {
+    const float r0[2] = {0.f, 0.f};
+    float cand[2];
+    scores(sK(0), r0, sa);
+    if (0 >= kmask || klast == 0) mask(0, sa);
+    if (prepare(sa, r0, cand)) rescale(sa, r0, cand);
+  }
+  auto step = [&](auto last_tag, auto buf_tag, int kt, f32x4 (&sc)[4][2], f32x4 (&sn)[4][2]) {
     constexpr bool LAST = decltype(last_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
     // K tile kt+1 and V tile kt have landed for every wave, and every wave
     // is done with K tile kt and V tile kt-1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -767,84 +832,44 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
       if (kt + 2 <= klast) issue_k(kt + 2);
       issue_v(kt + 1);
     }
-    if (LAST || kt >= kmask) {                      // causal mask near the diagonal
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int q = p.start_pos + q0 + nt * 16 + col;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kt * AK + 32 * (mt >> 1) + rg * 8 + (mt & 1) * 4 + e;
-            if (key > q) s[mt][nt][e] = -INFINITY;
-          }
-      }
-    }
-    // Lazy rescaling: the reference maximum only moves (and O, l are only
-    // rescaled) when a column's maximum grows by more than 2^8 over it, so
-    // p = exp2(s - m) <= 256 (exact in range for fp16).  The decision is
-    // wave-uniform, and most tiles skip the rescale entirely.
-    float m_new[2];
-    bool grow = false;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float t = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t = fmaxf(t, s[mt][nt][e]);
-      t = max_xor32(max_xor16(t));
-      m_new[nt] = fmaxf(m_run[nt], t);
-      grow |= t > m_run[nt] + kLazyRescale;
-    }
-    const bool rescale = __any(grow);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) m_new[nt] = rescale ? m_new[nt] : m_run[nt];
-    if (rescale) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
-        l_run[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[dt][nt] *= alpha;
-      }
-    }
+    const float r[2] = {m_run[0], m_run[1]};
+    if (!LAST) scores(sK(BUF ^ 1), r, sn);
 
-    f32x4 sn[4][2];
-    if (!LAST) scores(sK(kt + 1), sn);
-
+    // P = exp2(sc) as fp16 pairs (the B operand of P.V); l gathers the same
+    // fp16 values that O does
     u32x4 pf[2][2];
-    float psum[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const float m_ref = m_new[nt];
-      float ps = 0.f;
       uint32_t pk[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const int mt = half * 2 + sub;
-          const float p0 = __builtin_amdgcn_exp2f(s[mt][nt][0] - m_ref);
-          const float p1 = __builtin_amdgcn_exp2f(s[mt][nt][1] - m_ref);
-          const float p2 = __builtin_amdgcn_exp2f(s[mt][nt][2] - m_ref);
-          const float p3 = __builtin_amdgcn_exp2f(s[mt][nt][3] - m_ref);
-          ps += (p0 + p1) + (p2 + p3);
-          pk[half][sub * 2] = pack_f16x2(p0, p1);
-          pk[half][sub * 2 + 1] = pack_f16x2(p2, p3);
+          pk[half][sub * 2] = pack_f16x2(__builtin_amdgcn_exp2f(sc[mt][nt][0]),
+                                         __builtin_amdgcn_exp2f(sc[mt][nt][1]));
+          pk[half][sub * 2 + 1] = pack_f16x2(__builtin_amdgcn_exp2f(sc[mt][nt][2]),
+                                             __builtin_amdgcn_exp2f(sc[mt][nt][3]));
         }
-      psum[nt] = ps;
+      float ps = l_run[nt];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ps = dot2_f16(pk[half][j], 0x3c003c00u, ps);
+      l_run[nt] = ps;
       pf[nt][0] = u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]};
       pf[nt][1] = u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      m_run[nt] = m_new[nt];
-      l_run[nt] += psum[nt];
+
+    bool rs = false;
+    float cand[2];
+    if (!LAST) {
+      if (kt + 1 >= kmask || kt + 1 == klast) mask(kt + 1, sn);
+      rs = prepare(sn, r, cand);
     }
 
     // ---- O^T += V^T P^T ----
-    const char* v_lds = sV(kt);
+    const char* v_lds = sV(BUF);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -856,15 +881,23 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
         for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = mfma_f16(vf, pf[nt][half], oacc[dt][nt]);
       }
     }
-    if (!LAST) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s[mt][nt] = sn[mt][nt];
-    }
+    if (!LAST && rs) rescale(sn, r, cand);
   };
-  for (int kt = 0; kt < klast; ++kt) step(std::false_type{}, kt);
-  step(std::true_type{}, klast);
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int kt = 0;
+  for (; kt + 2 <= klast; kt += 2) {
+    step(F{}, B0{}, kt, sa, sb);
+    step(F{}, B1{}, kt + 1, sb, sa);
+  }
+  if (kt < klast) {
+    step(F{}, B0{}, kt, sa, sb);
+    step(Tr{}, B1{}, kt + 1, sb, sa);
+  } else {
+    step(Tr{}, B0{}, kt, sa, sb);
+  }
 
   // ---- normalise, stage through LDS, store O (fp16) ----
   // Wave w's 32 x 128 block goes to its own 8 KiB of LDS, row = query, with
