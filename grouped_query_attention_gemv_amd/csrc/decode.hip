@@ -38,11 +38,67 @@ __device__ __forceinline__ int qkv_first_feature(int blk) {
   return D + KV * HD + g * HD + (r - QW - 16) * 8;
 }
 
+// RoPE, probe and stores of the output features (f, f+1) of token b (f
+// even): Q into the workspace, K and V rounded into the cache (fused: also
+// into the hand-off row that the attention workgroups poll).  cs is the RoPE
+// table entry of the pair at position start_pos (ignored for V).
+template <bool FUSED, int KV>
+__device__ __forceinline__ void qkv_emit_pair(const DecodeParams& p, int b, int f, float v0, float v1,
+                                              float2 cs) {
+  constexpr int kNqkv = D + 2 * KV * HD;
+  const bool is_v = f >= D + KV * HD;
+  const int pos = p.start_pos;
+  if (!is_v) {
+    // rotate the pair (2i, 2i+1) of this head by position * f_i
+    const float a = v0 * cs.x - v1 * cs.y;
+    const float c = v0 * cs.y + v1 * cs.x;
+    v0 = a;
+    v1 = c;
+  }
+  if (p.probe) {
+    *reinterpret_cast<float2*>(p.probe + (size_t)b * kNqkv + f) = make_float2(v0, v1);
+  }
+  if (f < D) {
+    float* qd = p.q + (size_t)b * D + f;
+    if (FUSED) {
+      // read by attention workgroups of this launch, which poll these
+      // words until they no longer hold the "not yet" marker: written
+      // through to the device-wide coherence point
+      st_dev(qd, v0);
+      st_dev(qd + 1, v1);
+    } else {
+      *reinterpret_cast<float2*>(qd) = make_float2(v0, v1);
+    }
+  } else {
+    const int rr = is_v ? f - D - KV * HD : f - D;
+    const int g = rr / HD, d = rr % HD;
+    const uint32_t pair = pack_bf16x2(v0, v1);
+    if (!is_v) {
+      uint16_t* dst = p.kcache + ((size_t)(b * KV + g) * p.T_max + pos) * HD + d;
+      *reinterpret_cast<uint32_t*>(dst) = pair;
+    } else {
+      uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max, KV);
+      dst[0] = (uint16_t)(pair & 0xffffu);
+      dst[VB] = (uint16_t)(pair >> 16);
+    }
+    // the attention workgroups of the same launch poll the new row here
+    if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KV + g) * (HD / 2) + d / 2, pair);
+  }
+}
+
+// RoPE table entry of the output feature pair (f, f+1) at position start_pos
+// ((1, 0), the identity, for V features).
+template <int KV>
+__device__ __forceinline__ float2 qkv_rope_entry(const DecodeParams& p, int f) {
+  if (f >= D + KV * HD) return make_float2(1.f, 0.f);
+  const int rr = f < D ? f : f - D;
+  return reinterpret_cast<const float2*>(p.rope)[(size_t)p.start_pos * PAIRS + ((rr & (HD - 1)) >> 1)];
+}
+
 // KV: kv heads of the projection (8, 16 or 32, both schedules); W: waves of
 // the workgroup.
 template <int NB, bool FUSED, int KV = KVH, int W = 4>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
-  constexpr int kNqkv = D + 2 * KV * HD;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = qkv_first_feature<FUSED, W, KV>(blk) + wave * 2;   // even feature
   const uint16_t* wbase;
@@ -59,9 +115,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   // gain; the 16 weight loads follow at once, and the rest has landed once
   // only they remain in flight
   stage_rows_async<NB, W>(xs, p.x + (size_t)b0 * D);
-  const bool is_v = r0 >= D + KV * HD;
-  float2 cs = make_float2(1.f, 0.f);
-  if (!is_v) cs = reinterpret_cast<const float2*>(p.rope)[(size_t)p.start_pos * PAIRS + ((rr & (HD - 1)) >> 1)];
+  const float2 cs = qkv_rope_entry<KV>(p, r0);
   uint32_t gp[(D / 2) / (64 * W)];
   if (p.norm_w) load_norm_gain<W>(p.norm_w, gp);
   u32x4 wa[8], wb[8];
@@ -85,45 +139,7 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
     if (lane == t) { v0 = s0; v1 = s1; }
   }
 
-  if (lane < NB) {
-    const int b = b0 + lane;
-    const int pos = p.start_pos;
-    if (!is_v) {
-      // rotate the pair (2i, 2i+1) of this head by position * f_i
-      const float a = v0 * cs.x - v1 * cs.y;
-      const float c = v0 * cs.y + v1 * cs.x;
-      v0 = a;
-      v1 = c;
-    }
-    if (p.probe) {
-      *reinterpret_cast<float2*>(p.probe + (size_t)b * kNqkv + r0) = make_float2(v0, v1);
-    }
-    if (r0 < D) {
-      float* qd = p.q + (size_t)b * D + r0;
-      if (FUSED) {
-        // read by attention workgroups of this launch, which poll these
-        // words until they no longer hold the "not yet" marker: written
-        // through to the device-wide coherence point
-        st_dev(qd, v0);
-        st_dev(qd + 1, v1);
-      } else {
-        *reinterpret_cast<float2*>(qd) = make_float2(v0, v1);
-      }
-    } else {
-      const int g = rr / HD, d = rr % HD;
-      const uint32_t pair = pack_bf16x2(v0, v1);
-      if (!is_v) {
-        uint16_t* dst = p.kcache + ((size_t)(b * KV + g) * p.T_max + pos) * HD + d;
-        *reinterpret_cast<uint32_t*>(dst) = pair;
-      } else {
-        uint16_t* dst = p.vcache + vcache_index(b, g, pos, d, p.T_max, KV);
-        dst[0] = (uint16_t)(pair & 0xffffu);
-        dst[VB] = (uint16_t)(pair >> 16);
-      }
-      // the attention workgroups of the same launch poll the new row here
-      if (FUSED) st_dev(p.kv_new + ((size_t)(b * 2 + (is_v ? 1 : 0)) * KV + g) * (HD / 2) + d / 2, pair);
-    }
-  }
+  if (lane < NB) qkv_emit_pair<FUSED, KV>(p, b0 + lane, r0, v0, v1, cs);
 }
 
 // W waves a workgroup: 4, or 8 for 7 and 8 tokens, whose 56-64 KiB of staged
@@ -692,6 +708,28 @@ __global__ void __launch_bounds__(256, 3) decode_attn_kernel(DecodeParams p) {
 // wo projection (+ residual)
 // ---------------------------------------------------------------------------
 
+// Output features (f, f+1) of token b: out = Delta, out += Delta
+// (accumulate) or out = resid + Delta (layer), and the bf16 copy; NaN when
+// the producer's wait failed.
+__device__ __forceinline__ void wo_emit_pair(const DecodeParams& p, int b, int f, float v0, float v1,
+                                             bool failed) {
+  float2* o = reinterpret_cast<float2*>(p.out + (size_t)b * D + f);
+  float2 r = make_float2(v0, v1);
+  if (p.accumulate) {
+    const float2 prev = *o;
+    r.x += prev.x;
+    r.y += prev.y;
+  } else if (p.resid) {
+    const uint32_t xr = *reinterpret_cast<const uint32_t*>(p.resid + (size_t)b * D + f);
+    r.x += bf16_bits_to_f32(xr & 0xffffu);
+    r.y += bf16_bits_to_f32(xr >> 16);
+  }
+  if (failed) r = make_float2(__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u));
+  *o = r;
+  if (p.out_bf16)
+    *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + f) = pack_bf16x2(r.x, r.y);
+}
+
 // KV: kv heads of the fused schedule's attention (one O-ready word per
 // (sequence, kv head) in the workgroup's slot).
 template <int NB, bool FUSED, int W = 4, int KV = KVH>
@@ -783,32 +821,83 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
     const float s1 = wave_sum(acc[1][t]);
     if (lane == t) { v0 = s0; v1 = s1; }
   }
-  if (lane >= NB) return;
-  const int b = b0 + lane;
-  float2* o = reinterpret_cast<float2*>(p.out + (size_t)b * D + r0);
-  float2 r = make_float2(v0, v1);
-  if (p.accumulate) {
-    const float2 prev = *o;
-    r.x += prev.x;
-    r.y += prev.y;
-  } else if (p.resid) {
-    const uint32_t xr = *reinterpret_cast<const uint32_t*>(p.resid + (size_t)b * D + r0);
-    r.x += bf16_bits_to_f32(xr & 0xffffu);
-    r.y += bf16_bits_to_f32(xr >> 16);
-  }
-  if (FUSED && wo_state == 1) r = make_float2(__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u));
-  *o = r;
-  if (p.out_bf16)
-    *reinterpret_cast<uint32_t*>(p.out_bf16 + (size_t)b * D + r0) = pack_bf16x2(r.x, r.y);
+  if (lane < NB) wo_emit_pair(p, b0 + lane, r0, v0, v1, FUSED && wo_state == 1);
 }
 
-// W waves a workgroup: 4 up to 4 tokens, 8 above, where the staged hi/lo
-// parts (80-128 KiB) allow one workgroup per CU: 256 workgroups of 16 rows
-// then hold the whole weight stream in flight in one pass.
+// Up to 4 tokens (5 to 8 run on the matrix cores, decode_wo_mfma_kernel).
 template <int NB, int W>
 __global__ void __launch_bounds__(64 * W) decode_wo_kernel(DecodeParams p, int b0) {
   __shared__ uint32_t xs[2 * NB * (D / 2)];
   wo_body<NB, false, W>(p, b0, blockIdx.x, xs);
+}
+
+// ---------------------------------------------------------------------------
+// wo of 5 to 8 tokens on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// At 8 tokens the wo GEMV spends 1024 packed dot instructions per lane (the
+// hi and lo parts of O) on each pair of weight rows, with the LDS reads that
+// feed them, and that vector work lands behind the weight stream instead of
+// under it (15.5 us at 8 tokens against 10.5 us at 2).  Here the products
+// run on v_mfma_f32_16x16x32_bf16, C^T[16 rows x 16 columns] = Wo . X^T:
+//  - a workgroup owns 16 consecutive rows of Wo and its wave w the K range
+//    [1024w, 1024w + 1024); the wave's 32 A fragments (lane l: row l % 16,
+//    the 8 consecutive k at 8 (l / 16) of each 32-k step) all go out at
+//    once, 32 KiB a wave, the whole weight in flight in one pass;
+//  - the columns are the tokens' hi parts followed by their lo parts,
+//    staged in LDS by direct loads issued before the weights, each row
+//    padded by 16 bytes so that the B fragments (lane l: 8 consecutive k of
+//    column l % 16) fall on distinct banks; columns past the staged rows
+//    repeat row 0 and are dropped;
+//  - the 4 waves' partial tiles are summed in LDS in a fixed order, and each
+//    output adds its hi and lo columns.
+// (The same layout for the QKV projection measured no faster than its GEMV:
+// the A fragments read 64 bytes of 16 rows per instruction, and the stream
+// ran at about 2.8 TB/s against the GEMV's whole-row kilobytes.)
+constexpr int kWoMfmaMinNB = 5;                  // fewer tokens stay on the GEMV
+constexpr int kSkPitch = D / 2 + 4;              // u32 words per staged row
+template <int NB>
+constexpr size_t wo_mfma_lds_bytes() {
+  return ((size_t)2 * NB * kSkPitch + 4 * 16 * 16) * 4;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) decode_wo_mfma_kernel(DecodeParams p, int b0) {
+  static_assert(NB >= 1 && NB <= 8, "16 columns hold 8 tokens' hi and lo parts");
+  constexpr int NR = 2 * NB;                     // staged rows: hi parts, then lo parts
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs[];
+  float* red = reinterpret_cast<float*>(xs + NR * kSkPitch);   // [wave][16 rows][16 columns]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f0 = blockIdx.x * 16;
+
+  stage_rows_async<NB, 4, kSkPitch>(xs, p.o_hi + (size_t)b0 * D);
+  stage_rows_async<NB, 4, kSkPitch>(xs + NB * kSkPitch, p.o_lo + (size_t)b0 * D);
+  const uint16_t* wk = p.wo + (size_t)(f0 + (lane & 15)) * D + 1024 * wave + 8 * (lane >> 4);
+  u32x4 a[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) a[k] = ld_nt_u32x4(wk + 32 * k);
+  wait_loads_except<32>();
+  lds_barrier();
+
+  const int col = lane & 15;
+  const uint32_t* xb = xs + (col < NR ? col : 0) * kSkPitch + 512 * wave + 4 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 32; ++k) acc = mfma_bf16(a[k], *reinterpret_cast<const u32x4*>(xb + 16 * k), acc);
+  // lane l holds rows 4 (l / 16) + i of column l % 16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * (lane >> 4) + i) * 16 + col] = acc[i];
+  lds_barrier();
+  auto total = [&](int m, int c) {
+    return ((red[m * 16 + c] + red[(16 + m) * 16 + c]) + red[(32 + m) * 16 + c]) + red[(48 + m) * 16 + c];
+  };
+  // rows (2j, 2j+1) of token t: hi column t plus lo column NB + t
+  const int j = threadIdx.x & 7, t = threadIdx.x >> 3;
+  if (t < NB) {
+    const float v0 = total(2 * j, t) + total(2 * j, NB + t);
+    const float v1 = total(2 * j + 1, t) + total(2 * j + 1, NB + t);
+    wo_emit_pair(p, b0 + t, f0 + 2 * j, v0, v1, false);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1283,9 +1372,15 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
   for (int b0 = 0; b0 < p.B; b0 += kWoMaxNB) {
     const int nb = min(kWoMaxNB, p.B - b0);
 #define GQA_LAUNCH_WO(N)                                                                     \
-    {                                                                                        \
-      constexpr int W = (N) >= 5 ? 8 : 4;                                                    \
-      hipLaunchKernelGGL((decode_wo_kernel<N, W>), dim3(D / 2 / W), dim3(64 * W), 0, s, p, b0); \
+    if constexpr ((N) >= kWoMfmaMinNB) {                                                     \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wo_mfma_kernel<N>), \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,         \
+                                         (int)wo_mfma_lds_bytes<N>());                        \
+      if (e != hipSuccess) return e;                                                         \
+      hipLaunchKernelGGL(decode_wo_mfma_kernel<N>, dim3(D / 16), dim3(256),                   \
+                         (wo_mfma_lds_bytes<N>()), s, p, b0);                                \
+    } else {                                                                                 \
+      hipLaunchKernelGGL((decode_wo_kernel<N, 4>), dim3(D / 2 / 4), dim3(256), 0, s, p, b0);  \
     }
     GQA_NB_SWITCH(nb, GQA_LAUNCH_WO)
 #undef GQA_LAUNCH_WO

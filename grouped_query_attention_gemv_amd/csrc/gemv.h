@@ -59,19 +59,23 @@ __device__ __forceinline__ void load_rows2(const uint16_t* __restrict__ w0,
 
 // Start copying NB rows of 4096 bf16 (one part) from global memory into LDS
 // with direct-to-LDS loads (16 bytes a lane, 1 KiB a wave instruction),
-// spread over the W waves of the workgroup.  Issued before a wave's weight
-// loads, the copy is complete once no more than those weight loads remain in
-// flight (wait_loads_except<16>), instead of queueing behind them.
-template <int NB, int W>
+// spread over the W waves of the workgroup; row t starts at word t * PITCH.
+// Issued before a wave's weight loads, the copy is complete once no more
+// than those weight loads remain in flight (wait_loads_except), instead of
+// queueing behind them.
+template <int NB, int W, int PITCH = D / 2>
 __device__ __forceinline__ void stage_rows_async(uint32_t* xs, const uint16_t* __restrict__ src) {
   constexpr int kPieces = NB * (D * 2 / 1024);      // 8 KiB a row
   static_assert(kPieces % W == 0, "every wave copies the same number of pieces");
+  static_assert(PITCH % 4 == 0, "rows start on 16-byte boundaries");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < kPieces / W; ++j) {
     const int i = wave + W * j;
+    const int t = i >> 3, piece = i & 7;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + (size_t)i * 512 + lane * 8),
-                                     (lds_void*)(reinterpret_cast<char*>(xs) + i * 1024), 16, 0, 0);
+                                     (lds_void*)(reinterpret_cast<char*>(xs + t * PITCH) + piece * 1024),
+                                     16, 0, 0);
   }
   asm volatile("" ::: "memory");
 }

@@ -75,9 +75,11 @@ def test_decode_positions(P, schedule):
     _decode_full(2, P, 1024, schedule)
 
 
-@pytest.mark.parametrize("B", [3, 8, 9, 17])
+@pytest.mark.parametrize("B", [3, 5, 6, 7, 8, 9, 17])
 def test_decode_batches(B):
-    """Batch sizes across the 8-token GEMV chunking (ragged last chunk)."""
+    """Batch sizes across the projection paths: the GEMVs (wo below 5 tokens,
+    QKV up to 8), wo on the matrix cores for 5 to 8 tokens, the split-K
+    matrix-core projections above 8 (ragged last chunk)."""
     _decode_full(B, 300, 512)
 
 
@@ -639,7 +641,7 @@ def _layer_kv_bounds(xn_exact, w, n_kv):
 
 
 @pytest.mark.parametrize("B,P,mode", [(1, 1000, "fused"), (1, 1000, "split"), (4, 300, "auto"),
-                                      (16, 200, "auto")])
+                                      (6, 300, "auto"), (16, 200, "auto")])
 def test_layer_decode(B, P, mode):
     c = DecodeCase(B, P, ((P + 1 + 31) // 32) * 32 + 32, dev=DEV)
     g = synth.norm_gain(5)
@@ -668,11 +670,13 @@ def test_layer_decode(B, P, mode):
     print(f"layer decode B={B} P={P} {mode}", errs)
 
 
-@pytest.mark.parametrize("n_kv,B,P", [(16, 2, 300), (32, 1, 1000), (16, 12, 100), (32, 9, 65)])
+@pytest.mark.parametrize("n_kv,B,P", [(16, 2, 300), (32, 1, 1000), (16, 7, 100), (16, 12, 100),
+                                      (32, 9, 65)])
 def test_layer_decode_other_kv_head_counts(n_kv, B, P):
     """The layer (RMSNorm, block, residual) with 16 and 32 key/value heads, on
-    both projection paths (B <= 8 GEMV with the fused norm and residual, and
-    B > 8 with the norm pass and the accumulating block)."""
+    the projection paths: B <= 8 with the norm in the QKV GEMV and the
+    residual in the wo epilogue (GEMV up to 4 tokens, matrix cores above),
+    and B > 8 with the norm pass and the accumulating block."""
     c = DecodeCase(B, P, ((P + 1 + 31) // 32) * 32 + 32, dev=DEV, n_kv=n_kv)
     g = synth.norm_gain(7)
     ws = G.workspace(G.OP_LAYER_DECODE, B, c.T_max, DEV, n_kv_heads=n_kv)
