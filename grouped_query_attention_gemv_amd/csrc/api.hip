@@ -14,6 +14,7 @@
 using namespace gqa;
 
 static_assert(kSyncBytes == GQA_SYNC_BYTES, "sync region size differs from the header");
+static_assert(kVocabMfmaMinB == GQA_VOCAB_MFMA_MIN_B, "vocabulary path threshold differs from the header");
 
 namespace {
 
@@ -460,7 +461,7 @@ int gqa_vocab_logits(const gqa_bf16* h, const gqa_bf16* norm_w, float eps, const
     return GQA_ERR_ALIGN;
   if (norm_w && !(eps > 0.f && eps < 1.f)) return GQA_ERR_ARG;
   // the matrix-core path normalises into the workspace first
-  const bool mfma = B > kGemvMaxNB;
+  const bool mfma = B >= kVocabMfmaMinB;
   const bool uses_ws = mfma && norm_w;
   if (uses_ws) {
     if (!ws || ws_bytes < vocab_ws_bytes(B)) return GQA_ERR_WORKSPACE;

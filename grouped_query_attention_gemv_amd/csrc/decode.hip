@@ -875,7 +875,7 @@ __global__ void __launch_bounds__(256) decode_wo_mfma_kernel(DecodeParams p, int
   const uint16_t* wk = p.wo + (size_t)(f0 + (lane & 15)) * D + 1024 * wave + 8 * (lane >> 4);
   u32x4 a[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) a[k] = ld_nt_u32x4(wk + 32 * k);
+  for (int k = 0; k < 32; ++k) a[k] = ld_u32x4(wk + 32 * k);
   wait_loads_except<32>();
   lds_barrier();
 
@@ -1106,7 +1106,7 @@ __global__ void __launch_bounds__(256) decode_proj_kernel(DecodeParams p, int c_
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dst[ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kP2Kc + s * 32);
+      for (int s = 0; s < 4; ++s) dst[ft][s] = ld_u32x4(wrow[ft] + chunk * kP2Kc + s * 32);
   };
 
   f32x4 acc[FT][4];

@@ -184,8 +184,10 @@ struct VocabParams {
   int V, B;
 };
 
+// Below kVocabMfmaMinB tokens the bandwidth GEMV (norm fused), from there
+// the matrix-core path over z (h, or its norm written into the workspace).
+constexpr int kVocabMfmaMinB = 6;
 hipError_t launch_vocab_gemv(const VocabParams& p, hipStream_t s);
-// above kGemvMaxNB tokens: the matrix-core path over z (h, or its norm)
 hipError_t launch_vocab_mfma(const VocabParams& p, const uint16_t* z, hipStream_t s);
 
 // ---------------------------------------------------------------------------

@@ -6,12 +6,14 @@
 // front (the page's code: self.norm, an RMSNorm with norm_eps) is optional
 // here and read as in the layer pre-norm.
 //
-// Up to 8 sequences: a bandwidth GEMV over 1.05 GB of weights at V =
+// Up to 5 sequences: a bandwidth GEMV over 1.05 GB of weights at V =
 // 128,256: each wave takes pairs of weight rows in a grid-strided loop, with
 // the next pair's 16 loads issued before the current pair's products (two
 // pairs in flight per wave); the token vectors are staged (and normalised)
-// once per workgroup.  Above 8: the matrix-core kernel further down, one
-// weight pass per 64 sequences.
+// once per workgroup.  From 6: the matrix-core kernel further down, one
+// weight pass per 64 sequences (at V = 128,256: the GEMV takes 157, 185 and
+// 205 us at 1, 4 and 5 sequences and 224 us at 6, the matrix-core kernel
+// 219 us at 6 to 9 and 250 us at 64).
 #include <algorithm>
 #include <type_traits>
 
@@ -85,21 +87,26 @@ __global__ void __launch_bounds__(256) vocab_gemv_kernel(VocabParams p, int b0) 
 }
 
 // ---------------------------------------------------------------------------
-// Above 8 tokens: the matrix-core projection
+// From 6 tokens: the matrix-core projection
 // ---------------------------------------------------------------------------
 //
 // C^T[rows x tokens] = W[rows x 4096] . Z^T[4096 x tokens] on
 // v_mfma_f32_16x16x32_bf16, streaming the weights once per 64 tokens (the
-// GEMV above streams them once per 8).  The vocabulary is long enough to
-// fill the chip without splitting K:
+// GEMV above streams them once per 8, and its vector work grows with the
+// token count).  The vocabulary is long enough to fill the chip without
+// splitting K:
 //  - workgroup fb owns 128 vocabulary rows (its 4 waves two 16-row A tiles
 //    each) and the whole K; the last block's rows past V are clamped loads
 //    whose results are not stored;
+//  - a launch covers NT column tiles of 16 tokens (1 to 4), the fewest that
+//    hold its tokens, so that few tokens stage and multiply no more than
+//    they need;
 //  - K advances in chunks of 128.  The tokens' chunk is copied into LDS
-//    (global_load_lds, 16 KiB, XOR-swizzled rows) and read by all 4 waves
-//    as the B operand; each wave's weight rows come from HBM straight into
-//    registers (its A operand).  Both run three chunks ahead of the matrix
-//    work through a 4-slot ring;
+//    (global_load_lds, 4 KiB per column tile, XOR-swizzled rows) and read by
+//    all 4 waves as the B operand; each wave's weight rows come from HBM
+//    straight into registers (its A operand; plain loads, which streamed
+//    this 16-row pattern about 10% faster than non-temporal ones).  Both
+//    run three chunks ahead of the matrix work through a 4-slot ring;
 //  - the epilogue rounds each logit to bf16 as the GEMV does.
 // Z is the caller's h, or its norm written beforehand by the norm kernel.
 constexpr int kVcCols = 64;        // tokens per launch
@@ -108,12 +115,14 @@ constexpr int kVcKc = 128;         // K per chunk
 constexpr int kVcRing = 4;         // chunk slots: loaded three ahead
 constexpr int kVcChunks = D / kVcKc;
 
+template <int NT>
 __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const uint16_t* __restrict__ z,
                                                          int c_base) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[kVcRing][kVcCols * kVcKc];
+  static_assert(NT >= 1 && NT <= kVcCols / 16, "1 to 4 column tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sx[kVcRing][16 * NT * kVcKc];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int fb = blockIdx.x;
-  const int ncols = min(kVcCols, p.B - c_base);
+  const int ncols = min(16 * NT, p.B - c_base);
 
   // A operand: weight row of tile ft, k offset (lane >> 4) * 8 in each step
   const uint16_t* wrow[2];
@@ -122,14 +131,14 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
     const int f = fb * kVcFeat + 32 * w + 16 * ft + (lane & 15);
     wrow[ft] = p.w + (size_t)min(f, p.V - 1) * D + (lane >> 4) * 8;
   }
-  // token copies: instruction j of this wave fills rows (4w + j) * 4 .. + 3
+  // token copies: instruction j of this wave fills rows (NT w + j) * 4 .. + 3
   // of the chunk (256 bytes each); lane i writes row +i/16, 16-byte slot
   // i % 16, which holds logical slot (i % 16) ^ (row & 7).  Rows past the
   // last token copy the last token (their results are not stored).
-  const uint16_t* xsrc[4];
+  const uint16_t* xsrc[NT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (4 * w + j) * 4 + (lane >> 4);
+  for (int j = 0; j < NT; ++j) {
+    const int row = (NT * w + j) * 4 + (lane >> 4);
     const int lchunk = (lane & 15) ^ (row & 7);
     xsrc[j] = z + (size_t)(c_base + min(row, ncols - 1)) * D + lchunk * 8;
   }
@@ -139,23 +148,23 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wb[slot][ft][s] = ld_nt_u32x4(wrow[ft] + chunk * kVcKc + s * 32);
+      for (int s = 0; s < 4; ++s) wb[slot][ft][s] = ld_u32x4(wrow[ft] + chunk * kVcKc + s * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NT; ++j)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(xsrc[j] + chunk * kVcKc),
-                                       (lds_void*)(&sx[slot][(4 * w + j) * 4 * kVcKc]), 16, 0, 0);
+                                       (lds_void*)(&sx[slot][(NT * w + j) * 4 * kVcKc]), 16, 0, 0);
     asm volatile("" ::: "memory");              // chunks leave in order
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[2][NT];
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) acc[ft][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Chunk c has landed once no more than the loads of the chunks issued
-  // after it (12 a chunk: 8 weight, 4 copies) remain in flight.
-  constexpr int kPerChunk = 12;
+  // after it (8 weight loads and NT copies a chunk) remain in flight.
+  constexpr int kPerChunk = 8 + NT;
   static_assert(kVcChunks % kVcRing == 0, "the ring slot of a chunk is known at compile time");
   // one chunk: slot u, LATER chunks already issued after it
   auto step = [&](auto u_tag, auto later_tag, int c) {
@@ -167,11 +176,11 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (LATER == kVcRing - 2) load_chunk(c + kVcRing - 1, (u + kVcRing - 1) % kVcRing);
-    u32x4 xb[4][4];
+    u32x4 xb[4][NT];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const int row = 16 * t + (lane & 15);
         const int off = row * kVcKc + (((4 * s + (lane >> 4)) ^ (row & 7)) << 3);
         xb[s][t] = *reinterpret_cast<const u32x4*>(&sx[u][off]);
@@ -179,7 +188,7 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft) acc[ft][t] = mfma_bf16(wb[u][ft][s], xb[s][t], acc[ft][t]);
   };
@@ -205,7 +214,7 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
   // lane holds rows 32w + 16ft + 4(lane >> 4) + e of the block for token
   // 16t + (lane & 15)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     const int col = 16 * t + (lane & 15);
     if (col >= ncols) continue;
     float* lrow = p.logits + (size_t)(c_base + col) * p.V;
@@ -222,7 +231,12 @@ __global__ void __launch_bounds__(256) vocab_mfma_kernel(VocabParams p, const ui
 hipError_t launch_vocab_mfma(const VocabParams& p, const uint16_t* z, hipStream_t s) {
   const int nfb = (p.V + kVcFeat - 1) / kVcFeat;
   for (int c = 0; c < p.B; c += kVcCols) {
-    hipLaunchKernelGGL(vocab_mfma_kernel, dim3(nfb), dim3(256), 0, s, p, z, c);
+    switch ((std::min(kVcCols, p.B - c) + 15) / 16) {
+      case 1: hipLaunchKernelGGL(vocab_mfma_kernel<1>, dim3(nfb), dim3(256), 0, s, p, z, c); break;
+      case 2: hipLaunchKernelGGL(vocab_mfma_kernel<2>, dim3(nfb), dim3(256), 0, s, p, z, c); break;
+      case 3: hipLaunchKernelGGL(vocab_mfma_kernel<3>, dim3(nfb), dim3(256), 0, s, p, z, c); break;
+      default: hipLaunchKernelGGL(vocab_mfma_kernel<4>, dim3(nfb), dim3(256), 0, s, p, z, c); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

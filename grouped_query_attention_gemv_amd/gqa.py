@@ -24,6 +24,7 @@ V_BLOCK = 32
 DECODE_STAGES = 3
 PREFILL_STAGES = 4
 SYNC_BYTES = 540672
+VOCAB_MFMA_MIN_B = 6   # gqa_vocab_logits: matrix cores (and, with a norm, a workspace) from here
 NOALLOC_SCRATCH_BYTES = 16 << 20   # the no-allocation decode's scratch array per GPU
 DECODE_AUTO, DECODE_SPLIT, DECODE_FUSED = 0, 1, 2
 OP_PREFILL, OP_DECODE, OP_LAYER_PREFILL, OP_LAYER_DECODE, OP_VOCAB = 0, 1, 2, 3, 4
@@ -461,9 +462,9 @@ VOCAB = 128256    # vocabulary size of Llama 3
 def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None,
                  ws=None) -> torch.Tensor:
     """Logits [B, V] fp32 (bf16-rounded values) = z W_out^T for h [B, 4096]
-    bf16, z = RMSNorm(h) * norm_w when norm_w is given, else h.  Above 8
-    sequences with a norm the call needs a workspace (allocated here unless
-    ``ws`` is given)."""
+    bf16, z = RMSNorm(h) * norm_w when norm_w is given, else h.  From
+    VOCAB_MFMA_MIN_B sequences on, with a norm, the call needs a workspace
+    (allocated here unless ``ws`` is given)."""
     if h.dim() != 2 or w_out.dim() != 2:
         raise ValueError("h must be [B, 4096] and w_out [V, 4096]")
     dev = h.device
@@ -477,7 +478,7 @@ def vocab_logits(h, w_out, norm_w=None, eps: float = NORM_EPS, logits=None,
     if logits is None:
         logits = torch.empty((B, V), dtype=torch.float32, device=dev)
     _need(logits, "logits", torch.float32, (B, V), dev)
-    if ws is None and B > 8 and norm_w is not None:
+    if ws is None and B >= VOCAB_MFMA_MIN_B and norm_w is not None:
         ws = workspace(OP_VOCAB, B, 1, dev)
     _check(lib().gqa_vocab_logits(_ptr(h), _ptr(norm_w), float(eps), _ptr(w_out), int(V), int(B),
                                   _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),

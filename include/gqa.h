@@ -87,6 +87,11 @@ extern "C" {
  * buffers of the one-launch decode (gqa_workspace_init prepares both). */
 #define GQA_SYNC_BYTES  540672
 
+/* gqa_vocab_logits runs on the matrix cores from this many sequences on
+ * (below, a GEMV with the norm fused); with a norm it then needs a
+ * workspace for the normalised input. */
+#define GQA_VOCAB_MFMA_MIN_B  6
+
 /* Bits of the workspace error word (its first int). */
 #define GQA_WS_ERR_WAIT        0x1   /* a bounded wait of the one-launch decode timed out */
 #define GQA_WS_ERR_WO_WAIT     0x2   /* the same, in its output projection */
@@ -378,13 +383,14 @@ int gqa_layer_decode(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
  *   norm_w  NULL or [4096] bf16; eps as for the layers (ignored when NULL)
  *   w_out   [V][4096] bf16; V = 128256 for Llama 3.1 (1 .. GQA_MAX_VOCAB)
  *   logits  [B][V] fp32, written
- *   ws      needed only when B > 8 and norm_w is non-NULL (else it may be
- *           NULL, ws_bytes 0): ws_bytes >= gqa_workspace_bytes(GQA_OP_VOCAB,
- *           8, B, 0, 1, 1); the normalised z is written after its
- *           synchronisation region, which is left untouched
- * Up to 8 sequences: a bandwidth GEMV over the weight with the norm fused,
- * one weight pass.  Above 8: the norm first (into ws), then the matrix
- * cores, one weight pass per 64 sequences.
+ *   ws      needed only when B >= GQA_VOCAB_MFMA_MIN_B and norm_w is
+ *           non-NULL (else it may be NULL, ws_bytes 0): ws_bytes >=
+ *           gqa_workspace_bytes(GQA_OP_VOCAB, 8, B, 0, 1, 1); the normalised
+ *           z is written after its synchronisation region, which is left
+ *           untouched
+ * Below GQA_VOCAB_MFMA_MIN_B sequences: a bandwidth GEMV over the weight
+ * with the norm fused, one weight pass.  From there: the norm first (into
+ * ws), then the matrix cores, one weight pass per 64 sequences.
  * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_ALIGN, GQA_ERR_ARG (eps),
  * GQA_ERR_WORKSPACE (ws missing or too small where needed), GQA_ERR_ALIAS
  * (logits or the used workspace overlapping an input or each other),

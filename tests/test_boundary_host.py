@@ -145,6 +145,7 @@ def test_workspace_starts_with_the_sync_region():
         assert _wsb(op, B, Tm, T) > G.SYNC_BYTES
     src = open(HEADER).read()
     assert "#define GQA_SYNC_BYTES  540672" in src
+    assert f"#define GQA_VOCAB_MFMA_MIN_B  {G.VOCAB_MFMA_MIN_B}" in src
 
 
 def test_workspace_init_rejections():
@@ -414,8 +415,9 @@ def _vocab_ws(B):
     (dict(logits=ctypes.c_void_p(BASE + (2 << 32) + 4)), EALIGN),
     (dict(g=_fake(3), eps=ctypes.c_float(-1.0)), EARG),
     (dict(logits=_fake(1)), EALIAS), (dict(logits=_fake(0)), EALIAS),
-    # above 8 sequences with a norm the normalised tokens need the workspace
-    (dict(B=9, g=_fake(3)), EWS),
+    # from GQA_VOCAB_MFMA_MIN_B sequences on, with a norm, the normalised
+    # tokens need the workspace
+    (dict(B=6, g=_fake(3)), EWS), (dict(B=9, g=_fake(3)), EWS),
     (dict(B=9, g=_fake(3), ws=_fake(4), ws_bytes=_vocab_ws(9) - 1), EWS),
     (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE + (4 << 32) + 8), ws_bytes=_vocab_ws(9)), EALIGN),
     (dict(B=9, g=_fake(3), ws=ctypes.c_void_p(BASE - G.SYNC_BYTES), ws_bytes=_vocab_ws(9)), EALIAS),

@@ -788,10 +788,12 @@ def _vocab_exact(h, w, g):
     return z @ w.T, round_bounds(z, w, rotated=False) + tie_slack(zx, w)
 
 
-@pytest.mark.parametrize("B,V,norm", [(3, 1001, True), (8, 130, True),
-                                      # above 8 sequences: the matrix-core path (a partial last
-                                      # block of 128 rows; 70: two launches, the second ragged)
-                                      (11, 4096, False), (9, 4096, True), (20, 1001, True),
+@pytest.mark.parametrize("B,V,norm", [(3, 1001, True), (5, 130, False),
+                                      # from 6 sequences: the matrix-core path, 1 to 4 column
+                                      # tiles of 16 (a partial last block of 128 rows; 70: two
+                                      # launches, the second ragged)
+                                      (6, 130, True), (8, 130, True), (11, 4096, False),
+                                      (9, 4096, True), (20, 1001, True), (40, 300, False),
                                       (70, 130, True), (64, 257, False)])
 def test_vocab_logits_small(B, V, norm):
     from grouped_query_attention_gemv_amd import synth
@@ -807,11 +809,11 @@ def test_vocab_logits_small(B, V, norm):
     print(f"vocab B={B} V={V} norm={norm}", _check_logits(L, exact, bound, "logits"))
 
 
-@pytest.mark.parametrize("B", [2, 24])
+@pytest.mark.parametrize("B", [2, 6, 24])
 def test_vocab_logits_llama31_size(B):
     """V = 128,256 (the Llama 3 vocabulary), final norm on: weights drawn on
     the device, 4,096 sampled rows checked against the oracle.  B = 2 runs
-    the GEMV, B = 24 the matrix-core path."""
+    the GEMV, B = 6 and 24 the matrix-core path (one and two column tiles)."""
     from grouped_query_attention_gemv_amd import synth
     V = G.VOCAB
     gen = synth.generator(50)
