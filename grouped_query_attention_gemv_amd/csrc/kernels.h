@@ -70,12 +70,14 @@ constexpr int fused_qkv_wg(int kv) { return kv * (16 * (H / kv) + 32); }
 constexpr int kFusedMaxChunk = 2 * kAttnWaves * kAttnTile;
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
 // The fused schedule's wo workgroups start streaming their weights this many
-// real-time ticks (100 MHz: 5 us) after they start.  They are dispatched as
+// real-time ticks (100 MHz: 4 us) after they start.  They are dispatched as
 // the QKV workgroups retire and do not need the weights until O is complete;
 // starting at once, their 32 MiB competed with the tail of the QKV stream
-// that the attention chain waits on.  Measured at B = 1: P = 128, 1000, 2000
-// take 23.6, 24.9, 27.2 us instead of 25.5, 26.8, 28.3 us (0 to 8 us swept).
-constexpr unsigned kWoHoldTicks = 500;
+// that the attention chain waits on.  Swept at B = 1 with the marker
+// hand-offs: 3, 3.5, 4, 4.5, 5 and 6 us give 24.2, 22.5, 22.4-22.7, 22.8,
+// 23.4 and 23.8 us at P = 1000, and 3.5, 4, 4.5 us give 20.4, 20.6, 20.9 us
+// at P = 128.
+constexpr unsigned kWoHoldTicks = 400;
 static_assert(kSyncGroup + 32 * kFusedMaxKv <= kSyncProj, "head counters overlap");
 static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncWordsBytes / 4,
               "sync region too small for the projection counters of 32 kv heads");
