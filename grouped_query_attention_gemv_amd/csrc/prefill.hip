@@ -781,10 +781,14 @@ __global__ void __launch_bounds__(512, 1) prefill_attn_kernel(PrefillParams p) {
     bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float t = -INFINITY;
+      // the column's 16 scores of this lane as a tree of 3-input maxima
+      // (v_max3_f32): 5 + 2 + 1 instructions
+      float a[5];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) t = fmaxf(t, fmaxf(fmaxf(sc[mt][nt][0], sc[mt][nt][1]),
-                                                         fmaxf(sc[mt][nt][2], sc[mt][nt][3])));
+      for (int i = 0; i < 5; ++i)
+        a[i] = fmaxf(fmaxf(sc[(3 * i) >> 2][nt][(3 * i) & 3], sc[(3 * i + 1) >> 2][nt][(3 * i + 1) & 3]),
+                     sc[(3 * i + 2) >> 2][nt][(3 * i + 2) & 3]);
+      float t = fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]), fmaxf(fmaxf(a[3], a[4]), sc[3][nt][3]));
       t = max_xor32(max_xor16(t));
       cand[nt] = r[nt] + t;
       grow |= cand[nt] > m_run[nt] + kLazyRescale;
