@@ -18,14 +18,16 @@ Every record carries a ``roofline`` object for its dominant kernel: the
 algorithmic bytes (or FLOPs) of one launch divided by that kernel's average
 duration, measured here with HIP events on the stream the library launches
 on, and ``traffic``, the HBM bytes per launch from the rocprofv3
-FETCH_SIZE/WRITE_SIZE summaries in profiles/ (null when the kernel's source
+FETCH_SIZE/WRITE_SIZE summaries in profiles/ (null when the kernel's code
 changed since they were taken).  Inputs are seeded synthetic bf16 tensors
 already resident in HBM; decode workloads that read less than the 256 MB
 Infinity Cache rotate 8 independent weight + cache sets.  After every timed
 loop the workspace's error word is checked.
 
 ``cpu_baseline`` times the fp64 oracle on this host's cores on a bounded
-sample (whole decode block-steps at B = 1, P = 1,000).
+sample of the headline workload (one block's decode step for one of its 8
+sequences at P = 131,071, scaled to the block-step); the B = 1, P = 1,000
+sub-record carries its own (whole block-steps).
 
 Other workloads: --workload decode_p128 | decode_p1000 | prefill | batched |
 stacked_long | mha_batched | mha_decode_p1000 | kv16_decode_p1000 |
@@ -426,10 +428,11 @@ def record_batched(G, synth, kvh=KVH):
     }
 
 
-def run_stacked(G, synth, steps, warmup, B=8, P=131071, T_max=131072, L=32):
+def run_stacked(G, synth, steps, warmup, B=8, P=131071, T_max=131072, L=32, cpu_sample=False):
     """32 stacked blocks, B = 8, 131,071 cached positions per sequence per
     block (128 GiB of cache), residual h <- h + Delta, no norms or FFN.  One
-    step runs all 32 blocks."""
+    step runs all 32 blocks.  With cpu_sample, also returns a host copy of
+    one block's inputs for one sequence (the oracle's sample)."""
     dev = torch.device("cuda:0")
     dgen = synth.generator(0, dev)
     x0 = synth.randn_bf16(dgen, (B, D), device=dev)
@@ -481,11 +484,19 @@ def run_stacked(G, synth, steps, warmup, B=8, P=131071, T_max=131072, L=32):
         e.close()
     _assert_clean(G, ws, "stacked decode stages")
     kern = dict(zip(["qkv", "attn", "wo"], (per.mean(axis=0) * 1000.0).tolist()))
-    return us_step, kern, decode_bytes(B, P), finite
+    sample = None
+    if cpu_sample:
+        # block 0, sequence 0: its input and cached rows 0 .. P-1 (decode
+        # writes only row P, so these are the rows every step read)
+        w, kc, vc = blocks[0]
+        sample = dict(x=x0[0:1].cpu(), w=[t.cpu() for t in w], P=P, B=B,
+                      k=G.kcache_by_position(kc[0:1])[:, :P].cpu(),
+                      v=G.vcache_read(vc[0:1], 0, P).cpu())
+    return us_step, kern, decode_bytes(B, P), finite, sample
 
 
-def record_stacked(G, synth, steps, warmup):
-    us, kern, nb, finite = run_stacked(G, synth, steps, warmup)
+def record_stacked(G, synth, steps, warmup, cpu_sample=False):
+    us, kern, nb, finite, sample = run_stacked(G, synth, steps, warmup, cpu_sample=cpu_sample)
     per_block = us / 32
     tbs = nb["step"] / (per_block * 1e-6) / 1e12
     kname = "decode_attn_kernel<8>"
@@ -502,7 +513,48 @@ def record_stacked(G, synth, steps, warmup):
         "outputs_finite": finite,
         "roofline": roofline(kname, "hbm", nb["attn"], kern["attn"],
                              counter_traffic("stacked_b8_p131071_hbm_traffic.md", kname)),
-    }
+    }, sample
+
+
+def _blas_threads(cores):
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=cores)
+    except Exception:
+        return None
+
+
+def cpu_baseline_stacked(sample, budget_s=15.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the
+    32-block workload: one block's decode step for one of its B sequences at
+    P = 131,071 (the same inputs the GPU read), repeated for about budget_s of
+    wall time and scaled by B to the unit of the headline, microseconds per
+    block-step (each block-step decodes B sequences)."""
+    from oracle import gqa_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    f = lambda t: t.float().numpy().astype(np.float64)
+    x = f(sample["x"])[:, None, :]
+    w = [f(t) for t in sample["w"]]
+    kc, vc = f(sample["k"]), f(sample["v"])
+    P, B = sample["P"], sample["B"]
+    limiter = _blas_threads(cores)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.gqa_block(x, *w, kc, vc, P)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": round(el / n * B * 1e6, 1), "unit": "us/block-step", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} single-sequence decode steps of one block at P={P} (block 0, "
+                      f"sequence 0 of the workload's inputs) of the fp64 NumPy oracle, "
+                      f"{el:.1f} s of wall time, scaled x{B} to a block-step of {B} sequences; "
+                      f"BLAS threads = {cores} (the cores this process may run on); inputs "
+                      f"already converted to fp64"}
 
 
 def cpu_baseline(synth, B=1, P=1000, budget_s=12.0):
@@ -516,11 +568,7 @@ def cpu_baseline(synth, B=1, P=1000, budget_s=12.0):
     f = lambda t: t.float().numpy().astype(np.float64)
     xs, ws = f(x)[:, None, :], [f(t) for t in w]
     kcs, vcs = f(kc), f(vc)
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=cores)
-    except Exception:
-        limiter = None
+    limiter = _blas_threads(cores)
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -610,7 +658,7 @@ def extra_workload(G, synth, args):
         rec.update(record_prefill(G, synth))
         rec["higher_is_better"] = True
     elif w == "stacked_long":
-        rec.update(record_stacked(G, synth, args.steps, args.warmup))
+        rec.update(record_stacked(G, synth, args.steps, args.warmup)[0])
         rec["higher_is_better"] = False
     elif w in ("mha_decode_p1000", "kv16_decode_p1000"):
         kvh = 32 if w.startswith("mha") else 16
@@ -787,6 +835,52 @@ def trace_summary(stats_csv: str, bench_log: str, title: str, command: str, out:
     print(f"wrote {out}")
 
 
+def counter_summary(csvs, title: str, commands, out: str):
+    """Write a profiles/ summary of rocprofv3 --pmc runs (one counter set per
+    CSV): each counter's mean per dispatch for every kernel of this library,
+    and the derived matrix-core and VALU figures.  SQ_VALU_MFMA_BUSY_CYCLES
+    reads 16 cycles per 16x16x32 MFMA summed over the chip's 1024 SIMDs, and
+    SQ_BUSY_CYCLES the busy cycles summed over its 32 shader engines (their
+    ratio to a kernel's duration gives its shader clock), so
+    busy / (SQ_BUSY_CYCLES / 32 * 1024) is the fraction of the kernel's
+    cycles the matrix cores worked."""
+    agg = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            name = _short_kernel(r["Kernel_Name"])
+            if not name or name.startswith("at::") or "rocclr" in name:
+                continue
+            agg.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for d in agg.values() for c in d})
+    lines = [f"# {title} — rocprofv3 counters", "", "Commands (repository root):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Mean per dispatch:", "", "| kernel | dispatches | " + " | ".join(names) + " |",
+              "|---|---|" + "---|" * len(names)]
+    for k in sorted(agg):
+        d = agg[k]
+        n = max(len(v) for v in d.values())
+        lines.append(f"| {k} | {n} | " + " | ".join(
+            f"{sum(d[c]) / len(d[c]):.4g}" if c in d else "" for c in names) + " |")
+    simds, engines = 1024, 32
+    lines += ["", f"Derived (MI355X: {simds} SIMDs, {engines} shader engines):", ""]
+    for k in sorted(agg):
+        d = {c: sum(v) / len(v) for c, v in agg[k].items()}
+        if d.get("SQ_BUSY_CYCLES", 0) <= 0 or d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) <= 0:
+            continue
+        cycles = d["SQ_BUSY_CYCLES"] / engines
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds)
+        parts = [f"matrix cores busy {busy:.1%} of {cycles:,.0f} cycles"]
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in d:
+            parts.append(f"VALU co-executing in {d['SQ_VALU_MFMA_COEXEC_CYCLES'] / d['SQ_VALU_MFMA_BUSY_CYCLES']:.1%} of them")
+        if d.get("SQ_INSTS_MFMA", 0) > 0 and "SQ_INSTS_VALU" in d:
+            parts.append(f"{(d['SQ_INSTS_VALU'] - d['SQ_INSTS_MFMA']) / d['SQ_INSTS_MFMA']:.2f} other VALU instructions per MFMA")
+        lines.append(f"- {k}: " + "; ".join(parts) + ".")
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}")
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -811,10 +905,17 @@ def main():
                          "(commands given with --pmc-commands, calibration copy with "
                          "--copy-probe-mib)")
     ap.add_argument("--pmc-commands", nargs="*", default=[])
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="TITLE OUT CSV [CSV ...]: write a profiles/ summary of rocprofv3 --pmc "
+                         "runs (commands given with --pmc-commands)")
     ap.add_argument("--trace-summary", nargs=5, metavar=("STATS_CSV", "BENCH_LOG", "TITLE", "COMMAND", "OUT"),
                     help="write a profiles/ summary of a kernel-trace run and exit")
     args = ap.parse_args()
 
+    if args.counter_summary:
+        title, out, *csvs = args.counter_summary
+        counter_summary(csvs, title, args.pmc_commands, out)
+        return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
         return
@@ -863,7 +964,7 @@ def main():
         print(f"bench: {msg} ({time.perf_counter() - t_all:.0f} s)", file=sys.stderr, flush=True)
 
     # headline: config 5, then release its 128 GiB before the others
-    head = record_stacked(G, synth, args.steps, args.warmup)
+    head, sample = record_stacked(G, synth, args.steps, args.warmup, cpu_sample=not args.no_cpu)
     note("stacked decode done")
     torch.cuda.empty_cache()
     subs = {}
@@ -886,8 +987,11 @@ def main():
     rec["higher_is_better"] = False
     rec["sub_records"] = subs
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(synth)
+        rec["cpu_baseline"] = cpu_baseline_stacked(sample)
+        del sample
         note("cpu baseline done")
+        subs["decode_b1_p1000"]["cpu_baseline"] = cpu_baseline(synth)
+        note("cpu baseline of the B=1 decode done")
     print(json.dumps(rec), flush=True)
 
 
