@@ -1373,10 +1373,8 @@ hipError_t launch_decode_wo(const DecodeParams& p, hipStream_t s) {
     const int nb = min(kWoMaxNB, p.B - b0);
 #define GQA_LAUNCH_WO(N)                                                                     \
     if constexpr ((N) >= kWoMfmaMinNB) {                                                     \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wo_mfma_kernel<N>), \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,         \
-                                         (int)wo_mfma_lds_bytes<N>());                        \
-      if (e != hipSuccess) return e;                                                         \
+      /* up to 131 KiB of dynamic LDS (gfx950 has 160 KiB; no attribute call, so */            \
+      /* the launch can sit in a captured graph) */                                          \
       hipLaunchKernelGGL(decode_wo_mfma_kernel<N>, dim3(D / 16), dim3(256),                   \
                          (wo_mfma_lds_bytes<N>()), s, p, b0);                                \
     } else {                                                                                 \

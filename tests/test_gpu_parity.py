@@ -333,12 +333,13 @@ def test_decode_in_hip_graph_matches_eager(schedule):
 
 
 def test_fused_decode_reads_this_calls_data():
-    """The one-launch schedule reads Q, the new K/V row and the split
-    partials through the L2 of the kv head's XCD, relying on those lines not
-    being cached there from an earlier kernel.  Calls on one workspace and
-    one set of buffers, each with a new x (so a new Q and new partials at the
-    same addresses), replayed from a graph with the input changed between
-    replays: every replay must equal a fresh three-launch result on that x."""
+    """The one-launch schedule hands Q, the new K/V row, the split partials
+    and O from workgroup to workgroup through memory that earlier calls wrote
+    at the same addresses (the wo workgroups read O through their L2, after
+    every producer's device-scope stores completed).  Calls on one workspace
+    and one set of buffers, each with a new x, replayed from a graph with the
+    input changed between replays: every replay must equal a fresh
+    three-launch result on that x."""
     B, P, T_max = 1, 777, 1024
     c = DecodeCase(B, P, T_max, dev=DEV)
     ws = G.workspace(G.OP_DECODE, B, T_max, DEV)
@@ -374,9 +375,53 @@ def test_fused_decode_reads_this_calls_data():
         torch.cuda.synchronize()
         assert torch.equal(out, reference(xi))
     assert G.workspace_errors(ws) == 0
-    # how often the dispatcher's XCD placement differed (the reads above are
-    # correct either way; this only records it)
+    # how often the first attention workgroup ran away from the XCD that its
+    # index modulo 8 would give (nothing relies on it; this only records it)
     print("fused launches placed away from their XCDs:", G.workspace_off_home(ws), "of 7")
+
+
+@pytest.mark.parametrize("B", [6, 16])
+def test_three_launch_decode_graph_replays_match_eager(B):
+    """The three-launch schedule captured in a graph: B = 6 runs wo on the
+    matrix cores (131 KiB of dynamic LDS), B = 16 the split-K projections.
+    Replayed with a new x each time, with eager work and synchronisations
+    between the replays; every replay equals an eager call on that x bit for
+    bit (caches restored before each)."""
+    P, T_max = 200, 224
+    c = DecodeCase(B, P, T_max, dev=DEV)
+    ws = G.workspace(G.OP_DECODE, B, T_max, DEV)
+    x = c.xd.clone()
+    out = torch.zeros((B, 4096), dtype=torch.float32, device=DEV)
+    k0, v0 = c.kcache.clone(), c.vcache.clone()
+    xs = [synth.randn_bf16(synth.generator(200 + i), (B, 4096)).to(DEV) for i in range(4)]
+    S = G.DECODE_SPLIT
+
+    def eager(xi):
+        kc, vc = k0.clone(), v0.clone()
+        r = G.block_decode(xi, *c.wd, kc, vc, c.rope, P, schedule=S)
+        torch.cuda.synchronize()
+        return r, kc, vc
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        G.block_decode(x, *c.wd, c.kcache, c.vcache, c.rope, P, out=out, ws=ws, schedule=S)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        G.block_decode(x, *c.wd, c.kcache, c.vcache, c.rope, P, out=out, ws=ws, schedule=S)
+    for xi in xs:
+        c.kcache.copy_(k0)
+        c.vcache.copy_(v0)
+        x.copy_(xi)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref, kc, vc = eager(xi)
+        assert torch.equal(out, ref)
+        assert torch.equal(c.kcache.view(torch.int16), kc.view(torch.int16))
+        assert torch.equal(c.vcache.view(torch.int16), vc.view(torch.int16))
+    assert G.workspace_errors(ws) == 0
 
 
 def test_decode_rejects_small_workspace_without_side_effects():
