@@ -7,7 +7,10 @@
 //   decode_attn_kernel  flash-decode on the matrix cores: positions split over
 //                       workgroups, online softmax, (m, l, o) merge by the
 //                       last-arriving workgroup of each (sequence, kv head)
-//   decode_wo_kernel    Delta = O Wo^T as a bandwidth GEMV (+ residual)
+//   decode_wo_kernel    Delta = O Wo^T as a bandwidth GEMV (+ residual), up to
+//                       4 tokens; decode_wo_mfma_kernel for 5 to 8
+//   decode_step_kernel  the three as roles of one launch (B <= 2)
+//   decode_proj_kernel  QKV or wo above 8 tokens: split-K on the matrix cores
 #include <math.h>
 
 #include <algorithm>
@@ -966,8 +969,9 @@ __global__ void __launch_bounds__(256, 3) decode_step_kernel(DecodeParams p) {
 //  - the KS K ranges of a feature block are summed by the last of its KS
 //    workgroups to finish (device-scope partials and counter, fixed order),
 //    which then runs the epilogue.
-// Workgroup i runs on XCD i % 8, and the K ranges alternate with i, so every
-// workgroup of an XCD reads the same activation range from its L2.
+// The K ranges alternate with the workgroup index, so that workgroups the
+// dispatcher's round-robin puts on one XCD (i % 8 on an idle chip) read the
+// same activation range from its L2; a locality heuristic only.
 // Columns are tokens.  For wo the input O is the sum of two bf16 parts: each
 // weight fragment multiplies both parts into the same accumulator.
 // QKV epilogue of one column (token b) and features f .. f+3 (one head):

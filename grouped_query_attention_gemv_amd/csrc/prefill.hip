@@ -244,9 +244,10 @@ __global__ void __launch_bounds__(512, 1) gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wm = w >> 2, wn = w & 3;
 
-  // XCD-aware tile order: workgroup id i runs on XCD i % 8; give each XCD a
-  // contiguous range of the grouped tile order so its L2 serves 4 m-tiles
-  // against a sweep of n-tiles.
+  // XCD-aware tile order: the dispatcher's round-robin puts workgroup i on
+  // XCD i % 8 on an idle chip; give each XCD a contiguous range of the
+  // grouped tile order so its L2 serves 4 m-tiles against a sweep of n-tiles
+  // (a locality heuristic: later workgroups go where slots free up).
   const int num_m = (g.M + GBM - 1) / GBM, num_n = g.N / GBN;
   const int total = num_m * num_n;
   int tl = blockIdx.x;
