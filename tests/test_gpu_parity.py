@@ -906,3 +906,57 @@ def test_decode_after_prefill_equals_prefill_1001():
     assert np.array_equal(bits(G.vcache_read(vc, 0, T)), bits(G.vcache_read(full.vcache, 0, T)))
     bk, _ = kv_bounds(f64(full.x[:, T]), [f64(t) for t in full.w], 8)
     assert_bf16_rows("row 1000", bits(G.kcache_by_position(kc)[:, T]), ref.k[:, T], bk)
+
+
+# ---------------------------------------------------------------------------
+# Seeded shape sweep: combinations the cases above do not spell out
+# ---------------------------------------------------------------------------
+
+def _sweep_cases():
+    rng = np.random.default_rng(20261203)
+    dec, pre = [], []
+    for i in range(16):
+        n_kv = int(rng.choice([8, 16, 32]))
+        B = int(rng.integers(1, 5 if n_kv == 32 else 13))
+        P = int(rng.integers(0, 2000))
+        T_max = (P + 1 + int(rng.integers(0, 64)) + 31) // 32 * 32
+        schedule = [G.DECODE_AUTO, G.DECODE_SPLIT, G.DECODE_FUSED][int(rng.integers(0, 3))]
+        dec.append((i, n_kv, B, P, T_max, schedule))
+    for i in range(8):
+        n_kv = int(rng.choice([8, 16, 32]))
+        B = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 300))
+        sp = 0 if rng.random() < 0.5 else int(rng.integers(1, 600))
+        T_max = (sp + T + int(rng.integers(0, 64)) + 31) // 32 * 32
+        pre.append((i, n_kv, B, T, sp, T_max))
+    return dec, pre
+
+
+_SWEEP_DECODE, _SWEEP_PREFILL = _sweep_cases()
+
+
+@pytest.mark.parametrize("i,n_kv,B,P,T_max,schedule", _SWEEP_DECODE)
+def test_decode_shape_sweep(i, n_kv, B, P, T_max, schedule):
+    """Seeded random (kv heads, batch, position, cache length, schedule):
+    Delta, Q, K, V and the appended rows against the oracle, every other
+    cache bit unchanged.  A one-launch request the shape does not admit runs
+    the library's choice instead."""
+    if schedule == G.DECODE_FUSED:
+        try:
+            G.decode_schedule(B, P, T_max, n_kv, schedule)
+        except G.GQAError:
+            schedule = G.DECODE_AUTO
+    c = DecodeCase(B, P, T_max, seed=300 + i, dev=DEV, n_kv=n_kv)
+    c.run(schedule=schedule)
+    c.check(c.oracle())
+    c.check_untouched()
+
+
+@pytest.mark.parametrize("i,n_kv,B,T,start_pos,T_max", _SWEEP_PREFILL)
+def test_prefill_shape_sweep(i, n_kv, B, T, start_pos, T_max):
+    """Seeded random (kv heads, batch, new tokens, cached prefix, cache
+    length) prefill against the oracle, every other cache bit unchanged."""
+    c = PrefillCase(B, T, T_max, seed=400 + i, dev=DEV, start_pos=start_pos, n_kv=n_kv)
+    c.run()
+    c.check(c.oracle())
+    c.check_untouched()
