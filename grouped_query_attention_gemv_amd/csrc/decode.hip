@@ -25,20 +25,21 @@ namespace gqa {
 // ---------------------------------------------------------------------------
 
 // Output features of QKV workgroup `blk` of W waves: 2W consecutive
-// features, 2 per wave.  The three-launch schedule takes them in feature
-// order.  The fused schedule (W = 4) gives kv head g the workgroups
-// blk = g (mod KV), like the head's attention workgroups (Q of its 32 / KV
-// query heads: 16 per head, then K: 16, then V: 16).  No hand-off depends on
-// the XCD a workgroup lands on.
+// features, 2 per wave, in feature order (three-launch schedule).  The fused
+// schedule (W = 4, RPW = fused_qkv_rpw(KV) row pairs a wave, 8 RPW features
+// a workgroup) gives kv head g the workgroups blk = g (mod KV), like the
+// head's attention workgroups: Q of its 32 / KV query heads, then K, then
+// V.  No hand-off depends on the XCD a workgroup lands on.
 template <bool FUSED, int W, int KV>
 __device__ __forceinline__ int qkv_first_feature(int blk) {
   static_assert(!FUSED || W == 4, "the fused schedule's roles are laid out for 4-wave workgroups");
   if (!FUSED) return blk * 2 * W;
-  constexpr int NR = H / KV, QW = 16 * NR;       // Q workgroups of a kv head
+  constexpr int FPW = 8 * fused_qkv_rpw(KV);    // features per workgroup
+  constexpr int NR = H / KV, QW = NR * HD / FPW, KW = HD / FPW;   // Q and K (= V) workgroups of a head
   const int g = blk % KV, r = blk / KV;
-  if (r < QW) return g * (NR * HD) + r * 8;
-  if (r < QW + 16) return D + g * HD + (r - QW) * 8;
-  return D + KV * HD + g * HD + (r - QW - 16) * 8;
+  if (r < QW) return g * (NR * HD) + r * FPW;
+  if (r < QW + KW) return D + g * HD + (r - QW) * FPW;
+  return D + KV * HD + g * HD + (r - QW - KW) * FPW;
 }
 
 // RoPE, probe and stores of the output features (f, f+1) of token b (f
@@ -99,11 +100,14 @@ __device__ __forceinline__ float2 qkv_rope_entry(const DecodeParams& p, int f) {
 }
 
 // KV: kv heads of the projection (8, 16 or 32, both schedules); W: waves of
-// the workgroup.
+// the workgroup; the fused schedule gives each wave fused_qkv_rpw(KV)
+// consecutive row pairs (the three-launch schedule one).
 template <int NB, bool FUSED, int KV = KVH, int W = 4>
 __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk, uint32_t* xs) {
+  constexpr int RPW = FUSED ? fused_qkv_rpw(KV) : 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = qkv_first_feature<FUSED, W, KV>(blk) + wave * 2;   // even feature
+  // first (even) feature of the wave; its RPW pairs lie in one of Q, K, V
+  const int r0 = qkv_first_feature<FUSED, W, KV>(blk) + wave * 2 * RPW;
   const uint16_t* wbase;
   int rr;
   if (r0 < D) {
@@ -113,17 +117,21 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   } else {
     wbase = p.wv; rr = r0 - D - KV * HD;
   }
-  // x goes to LDS by direct loads issued first, with the RoPE entry of the
-  // wave's feature pair (one position for the whole batch) and the norm
-  // gain; the 16 weight loads follow at once, and the rest has landed once
-  // only they remain in flight
+  // x goes to LDS by direct loads issued first, with the RoPE entries of the
+  // wave's feature pairs (one position for the whole batch) and the norm
+  // gain; the 16 RPW weight loads follow at once, and the rest has landed
+  // once only they remain in flight
   stage_rows_async<NB, W>(xs, p.x + (size_t)b0 * D);
-  const float2 cs = qkv_rope_entry<KV>(p, r0);
+  float2 cs[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) cs[j] = qkv_rope_entry<KV>(p, r0 + 2 * j);
   uint32_t gp[(D / 2) / (64 * W)];
   if (p.norm_w) load_norm_gain<W>(p.norm_w, gp);
-  u32x4 wa[8], wb[8];
-  load_rows2(wbase + (size_t)rr * D, wbase + (size_t)(rr + 1) * D, lane, wa, wb);
-  wait_loads_except<16>();
+  u32x4 wa[RPW][8], wb[RPW][8];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j)
+    load_rows2(wbase + (size_t)(rr + 2 * j) * D, wbase + (size_t)(rr + 2 * j + 1) * D, lane, wa[j], wb[j]);
+  wait_loads_except<16 * RPW>();
   if (!FUSED && blk == 0 && b0 == 0) {
     // the attention kernel that follows counts split arrivals from zero
     for (int i = threadIdx.x; i < p.B * KV; i += blockDim.x) p.counters[i] = 0;
@@ -131,18 +139,19 @@ __device__ __forceinline__ void qkv_body(const DecodeParams& p, int b0, int blk,
   lds_barrier();
   if (p.norm_w) norm_rows<NB, W>(xs, gp, p.norm_eps);
 
-  float acc[2][NB];
-  gemv_rows2<NB, 1>(wa, wb, xs, lane, acc);
-
-  float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    const float s0 = wave_sum(acc[0][t]);
-    const float s1 = wave_sum(acc[1][t]);
-    if (lane == t) { v0 = s0; v1 = s1; }
+  for (int j = 0; j < RPW; ++j) {
+    float acc[2][NB];
+    gemv_rows2<NB, 1>(wa[j], wb[j], xs, lane, acc);
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const float s0 = wave_sum(acc[0][t]);
+      const float s1 = wave_sum(acc[1][t]);
+      if (lane == t) { v0 = s0; v1 = s1; }
+    }
+    if (lane < NB) qkv_emit_pair<FUSED, KV>(p, b0 + lane, r0 + 2 * j, v0, v1, cs[j]);
   }
-
-  if (lane < NB) qkv_emit_pair<FUSED, KV>(p, b0 + lane, r0, v0, v1, cs);
 }
 
 // W waves a workgroup: 4, or 8 for 7 and 8 tokens, whose 56-64 KiB of staged

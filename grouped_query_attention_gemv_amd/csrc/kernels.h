@@ -62,9 +62,15 @@ constexpr int kSyncProj = 10752;     // + 16*fb: K ranges of projection feature 
 // LDS word where an attention workgroup of the fused schedule keeps Q of its
 // 4 heads (after the words of the 4-wave merge, 16-byte aligned)
 constexpr int kFusedAttnQWord = (kAttnWaves * REP * HD + 2 * kAttnWaves * REP + 1 + 3) / 4 * 4;
-// QKV workgroups of the fused schedule, 8 features each: per kv head
-// 16 * 32 / kv for Q, 16 for K, 16 for V (768 for 8 kv heads)
-constexpr int fused_qkv_wg(int kv) { return kv * (16 * (H / kv) + 32); }
+// Row pairs per wave of the fused schedule's QKV role: 2 at 16 and 32 kv
+// heads, so that their 6144 + 4096 or 12288 features fit one dispatch round
+// (at 1 the role took 1024 and 1536 workgroups against 768 resident)
+constexpr int fused_qkv_rpw(int kv) { return kv >= 16 ? 2 : 1; }
+// QKV workgroups of the fused schedule, 8 * rpw features each: 768 for 8 kv
+// heads (Q 64, K 16, V 16 per head), 512 for 16, 768 for 32
+constexpr int fused_qkv_wg(int kv) { return kv * ((H / kv) * HD + 2 * HD) / (8 * fused_qkv_rpw(kv)); }
+static_assert(fused_qkv_wg(8) == 768 && fused_qkv_wg(16) == 512 && fused_qkv_wg(32) == 768,
+              "QKV role sizes");
 // most positions an attention workgroup of the fused schedule covers (two
 // tiles per wave)
 constexpr int kFusedMaxChunk = 2 * kAttnWaves * kAttnTile;
