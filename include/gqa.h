@@ -200,9 +200,10 @@ int gqa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * consumer's HBM reads overlap its producer's; it admits B <= 2 and
  * contexts that fit in at most 128 attention workgroups of at most 256
  * positions (the three-launch schedule's splits of 128 positions, fewer and
- * longer where they would be too many): start_pos + 1 <= 4096 at 8 kv heads
- * and B = 1, <= 2048 at B = 2 or 16 kv heads, <= 1024 at 32 kv heads, <= 512
- * at 32 kv heads and B = 2.  GQA_DECODE_AUTO takes the one-launch schedule
+ * longer where they would be too many): start_pos + 1 <= 32768 / (n_kv_heads
+ * * B), i.e. 4096 at 8 kv heads and B = 1, 2048 at 8 kv heads and B = 2 or
+ * 16 and B = 1, 1024 at 16 and B = 2 or 32 and B = 1, 512 at 32 kv heads and
+ * B = 2.  GQA_DECODE_AUTO takes the one-launch schedule
  * where it is admitted, except at B = 2 with 16 or 32 kv heads.  Where both
  * schedules split the positions alike (always below those lengths halved)
  * their results agree bit for bit; each is deterministic.

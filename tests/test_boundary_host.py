@@ -286,6 +286,12 @@ def test_decode_schedule_selection():
     assert sch(16, 2, 1000, 1024, AUTO) == S
     assert sch(32, 2, 512, 1024, FUSED) == EARG
     assert sch(32, 1, 1024, 2048, FUSED) == EARG
+    # the documented limit, start_pos + 1 <= 32768 / (n_kv * B), at every admitted pair
+    for n_kv in (8, 16, 32):
+        for B in (1, 2):
+            lim = 32768 // (n_kv * B)
+            assert sch(n_kv, B, lim - 1, lim, FUSED) == F
+            assert sch(n_kv, B, lim, 2 * lim, FUSED) == EARG
     # explicit requests
     assert sch(8, 1, 1000, 1024, SPLIT) == S
     assert sch(8, 1, 1000, 1024, FUSED) == F
