@@ -874,6 +874,8 @@ def counter_summary(csvs, title: str, commands, out: str):
             parts.append(f"VALU co-executing in {d['SQ_VALU_MFMA_COEXEC_CYCLES'] / d['SQ_VALU_MFMA_BUSY_CYCLES']:.1%} of them")
         if d.get("SQ_INSTS_MFMA", 0) > 0 and "SQ_INSTS_VALU" in d:
             parts.append(f"{(d['SQ_INSTS_VALU'] - d['SQ_INSTS_MFMA']) / d['SQ_INSTS_MFMA']:.2f} other VALU instructions per MFMA")
+        if d.get("SQ_LDS_IDX_ACTIVE", 0) > 0 and "SQ_LDS_BANK_CONFLICT" in d:
+            parts.append(f"LDS bank conflicts in {d['SQ_LDS_BANK_CONFLICT'] / d['SQ_LDS_IDX_ACTIVE']:.1%} of LDS-active cycles")
         lines.append(f"- {k}: " + "; ".join(parts) + ".")
     lines.append("")
     with open(out, "w") as f:

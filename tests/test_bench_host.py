@@ -122,6 +122,12 @@ def test_counter_summary_derives_matrix_core_busy(bench, tmp_path):
     assert "gemm_kernel<0>: matrix cores busy 50.0% of 1,000 cycles" in text
     assert "VALU co-executing in 20.0% of them" in text
     assert "1.50 other VALU instructions per MFMA" in text
+    # the LDS figure appears when its two counters are there
+    assert "LDS bank conflicts" not in text
+    c2 = tmp_path / "c2.csv"
+    _write_counters(c2, [(k, "SQ_LDS_BANK_CONFLICT", 25.0), (k, "SQ_LDS_IDX_ACTIVE", 1000.0)])
+    bench.counter_summary([str(c), str(c2)], "t", ["cmd"], str(out))
+    assert "LDS bank conflicts in 2.5% of LDS-active cycles" in out.read_text()
 
 
 def test_more_than_one_gpu_is_refused():
