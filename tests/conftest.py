@@ -13,7 +13,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PROGRESS = os.path.join(ROOT, "gpurun_out", "progress.log")
+# Test logs (the progress log here, the parity error figures in parity.py)
+# go to GQA_TEST_LOG_DIR, by default the folder whose contents come back from
+# a remote GPU run.
+LOG_DIR = os.environ.get("GQA_TEST_LOG_DIR") or os.path.join(ROOT, "gpurun_out")
+PROGRESS = os.path.join(LOG_DIR, "progress.log")
 
 
 def pytest_configure(config):
@@ -30,8 +34,8 @@ def _library_built():
 
 @pytest.fixture(autouse=True)
 def _progress(request):
-    """Name each GPU test in gpurun_out/progress.log before it runs, so a run
-    that ends abruptly still shows which case was running."""
+    """Name each GPU test in the progress log before it runs, so a run that
+    ends abruptly still shows which case was running."""
     if request.node.get_closest_marker("gpu") is None:
         yield
         return

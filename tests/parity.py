@@ -57,12 +57,14 @@ def norm_err(gpu: np.ndarray, ref: np.ndarray):
     return float(d.max() / rms), float(d.mean() / rms)
 
 
-_LOG = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
-                    "parity_errors.log")
+_LOG = os.path.join(os.environ.get("GQA_TEST_LOG_DIR") or
+                    os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                 "gpurun_out"), "parity_errors.log")
 
 
 def log_errs(case: str, errs: dict):
-    """Append the measured error figures of a case to gpurun_out/parity_errors.log."""
+    """Append the measured error figures of a case to the parity error log
+    (parity_errors.log in the test log folder, see conftest.py)."""
     os.makedirs(os.path.dirname(_LOG), exist_ok=True)
     with open(_LOG, "a") as f:
         f.write(f"{case}: " + ", ".join(
