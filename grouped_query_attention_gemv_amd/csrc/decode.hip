@@ -632,19 +632,20 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
 
   if (FUSED) {
     // The last split merges.  The others publish their partial with
-    // device-scope stores into words that hold the "not yet" marker and are
-    // done; the merging workgroup polls those words itself (arrival and value
+    // device-scope stores into words that hold the "not yet" marker (8 bytes
+    // a store: m with l, and each thread's two values of o; the merger checks
+    // every 4-byte half, so a load that sees one store half landed only asks
+    // again) and are done; the merging workgroup polls those words itself (arrival and value
     // in one round trip), takes its own partial from registers, and writes
     // the markers back once every thread has read them.
     release_inputs();
     if (split != p.nsplit - 1) {
       if (merges) {
-        if (d2 == 0) {
-          st_dev(mine, M);
-          st_dev(mine + 1, lsum);
-        }
-        st_dev(mine + 4 + d2, o0);
-        st_dev(mine + 5 + d2, o1);
+        if (d2 == 0)
+          st_dev(reinterpret_cast<uint64_t*>(mine),
+                 (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(lsum) << 32));
+        st_dev(reinterpret_cast<uint64_t*>(mine + 4 + d2),
+               (uint64_t)__float_as_uint(o0) | ((uint64_t)__float_as_uint(o1) << 32));
       }
       return;
     }
@@ -654,10 +655,14 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
         return true;
       }
       const float* ps = part0 + (size_t)s * split_stride;
-      mv = ld_dev(ps);
-      lv = ld_dev(ps + 1);
-      ov0 = ld_dev(ps + 4 + d2);
-      ov1 = ld_dev(ps + 5 + d2);
+      const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(ps), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t oo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(ps + 4 + d2),
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mv = __uint_as_float((uint32_t)ml);
+      lv = __uint_as_float((uint32_t)(ml >> 32));
+      ov0 = __uint_as_float((uint32_t)oo);
+      ov1 = __uint_as_float((uint32_t)(oo >> 32));
       return __float_as_uint(mv) != kNotYet && __float_as_uint(lv) != kNotYet &&
              __float_as_uint(ov0) != kNotYet && __float_as_uint(ov1) != kNotYet;
     });
@@ -665,12 +670,9 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     if (merges) {
       for (int s = 0; s < p.nsplit - 1; ++s) {
         float* ps = part0 + (size_t)s * split_stride;
-        if (d2 == 0) {
-          st_dev(ps, __uint_as_float(kNotYet));
-          st_dev(ps + 1, __uint_as_float(kNotYet));
-        }
-        st_dev(ps + 4 + d2, __uint_as_float(kNotYet));
-        st_dev(ps + 5 + d2, __uint_as_float(kNotYet));
+        const uint64_t nn = (uint64_t)kNotYet | ((uint64_t)kNotYet << 32);
+        if (d2 == 0) st_dev(reinterpret_cast<uint64_t*>(ps), nn);
+        st_dev(reinterpret_cast<uint64_t*>(ps + 4 + d2), nn);
       }
     }
     return;
