@@ -571,8 +571,8 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
   };
 
   if (p.nsplit == 1) {
-    release_inputs();
     emit(o0 / lsum, o1 / lsum);
+    release_inputs();
     return;
   }
 
@@ -636,10 +636,12 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
     // device-scope stores into words that hold the "not yet" marker (8 bytes
     // a store: m with l, and each thread's two values of o; the merger checks
     // every 4-byte half, so a load that sees one store half landed only asks
-    // again) and are done; the merging workgroup polls those words itself (arrival and value
-    // in one round trip), takes its own partial from registers, and writes
-    // the markers back once every thread has read them.
-    release_inputs();
+    // again) and are done; the merging workgroup polls those words itself
+    // (arrival and value in one round trip), takes its own partial from
+    // registers, and writes the markers back once every thread has read
+    // them.  Every path releases the head's inputs last: release_inputs
+    // waits for the head counter's atomic, which should not hold up the
+    // partials or O.
     if (split != p.nsplit - 1) {
       if (merges) {
         if (d2 == 0)
@@ -648,6 +650,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
         st_dev(reinterpret_cast<uint64_t*>(mine + 4 + d2),
                (uint64_t)__float_as_uint(o0) | ((uint64_t)__float_as_uint(o1) << 32));
       }
+      release_inputs();
       return;
     }
     merge_splits([&](int s, float& mv, float& lv, float& ov0, float& ov1) {
@@ -676,6 +679,7 @@ __device__ __forceinline__ void attn_body(const DecodeParams& p, int blk, float*
         st_dev(reinterpret_cast<uint64_t*>(ps + 4 + d2), nn);
       }
     }
+    release_inputs();
     return;
   }
 
