@@ -55,7 +55,9 @@ METRIC = "decode µs/block-step & HBM TB/s (% peak); prefill tokens/s & MFMA uti
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
 MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense bf16/fp16
 N_SETS = 8
-DECODE_SRC = "grouped_query_attention_gemv_amd/csrc/decode.hip"
+# the decode kernels' whole source: decode.hip and the headers it includes
+DECODE_SRC = tuple(f"grouped_query_attention_gemv_amd/csrc/{f}"
+                   for f in ("decode.hip", "common.h", "gemv.h", "kernels.h"))
 
 D, NQKV, KVH, HD = 4096, 6144, 8, 128
 
@@ -102,14 +104,17 @@ def roofline(kernel: str, bound: str, work: float, us: float, traffic=None) -> d
             "algorithmic_flops": work, "kernel_us": round(us, 3)}
 
 
-def code_digest(path: str) -> str:
-    """sha256 of a C++ source with its comments and blank lines removed, so
-    that a counter summary stays valid across edits that change only
-    comments (string literals in these sources hold no comment markers)."""
-    text = open(os.path.join(ROOT, path)).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+def code_digest(paths) -> str:
+    """sha256 of C++ sources (one path or several, in order) with their
+    comments and blank lines removed, so that a counter summary stays valid
+    across edits that change only comments (string literals in these sources
+    hold no comment markers)."""
+    lines = []
+    for path in ((paths,) if isinstance(paths, str) else paths):
+        text = open(os.path.join(ROOT, path)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines += [ln.rstrip() for ln in text.splitlines() if ln.strip()]
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
@@ -793,8 +798,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: int, title: str, comma
         traffic[k] = t
         lines.append(f"| {k} | {n} | {fb:,.1f} | {wb:,.1f} | {t:,} |")
     lines += ["", "Figures read by bench.py (`roofline.traffic`; it reports null instead when "
-              "the code of decode.hip, comments aside, differs from the code these counters "
-              "were taken on):", ""]
+              "the code of the decode kernels (decode.hip, common.h, gemv.h, kernels.h), "
+              "comments aside, differs from the code these counters were taken on):", ""]
     lines += [f"    traffic_bytes_per_launch[{k}]: {v}" for k, v in traffic.items()]
     lines += [f"    kernel_code_sha256: {digest}", ""]
     with open(out, "w") as f:

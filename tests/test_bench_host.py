@@ -73,6 +73,16 @@ def test_code_digest_ignores_comments_only(bench, tmp_path, monkeypatch):
     assert bench.code_digest("k.hip") == d0
     src.write_text("int f() {\n  return 2;\n}\n")
     assert bench.code_digest("k.hip") != d0
+    # several sources: a change in any of them changes the digest
+    hdr = tmp_path / "k.h"
+    hdr.write_text("#define K 1\n")
+    d1 = bench.code_digest(("k.hip", "k.h"))
+    hdr.write_text("#define K 1  // one\n")
+    assert bench.code_digest(("k.hip", "k.h")) == d1
+    hdr.write_text("#define K 2\n")
+    assert bench.code_digest(("k.hip", "k.h")) != d1
+    assert set(bench.DECODE_SRC) >= {"grouped_query_attention_gemv_amd/csrc/decode.hip",
+                                     "grouped_query_attention_gemv_amd/csrc/common.h"}
 
 
 def test_committed_traffic_summaries_match_the_current_decode_code(bench):
