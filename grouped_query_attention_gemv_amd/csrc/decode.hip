@@ -758,9 +758,9 @@ __device__ __forceinline__ void wo_body(const DecodeParams& p, int b0, int blk, 
   const int r0 = (blk * W + wave) * 2;
   u32x4 wa[8], wb[8];
   if (FUSED) {
-    // hold the weight stream back while QKV finishes (kWoHoldTicks)
+    // hold the weight stream back while QKV finishes (fused_wo_hold_ticks)
     const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-    while (__builtin_amdgcn_s_memrealtime() - t0 < kWoHoldTicks) __builtin_amdgcn_s_sleep(8);
+    while (__builtin_amdgcn_s_memrealtime() - t0 < fused_wo_hold_ticks(KV)) __builtin_amdgcn_s_sleep(8);
   } else {
     // O (hi and lo parts) goes to LDS by direct loads ahead of the weights
     stage_rows_async<NB, W>(xs, p.o_hi + (size_t)b0 * D);

@@ -76,14 +76,19 @@ static_assert(fused_qkv_wg(8) == 768 && fused_qkv_wg(16) == 512 && fused_qkv_wg(
 constexpr int kFusedMaxChunk = 2 * kAttnWaves * kAttnTile;
 constexpr int kMaxPolls = 1 << 18;   // bound on every wait of the fused schedule
 // The fused schedule's wo workgroups start streaming their weights this many
-// real-time ticks (100 MHz: 4 us) after they start.  They are dispatched as
+// real-time ticks (100 MHz: 3.5 us at 8 kv heads, 4 us at 16 and 32) after
+// they start.  They are dispatched as
 // the QKV workgroups retire and do not need the weights until O is complete;
 // starting at once, their 32 MiB competed with the tail of the QKV stream
 // that the attention chain waits on.  Swept at B = 1 with the marker
-// hand-offs: 3, 3.5, 4, 4.5, 5 and 6 us give 24.2, 22.5, 22.4-22.7, 22.8,
-// 23.4 and 23.8 us at P = 1000, and 3.5, 4, 4.5 us give 20.4, 20.6, 20.9 us
-// at P = 128.
-constexpr unsigned kWoHoldTicks = 400;
+// hand-offs: 3, 3.5, 4, 4.5, 5 and 6 us gave 24.2, 22.5, 22.4-22.7, 22.8,
+// 23.4 and 23.8 us at P = 1000; after the 8-byte partials, the release
+// reordering and the hardware bf16 conversion, 3, 3.5, 4 and 4.5 us give
+// 22.60, 21.47-21.61, 21.74-21.77 and 21.98-22.02 us at P = 1000 and 19.68,
+// 19.70-19.76, 19.86-19.88 and 19.77-19.80 us at P = 128.  At 16 and 32 kv
+// heads 4 us stays ahead (26.02-26.05 against 26.08-26.15 us and 34.04-34.12
+// against 34.24-34.27 us).
+constexpr unsigned fused_wo_hold_ticks(int kv) { return kv == 8 ? 350 : 400; }
 static_assert(kSyncGroup + 32 * kFusedMaxKv <= kSyncProj, "head counters overlap");
 static_assert(kSyncProj + 16 * ((4096 + 2 * 32 * 128) / 64) <= kSyncWordsBytes / 4,
               "sync region too small for the projection counters of 32 kv heads");
